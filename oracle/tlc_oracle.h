@@ -1,0 +1,91 @@
+/*
+ * tlc_oracle.h -- plain, single-threaded CPU oracle of the 3LC codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this code: it exists so that tests, the smoke check and the benchmark's
+ * CPU-baseline leg can check the GPU library against an obviously correct
+ * implementation.  It shares no code, table or header with the GPU library.
+ *
+ * What is computed follows the 3LC review page ("3LC: Lightweight and
+ * Effective Traffic Compression for Distributed Machine Learning"), section
+ * "Proposed method": ternary quantization with a sparsity multiplier and an
+ * error-accumulation buffer, quartic encoding (five ternary values per byte),
+ * and zero-run encoding of runs of the all-zero byte.  The page gives no
+ * formulas; the concrete definitions used here are:
+ *   v_i   = x_i + err_i                         (fp32 add)
+ *   M     = max_i |v_i|                         (per tensor)
+ *   Ms    = M * s                               (fp32 multiply, 1 <= s < 2)
+ *   q_i   = rint(v_i / Ms)   in {-1, 0, 1}      (fp32 IEEE divide, ties-to-even)
+ *   err_i = v_i - q_i * Ms                      (fp32)
+ *   byte_k = sum_{j<5} (q_{5k+j} + 1) * 3^j     (0..242; 121 = five zeros)
+ *   zero-run encoding: a maximal run of r bytes equal to 121 is written as
+ *   floor(r/14) codes 255 followed by the remainder m = r mod 14 as nothing
+ *   (m = 0), the literal 121 (m = 1) or the code 241 + m (m = 2..13);
+ *   every other byte is copied.  Codes 243..255 therefore mean runs of 2..14.
+ *
+ * Parity unpinned (conventions the page does not fix; pinned only by the
+ * worked examples in tests/golden): ties of v/Ms at exactly +-0.5 round to
+ * even; element i goes to byte i/5 as digit i%5 with weight 3^(i%5); a run
+ * longer than 14 is split greedily from its start.
+ */
+#ifndef TLC_ORACLE_H
+#define TLC_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TLCO_OK = 0,
+    TLCO_ERR_INVALID_ARG = 1, /* null pointer, n == 0, s outside [1,2) or not finite */
+    TLCO_ERR_CAPACITY = 2,    /* output buffer smaller than needed */
+    TLCO_ERR_CORRUPT = 5,     /* malformed zero-run stream, or a byte > 242 */
+    TLCO_ERR_RANGE = 6,       /* a ternary code outside {-1,0,1} (cannot happen for 1 <= s < 2) */
+    TLCO_ERR_NOMEM = 7
+};
+
+/* Number of quartic bytes for n values: ceil(n / 5). */
+uint64_t tlco_quartic_len(uint64_t n);
+
+/* Error accumulation + per-tensor scale + ternary quantization.
+ * x[n] (read), err[n] (read, then overwritten with the new error), s.
+ * Writes q[n] in {-1,0,1} and *M.  Returns TLCO_OK or an error code. */
+int tlco_quantize(const float* x, float* err, uint64_t n, float s, int8_t* q, float* M);
+
+/* Quartic encoding of q[n] into b[ceil(n/5)]; missing trailing digits are 0. */
+int tlco_quartic_pack(const int8_t* q, uint64_t n, uint8_t* b);
+
+/* Quartic decoding of b[ceil(n/5)] into q[n]; digits past n are ignored.
+ * Returns TLCO_ERR_CORRUPT if a byte exceeds 242. */
+int tlco_quartic_unpack(const uint8_t* b, uint64_t n, int8_t* q);
+
+/* Zero-run encoding of in[B] into out (capacity cap bytes).  *L receives the
+ * stream length (always <= B). */
+int tlco_zre_encode(const uint8_t* in, uint64_t B, uint8_t* out, uint64_t cap, uint64_t* L);
+
+/* Zero-run decoding of in[L] into out[B].  The expansion must be exactly B
+ * bytes, otherwise TLCO_ERR_CORRUPT. */
+int tlco_zre_decode(const uint8_t* in, uint64_t L, uint8_t* out, uint64_t B);
+
+/* Whole compress path: quantize, pack, zero-run encode.  err is updated in
+ * place; out needs tlco_quartic_len(n) bytes; *L and *M are written. */
+int tlco_compress(const float* x, float* err, uint64_t n, float s,
+                  uint8_t* out, uint64_t cap, uint64_t* L, float* M);
+
+/* Whole decompress path: zero-run decode, quartic decode, dequantize.
+ * y[i] = q_i * (M*s). */
+int tlco_decompress(const uint8_t* in, uint64_t L, float M, uint64_t n, float s, float* y);
+
+/* As tlco_decompress, but acc[i] += q_i * (M*s) for q_i != 0 only; elements
+ * with q_i == 0 are left untouched (a -0.0 stays -0.0). */
+int tlco_decompress_accumulate(const uint8_t* in, uint64_t L, float M, uint64_t n, float s,
+                               float* acc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLC_ORACLE_H */
