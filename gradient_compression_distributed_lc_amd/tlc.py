@@ -1,0 +1,300 @@
+"""Python binding of libtlc.so (the C ABI in include/tlc.h).
+
+Argument marshalling only: PyTorch allocates device memory and provides the
+HIP stream; every step of the codec runs in the library's HIP kernels.  The
+entry points have the same names as the C functions without the ``tlc_``
+prefix.  If the library is missing this module raises instead of falling
+back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import build as _build
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_CAPACITY = 2
+ERR_WORKSPACE = 3
+ERR_HIP = 4
+ERR_CORRUPT = 5
+ERR_INTERNAL = 6
+
+
+class TLCError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} (code {code})")
+        self.code = code
+
+
+class GroupInfo(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_uint64), ("total_elems", ctypes.c_uint64),
+                ("stream_bytes", ctypes.c_uint64), ("table_bytes", ctypes.c_uint64),
+                ("workspace_bytes", ctypes.c_uint64), ("tiles", ctypes.c_uint64),
+                ("chunks", ctypes.c_uint64)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_U64 = ctypes.c_uint64
+_F = ctypes.c_float
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "tlc_status_string": (ctypes.c_char_p, [_I]),
+    "tlc_version": (ctypes.c_char_p, []),
+    "tlc_compress_bound": (_U64, [_U64]),
+    "tlc_workspace_size": (_SZ, [_U64]),
+    "tlc_compress": (_I, [_P, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_accumulate": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
+    "tlc_group_plan": (_I, [_P, _U64, ctypes.POINTER(GroupInfo), _P, _SZ, _P]),
+    "tlc_compress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_accumulate_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ,
+                                             _P, _P]),
+    "tlc_copy_probe": (_I, [_P, _P, _U64, _P]),
+    "tlc_profile_enable": (_I, [_I]),
+    "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
+}
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m gradient_compression_distributed_lc_amd.build`"
+                               " (or __graft_entry__.build())")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    try:
+        return lib().tlc_status_string(int(code)).decode()
+    except RuntimeError:
+        return f"status {code}"
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise TLCError(rc, what)
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def compress_bound(n: int) -> int:
+    return int(lib().tlc_compress_bound(n))
+
+
+def workspace_size(n: int) -> int:
+    return int(lib().tlc_workspace_size(n))
+
+
+def version() -> str:
+    return lib().tlc_version().decode()
+
+
+@dataclass
+class Compressed:
+    """A compressed tensor.  ``out`` has capacity ``ceil(n/5)``; the stream is
+    ``out[:length]`` where ``length`` is the device scalar ``out_len``."""
+    out: torch.Tensor       # uint8[ceil(n/5)]
+    out_len: torch.Tensor   # int64[1] (the C side writes a uint64)
+    scale: torch.Tensor     # float32[1]
+    status: torch.Tensor    # int32[1]
+    n: int
+    s: float
+
+    def stream(self) -> torch.Tensor:
+        return self.out[: int(self.out_len.item())]
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def compress(x: torch.Tensor, err: torch.Tensor, s: float, *, out=None, out_len=None, scale=None,
+             workspace=None, status=None, stream=None) -> Compressed:
+    n = x.numel()
+    dev = x.device
+    if err.numel() != n:
+        raise ValueError("err must have as many elements as x")
+    out = out if out is not None else torch.empty(max(compress_bound(n), 1), dtype=torch.uint8, device=dev)
+    out_len = out_len if out_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace_size(n), dev, workspace)
+    rc = lib().tlc_compress(_ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), n, s,
+                            _ptr(out, torch.uint8, "out"), out.numel(), _ptr(out_len, torch.int64, "out_len"),
+                            _ptr(scale, torch.float32, "scale"), _ptr(workspace, torch.uint8, "workspace"),
+                            workspace.numel(), _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_compress")
+    return Compressed(out, out_len, scale, status, n, s)
+
+
+def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float, *, y=None,
+               workspace=None, status=None, stream=None):
+    """Returns (y, status)."""
+    dev = inp.device
+    y = y if y is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace_size(n), dev, workspace)
+    rc = lib().tlc_decompress(_ptr(inp, torch.uint8, "in"), _ptr(in_len, torch.int64, "in_len"),
+                              _ptr(scale, torch.float32, "scale"), n, s, _ptr(y, torch.float32, "y"),
+                              _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                              _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_decompress")
+    return y, status
+
+
+def decompress_accumulate(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float,
+                          acc: torch.Tensor, *, workspace=None, status=None, stream=None):
+    """acc is updated in place.  Returns (acc, status)."""
+    dev = inp.device
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace_size(n), dev, workspace)
+    rc = lib().tlc_decompress_accumulate(_ptr(inp, torch.uint8, "in"), _ptr(in_len, torch.int64, "in_len"),
+                                         _ptr(scale, torch.float32, "scale"), n, s,
+                                         _ptr(acc, torch.float32, "acc"),
+                                         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                         _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_decompress_accumulate")
+    return acc, status
+
+
+def group_plan(sizes) -> tuple[GroupInfo, bytes, list[int]]:
+    """Host-only: (info, table bytes, stream offsets) for tensors of the given sizes."""
+    count = len(sizes)
+    arr = (ctypes.c_uint64 * max(count, 1))(*[int(v) for v in sizes])
+    info = GroupInfo()
+    _check(lib().tlc_group_plan(arr, count, ctypes.byref(info), None, 0, None), "tlc_group_plan")
+    table = ctypes.create_string_buffer(int(info.table_bytes))
+    offs = (ctypes.c_uint64 * max(count, 1))()
+    _check(lib().tlc_group_plan(arr, count, ctypes.byref(info), table, len(table), offs), "tlc_group_plan")
+    return info, table.raw, [int(v) for v in offs[:count]]
+
+
+class Group:
+    """Tensors packed back to back in one flat fp32 buffer (a gradient bucket),
+    compressed with one launch sequence.  M, error state and stream are per
+    tensor; stream t lives at ``out[offsets[t]:]``."""
+
+    def __init__(self, sizes, device="cuda"):
+        self.sizes = [int(v) for v in sizes]
+        self.info, table, self.offsets = group_plan(self.sizes)
+        self.device = torch.device(device)
+        host = torch.frombuffer(bytearray(table), dtype=torch.uint8)
+        self.d_table = host.to(self.device)
+        self.total = int(self.info.total_elems)
+        self.stream_bytes = int(self.info.stream_bytes)
+        self.workspace_bytes = int(self.info.workspace_bytes)
+        self.count = len(self.sizes)
+        eo = [0]
+        for v in self.sizes:
+            eo.append(eo[-1] + v)
+        self.elem_offsets = eo
+
+    def workspace(self) -> torch.Tensor:
+        return torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
+
+    def compress(self, x, err, s, *, out=None, out_lens=None, scales=None, workspace=None, status=None,
+                 stream=None):
+        """Returns (out, out_lens, scales, status)."""
+        if x.numel() != self.total or err.numel() != self.total:
+            raise ValueError("x and err must hold the whole group")
+        dev = self.device
+        out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
+        out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
+        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        workspace = workspace if workspace is not None else self.workspace()
+        rc = lib().tlc_compress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                      _ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), s,
+                                      _ptr(out, torch.uint8, "out"), _ptr(out_lens, torch.int64, "out_lens"),
+                                      _ptr(scales, torch.float32, "scales"),
+                                      _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                      _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_compress_group")
+        return out, out_lens, scales, status
+
+    def decompress(self, inp, in_lens, scales, s, *, y=None, workspace=None, status=None, stream=None):
+        """Returns (y, status)."""
+        dev = self.device
+        y = y if y is not None else torch.empty(self.total, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        workspace = workspace if workspace is not None else self.workspace()
+        rc = lib().tlc_decompress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                        _ptr(inp, torch.uint8, "in"), _ptr(in_lens, torch.int64, "in_lens"),
+                                        _ptr(scales, torch.float32, "scales"), s, _ptr(y, torch.float32, "y"),
+                                        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                        _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_decompress_group")
+        return y, status
+
+    def decompress_accumulate(self, inp, in_lens, scales, s, acc, *, workspace=None, status=None, stream=None):
+        """acc is updated in place.  Returns (acc, status)."""
+        dev = self.device
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        workspace = workspace if workspace is not None else self.workspace()
+        rc = lib().tlc_decompress_accumulate_group(
+            ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"), _ptr(inp, torch.uint8, "in"),
+            _ptr(in_lens, torch.int64, "in_lens"), _ptr(scales, torch.float32, "scales"), s,
+            _ptr(acc, torch.float32, "acc"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_decompress_accumulate_group")
+        return acc, status
+
+
+def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
+    _check(lib().tlc_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "tlc_copy_probe")
+
+
+def profile_enable(on: bool = True):
+    _check(lib().tlc_profile_enable(1 if on else 0), "tlc_profile_enable")
+
+
+def profile_read(capacity: int = 32) -> dict[str, tuple[int, float]]:
+    """{kernel name: (launches, total ms)} since the last read (synchronises)."""
+    buf = (KernelTime * capacity)()
+    cnt = ctypes.c_int()
+    _check(lib().tlc_profile_read(buf, capacity, ctypes.byref(cnt)), "tlc_profile_read")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(cnt.value)}

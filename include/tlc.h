@@ -1,0 +1,187 @@
+/*
+ * tlc.h -- C ABI of the 3LC state-change codec on AMD Instinct MI355X (gfx950).
+ *
+ * The codec is the one described by the 3LC review page ("3LC: Lightweight
+ * and Effective Traffic Compression for Distributed Machine Learning"),
+ * section "Proposed method":
+ *   - error accumulation + 3-value quantization with a sparsity multiplier s:
+ *       v = x + err,  M = max|v| (per tensor),  q = round-half-even(v / (M*s)),
+ *       err <- v - q*M*s,  q in {-1, 0, 1};
+ *   - quartic encoding: five ternary values per byte, byte = sum_j (q_j+1)*3^j
+ *     over five consecutive elements (first element = least significant
+ *     digit), values 0..242, 121 = five zeros;
+ *   - zero-run encoding: a maximal run of r bytes equal to 121 becomes
+ *     floor(r/14) codes 255 and then the remainder m = r mod 14 as nothing
+ *     (m = 0), a literal 121 (m = 1) or the code 241+m (m = 2..13); all other
+ *     bytes are copied.  Codes 243..255 mean runs of 2..14.
+ *   Decompression reverses the two encodings and dequantizes y = q*M*s, or
+ *   adds q*M*s into a dense fp32 accumulator where q != 0.
+ * The page calls the pipeline a drop-in transform of gradient and
+ * model-delta traffic ("Proposed method", fourth and sixth items); the
+ * grouped calls below apply it to many tensors in one launch sequence, the
+ * tensor-fusion idea of the SparCML review page ("SparCML: High-Performance
+ * Sparse Communication for Machine Learning", "Proposed method", fifth item).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the parameter says "host".
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream) and the call returns without synchronising.  Results written to
+ *     device memory (out_len, scale, status, ...) are valid once the stream
+ *     reaches that point.
+ *   - The library never allocates, frees or synchronises device memory; the
+ *     caller owns every buffer.  Scratch memory is the caller's `workspace`
+ *     (device, 256-byte aligned, at least the size the *_workspace_size call
+ *     returns).  Calls that may run at the same time need separate
+ *     workspaces and separate status words.
+ *   - fp32 buffers (x, err, y, acc) must be 16-byte aligned and must not
+ *     alias each other or the byte streams.
+ *   - Return value: TLC_OK, or a synchronous error (invalid argument, too
+ *     small capacity or workspace, HIP launch failure) detected before or at
+ *     launch; on such an error nothing that matters was enqueued.
+ *   - `status` (device int) is set to TLC_OK by the call's first kernel and
+ *     raised by later kernels if the data are bad (TLC_ERR_CORRUPT) or an
+ *     internal bounded wait expired (TLC_ERR_INTERNAL).  Read it after
+ *     synchronising the stream.
+ *   - Limits: a tensor holds 1 .. 2^32-1 elements; 1 <= s < 2; inputs are
+ *     finite and M*s does not overflow (otherwise the output is unspecified).
+ */
+#ifndef TLC_H
+#define TLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* tlc_stream_t; /* a hipStream_t */
+
+enum tlc_status {
+    TLC_OK = 0,
+    TLC_ERR_INVALID_ARG = 1, /* null pointer, n == 0 or too large, s outside [1,2), misaligned buffer */
+    TLC_ERR_CAPACITY = 2,    /* output capacity below tlc_compress_bound(n) */
+    TLC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+    TLC_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+    TLC_ERR_CORRUPT = 5,     /* (device status) stream does not expand to exactly ceil(n/5) bytes */
+    TLC_ERR_INTERNAL = 6     /* (device status) a bounded inter-block wait expired */
+};
+
+/* Human-readable name of a status code.  Host only; never NULL. */
+const char* tlc_status_string(int code);
+
+/* Library version string.  Host only. */
+const char* tlc_version(void);
+
+/* Bytes a compressed stream of n values can take: ceil(n/5) (zero-run
+ * encoding never expands the quartic bytes).  Host only; 0 for n == 0. */
+uint64_t tlc_compress_bound(uint64_t n);
+
+/* Workspace bytes for any single-tensor call on n values.  Host only. */
+size_t tlc_workspace_size(uint64_t n);
+
+/* Compress one tensor (all steps of the 3LC compress path).
+ *   x[n]        fp32 state change (gradient or model delta), read only.
+ *   err[n]      fp32 error-accumulation buffer, read and overwritten with the
+ *               new error.  Zero it before the first step; keep one per
+ *               tensor and worker across steps.
+ *   s           sparsity multiplier, 1 <= s < 2.
+ *   out         stream bytes, capacity out_capacity >= tlc_compress_bound(n).
+ *   out_len     (device uint64) receives the stream length L <= ceil(n/5).
+ *   scale       (device fp32) receives M = max|x+err|.
+ *   status      (device int), see above. */
+int tlc_compress(const float* x, float* err, uint64_t n, float s,
+                 uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
+                 void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* Decompress one tensor: y[i] = q_i * (M*s) for i < n, with q decoded from
+ * the stream in[0 .. *in_len) (device length, so no host round trip is
+ * needed after tlc_compress).  `in` must be readable for *in_len bytes.
+ * scale: device fp32 M.  A stream that does not expand to exactly ceil(n/5)
+ * bytes sets *status = TLC_ERR_CORRUPT (y is then partly written). */
+int tlc_decompress(const uint8_t* in, const uint64_t* in_len, const float* scale,
+                   uint64_t n, float s, float* y,
+                   void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* As tlc_decompress, but acc[i] += q_i * (M*s) where q_i != 0; every other
+ * element of acc keeps its bits.  Applying the payloads of several workers
+ * one call after another gives their sum in call order. */
+int tlc_decompress_accumulate(const uint8_t* in, const uint64_t* in_len, const float* scale,
+                              uint64_t n, float s, float* acc,
+                              void* workspace, size_t workspace_bytes, int* status,
+                              tlc_stream_t stream);
+
+/* ---- grouped calls: many tensors, one launch sequence ----------------------
+ * The tensors of a group lie back to back in one flat fp32 buffer (tensor t
+ * at element offset sum_{u<t} n_u), like a gradient bucket.  M, the error
+ * state and the stream are per tensor exactly as in the single-tensor calls;
+ * stream t occupies out[stream_offset[t] .. + ceil(n_t/5)) (offsets are
+ * 16-byte aligned; their total is info->stream_bytes).
+ *
+ * tlc_group_plan (host only) describes the group: it fills *info and, when
+ * `table` is not NULL, writes info->table_bytes of host memory that the
+ * caller copies once to device memory (any 16-byte aligned buffer) and
+ * passes as d_table to the grouped calls; stream_offset (host, count
+ * entries) is filled when not NULL.  The plan depends only on the sizes and
+ * can be reused for every step. */
+typedef struct tlc_group_info {
+    uint64_t count;           /* tensors */
+    uint64_t total_elems;     /* sum of sizes */
+    uint64_t stream_bytes;    /* capacity of the grouped out/in buffer */
+    uint64_t table_bytes;     /* bytes of the device table */
+    uint64_t workspace_bytes; /* workspace for any grouped call on this group */
+    uint64_t tiles;           /* compress work units (internal) */
+    uint64_t chunks;          /* decompress work units (internal) */
+} tlc_group_info;
+
+int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info,
+                   void* table, size_t table_capacity, uint64_t* stream_offset);
+
+/* Grouped compress.  x/err: flat fp32[info->total_elems]; out: bytes
+ * [info->stream_bytes]; out_lens: device uint64[count]; scales: device
+ * fp32[count]. */
+int tlc_compress_group(const tlc_group_info* info, const void* d_table,
+                       const float* x, float* err, float s,
+                       uint8_t* out, uint64_t* out_lens, float* scales,
+                       void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* Grouped decompress into flat y[info->total_elems].  in: the grouped stream
+ * buffer laid out as by tlc_compress_group; in_lens: device uint64[count];
+ * scales: device fp32[count]. */
+int tlc_decompress_group(const tlc_group_info* info, const void* d_table,
+                         const uint8_t* in, const uint64_t* in_lens, const float* scales, float s,
+                         float* y, void* workspace, size_t workspace_bytes, int* status,
+                         tlc_stream_t stream);
+
+/* Grouped decompress-and-accumulate into flat acc[info->total_elems]. */
+int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_table,
+                                    const uint8_t* in, const uint64_t* in_lens,
+                                    const float* scales, float s, float* acc,
+                                    void* workspace, size_t workspace_bytes, int* status,
+                                    tlc_stream_t stream);
+
+/* ---- measurement helpers (not part of the codec) -------------------------- */
+
+/* Streaming copy of `bytes` bytes (a multiple of 16, both pointers 16-byte
+ * aligned): the achievable-HBM-bandwidth yardstick for the codec kernels. */
+int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream);
+
+/* Kernel timing with HIP events.  While enabled, every kernel the library
+ * launches is bracketed by two events recorded on the same stream.
+ * tlc_profile_read synchronises those events and returns, per kernel name,
+ * the number of launches and their summed duration in milliseconds, then
+ * forgets them.  Host only; a diagnostic facility, not thread-safe. */
+typedef struct tlc_kernel_time {
+    char name[48];
+    uint64_t launches;
+    double total_ms;
+} tlc_kernel_time;
+
+int tlc_profile_enable(int enable);
+int tlc_profile_read(tlc_kernel_time* out, int capacity, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLC_H */

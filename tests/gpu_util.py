@@ -1,0 +1,125 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and the CPU oracle on the same arrays, and compare them bit for bit."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def gpu_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None):
+    """Compress, decompress (and accumulate into acc) one tensor on the GPU."""
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    n = x.size
+    xd, ed = to_dev(x), to_dev(err)
+    c = tlc.compress(xd, ed, s)
+    y, st_d = tlc.decompress(c.out, c.out_len, c.scale, n, s)
+    res = {}
+    if acc is not None:
+        ad = to_dev(acc)
+        _, st_a = tlc.decompress_accumulate(c.out, c.out_len, c.scale, n, s, ad)
+    torch.cuda.synchronize()
+    res["status"] = int(c.status.item())
+    res["status_d"] = int(st_d.item())
+    L = int(c.out_len.item())
+    res["L"] = L
+    res["stream"] = c.out[:L].cpu().numpy()
+    res["M"] = np.float32(c.scale.item())
+    res["err"] = ed.cpu().numpy()
+    res["y"] = y.cpu().numpy()
+    if acc is not None:
+        res["status_a"] = int(st_a.item())
+        res["acc"] = ad.cpu().numpy()
+    return res
+
+
+def check_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None, label=""):
+    n = x.size
+    want_stream, want_M, want_err = oracle.compress(x, err, s)
+    want_y = oracle.decompress(want_stream, want_M, n, s)
+    got = gpu_single(x, err, s, acc)
+    assert got["status"] == 0 and got["status_d"] == 0, (label, got["status"], got["status_d"])
+    assert got["M"] == want_M, (label, got["M"], want_M)
+    assert got["L"] == want_stream.size, (label, got["L"], want_stream.size)
+    if not np.array_equal(got["stream"], want_stream):
+        i = int(np.flatnonzero(got["stream"] != want_stream)[0])
+        raise AssertionError(f"{label}: stream differs first at byte {i}: got {got['stream'][i:i+8]} "
+                             f"want {want_stream[i:i+8]}")
+    if not np.array_equal(bits(got["err"]), bits(want_err)):
+        i = int(np.flatnonzero(bits(got["err"]) != bits(want_err))[0])
+        raise AssertionError(f"{label}: err differs first at {i}: {got['err'][i]} vs {want_err[i]}")
+    assert np.array_equal(bits(got["y"]), bits(want_y)), label
+    if acc is not None:
+        want_acc = oracle.decompress_accumulate(want_stream, want_M, n, s, acc.copy())
+        assert got["status_a"] == 0, label
+        assert np.array_equal(bits(got["acc"]), bits(want_acc)), label
+    return got
+
+
+def oracle_group_compress(x: np.ndarray, err: np.ndarray, sizes, s: float):
+    """Per-tensor oracle over a flat buffer: (streams, Ms, new err)."""
+    streams, Ms = [], []
+    e_new = np.empty_like(err)
+    off = 0
+    for n in sizes:
+        st, M, e = oracle.compress(x[off:off + n], err[off:off + n], s)
+        streams.append(st)
+        Ms.append(M)
+        e_new[off:off + n] = e
+        off += n
+    return streams, np.array(Ms, dtype=np.float32), e_new
+
+
+def check_group(group, x: np.ndarray, err: np.ndarray, s: float, label="", want=None):
+    """Grouped compress + decompress on the GPU against the per-tensor oracle.
+    Returns the device payload (out, out_lens, scales) for further use."""
+    import torch
+    sizes = group.sizes
+    xd, ed = to_dev(x), to_dev(err)
+    out, lens, scales, st = group.compress(xd, ed, s)
+    y, st_d = group.decompress(out, lens, scales, s)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st_d.item()) == 0, (label, int(st.item()), int(st_d.item()))
+    streams, Ms, e_new = want if want is not None else oracle_group_compress(x, err, sizes, s)
+    got_out = out.cpu().numpy()
+    got_lens = lens.cpu().numpy()
+    got_M = scales.cpu().numpy()
+    assert np.array_equal(bits(got_M), bits(Ms)), label
+    for t, n in enumerate(sizes):
+        o = group.offsets[t]
+        L = int(got_lens[t])
+        assert L == streams[t].size, (label, t, n, L, streams[t].size)
+        if not np.array_equal(got_out[o:o + L], streams[t]):
+            i = int(np.flatnonzero(got_out[o:o + L] != streams[t])[0])
+            raise AssertionError(f"{label}: tensor {t} (n={n}) stream differs at byte {i}")
+    assert np.array_equal(bits(ed.cpu().numpy()), bits(e_new)), label
+    # decompressed values: q * M * s per tensor
+    want_y = np.empty_like(x)
+    off = 0
+    for t, n in enumerate(sizes):
+        want_y[off:off + n] = oracle.decompress(streams[t], Ms[t], n, s)
+        off += n
+    assert np.array_equal(bits(y.cpu().numpy()), bits(want_y)), label
+    return out, lens, scales, (streams, Ms)

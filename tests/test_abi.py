@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every function include/tlc.h declares,
+and its host-only logic (bounds, workspace sizes, group plans, argument
+checks that fail before any launch) behaves as documented.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gradient_compression_distributed_lc_amd import tlc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tlc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tlc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = tlc.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in tlc.h but not exported"
+    # and the binding covers every declaration
+    assert set(names) == set(tlc._SIGS)
+
+
+def test_status_strings():
+    for code in range(7):
+        assert tlc.status_string(code)
+    assert tlc.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n", [1, 4, 5, 6, 1_048_576, 16_777_216, 2 ** 32 - 1])
+def test_compress_bound_is_ceil_n_over_5(n):
+    assert tlc.compress_bound(n) == -(-n // 5)
+
+
+def test_workspace_size():
+    assert tlc.workspace_size(0) == 0
+    assert tlc.workspace_size(2 ** 32) == 0
+    small, big = tlc.workspace_size(1), tlc.workspace_size(335_000_000)
+    assert 0 < small < 4096 and small % 256 == 0
+    assert big < 2_000_000  # a few bytes per 5120-element tile
+    assert big % 256 == 0
+
+
+def test_group_plan_layout():
+    sizes = [10, 5120, 5121, 1, 33_000, 4 * 5120 * 5]
+    info, table, offs = tlc.group_plan(sizes)
+    assert info.count == len(sizes)
+    assert info.total_elems == sum(sizes)
+    tiles = sum(-(-n // 5120) for n in sizes)
+    chunks = sum(-(-(-(-n // 5)) // 4096) for n in sizes)
+    assert info.tiles == tiles and info.chunks == chunks
+    assert len(table) == info.table_bytes
+    # stream slots: 16-byte aligned, in order, each ceil(n/5) long, inside the buffer
+    prev_end = 0
+    for n, o in zip(sizes, offs):
+        assert o % 16 == 0 and o >= prev_end
+        prev_end = o + -(-n // 5)
+    assert prev_end <= info.stream_bytes
+    # table: header, then per-tensor records (elem_off, n, stream_off, tile0, chunk0)
+    hdr = np.frombuffer(table[:64], dtype=np.uint64)
+    assert hdr[1] == len(sizes) and hdr[2] == tiles and hdr[3] == chunks and hdr[4] == sum(sizes)
+    rec = np.frombuffer(table[64:64 + 32 * len(sizes)], dtype=np.uint64).reshape(-1, 4)
+    assert rec[:, 1].tolist() == sizes
+    assert rec[:, 0].tolist() == np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+    assert rec[:, 2].tolist() == offs
+
+
+def test_group_plan_rejects_bad_sizes():
+    info = tlc.GroupInfo()
+    arr = (ctypes.c_uint64 * 2)(5, 0)
+    assert tlc.lib().tlc_group_plan(arr, 2, ctypes.byref(info), None, 0, None) == tlc.ERR_INVALID_ARG
+    arr = (ctypes.c_uint64 * 1)(2 ** 32)
+    assert tlc.lib().tlc_group_plan(arr, 1, ctypes.byref(info), None, 0, None) == tlc.ERR_INVALID_ARG
+    assert tlc.lib().tlc_group_plan(arr, 0, ctypes.byref(info), None, 0, None) == tlc.ERR_INVALID_ARG
+    arr = (ctypes.c_uint64 * 1)(100)
+    small = ctypes.create_string_buffer(8)
+    assert tlc.lib().tlc_group_plan(arr, 1, ctypes.byref(info), small, 8, None) == tlc.ERR_CAPACITY
+
+
+def test_argument_errors_return_before_any_launch():
+    L = tlc.lib()
+    V = ctypes.c_void_p
+    fake = V(0x10000)          # never dereferenced: every case below fails validation first
+    odd = V(0x10004)
+    ws = V(0x20000)
+    # n == 0, s out of range, capacity too small, null pointers, misaligned fp32, bad workspace
+    assert L.tlc_compress(fake, fake, 0, 1.5, fake, 10, fake, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(fake, fake, 10, 2.0, fake, 10, fake, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(fake, fake, 10, 0.5, fake, 10, fake, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(fake, fake, 10, float("nan"), fake, 10, fake, fake, ws, 4096, fake,
+                          None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(fake, fake, 11, 1.5, fake, 2, fake, fake, ws, 4096, fake, None) == tlc.ERR_CAPACITY
+    assert L.tlc_compress(None, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(odd, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, None, 4096, fake, None) == tlc.ERR_WORKSPACE
+    assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, ws, 16, fake, None) == tlc.ERR_WORKSPACE
+    assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, V(0x20010), 4096, fake,
+                          None) == tlc.ERR_WORKSPACE
+    assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, None, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, fake, fake, 0, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, fake, fake, 10, 1.5, odd, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, None, fake, 10, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_accumulate(fake, fake, fake, 10, 1.99, fake, ws, 1, fake, None) == tlc.ERR_WORKSPACE
+    assert L.tlc_copy_probe(fake, fake, 17, None) == tlc.ERR_INVALID_ARG
+    # grouped calls: the info/table pair must be consistent
+    info, _, _ = tlc.group_plan([100, 200])
+    bad = tlc.GroupInfo.from_buffer_copy(info)
+    bad.table_bytes += 16
+    assert L.tlc_compress_group(ctypes.byref(bad), fake, fake, fake, 1.5, fake, fake, fake, ws, 1 << 20, fake,
+                                None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress_group(ctypes.byref(info), None, fake, fake, 1.5, fake, fake, fake, ws, 1 << 20, fake,
+                                None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_group(ctypes.byref(info), fake, fake, fake, fake, 1.5, fake, ws, 16, fake,
+                                  None) == tlc.ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tlc, "_lib", None)
+    monkeypatch.setattr(tlc, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        tlc.lib()
