@@ -1,0 +1,285 @@
+"""Benchmark of the 3LC codec hot path on one MI355X.
+
+One step = one worker's grouped compress of a whole gradient set (error
+accumulation, per-tensor scale, ternary quantization, quartic packing,
+zero-run encoding) followed by the grouped decompress of that payload
+(zero-run decoding, quartic decoding, dequantization).  The error buffer is
+carried from step to step, as in training.  Inputs are generated once on the
+host (seeded, synthetic) and are resident in HBM before timing starts.
+
+Default workload: the BERT-large gradient set (391 tensors, 335,141,888
+fp32 values, 30% exact zeros, the rest N(0, 1e-4)), s = 1.75.
+
+Printed: one JSON line with the whole-job throughput in GB/s of fp32 input
+(4 bytes x values / (compress + decompress time)), the roofline of the
+dominant kernel (the 12-byte/element pass over x and err) measured with HIP
+events inside the timed region, bits per value, and the CPU oracle timed on
+the host over the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload bert_large] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+DOMINANT = "tlc_accum_max"      # reads x and err, writes err: 12 B per element
+DOMINANT_BYTES_PER_ELEM = 12
+METRIC = "3LC compress+decompress GB/s (fp32 in) and % of HBM roofline; bits/value"
+
+
+def kernel_source_hash() -> str:
+    with open(os.path.join(ROOT, "gradient_compression_distributed_lc_amd", "csrc", "tlc.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(DOMINANT)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(x: np.ndarray, sizes, s: float, passes: int):
+    """The oracle, untuned, single-threaded, over the whole workload."""
+    import oracle
+    from gradient_compression_distributed_lc_amd import workloads
+    offs = workloads.offsets(sizes)
+    streams, Ms = [], []
+    tc = td = 0.0
+    y = np.empty(max(sizes), dtype=np.float32)
+    err0 = None
+    for p in range(passes):
+        err = np.zeros(x.size, dtype=np.float32)
+        cur_streams, cur_M = [], []
+        t0 = time.perf_counter()
+        for t, n in enumerate(sizes):
+            out = np.empty(-(-n // 5), dtype=np.uint8)
+            L, M = oracle.compress_inplace(x[offs[t]:offs[t + 1]], err[offs[t]:offs[t + 1]], s, out)
+            cur_streams.append(out[:L])
+            cur_M.append(M)
+        t1 = time.perf_counter()
+        for t, n in enumerate(sizes):
+            oracle.decompress(cur_streams[t], cur_M[t], n, s, out=y[:n])
+        t2 = time.perf_counter()
+        tc += t1 - t0
+        td += t2 - t1
+        if p == 0:
+            streams, Ms, err0 = cur_streams, cur_M, err
+    elems = passes * x.size
+    return {
+        "value": round(4.0 * elems / (tc + td) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole workload ({len(sizes)} tensors, {x.size} values), {passes} pass(es) of "
+                  f"compress+decompress, single-threaded C oracle",
+        "compress_s": round(tc / passes, 3),
+        "decompress_s": round(td / passes, 3),
+    }, streams, Ms, err0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--s", type=float, default=None)
+    ap.add_argument("--cpu-passes", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy-bandwidth yardstick")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the codec runs on one device and this build has no "
+              "multi-GPU exchange; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gradient_compression_distributed_lc_amd import tlc, workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.get(args.workload)
+    s = args.s if args.s is not None else wl.s_values[0]
+    sizes = wl.sizes
+    N = wl.total
+
+    t_gen = time.perf_counter()
+    x_host = workloads.generate(args.workload)
+    print(f"[bench] generated {args.workload}: {len(sizes)} tensors, {N} values in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    group = tlc.Group(sizes, device=dev)
+    xd = torch.from_numpy(x_host).to(dev)
+    ed = torch.zeros(N, dtype=torch.float32, device=dev)
+    yd = torch.empty(N, dtype=torch.float32, device=dev)
+    out = torch.empty(group.stream_bytes, dtype=torch.uint8, device=dev)
+    lens = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+    scales = torch.empty(len(sizes), dtype=torch.float32, device=dev)
+    st_c = torch.empty(1, dtype=torch.int32, device=dev)
+    st_d = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = group.workspace()
+
+    def step():
+        group.compress(xd, ed, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st_c)
+        group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d)
+
+    # first step from a zero error buffer: kept for the parity check
+    step()
+    torch.cuda.synchronize()
+    first = {"out": out.cpu().numpy(), "lens": lens.cpu().numpy(), "scales": scales.cpu().numpy(),
+             "err": ed.cpu().numpy(), "status": (int(st_c.item()), int(st_d.item()))}
+    for _ in range(max(args.warmup - 1, 0)):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every library kernel on its stream
+    tlc.profile_read()
+    tlc.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    tlc.profile_enable(False)
+    kt = tlc.profile_read()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    if (int(st_c.item()), int(st_d.item())) != (0, 0) or first["status"] != (0, 0):
+        raise SystemExit(f"device status not ok: {first['status']} / {(int(st_c.item()), int(st_d.item()))}")
+
+    def per_launch(name):
+        n, ms = kt.get(name, (0, 0.0))
+        return ms / n if n else 0.0
+
+    comp_ms = sum(per_launch(k) for k in ("tlc_accum_max", "tlc_seg_scale", "tlc_quant_pack", "tlc_emit"))
+    dec_ms = sum(per_launch(k) for k in ("tlc_prep_fill", "tlc_decode"))
+    dom_ms = per_launch(DOMINANT)
+    achieved = DOMINANT_BYTES_PER_ELEM * N / (dom_ms * 1e-3) / 1e9 if dom_ms else 0.0
+
+    # accumulate of the same payload, 8 times (the 8-worker receive side)
+    acc = torch.zeros(N, dtype=torch.float32, device=dev)
+    st_a = torch.empty(1, dtype=torch.int32, device=dev)
+    group.decompress_accumulate(out, lens, scales, s, acc, workspace=ws, status=st_a)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(8):
+        group.decompress_accumulate(out, lens, scales, s, acc, workspace=ws, status=st_a)
+    a1.record()
+    torch.cuda.synchronize()
+    acc_ms = a0.elapsed_time(a1) / 8
+
+    # copy yardstick: what a plain streaming copy reaches on this GPU
+    copy_gbps = None
+    if not args.no_copy:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            tlc.copy_probe(src, dst, nbytes)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            tlc.copy_probe(src, dst, nbytes)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+
+    L_total = int(first["lens"].sum())
+    bits = 8.0 * L_total / N
+    bits_hdr = 8.0 * (L_total + 4 * len(sizes)) / N
+    alg_bytes_comp = 12.0 * N + L_total + 4 * len(sizes)
+    alg_bytes_dec = 4.0 * N + L_total
+    gbps = 4.0 * N / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    parity = "not checked (--no-cpu)"
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu, streams, Ms, err0 = cpu_baseline(x_host, sizes, s, args.cpu_passes)
+        ok = np.array_equal(first["scales"].view(np.uint32), np.asarray(Ms, np.float32).view(np.uint32))
+        ok &= np.array_equal(first["err"].view(np.uint32), err0.view(np.uint32))
+        for t in range(len(sizes)):
+            o = group.offsets[t]
+            L = int(first["lens"][t])
+            ok &= L == streams[t].size and np.array_equal(first["out"][o:o + L], streams[t])
+        parity = "bit-exact vs oracle (streams, M, error buffer; first step)" if ok else "MISMATCH"
+        if not ok:
+            print("[bench] PARITY MISMATCH", file=sys.stderr, flush=True)
+
+    traffic = stored_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tensors": len(sizes), "values": N, "s": s,
+                   "values_dist": wl.description, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "bytes_per_elem": DOMINANT_BYTES_PER_ELEM,
+                     "avg_ms": round(dom_ms, 4)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "bits_per_value": round(bits, 4),
+        "bits_per_value_with_scale": round(bits_hdr, 4),
+        "compression_ratio_vs_fp32": round(32.0 / bits_hdr, 1),
+        "compress_ms": round(comp_ms, 4),
+        "decompress_ms": round(dec_ms, 4),
+        "compress_GBps_fp32_in": round(4.0 * N / (comp_ms * 1e-3) / 1e9, 1) if comp_ms else None,
+        "decompress_GBps_fp32_in": round(4.0 * N / (dec_ms * 1e-3) / 1e9, 1) if dec_ms else None,
+        "path_roofline_frac": round((alg_bytes_comp + alg_bytes_dec) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                    4),
+        "compress_roofline_frac": round(alg_bytes_comp / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if comp_ms else None,
+        "decompress_roofline_frac": round(alg_bytes_dec / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if dec_ms else None,
+        "accumulate_ms_per_payload": round(acc_ms, 4),
+        "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
+        "kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kt.items() if v[0]},
+        "wall_s_timed": round(wall, 3),
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

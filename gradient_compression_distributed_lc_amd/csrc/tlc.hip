@@ -6,28 +6,31 @@
 // accumulation and 3-value quantization with a sparsity multiplier, quartic
 // encoding (five ternary values per byte), zero-run encoding of the all-zero
 // byte, and the reverse path.  The page's implementation is vectorised CPU
-// code; here every step runs in the kernels below, laid out for CDNA4:
+// code; here every step runs in the kernels below, laid out for CDNA4.
 //
-//   compress  = k_accum_max -> k_seg_scale -> k_encode
-//     k_accum_max  one HBM pass over x and err: v = x + err written back to
-//                  err, plus the max |v| of each 5120-element tile.  This is
-//                  the 12-byte/element stream that bounds the codec.
-//     k_seg_scale  one block per tensor: M = max of its tile maxima, M*s, and
-//                  the fp32 selection threshold (see select_threshold).
-//     k_encode     one block per tile, in ticket order.  A tile whose max is
-//                  below the threshold holds only zero codes: it never touches
-//                  x or err again and contributes a run of byte 121.  Other
-//                  tiles re-read v, write err = v - q*M*s where q != 0, pack
-//                  the quartic bytes in LDS and zero-run encode them.  The
-//                  output position of every tile comes from a decoupled
-//                  look-back scan whose carry is the small state (bytes
-//                  emitted, pending run length mod 14).
-//   decompress = k_fill_reset -> k_decode ; accumulate = k_reset -> k_decode
-//     k_fill_reset dense zero fill of y (every code 0 dequantizes to +0.0)
-//     k_decode     one block per 4096 stream bytes: expansion lengths, block
-//                  scan, look-back scan for the quartic byte index, then only
-//                  the literal bytes are decoded and their nonzero codes
-//                  written (or added) to y.
+// compress (five launches):
+//   k_accum_max   the one full HBM pass: v = x + err written back to err, and
+//                 the max |v| of every 1024-element flat tile (256 lanes x one
+//                 16-byte load each: many small blocks keep the most bytes in
+//                 flight).  A tile that spans tensors keeps one partial max per
+//                 tensor, in slot tile + tensor.  12 bytes per element.
+//   k_seg_scale   one block per tensor: M = max of its partial maxima, M*s,
+//                 the exact fp32 selection threshold (select_threshold), and
+//                 the list of encode tiles (5120 elements = 1024 quartic bytes)
+//                 whose partial maxima reach it.  Every other encode tile
+//                 holds only zero codes: it is summarised as a run of byte 121
+//                 without touching x or err again.
+//   k_quant_pack  the listed tiles only: re-read v, write err = v - q*M*s
+//                 where q != 0, pack quartic bytes in LDS and zero-run encode
+//                 them from the tile's first literal on into a staging slot.
+//   k_emit        spans of 256 encode tiles: block scan of the tiles' carry
+//                 summaries, decoupled look-back across spans for the span's
+//                 input state, then the span's stream bytes are written
+//                 cooperatively (255 runs, remainder codes, staged bytes).
+// decompress: k_prep (zero fill of y, decoder state, list of stream chunks)
+//             -> k_decode (one block per 16 KiB of stream bytes: expansion
+//             scan + look-back for the quartic byte index, then only literal
+//             bytes are decoded and their nonzero codes written or added).
 //
 // No matrix-core work exists on this path: it is bound by HBM bandwidth.
 
@@ -48,14 +51,17 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kTileElems = 5120;             // 1280 float4 = 5 per thread
-constexpr uint32_t kTileBytes = kTileElems / 5;   // 1024 quartic bytes = 4 per thread
-constexpr uint32_t kChunk = 4096;                 // decoder stream bytes per block = 16 per thread
+constexpr uint32_t kFTile = 1024;                 // flat tile of k_accum_max: one float4 per lane
+constexpr uint32_t kETile = 5120;                 // encode tile: elements
+constexpr uint32_t kETileBytes = kETile / 5;      // 1024 quartic bytes = 4 per lane
+constexpr uint32_t kSpan = 256;                   // encode tiles per k_emit block (one per lane)
+constexpr uint32_t kChunk = 16384;                // decoder stream bytes per block = 64 per lane
 constexpr uint32_t kZero = 121;                   // quartic byte of five zero codes
 constexpr uint32_t kRunMax = 14;                  // codes 243..255 = runs of 2..14
 constexpr uint32_t kRunBase = 241;
 constexpr uint64_t kMaxN = 0xFFFFFFFFull;
 constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (about a second)
+constexpr uint32_t kPackGrid = 2048;              // persistent blocks of k_quant_pack
 
 // look-back word: 2 status bits | 62 payload bits
 constexpr uint64_t kInvalid = 0, kAggregate = 1, kPrefix = 2, kPoison = 3;
@@ -63,34 +69,34 @@ constexpr uint64_t kPayloadMask = (1ull << 62) - 1;
 
 struct Seg {
     uint64_t elem_off;    // first element in the flat fp32 buffers
-    uint64_t n;           // elements
+    uint32_t n;           // elements
+    uint32_t etile0;      // first encode tile
     uint64_t stream_off;  // first byte of this tensor's stream slot
-    uint32_t tile0;       // first compress tile
-    uint32_t chunk0;      // first decompress chunk
+    uint32_t span0;       // first k_emit span
+    uint32_t chunk0;      // first decoder chunk slot (capacity numbering)
 };
 static_assert(sizeof(Seg) == 32, "table layout");
 
 struct TableHeader {
-    uint64_t magic, count, tiles, chunks, total_elems, stream_bytes, reserved0, reserved1;
+    uint64_t magic, count, ftiles, etiles, spans, chunks, total_elems, stream_bytes;
 };
 static_assert(sizeof(TableHeader) == 64, "table layout");
-constexpr uint64_t kMagic = 0x31434c5433ull;  // "3TLC1"
+constexpr uint64_t kMagic = 0x32434c5433ull;  // "3TLC2"
+constexpr uint32_t kStraddle = 0x80000000u;   // ftile_info flag: the flat tile spans tensors
 
 struct GroupView {
-    const Seg* segs;          // device table, or nullptr for one tensor
-    const uint32_t* tile_seg;
-    const uint32_t* chunk_seg;
+    const Seg* segs;            // device table, or nullptr for one tensor
+    const uint32_t* ftile_info; // per flat tile: tensor of its first element | kStraddle
+    const uint32_t* span_seg;   // per k_emit span: tensor
+    uint32_t count;
     Seg one;
 };
 
-__device__ __forceinline__ uint32_t tile_segment(const GroupView& g, uint32_t t) {
-    return g.segs ? g.tile_seg[t] : 0u;
-}
-__device__ __forceinline__ uint32_t chunk_segment(const GroupView& g, uint32_t c) {
-    return g.segs ? g.chunk_seg[c] : 0u;
-}
-__device__ __forceinline__ Seg load_seg(const GroupView& g, uint32_t i) {
-    return g.segs ? g.segs[i] : g.one;
+__device__ __forceinline__ Seg load_seg(const GroupView& g, uint32_t i) { return g.segs ? g.segs[i] : g.one; }
+
+__device__ __forceinline__ uint32_t quartic_len(uint32_t n) { return (uint32_t)(((uint64_t)n + 4) / 5); }
+__device__ __forceinline__ uint32_t etiles_of(uint32_t n) {
+    return (uint32_t)(((uint64_t)n + kETile - 1) / kETile);
 }
 
 // ---------------------------------------------------------------------------
@@ -172,6 +178,32 @@ __device__ int block_excl_max(int v, int* sm, int* total) {
     return max(before, prev);
 }
 
+// exclusive scan of 62-bit payloads under an associative (not necessarily
+// commutative) operation op(a, b) = "a, then b"
+template <typename Op>
+__device__ uint64_t block_excl_scan(uint64_t v, uint64_t identity, Op op, uint64_t* sm, uint64_t* total) {
+    const int lane = lane_id(), w = wave_id();
+    uint64_t inc = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc = op(o, inc);
+    }
+    uint64_t ex = __shfl_up(inc, 1, 64);
+    if (lane == 0) ex = identity;
+    if (lane == 63) sm[w] = inc;
+    __syncthreads();
+    uint64_t before = identity, tot = identity;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const uint64_t t = sm[i];
+        if (i < w) before = op(before, t);
+        tot = op(tot, t);
+    }
+    __syncthreads();
+    *total = tot;
+    return op(before, ex);
+}
+
 __device__ __forceinline__ void publish(uint64_t* flags, uint32_t idx, uint64_t status, uint64_t payload) {
     __hip_atomic_store(flags + idx, (status << 62) | (payload & kPayloadMask), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -237,7 +269,8 @@ __device__ bool look_back(const uint64_t* flags, uint32_t idx, uint32_t first, u
 //              leaves c = trailing run mod 14 pending:
 //              (E, r) -> (E + ceil((r+p)/14) + K, c)
 // Both shapes are closed under composition, so tile summaries can be scanned.
-// Payload bits: 61 = Lit, 60..57 = p, 56..53 = c, 31..0 = Q or K.
+// Payload bits: 61 = Lit, 60..57 = p, 56..53 = c, 31..0 = Q or K.  Per-tile
+// words also carry K - F (the staged byte count) in bits 32..42.
 
 struct Carry {
     uint32_t K;
@@ -327,112 +360,159 @@ __device__ float select_threshold(float m, float ms) {
     return a;
 }
 
+__device__ __forceinline__ int ternary(float v, float thr) {
+    return fabsf(v) >= thr ? (v > 0.0f ? 1 : -1) : 0;
+}
+
+// tensor holding element e: largest k in [lo, hi) with segs[k].elem_off <= e
+__device__ uint32_t find_segment(const Seg* segs, uint32_t lo, uint32_t hi, uint64_t e) {
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (segs[mid].elem_off <= e) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // ---------------------------------------------------------------------------
 // compress kernels
 
-__global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, const float* __restrict__ x,
-                                                        float* __restrict__ err,
-                                                        float* __restrict__ tile_max,
-                                                        uint64_t* __restrict__ flags,
-                                                        uint32_t* __restrict__ ctrl,
-                                                        int* __restrict__ status) {
+__global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, uint64_t N, const float* __restrict__ x,
+                                                        float* __restrict__ err, float* __restrict__ pmax,
+                                                        uint64_t* __restrict__ span_flags, uint64_t spans,
+                                                        uint32_t* __restrict__ ctrl, int* __restrict__ status) {
     __shared__ float sm[kWaves];
-    const uint32_t tile = blockIdx.x;
-    const Seg sg = load_seg(g, tile_segment(g, tile));
-    const uint64_t lt = tile - sg.tile0;
-    const uint64_t e0 = sg.elem_off + lt * kTileElems;
-    const uint64_t e1 = min(sg.elem_off + sg.n, e0 + kTileElems);
-    float m = 0.0f;
-    if ((e0 & 3) == 0 && e1 - e0 == kTileElems) {
-        const float4* xs = reinterpret_cast<const float4*>(x + e0);
-        float4* es = reinterpret_cast<float4*>(err + e0);
-        float4 a[5], b[5];
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            a[k] = xs[threadIdx.x + k * kThreads];
-            b[k] = es[threadIdx.x + k * kThreads];
-        }
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            const float4 v = make_float4(a[k].x + b[k].x, a[k].y + b[k].y, a[k].z + b[k].z, a[k].w + b[k].w);
-            es[threadIdx.x + k * kThreads] = v;
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
+    __shared__ uint32_t s_part[kFTile];  // per-tensor maxima of a tile that spans tensors
+    __shared__ uint32_t s_last;
+    const uint32_t t = blockIdx.x;
+    const uint64_t i4 = (uint64_t)t * (kFTile / 4) + threadIdx.x;
+    const uint64_t el = i4 << 2;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (el + 4 <= N) {
+        const float4 a = reinterpret_cast<const float4*>(x)[i4];
+        const float4 b = reinterpret_cast<const float4*>(err)[i4];
+        const float4 r = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        reinterpret_cast<float4*>(err)[i4] = r;
+        v[0] = r.x;
+        v[1] = r.y;
+        v[2] = r.z;
+        v[3] = r.w;
     } else {
-        for (uint64_t i = e0 + threadIdx.x; i < e1; i += kThreads) {
-            const float v = x[i] + err[i];
-            err[i] = v;
-            m = fmaxf(m, fabsf(v));
+        for (int j = 0; j < 4; ++j) {
+            if (el + j < N) {
+                v[j] = x[el + j] + err[el + j];
+                err[el + j] = v[j];
+            }
         }
     }
-    m = block_max(m, sm);
-    if (threadIdx.x == 0) {
-        tile_max[tile] = m;
-        flags[tile] = 0;
-        if (tile == 0) {
-            ctrl[0] = 0;
-            *status = TLC_OK;
+    const uint32_t info = g.segs ? g.ftile_info[t] : 0u;
+    if (!(info & kStraddle)) {
+        const float m = block_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))), sm);
+        if (threadIdx.x == 0) pmax[t + info] = m;
+    } else {
+        // the tile spans tensors g0..g1: one partial max per tensor, in slot t + g
+        const uint32_t g0 = info & ~kStraddle;
+        const uint32_t hi = min(g.count, g0 + kFTile + 1);
+        for (uint32_t k = threadIdx.x; k < kFTile; k += kThreads) s_part[k] = 0;
+        if (threadIdx.x == 0) {
+            const uint64_t last = min(N, (uint64_t)(t + 1) * kFTile) - 1;
+            s_last = find_segment(g.segs, g0, hi, last);
         }
+        __syncthreads();
+        for (int j = 0; j < 4; ++j) {
+            if (el + j < N) {
+                const uint32_t k = find_segment(g.segs, g0, hi, el + j) - g0;
+                atomicMax(&s_part[k], __float_as_uint(fabsf(v[j])));  // order of non-negative floats
+            }
+        }
+        __syncthreads();
+        for (uint32_t k = threadIdx.x; k <= s_last - g0; k += kThreads) pmax[t + g0 + k] = __uint_as_float(s_part[k]);
+    }
+    // look-back state of k_emit starts empty on every call
+    for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < spans; i += (uint64_t)gridDim.x * kThreads)
+        span_flags[i] = 0;
+    if (t == 0 && threadIdx.x == 0) {
+        ctrl[0] = 0;  // k_emit tickets
+        ctrl[1] = 0;  // active encode tiles
+        *status = TLC_OK;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_seg_scale(GroupView g, float s, const float* __restrict__ tile_max,
+__global__ __launch_bounds__(kThreads) void k_seg_scale(GroupView g, float s, const float* __restrict__ pmax,
                                                         float* __restrict__ scales, float* __restrict__ seg_thr,
-                                                        float* __restrict__ seg_ms) {
+                                                        float* __restrict__ seg_ms,
+                                                        uint64_t* __restrict__ etile_agg,
+                                                        uint64_t* __restrict__ active,
+                                                        uint32_t* __restrict__ ctrl) {
     __shared__ float sm[kWaves];
-    const uint32_t si = blockIdx.x;
-    const Seg sg = load_seg(g, si);
-    const uint32_t nt = (uint32_t)((sg.n + kTileElems - 1) / kTileElems);
+    __shared__ uint32_t s_u[kWaves];
+    __shared__ float s_thr;
+    __shared__ uint32_t s_base;
+    const uint32_t gi = blockIdx.x;
+    const Seg sg = load_seg(g, gi);
+    const uint64_t tf = sg.elem_off / kFTile, tl = (sg.elem_off + sg.n - 1) / kFTile;
     float m = 0.0f;
-    for (uint32_t t = threadIdx.x; t < nt; t += kThreads) m = fmaxf(m, tile_max[sg.tile0 + t]);
+    for (uint64_t t = tf + threadIdx.x; t <= tl; t += kThreads) m = fmaxf(m, pmax[t + gi]);
     m = block_max(m, sm);
     if (threadIdx.x == 0) {
         const float ms = m * s;
-        scales[si] = m;
-        seg_ms[si] = ms;
-        seg_thr[si] = select_threshold(m, ms);
+        const float thr = select_threshold(m, ms);
+        scales[gi] = m;
+        seg_ms[gi] = ms;
+        seg_thr[gi] = thr;
+        s_thr = thr;
+    }
+    __syncthreads();
+    const float thr = s_thr;
+    const uint32_t B = quartic_len(sg.n), ne = etiles_of(sg.n);
+    for (uint32_t base = 0; base < ne; base += kThreads) {
+        const uint32_t j = base + threadIdx.x;
+        bool act = false;
+        if (j < ne) {
+            const uint64_t a = sg.elem_off + (uint64_t)j * kETile;
+            const uint64_t b = sg.elem_off + min((uint64_t)sg.n, (uint64_t)(j + 1) * kETile) - 1;
+            float pm = 0.0f;
+            for (uint64_t t = a / kFTile; t <= b / kFTile; ++t) pm = fmaxf(pm, pmax[t + gi]);
+            act = pm >= thr;
+            if (!act) etile_agg[sg.etile0 + j] = carry_pack(carry_run(min(kETileBytes, B - j * kETileBytes)));
+        }
+        uint32_t cnt;
+        const uint32_t pos = block_excl_sum(act ? 1u : 0u, s_u, &cnt);
+        if (cnt) {
+            if (threadIdx.x == 0) s_base = atomicAdd(ctrl + 1, cnt);
+            __syncthreads();
+            if (act) active[s_base + pos] = ((uint64_t)gi << 32) | (sg.etile0 + j);
+            __syncthreads();
+        }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_encode(GroupView g, float* __restrict__ err,
-                                                     const float* __restrict__ tile_max,
-                                                     const float* __restrict__ seg_thr,
-                                                     const float* __restrict__ seg_ms,
-                                                     uint64_t* __restrict__ flags, uint32_t* __restrict__ ctrl,
-                                                     uint8_t* __restrict__ out, uint64_t* __restrict__ out_lens,
-                                                     int* __restrict__ status) {
-    __shared__ __align__(16) int8_t s_q[kTileElems];
+__global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __restrict__ err,
+                                                         const float* __restrict__ seg_thr,
+                                                         const float* __restrict__ seg_ms,
+                                                         const uint64_t* __restrict__ active,
+                                                         const uint32_t* __restrict__ ctrl,
+                                                         uint64_t* __restrict__ etile_agg,
+                                                         uint8_t* __restrict__ staging) {
+    __shared__ __align__(16) int8_t s_q[kETile];
     __shared__ uint32_t s_u[kWaves];
     __shared__ int s_i[kWaves];
-    __shared__ uint32_t s_tile, s_E, s_r, s_ok;
+    const uint32_t na = ctrl[1];
+    const uint32_t kb = 4 * threadIdx.x;  // this lane's first tile byte
+    for (uint32_t ai = blockIdx.x; ai < na; ai += gridDim.x) {
+        const uint64_t entry = active[ai];
+        const uint32_t gi = (uint32_t)(entry >> 32), et = (uint32_t)entry;
+        const Seg sg = load_seg(g, gi);
+        const uint32_t j = et - sg.etile0;
+        const uint32_t nbytes = min(kETileBytes, quartic_len(sg.n) - j * kETileBytes);
+        const uint32_t nel = min(kETile, sg.n - j * kETile);
+        const uint64_t e0 = sg.elem_off + (uint64_t)j * kETile;
+        const float thr = seg_thr[gi];
+        const float ms = seg_ms[gi];
 
-    if (threadIdx.x == 0) s_tile = atomicAdd(ctrl, 1u);
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint32_t si = tile_segment(g, tile);
-    const Seg sg = load_seg(g, si);
-    const uint32_t lt = tile - sg.tile0;
-    const uint32_t n = (uint32_t)sg.n;
-    const uint32_t B = (uint32_t)(((uint64_t)n + 4) / 5);
-    const uint32_t nt = (uint32_t)(((uint64_t)n + kTileElems - 1) / kTileElems);
-    const uint32_t nbytes = min(kTileBytes, B - lt * kTileBytes);
-    const uint32_t nel = min(kTileElems, n - lt * kTileElems);
-    const uint64_t e0 = sg.elem_off + (uint64_t)lt * kTileElems;
-    const float thr = seg_thr[si];
-    const float ms = seg_ms[si];
-    const bool active = tile_max[tile] >= thr;  // same for every thread
-    uint8_t* const o = out + sg.stream_off;
-
-    Carry agg = carry_run(nbytes);
-    uint32_t b[4] = {kZero, kZero, kZero, kZero};
-    const uint32_t kb = 4 * threadIdx.x;  // this thread's first tile byte
-    int first = INT_MAX, last = -1, prev_excl = -1;
-    uint32_t emit_excl = 0, k_int = 0;
-
-    if (active) {
         // ternary codes of the tile into LDS; pad codes past the tensor are 0
         for (uint32_t u = nel + threadIdx.x; u < 5 * nbytes; u += kThreads) s_q[u] = 0;
-        if ((e0 & 3) == 0 && nel == kTileElems) {
+        if ((e0 & 3) == 0 && nel == kETile) {
             float4* es = reinterpret_cast<float4*>(err + e0);
             float4 v[5];
 #pragma unroll
@@ -443,17 +523,17 @@ __global__ __launch_bounds__(kThreads) void k_encode(GroupView g, float* __restr
                 const float vv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
                 uint32_t packed = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int q = fabsf(vv[j]) >= thr ? (vv[j] > 0.0f ? 1 : -1) : 0;
-                    if (q) err[e0 + 4 * slot + j] = vv[j] - (float)q * ms;
-                    packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * j);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int q = ternary(vv[jj], thr);
+                    if (q) err[e0 + 4 * slot + jj] = vv[jj] - (float)q * ms;
+                    packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * jj);
                 }
                 reinterpret_cast<uint32_t*>(s_q)[slot] = packed;
             }
         } else {
             for (uint32_t u = threadIdx.x; u < nel; u += kThreads) {
                 const float vv = err[e0 + u];
-                const int q = fabsf(vv) >= thr ? (vv > 0.0f ? 1 : -1) : 0;
+                const int q = ternary(vv, thr);
                 if (q) err[e0 + u] = vv - (float)q * ms;
                 s_q[u] = (int8_t)q;
             }
@@ -464,40 +544,44 @@ __global__ __launch_bounds__(kThreads) void k_encode(GroupView g, float* __restr
         uint32_t words[5];
 #pragma unroll
         for (int i = 0; i < 5; ++i) words[i] = reinterpret_cast<const uint32_t*>(s_q)[5 * threadIdx.x + i];
+        uint32_t b[4] = {kZero, kZero, kZero, kZero};
         int tfirst = INT_MAX, tlast = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int jj = 0; jj < 4; ++jj) {
             uint32_t byte = 0, w3 = 1;
 #pragma unroll
             for (int d = 0; d < 5; ++d) {
-                const int idx = 5 * j + d;
+                const int idx = 5 * jj + d;
                 const int q = (int)(int8_t)(words[idx >> 2] >> (8 * (idx & 3)));
                 byte += (uint32_t)(q + 1) * w3;
                 w3 *= 3;
             }
-            const uint32_t k = kb + j;
+            const uint32_t k = kb + jj;
             if (k < nbytes) {
-                b[j] = byte;
+                b[jj] = byte;
                 if (byte != kZero) {
                     tfirst = min(tfirst, (int)k);
                     tlast = (int)k;
                 }
             }
         }
-        prev_excl = block_excl_max(tlast, s_i, &last);
-        first = block_min_int(tfirst, s_i);
+        int last;
+        const int prev_excl = block_excl_max(tlast, s_i, &last);
+        const int first = block_min_int(tfirst, s_i);
 
+        Carry agg = carry_run(nbytes);
+        uint32_t k_int = 0;
         if (last >= 0) {
-            // stream bytes emitted from the first literal on: a literal emits
-            // the remainder code of the run before it (if any) and itself; a
-            // 121 emits a 255 when it completes a 14-byte chunk of its run
+            // stream bytes from the first literal on: a literal emits the
+            // remainder code of the run before it (if any) and itself; a 121
+            // emits a 255 when it completes a 14-byte chunk of its run
             uint32_t te = 0;
             int prev = prev_excl;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = (int)kb + j;
+            for (int jj = 0; jj < 4; ++jj) {
+                const int k = (int)kb + jj;
                 if (k < (int)nbytes && k >= first) {
-                    if (b[j] != kZero) {
+                    if (b[jj] != kZero) {
                         te += (k == first) ? 1u : 1u + (((k - prev - 1) % (int)kRunMax) != 0);
                         prev = k;
                     } else {
@@ -505,35 +589,86 @@ __global__ __launch_bounds__(kThreads) void k_encode(GroupView g, float* __restr
                     }
                 }
             }
-            emit_excl = block_excl_sum(te, s_u, &k_int);
+            uint32_t pos = block_excl_sum(te, s_u, &k_int);
+            uint8_t* const st = staging + (uint64_t)et * kETileBytes;
+            prev = prev_excl;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int k = (int)kb + jj;
+                if (k < (int)nbytes && k >= first) {
+                    if (b[jj] != kZero) {
+                        if (k != first) {
+                            const uint32_t gap = (uint32_t)((k - prev - 1) % (int)kRunMax);
+                            if (gap) st[pos++] = remainder_code(gap);
+                        }
+                        st[pos++] = (uint8_t)b[jj];
+                        prev = k;
+                    } else if (((k - prev) % (int)kRunMax) == 0) {
+                        st[pos++] = 255;
+                    }
+                }
+            }
             agg.lit = 1;
             agg.p = (uint32_t)first % kRunMax;
             agg.K = (uint32_t)first / kRunMax + k_int;
             agg.c = (nbytes - 1 - (uint32_t)last) % kRunMax;
         }
+        if (threadIdx.x == 0) etile_agg[et] = carry_pack(agg) | ((uint64_t)k_int << 32);
+        __syncthreads();  // s_q is rewritten by the next tile
     }
+}
 
-    // publish this tile's summary, look back for the state before it
+__global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* __restrict__ etile_agg,
+                                                   const uint8_t* __restrict__ staging,
+                                                   uint64_t* __restrict__ flags, uint32_t* __restrict__ ctrl,
+                                                   uint8_t* __restrict__ out, uint64_t* __restrict__ out_lens,
+                                                   int* __restrict__ status) {
+    __shared__ uint64_t s_sm[kWaves];
+    __shared__ uint32_t s_u[kWaves];
+    __shared__ uint32_t s_off[kThreads + 1];  // output offset of each tile within the span
+    __shared__ uint32_t s_dst[kThreads];      // stream position of each tile's first byte
+    __shared__ uint32_t s_lead[kThreads];     // 255 codes that open the tile's output
+    __shared__ uint16_t s_kint[kThreads];     // staged bytes after the lead (and remainder code)
+    __shared__ uint8_t s_rem[kThreads];       // remainder code after the 255s, or 0
+    __shared__ uint8_t s_fin[kThreads];       // closing remainder code of the tensor's last tile, or 0
+    __shared__ uint32_t s_span, s_E, s_r, s_ok;
+
+    if (threadIdx.x == 0) s_span = atomicAdd(ctrl, 1u);
+    __syncthreads();
+    const uint32_t sp = s_span;
+    const uint32_t gi = g.segs ? g.span_seg[sp] : 0u;
+    const Seg sg = load_seg(g, gi);
+    const uint32_t B = quartic_len(sg.n), ne = etiles_of(sg.n);
+    const uint32_t lsp = sp - sg.span0;
+    const uint32_t j = lsp * kSpan + threadIdx.x;  // tensor-relative encode tile
+    const bool valid = j < ne;
+    const uint32_t nb = valid ? min(kETileBytes, B - j * kETileBytes) : 0u;
+    const uint64_t word = valid ? etile_agg[sg.etile0 + j] : 0ull;
+    const Carry a = carry_unpack(word);
+    uint32_t kint = (uint32_t)(word >> 32) & 0x7FFu;
+    uint64_t total;
+    const uint64_t excl = block_excl_scan(carry_pack(a), 0ull, CarryCompose(), s_sm, &total);
+
     if (threadIdx.x < 64) {
         uint32_t E = 0, r = 0, ok = 1;
-        if (lt == 0) {
+        if (lsp == 0) {
             if (threadIdx.x == 0) {
                 uint32_t E2, r2;
-                carry_apply(agg, 0, 0, &E2, &r2);
-                publish(flags, tile, kPrefix, (uint64_t)E2 | ((uint64_t)r2 << 57));
+                carry_apply(carry_unpack(total), 0, 0, &E2, &r2);
+                publish(flags, sp, kPrefix, (uint64_t)E2 | ((uint64_t)r2 << 57));
             }
         } else {
-            if (threadIdx.x == 0) publish(flags, tile, kAggregate, carry_pack(agg));
+            if (threadIdx.x == 0) publish(flags, sp, kAggregate, total);
             uint64_t f = 0;
-            ok = look_back(flags, tile, sg.tile0, carry_pack(carry_run(0)), CarryCompose(), &f) ? 1u : 0u;
+            ok = look_back(flags, sp, sg.span0, 0ull, CarryCompose(), &f) ? 1u : 0u;
             if (ok) carry_apply(carry_unpack(f), 0, 0, &E, &r);
             if (threadIdx.x == 0) {
                 if (ok) {
                     uint32_t E2, r2;
-                    carry_apply(agg, E, r, &E2, &r2);
-                    publish(flags, tile, kPrefix, (uint64_t)E2 | ((uint64_t)r2 << 57));
+                    carry_apply(carry_unpack(total), E, r, &E2, &r2);
+                    publish(flags, sp, kPrefix, (uint64_t)E2 | ((uint64_t)r2 << 57));
                 } else {
-                    publish(flags, tile, kPoison, 0);
+                    publish(flags, sp, kPoison, 0);
                 }
             }
         }
@@ -548,86 +683,117 @@ __global__ __launch_bounds__(kThreads) void k_encode(GroupView g, float* __restr
         if (threadIdx.x == 0) raise_status(status, TLC_ERR_INTERNAL);
         return;
     }
-    const uint32_t E_in = s_E, r_in = s_r;
-    uint32_t E_out, r_out;
-    if (!agg.lit) {
-        const uint32_t t = r_in + nbytes;
-        const uint32_t n255 = t / kRunMax;
-        for (uint32_t i = threadIdx.x; i < n255; i += kThreads)
-            if (E_in + i < B) o[E_in + i] = 255;
-        E_out = E_in + n255;
-        r_out = t % kRunMax;
-    } else {
-        const uint32_t t = r_in + (uint32_t)first;
-        const uint32_t n255 = t / kRunMax, rem = t % kRunMax;
-        for (uint32_t i = threadIdx.x; i < n255; i += kThreads)
-            if (E_in + i < B) o[E_in + i] = 255;
-        if (rem && threadIdx.x == 0 && E_in + n255 < B) o[E_in + n255] = remainder_code(rem);
-        const uint32_t base = E_in + n255 + (rem ? 1u : 0u);
-        uint32_t pos = base + emit_excl;
-        int prev = prev_excl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = (int)kb + j;
-            if (k < (int)nbytes && k >= first) {
-                if (b[j] != kZero) {
-                    if (k != first) {
-                        const uint32_t gap = (uint32_t)((k - prev - 1) % (int)kRunMax);
-                        if (gap) {
-                            if (pos < B) o[pos] = remainder_code(gap);
-                            ++pos;
-                        }
-                    }
-                    if (pos < B) o[pos] = (uint8_t)b[j];
-                    ++pos;
-                    prev = k;
-                } else if (((k - prev) % (int)kRunMax) == 0) {
-                    if (pos < B) o[pos] = 255;
-                    ++pos;
-                }
-            }
+
+    uint32_t E_in, r_in;
+    carry_apply(carry_unpack(excl), s_E, s_r, &E_in, &r_in);
+    uint32_t lead = 0, rem = 0, fin = 0, len = 0;
+    if (valid) {
+        uint32_t E_out, r_out;
+        if (!a.lit) {
+            const uint32_t t = r_in + nb;
+            lead = t / kRunMax;
+            kint = 0;
+            E_out = E_in + lead;
+            r_out = t % kRunMax;
+        } else {
+            const uint32_t f = kRunMax * (a.K - kint) + a.p;  // first literal of the tile
+            const uint32_t t = r_in + f;
+            lead = t / kRunMax;
+            rem = (t % kRunMax) ? remainder_code(t % kRunMax) : 0u;
+            E_out = E_in + lead + (rem ? 1u : 0u) + kint;
+            r_out = a.c;
         }
-        E_out = base + k_int;
-        r_out = agg.c;
+        len = E_out - E_in;
+        if (j == ne - 1) {
+            if (r_out) {
+                fin = remainder_code(r_out);
+                len += 1;
+            }
+            const uint64_t L = (uint64_t)E_out + (r_out ? 1u : 0u);
+            if (L > B) raise_status(status, TLC_ERR_INTERNAL);
+            out_lens[gi] = L;
+        }
     }
-    if (lt == nt - 1 && threadIdx.x == 0) {
-        // the stream never outgrows ceil(n/5); the guards above keep even a
-        // wrong length from writing past the tensor's slot
-        const uint64_t len = (uint64_t)E_out + (r_out ? 1u : 0u);
-        if (r_out && E_out < B) o[E_out] = remainder_code(r_out);
-        if (len > B) raise_status(status, TLC_ERR_INTERNAL);
-        out_lens[si] = len;
+    s_dst[threadIdx.x] = E_in;
+    s_lead[threadIdx.x] = lead;
+    s_kint[threadIdx.x] = (uint16_t)kint;
+    s_rem[threadIdx.x] = (uint8_t)rem;
+    s_fin[threadIdx.x] = (uint8_t)fin;
+    uint32_t tot_len;
+    s_off[threadIdx.x] = block_excl_sum(len, s_u, &tot_len);
+    if (threadIdx.x == 0) s_off[kThreads] = tot_len;
+    __syncthreads();
+
+    // the span's output bytes, spread evenly over the lanes
+    uint8_t* const o = out + sg.stream_off;
+    const uint8_t* const stg = staging + (uint64_t)(sg.etile0 + lsp * kSpan) * kETileBytes;
+    for (uint32_t p = threadIdx.x; p < tot_len; p += kThreads) {
+        uint32_t lo = 0, hi = kThreads;  // last tile whose offset is <= p
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s_off[mid] <= p) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t u = p - s_off[lo];
+        const uint32_t ld = s_lead[lo];
+        const uint32_t rm = s_rem[lo];
+        uint8_t byte;
+        if (u < ld) {
+            byte = 255;
+        } else if (rm && u == ld) {
+            byte = (uint8_t)rm;
+        } else {
+            const uint32_t w = u - ld - (rm ? 1u : 0u);
+            byte = (w < s_kint[lo]) ? stg[(uint64_t)lo * kETileBytes + w] : s_fin[lo];
+        }
+        const uint32_t dst = s_dst[lo] + u;
+        if (dst < B) o[dst] = byte;
     }
 }
 
 // ---------------------------------------------------------------------------
 // decompress kernels
 
-__global__ __launch_bounds__(kThreads) void k_fill_reset(float* __restrict__ y, uint64_t n,
-                                                         uint64_t* __restrict__ flags, uint64_t nflags,
-                                                         uint32_t* __restrict__ ctrl, int* __restrict__ status) {
-    const uint64_t n4 = n >> 2;
+// Zero fill of y (when fill != 0), decoder state reset, and the list of
+// stream chunks: tensor i has max(1, ceil(min(L_i, B_i) / kChunk)) chunks,
+// numbered dec_first[i] ...; chunk r belongs to tensor dec_map[r].
+__global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restrict__ y, uint64_t n_fill,
+                                                   const uint64_t* __restrict__ in_lens,
+                                                   uint64_t* __restrict__ flags, uint64_t nflags,
+                                                   uint32_t* __restrict__ dec_map, uint32_t* __restrict__ dec_first,
+                                                   uint32_t* __restrict__ ctrl, int* __restrict__ status) {
+    __shared__ uint32_t s_u[kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint64_t n4 = n_fill >> 2;
     float4* y4 = reinterpret_cast<float4*>(y);
     const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (uint64_t i = tid; i < n4; i += stride) y4[i] = z;
-    if (tid < (n & 3)) y[(n4 << 2) + tid] = 0.0f;
+    if (tid < (n_fill & 3)) y[(n4 << 2) + tid] = 0.0f;
     for (uint64_t i = tid; i < nflags; i += stride) flags[i] = 0;
-    if (tid == 0) {
-        ctrl[1] = 0;
-        *status = TLC_OK;
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void k_reset(uint64_t* __restrict__ flags, uint64_t nflags,
-                                                    uint32_t* __restrict__ ctrl, int* __restrict__ status) {
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (uint64_t i = tid; i < nflags; i += stride) flags[i] = 0;
-    if (tid == 0) {
-        ctrl[1] = 0;
-        *status = TLC_OK;
+    if (blockIdx.x == 0) {
+        uint32_t carry = 0;
+        for (uint32_t base = 0; base < g.count; base += kThreads) {
+            const uint32_t gi = base + threadIdx.x;
+            uint32_t rc = 0;
+            if (gi < g.count) {
+                const Seg sg = load_seg(g, gi);
+                const uint64_t L = min(in_lens[gi], (uint64_t)quartic_len(sg.n));
+                rc = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
+            }
+            uint32_t tot;
+            const uint32_t first = carry + block_excl_sum(rc, s_u, &tot);
+            if (gi < g.count) {
+                dec_first[gi] = first;
+                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = gi;
+            }
+            carry += tot;
+        }
+        if (threadIdx.x == 0) {
+            ctrl[2] = 0;      // decoder tickets
+            ctrl[3] = carry;  // decoder chunks
+            *status = TLC_OK;
+        }
     }
 }
 
@@ -635,52 +801,62 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                                                      const uint64_t* __restrict__ in_lens,
                                                      const float* __restrict__ scales, float s,
                                                      float* __restrict__ y, uint64_t* __restrict__ flags,
+                                                     const uint32_t* __restrict__ dec_map,
+                                                     const uint32_t* __restrict__ dec_first,
                                                      uint32_t* __restrict__ ctrl, int* __restrict__ status,
                                                      int accumulate) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_chunk, s_ok;
     __shared__ uint64_t s_base;
 
-    if (threadIdx.x == 0) s_chunk = atomicAdd(ctrl + 1, 1u);
+    if (blockIdx.x >= ctrl[3]) return;  // the grid is sized for the largest possible streams
+    if (threadIdx.x == 0) s_chunk = atomicAdd(ctrl + 2, 1u);
     __syncthreads();
     const uint32_t c = s_chunk;
-    const uint32_t si = chunk_segment(g, c);
-    const Seg sg = load_seg(g, si);
-    const uint32_t lc = c - sg.chunk0;
-    const uint32_t n = (uint32_t)sg.n;
-    const uint64_t B = ((uint64_t)n + 4u) / 5u;
-    uint64_t L = in_lens[si];
+    const uint32_t gi = dec_map[c];
+    const uint32_t c0 = dec_first[gi];
+    const uint32_t lc = c - c0;
+    const Seg sg = load_seg(g, gi);
+    const uint32_t n = sg.n;
+    const uint64_t B = quartic_len(n);
+    uint64_t L = in_lens[gi];
     if (L > B) {
         if (lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
         L = B;
     }
     const uint64_t start = (uint64_t)lc * kChunk;
     if (start >= L) {
-        // past the end of this stream (or an empty stream, which is corrupt
-        // because ceil(n/5) >= 1); later chunks of the tensor exit here too,
-        // so nothing waits for this block
-        if (lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
+        // only an empty stream gets here (chunk 0 of a tensor with L == 0),
+        // which is corrupt because ceil(n/5) >= 1
+        if (threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
         return;
     }
     const uint32_t cnt = (uint32_t)min((uint64_t)kChunk, L - start);
     const uint8_t* p = in + sg.stream_off + start;
-    const uint32_t off = 16u * threadIdx.x;
-    const uint32_t nv = cnt > off ? min(16u, cnt - off) : 0u;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (nv == 16 && ((reinterpret_cast<uintptr_t>(p + off) & 15) == 0)) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p + off);
-        w[0] = v.x;
-        w[1] = v.y;
-        w[2] = v.z;
-        w[3] = v.w;
+    const uint32_t off = 64u * threadIdx.x;
+    const uint32_t nv = cnt > off ? min(64u, cnt - off) : 0u;
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0;
+    if (nv == 64 && ((reinterpret_cast<uintptr_t>(p + off) & 15) == 0)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = reinterpret_cast<const uint4*>(p + off)[q];
+            w[4 * q] = v.x;
+            w[4 * q + 1] = v.y;
+            w[4 * q + 2] = v.z;
+            w[4 * q + 3] = v.w;
+        }
     } else {
         for (uint32_t i = 0; i < nv; ++i) w[i >> 2] |= (uint32_t)p[off + i] << (8 * (i & 3));
     }
-    uint32_t tsum = 0;
+    uint32_t tsum = 0, nlit = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < 16; ++i) {
+    for (uint32_t i = 0; i < 64; ++i) {
         const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 255u;
-        tsum += (i < nv) ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
+        const bool inr = i < nv;
+        tsum += inr ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
+        nlit += (inr && byte < 243u && byte != kZero) ? 1u : 0u;
     }
     uint32_t csum;
     const uint32_t texcl = block_excl_sum(tsum, s_u, &csum);
@@ -692,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             if (threadIdx.x == 0) publish(flags, c, kPrefix, csum);
         } else {
             if (threadIdx.x == 0) publish(flags, c, kAggregate, csum);
-            ok = look_back(flags, c, sg.chunk0, 0, SumCompose(), &base) ? 1u : 0u;
+            ok = look_back(flags, c, c0, 0, SumCompose(), &base) ? 1u : 0u;
             if (threadIdx.x == 0) publish(flags, c, ok ? kPrefix : kPoison, base + csum);
         }
         if (threadIdx.x == 0) {
@@ -706,44 +882,46 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
         return;
     }
     const uint64_t base = s_base;
-    const float ms = scales[si] * s;
-    float* const yy = y + sg.elem_off;
-    uint64_t pos = base + texcl;
-    bool bad = false;
-    for (uint32_t i = 0; i < nv; ++i) {
-        const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 255u;
-        if (byte < 243u) {
-            if (pos >= B) {
-                bad = true;
-            } else if (byte != kZero) {
-                uint32_t rest = byte;
+    if (nlit) {
+        const float ms = scales[gi] * s;
+        float* const yy = y + sg.elem_off;
+        uint64_t pos = base + texcl;
+        bool bad = false;
+        for (uint32_t i = 0; i < nv; ++i) {
+            const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 255u;
+            if (byte < 243u) {
+                if (pos >= B) {
+                    bad = true;
+                } else if (byte != kZero) {
+                    uint32_t rest = byte;
 #pragma unroll
-                for (uint32_t d = 0; d < 5; ++d) {
-                    const uint32_t digit = rest % 3u;
-                    rest /= 3u;
-                    const uint64_t e = 5u * pos + d;
-                    if (digit != 1u && e < n) {
-                        const float val = (float)((int)digit - 1) * ms;
-                        yy[e] = accumulate ? yy[e] + val : val;
+                    for (uint32_t d = 0; d < 5; ++d) {
+                        const uint32_t digit = rest % 3u;
+                        rest /= 3u;
+                        const uint64_t e = 5u * pos + d;
+                        if (digit != 1u && e < n) {
+                            const float val = (float)((int)digit - 1) * ms;
+                            yy[e] = accumulate ? yy[e] + val : val;
+                        }
                     }
                 }
+                pos += 1;
+            } else {
+                pos += byte - kRunBase;
             }
-            pos += 1;
-        } else {
-            pos += byte - kRunBase;
         }
+        if (bad) raise_status(status, TLC_ERR_CORRUPT);
     }
-    if (bad) raise_status(status, TLC_ERR_CORRUPT);
     if (threadIdx.x == 0 && start + cnt == L && base + csum != B) raise_status(status, TLC_ERR_CORRUPT);
 }
 
 // ---------------------------------------------------------------------------
-// bandwidth yardstick
+// bandwidth yardstick: one 16-byte load and store per lane, many small blocks
 
 __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ src, float4* __restrict__ dst,
                                                    uint64_t n4) {
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n4) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -781,87 +959,96 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
 
 constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-struct Layout {
-    size_t ctrl, tile_max, enc_flags, seg_thr, seg_ms, dec_flags, total;
+uint64_t ftiles_of(uint64_t total) { return (total + kFTile - 1) / kFTile; }
+uint64_t etiles_host(uint64_t n) { return (n + kETile - 1) / kETile; }
+uint64_t spans_host(uint64_t n) { return (etiles_host(n) + kSpan - 1) / kSpan; }
+uint64_t chunks_host(uint64_t n) { return std::max<uint64_t>(1, ((n + 4) / 5 + kChunk - 1) / kChunk); }
+
+// Sizes of everything a call needs, for one tensor or a group.
+struct Dims {
+    uint64_t count, total, ftiles, etiles, spans, chunks;
 };
 
-Layout ws_layout(uint64_t count, uint64_t tiles, uint64_t chunks) {
+struct Layout {
+    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, active, span_flags, staging, dec_flags, dec_map, dec_first,
+        total;
+};
+
+Layout ws_layout(const Dims& d) {
     Layout l;
     size_t off = 0;
-    l.ctrl = off;
-    off += 256;
-    l.tile_max = off;
-    off = align_up(off + tiles * sizeof(float), 256);
-    l.enc_flags = off;
-    off = align_up(off + tiles * sizeof(uint64_t), 256);
-    l.seg_thr = off;
-    off = align_up(off + count * sizeof(float), 256);
-    l.seg_ms = off;
-    off = align_up(off + count * sizeof(float), 256);
-    l.dec_flags = off;
-    off = align_up(off + chunks * sizeof(uint64_t), 256);
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    l.ctrl = take(256);
+    l.pmax = take((d.ftiles + d.count) * sizeof(float));
+    l.seg_thr = take(d.count * sizeof(float));
+    l.seg_ms = take(d.count * sizeof(float));
+    l.etile_agg = take(d.etiles * sizeof(uint64_t));
+    l.active = take(d.etiles * sizeof(uint64_t));
+    l.span_flags = take(d.spans * sizeof(uint64_t));
+    l.staging = take(d.etiles * kETileBytes);
+    l.dec_flags = take(d.chunks * sizeof(uint64_t));
+    l.dec_map = take(d.chunks * sizeof(uint32_t));
+    l.dec_first = take(d.count * sizeof(uint32_t));
     l.total = off;
     return l;
 }
 
-uint64_t tiles_of(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
-uint64_t chunks_of(uint64_t n) { return ((n + 4) / 5 + kChunk - 1) / kChunk; }
+Dims single_dims(uint64_t n) { return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n)}; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_s(float s) { return s >= 1.0f && s < 2.0f; }  // false for NaN
 
 struct Plan {
     GroupView g;
-    uint64_t count, tiles, chunks, total_elems;
+    Dims d;
 };
 
 Plan single_plan(uint64_t n) {
     Plan p;
-    p.g.segs = nullptr;
-    p.g.tile_seg = nullptr;
-    p.g.chunk_seg = nullptr;
-    p.g.one.elem_off = 0;
-    p.g.one.n = n;
-    p.g.one.stream_off = 0;
-    p.g.one.tile0 = 0;
-    p.g.one.chunk0 = 0;
-    p.count = 1;
-    p.tiles = tiles_of(n);
-    p.chunks = chunks_of(n);
-    p.total_elems = n;
+    memset(&p.g, 0, sizeof(p.g));
+    p.g.count = 1;
+    p.g.one.n = (uint32_t)n;
+    p.d = single_dims(n);
     return p;
 }
 
 struct TableLayout {
-    size_t segs, tile_seg, chunk_seg, total;
+    size_t segs, ftile_info, span_seg, total;
 };
-TableLayout table_layout(uint64_t count, uint64_t tiles, uint64_t chunks) {
+TableLayout table_layout(const Dims& d) {
     TableLayout t;
     t.segs = sizeof(TableHeader);
-    t.tile_seg = align_up(t.segs + count * sizeof(Seg), 16);
-    t.chunk_seg = align_up(t.tile_seg + tiles * sizeof(uint32_t), 16);
-    t.total = align_up(t.chunk_seg + chunks * sizeof(uint32_t), 16);
+    t.ftile_info = align_up(t.segs + d.count * sizeof(Seg), 16);
+    t.span_seg = align_up(t.ftile_info + d.ftiles * sizeof(uint32_t), 16);
+    t.total = align_up(t.span_seg + d.spans * sizeof(uint32_t), 16);
     return t;
 }
 
+Dims dims_of(const tlc_group_info* info) {
+    return {info->count, info->total_elems, ftiles_of(info->total_elems), info->tiles, info->spans, info->chunks};
+}
+
 int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
-    if (!info || !d_table || !aligned16(d_table) || info->count == 0) return TLC_ERR_INVALID_ARG;
-    const TableLayout t = table_layout(info->count, info->tiles, info->chunks);
-    if (t.total != info->table_bytes) return TLC_ERR_INVALID_ARG;
+    if (!info || !d_table || !aligned16(d_table) || info->count == 0 || info->count > 0xFFFFFFFFull)
+        return TLC_ERR_INVALID_ARG;
+    p->d = dims_of(info);
+    const TableLayout t = table_layout(p->d);
+    if (t.total != info->table_bytes || ws_layout(p->d).total != info->workspace_bytes) return TLC_ERR_INVALID_ARG;
     const char* base = static_cast<const char*>(d_table);
+    memset(&p->g, 0, sizeof(p->g));
     p->g.segs = reinterpret_cast<const Seg*>(base + t.segs);
-    p->g.tile_seg = reinterpret_cast<const uint32_t*>(base + t.tile_seg);
-    p->g.chunk_seg = reinterpret_cast<const uint32_t*>(base + t.chunk_seg);
-    memset(&p->g.one, 0, sizeof(Seg));
-    p->count = info->count;
-    p->tiles = info->tiles;
-    p->chunks = info->chunks;
-    p->total_elems = info->total_elems;
+    p->g.ftile_info = reinterpret_cast<const uint32_t*>(base + t.ftile_info);
+    p->g.span_seg = reinterpret_cast<const uint32_t*>(base + t.span_seg);
+    p->g.count = (uint32_t)info->count;
     return TLC_OK;
 }
 
 int check_ws(const Plan& p, void* ws, size_t ws_bytes, Layout* l) {
-    *l = ws_layout(p.count, p.tiles, p.chunks);
+    *l = ws_layout(p.d);
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < l->total) return TLC_ERR_WORKSPACE;
     return TLC_OK;
 }
@@ -875,22 +1062,31 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     if (rc) return rc;
     char* w = static_cast<char*>(ws);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
-    float* tile_max = reinterpret_cast<float*>(w + l.tile_max);
-    uint64_t* flags = reinterpret_cast<uint64_t*>(w + l.enc_flags);
+    float* pmax = reinterpret_cast<float*>(w + l.pmax);
     float* thr = reinterpret_cast<float*>(w + l.seg_thr);
     float* ms = reinterpret_cast<float*>(w + l.seg_ms);
+    uint64_t* etile_agg = reinterpret_cast<uint64_t*>(w + l.etile_agg);
+    uint64_t* active = reinterpret_cast<uint64_t*>(w + l.active);
+    uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
+    uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
     const GroupView g = p.g;
-    const uint32_t tiles = (uint32_t)p.tiles, count = (uint32_t)p.count;
+    const uint64_t N = p.d.total;
+    const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
+    const uint32_t pack_grid = (uint32_t)std::min<uint64_t>(p.d.etiles, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<tiles, kThreads, 0, st>>>(g, x, err, tile_max, flags, ctrl, status);
+        k_accum_max<<<ftiles, kThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, ctrl, status);
     });
     if (rc) return rc;
     rc = launch("tlc_seg_scale", st, [&] {
-        k_seg_scale<<<count, kThreads, 0, st>>>(g, s, tile_max, scales, thr, ms);
+        k_seg_scale<<<count, kThreads, 0, st>>>(g, s, pmax, scales, thr, ms, etile_agg, active, ctrl);
     });
     if (rc) return rc;
-    return launch("tlc_encode", st, [&] {
-        k_encode<<<tiles, kThreads, 0, st>>>(g, err, tile_max, thr, ms, flags, ctrl, out, out_lens, status);
+    rc = launch("tlc_quant_pack", st, [&] {
+        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(g, err, thr, ms, active, ctrl, etile_agg, staging);
+    });
+    if (rc) return rc;
+    return launch("tlc_emit", st, [&] {
+        k_emit<<<spans, kThreads, 0, st>>>(g, etile_agg, staging, span_flags, ctrl, out, out_lens, status);
     });
 }
 
@@ -904,25 +1100,22 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     char* w = static_cast<char*>(ws);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
     uint64_t* flags = reinterpret_cast<uint64_t*>(w + l.dec_flags);
+    uint32_t* dec_map = reinterpret_cast<uint32_t*>(w + l.dec_map);
+    uint32_t* dec_first = reinterpret_cast<uint32_t*>(w + l.dec_first);
     const GroupView g = p.g;
-    const uint64_t chunks = p.chunks;
-    if (accumulate) {
-        const uint32_t grid = (uint32_t)std::min<uint64_t>(1024, (chunks + kThreads - 1) / kThreads + 1);
-        rc = launch("tlc_reset", st, [&] { k_reset<<<grid, kThreads, 0, st>>>(flags, chunks, ctrl, status); });
-    } else {
-        const uint64_t n4 = p.total_elems >> 2;
-        uint64_t blocks = (n4 + kThreads * 8 - 1) / (kThreads * 8);
-        blocks = std::max<uint64_t>(blocks, (chunks + kThreads - 1) / kThreads);
-        blocks = std::max<uint64_t>(blocks, 1);
-        const uint32_t grid = (uint32_t)std::min<uint64_t>(blocks, 1u << 20);
-        rc = launch("tlc_fill_reset", st, [&] {
-            k_fill_reset<<<grid, kThreads, 0, st>>>(y, p.total_elems, flags, chunks, ctrl, status);
-        });
-    }
+    const uint64_t chunks = p.d.chunks;
+    const uint64_t n_fill = accumulate ? 0 : p.d.total;
+    uint64_t blocks = std::max<uint64_t>((n_fill / 4 + kThreads * 8 - 1) / (kThreads * 8),
+                                         (chunks + kThreads - 1) / kThreads);
+    blocks = std::max<uint64_t>(blocks, 1);
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(blocks, 1u << 20);
+    rc = launch(accumulate ? "tlc_prep" : "tlc_prep_fill", st, [&] {
+        k_prep<<<grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, dec_map, dec_first, ctrl, status);
+    });
     if (rc) return rc;
     return launch("tlc_decode", st, [&] {
-        k_decode<<<(uint32_t)chunks, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, flags, ctrl, status,
-                                                         accumulate);
+        k_decode<<<(uint32_t)chunks, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, flags, dec_map, dec_first,
+                                                         ctrl, status, accumulate);
     });
 }
 
@@ -946,13 +1139,13 @@ const char* tlc_status_string(int code) {
     }
 }
 
-const char* tlc_version(void) { return "tlc-gfx950 0.1"; }
+const char* tlc_version(void) { return "tlc-gfx950 0.2"; }
 
 uint64_t tlc_compress_bound(uint64_t n) { return (n + 4) / 5; }
 
 size_t tlc_workspace_size(uint64_t n) {
     if (n == 0 || n > kMaxN) return 0;
-    return ws_layout(1, tiles_of(n), chunks_of(n)).total;
+    return ws_layout(single_dims(n)).total;
 }
 
 int tlc_compress(const float* x, float* err, uint64_t n, float s, uint8_t* out, uint64_t out_capacity,
@@ -981,34 +1174,41 @@ int tlc_decompress_accumulate(const uint8_t* in, const uint64_t* in_len, const f
 
 int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, void* table,
                    size_t table_capacity, uint64_t* stream_offset) {
-    if (!sizes || !info || count == 0 || count > 0xFFFFFFFFull) return TLC_ERR_INVALID_ARG;
-    uint64_t tiles = 0, chunks = 0, elems = 0, stream = 0;
+    if (!sizes || !info || count == 0 || count > 0x7FFFFFFFull) return TLC_ERR_INVALID_ARG;
+    Dims d = {count, 0, 0, 0, 0, 0};
+    uint64_t stream = 0;
     for (uint64_t i = 0; i < count; ++i) {
         const uint64_t n = sizes[i];
         if (n == 0 || n > kMaxN) return TLC_ERR_INVALID_ARG;
-        tiles += tiles_of(n);
-        chunks += chunks_of(n);
-        elems += n;
+        d.total += n;
+        d.etiles += etiles_host(n);
+        d.spans += spans_host(n);
+        d.chunks += chunks_host(n);
         stream = align_up(stream, 16) + tlc_compress_bound(n);
     }
-    if (tiles > 0xFFFFFFFFull || chunks > 0xFFFFFFFFull) return TLC_ERR_INVALID_ARG;
-    const TableLayout t = table_layout(count, tiles, chunks);
+    d.ftiles = ftiles_of(d.total);
+    if (d.ftiles + d.count > 0xFFFFFFFFull || d.etiles > 0xFFFFFFFFull || d.chunks > 0xFFFFFFFFull)
+        return TLC_ERR_INVALID_ARG;
+    const TableLayout t = table_layout(d);
     info->count = count;
-    info->total_elems = elems;
+    info->total_elems = d.total;
     info->stream_bytes = align_up(stream, 16);
     info->table_bytes = t.total;
-    info->workspace_bytes = ws_layout(count, tiles, chunks).total;
-    info->tiles = tiles;
-    info->chunks = chunks;
+    info->workspace_bytes = ws_layout(d).total;
+    info->tiles = d.etiles;
+    info->chunks = d.chunks;
+    info->spans = d.spans;
     if (!table && !stream_offset) return TLC_OK;
     if (table && table_capacity < t.total) return TLC_ERR_CAPACITY;
     char* base = static_cast<char*>(table);
+    uint32_t* ftile_info = table ? reinterpret_cast<uint32_t*>(base + t.ftile_info) : nullptr;
+    uint32_t* span_seg = table ? reinterpret_cast<uint32_t*>(base + t.span_seg) : nullptr;
     if (table) {
         memset(base, 0, t.total);
-        TableHeader h = {kMagic, count, tiles, chunks, elems, info->stream_bytes, 0, 0};
+        TableHeader h = {kMagic, count, d.ftiles, d.etiles, d.spans, d.chunks, d.total, info->stream_bytes};
         memcpy(base, &h, sizeof(h));
     }
-    uint64_t tile = 0, chunk = 0, eoff = 0, soff = 0;
+    uint64_t etile = 0, span = 0, chunk = 0, eoff = 0, soff = 0, ft = 0;
     for (uint64_t i = 0; i < count; ++i) {
         const uint64_t n = sizes[i];
         soff = align_up(soff, 16);
@@ -1016,18 +1216,23 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
         if (table) {
             Seg sg;
             sg.elem_off = eoff;
-            sg.n = n;
+            sg.n = (uint32_t)n;
+            sg.etile0 = (uint32_t)etile;
             sg.stream_off = soff;
-            sg.tile0 = (uint32_t)tile;
+            sg.span0 = (uint32_t)span;
             sg.chunk0 = (uint32_t)chunk;
             memcpy(base + t.segs + i * sizeof(Seg), &sg, sizeof(Seg));
-            uint32_t* ts = reinterpret_cast<uint32_t*>(base + t.tile_seg);
-            uint32_t* cs = reinterpret_cast<uint32_t*>(base + t.chunk_seg);
-            for (uint64_t k = 0; k < tiles_of(n); ++k) ts[tile + k] = (uint32_t)i;
-            for (uint64_t k = 0; k < chunks_of(n); ++k) cs[chunk + k] = (uint32_t)i;
+            for (uint64_t k = 0; k < spans_host(n); ++k) span_seg[span + k] = (uint32_t)i;
+            // flat tiles whose first element lies in this tensor
+            const uint64_t end = eoff + n;
+            for (; ft < d.ftiles && ft * kFTile < end; ++ft) {
+                const uint64_t last = std::min<uint64_t>(d.total, (ft + 1) * kFTile) - 1;
+                ftile_info[ft] = (uint32_t)i | (last >= end ? kStraddle : 0u);
+            }
         }
-        tile += tiles_of(n);
-        chunk += chunks_of(n);
+        etile += etiles_host(n);
+        span += spans_host(n);
+        chunk += chunks_host(n);
         eoff += n;
         soff += tlc_compress_bound(n);
     }
@@ -1069,9 +1274,11 @@ int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stre
     if (bytes == 0) return TLC_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint64_t n4 = bytes / 16;
-    const uint32_t grid = (uint32_t)std::min<uint64_t>((n4 + kThreads * 8 - 1) / (kThreads * 8), 1u << 20);
+    const uint64_t blocks = (n4 + kThreads - 1) / kThreads;
+    if (blocks > 0xFFFFFFFFull) return TLC_ERR_INVALID_ARG;
     return launch("tlc_copy_probe", st, [&] {
-        k_copy<<<grid, kThreads, 0, st>>>(static_cast<const float4*>(src), static_cast<float4*>(dst), n4);
+        k_copy<<<(uint32_t)blocks, kThreads, 0, st>>>(static_cast<const float4*>(src), static_cast<float4*>(dst),
+                                                       n4);
     });
 }
 

@@ -35,7 +35,7 @@ class GroupInfo(ctypes.Structure):
     _fields_ = [("count", ctypes.c_uint64), ("total_elems", ctypes.c_uint64),
                 ("stream_bytes", ctypes.c_uint64), ("table_bytes", ctypes.c_uint64),
                 ("workspace_bytes", ctypes.c_uint64), ("tiles", ctypes.c_uint64),
-                ("chunks", ctypes.c_uint64)]
+                ("chunks", ctypes.c_uint64), ("spans", ctypes.c_uint64)]
 
 
 class KernelTime(ctypes.Structure):

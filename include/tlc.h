@@ -130,8 +130,9 @@ typedef struct tlc_group_info {
     uint64_t stream_bytes;    /* capacity of the grouped out/in buffer */
     uint64_t table_bytes;     /* bytes of the device table */
     uint64_t workspace_bytes; /* workspace for any grouped call on this group */
-    uint64_t tiles;           /* compress work units (internal) */
-    uint64_t chunks;          /* decompress work units (internal) */
+    uint64_t tiles;           /* internal: encode tiles */
+    uint64_t chunks;          /* internal: decoder chunk slots */
+    uint64_t spans;           /* internal: zero-run emit spans */
 } tlc_group_info;
 
 int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info,

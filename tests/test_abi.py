@@ -45,18 +45,22 @@ def test_workspace_size():
     assert tlc.workspace_size(2 ** 32) == 0
     small, big = tlc.workspace_size(1), tlc.workspace_size(335_000_000)
     assert 0 < small < 4096 and small % 256 == 0
-    assert big < 2_000_000  # a few bytes per 5120-element tile
+    # staging for the zero-run bytes of tiles with nonzero codes (ceil(n/5)) plus a few bytes per tile
+    assert big < 335_000_000 // 5 + 4_000_000
     assert big % 256 == 0
 
 
 def test_group_plan_layout():
-    sizes = [10, 5120, 5121, 1, 33_000, 4 * 5120 * 5]
+    sizes = [10, 5120, 5121, 1, 33_000, 4 * 5120 * 5, 1023, 1025]
     info, table, offs = tlc.group_plan(sizes)
+    N = sum(sizes)
     assert info.count == len(sizes)
-    assert info.total_elems == sum(sizes)
-    tiles = sum(-(-n // 5120) for n in sizes)
-    chunks = sum(-(-(-(-n // 5)) // 4096) for n in sizes)
-    assert info.tiles == tiles and info.chunks == chunks
+    assert info.total_elems == N
+    etiles = sum(-(-n // 5120) for n in sizes)
+    spans = sum(-(-(-(-n // 5120)) // 256) for n in sizes)
+    chunks = sum(max(1, -(-(-(-n // 5)) // 16384)) for n in sizes)
+    ftiles = -(-N // 1024)
+    assert info.tiles == etiles and info.chunks == chunks and info.spans == spans
     assert len(table) == info.table_bytes
     # stream slots: 16-byte aligned, in order, each ceil(n/5) long, inside the buffer
     prev_end = 0
@@ -64,13 +68,26 @@ def test_group_plan_layout():
         assert o % 16 == 0 and o >= prev_end
         prev_end = o + -(-n // 5)
     assert prev_end <= info.stream_bytes
-    # table: header, then per-tensor records (elem_off, n, stream_off, tile0, chunk0)
+    # table: header, per-tensor records, flat-tile info, span owners
     hdr = np.frombuffer(table[:64], dtype=np.uint64)
-    assert hdr[1] == len(sizes) and hdr[2] == tiles and hdr[3] == chunks and hdr[4] == sum(sizes)
-    rec = np.frombuffer(table[64:64 + 32 * len(sizes)], dtype=np.uint64).reshape(-1, 4)
-    assert rec[:, 1].tolist() == sizes
-    assert rec[:, 0].tolist() == np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
-    assert rec[:, 2].tolist() == offs
+    assert hdr[1] == len(sizes) and hdr[2] == ftiles and hdr[3] == etiles and hdr[4] == spans
+    assert hdr[5] == chunks and hdr[6] == N
+    rec_t = np.dtype([("elem_off", "<u8"), ("n", "<u4"), ("etile0", "<u4"), ("stream_off", "<u8"),
+                      ("span0", "<u4"), ("chunk0", "<u4")])
+    rec = np.frombuffer(table[64:64 + 32 * len(sizes)], dtype=rec_t)
+    assert rec["n"].tolist() == sizes
+    starts = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    assert rec["elem_off"].tolist() == starts.tolist()
+    assert rec["stream_off"].tolist() == offs
+    assert rec["etile0"].tolist() == np.concatenate([[0], np.cumsum([-(-n // 5120) for n in sizes])[:-1]]).tolist()
+    # flat tile t: tensor of its first element, high bit if it also holds a later tensor
+    fi_at = -(-(64 + 32 * len(sizes)) // 16) * 16
+    info_arr = np.frombuffer(table[fi_at:fi_at + 4 * ftiles], dtype=np.uint32)
+    seg_of = np.searchsorted(np.cumsum(sizes), np.arange(N), side="right")
+    for t in range(ftiles):
+        first, last = t * 1024, min(N, (t + 1) * 1024) - 1
+        want = int(seg_of[first]) | (0x80000000 if seg_of[last] != seg_of[first] else 0)
+        assert int(info_arr[t]) == want, t
 
 
 def test_group_plan_rejects_bad_sizes():

@@ -219,3 +219,43 @@ def test_corrupt_streams_set_status():
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert np.array_equal(bits(y.cpu().numpy()), bits(oracle.decompress(st, M, n, 1.0)))
+
+
+def test_workspace_reused_across_calls():
+    # stale decoder/encoder state from an earlier call must not leak into the next
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    sizes = [300 * TILE + 5, 17, 9 * TILE]
+    g = tlc.Group(sizes)
+    ws = g.workspace()
+    N = sum(sizes)
+    inputs = [rand(N, 900 + k, zeros=z) for k, z in enumerate((0.0, 0.5, 0.0))]
+    inputs.append((np.zeros(N, np.float32), np.zeros(N, np.float32)))
+    for k, (x, e) in enumerate(inputs + inputs[:2]):
+        say(f"case workspace reuse {k}")
+        xd, ed = to_dev(x), to_dev(e)
+        out, lens, scales, st = g.compress(xd, ed, 1.5, workspace=ws)
+        y, st_d = g.decompress(out, lens, scales, 1.5, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0 and int(st_d.item()) == 0
+        off = 0
+        for t, n in enumerate(sizes):
+            want, M, _ = oracle.compress(x[off:off + n], e[off:off + n], 1.5)
+            L = int(lens[t].item())
+            assert L == want.size
+            assert np.array_equal(out[g.offsets[t]:g.offsets[t] + L].cpu().numpy(), want)
+            assert np.array_equal(bits(y[off:off + n].cpu().numpy()), bits(oracle.decompress(want, M, n, 1.5)))
+            off += n
+
+
+def test_group_of_tiny_tensors():
+    # thousands of 1..7-element tensors: flat tiles of the first pass span
+    # hundreds of tensors each
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(31)
+    sizes = [int(v) for v in rng.integers(1, 8, 3000)] + [2000, 1, 1025, 3]
+    g = tlc.Group(sizes)
+    x, e = rand(sum(sizes), 32)
+    for s in (1.0, 1.9):
+        say(f"case tiny tensors s={s}")
+        check_group(g, x, e, s, label=f"tiny s={s}")
