@@ -4,8 +4,10 @@ One step = one worker's grouped compress of a whole gradient set (error
 accumulation, per-tensor scale, ternary quantization, quartic packing,
 zero-run encoding) followed by the grouped decompress of that payload
 (zero-run decoding, quartic decoding, dequantization).  The error buffer is
-carried from step to step, as in training.  Inputs are generated once on the
-host (seeded, synthetic) and are resident in HBM before timing starts.
+carried from step to step, as in training, and every step sees a different
+gradient set (the generated set rotated by k * 1,000,003 elements).  Inputs
+are generated once on the host (seeded, synthetic) and are resident in HBM
+before timing starts.
 
 Default workload: the BERT-large gradient set (391 tensors, 335,141,888
 fp32 values, 30% exact zeros, the rest N(0, 1e-4)), s = 1.75.
@@ -105,6 +107,7 @@ def main():
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--s", type=float, default=None)
     ap.add_argument("--cpu-passes", type=int, default=2)
+    ap.add_argument("--pool", type=int, default=32, help="distinct gradient sets cycled through (HBM: 4 B/value each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-bandwidth yardstick")
     args = ap.parse_args()
@@ -134,7 +137,13 @@ def main():
           f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     group = tlc.Group(sizes, device=dev)
-    xd = torch.from_numpy(x_host).to(dev)
+    x0 = torch.from_numpy(x_host).to(dev)
+    # A training step sees a fresh gradient: step k compresses the gradient set
+    # rotated by k * 1,000,003 elements (same distribution, different values),
+    # so the error buffer evolves as it does in training.  Repeating one
+    # gradient instead makes the buffer pile up and is not the workload.
+    pool = max(1, min(args.steps + args.warmup, args.pool))
+    xs = [x0] + [torch.roll(x0, shifts=k * 1_000_003) for k in range(1, pool)]
     ed = torch.zeros(N, dtype=torch.float32, device=dev)
     yd = torch.empty(N, dtype=torch.float32, device=dev)
     out = torch.empty(group.stream_bytes, dtype=torch.uint8, device=dev)
@@ -144,11 +153,15 @@ def main():
     st_d = torch.empty(1, dtype=torch.int32, device=dev)
     ws = group.workspace()
 
+    counter = [0]
+
     def step():
+        xd = xs[counter[0] % pool]
+        counter[0] += 1
         group.compress(xd, ed, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st_c)
         group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d)
 
-    # first step from a zero error buffer: kept for the parity check
+    # first step from a zero error buffer on the unrotated set: kept for the parity check
     step()
     torch.cuda.synchronize()
     first = {"out": out.cpu().numpy(), "lens": lens.cpu().numpy(), "scales": scales.cpu().numpy(),
@@ -157,8 +170,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, HIP events around every library kernel on its stream
+    # timed region: K steps; HIP events bracket the dominant kernel on its stream
     tlc.profile_read()
+    tlc.profile_only(DOMINANT)
     tlc.profile_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -171,18 +185,29 @@ def main():
     wall = time.perf_counter() - wall0
     tlc.profile_enable(False)
     kt = tlc.profile_read()
+    last_bits = 8.0 * float(lens.sum().item()) / N
+
+    # per-kernel breakdown: a separate, shorter pass with every kernel bracketed
+    # (events add a small gap around each kernel, so this pass is not the step time)
+    tlc.profile_only(None)
+    tlc.profile_enable(True)
+    for _ in range(min(args.steps, 5)):
+        step()
+    torch.cuda.synchronize()
+    tlc.profile_enable(False)
+    kt_all = tlc.profile_read()
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     if (int(st_c.item()), int(st_d.item())) != (0, 0) or first["status"] != (0, 0):
         raise SystemExit(f"device status not ok: {first['status']} / {(int(st_c.item()), int(st_d.item()))}")
 
-    def per_launch(name):
-        n, ms = kt.get(name, (0, 0.0))
+    def per_launch(name, table):
+        n, ms = table.get(name, (0, 0.0))
         return ms / n if n else 0.0
 
-    comp_ms = sum(per_launch(k) for k in ("tlc_accum_max", "tlc_seg_scale", "tlc_quant_pack", "tlc_emit"))
-    dec_ms = sum(per_launch(k) for k in ("tlc_prep_fill", "tlc_decode"))
-    dom_ms = per_launch(DOMINANT)
+    comp_ms = sum(per_launch(k, kt_all) for k in ("tlc_accum_max", "tlc_seg_scale", "tlc_quant_pack", "tlc_emit"))
+    dec_ms = sum(per_launch(k, kt_all) for k in ("tlc_prep_fill", "tlc_decode"))
+    dom_ms = per_launch(DOMINANT, kt)
     achieved = DOMINANT_BYTES_PER_ELEM * N / (dom_ms * 1e-3) / 1e9 if dom_ms else 0.0
 
     # accumulate of the same payload, 8 times (the 8-worker receive side)
@@ -274,7 +299,8 @@ def main():
         if dec_ms else None,
         "accumulate_ms_per_payload": round(acc_ms, 4),
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
-        "kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kt.items() if v[0]},
+        "bits_per_value_last_step": round(last_bits, 4),
+        "kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "wall_s_timed": round(wall, 3),
         "kernel_source": kernel_source_hash(),
     }

@@ -66,6 +66,7 @@ _SIGS = {
     "tlc_copy_probe": (_I, [_P, _P, _U64, _P]),
     "tlc_profile_enable": (_I, [_I]),
     "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
+    "tlc_profile_only": (_I, [ctypes.c_char_p]),
 }
 
 
@@ -290,6 +291,10 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
 
 def profile_enable(on: bool = True):
     _check(lib().tlc_profile_enable(1 if on else 0), "tlc_profile_enable")
+
+
+def profile_only(kernel_name: str | None):
+    _check(lib().tlc_profile_only(kernel_name.encode() if kernel_name else None), "tlc_profile_only")
 
 
 def profile_read(capacity: int = 32) -> dict[str, tuple[int, float]]:

@@ -181,6 +181,11 @@ typedef struct tlc_kernel_time {
 int tlc_profile_enable(int enable);
 int tlc_profile_read(tlc_kernel_time* out, int capacity, int* count);
 
+/* Restrict the timing above to the kernel of this name (for example
+ * "tlc_accum_max"), so that the events perturb the other kernels of a call
+ * as little as possible; NULL brackets every kernel again.  Host only. */
+int tlc_profile_only(const char* kernel_name);
+
 #ifdef __cplusplus
 }
 #endif
