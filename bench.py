@@ -40,9 +40,15 @@ DOMINANT_BYTES_PER_ELEM = 12
 METRIC = "3LC compress+decompress GB/s (fp32 in) and % of HBM roofline; bits/value"
 
 
-def kernel_source_hash() -> str:
-    with open(os.path.join(ROOT, "gradient_compression_distributed_lc_amd", "csrc", "tlc.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str = "k_accum_max") -> str:
+    """Hash of one kernel's source text (from its signature to the closing
+    brace at column 0), so that counters taken on it stay valid while other
+    kernels change, and are dropped once it changes."""
+    with open(os.path.join(ROOT, "gradient_compression_distributed_lc_amd", "csrc", "tlc.hip")) as f:
+        src = f.read()
+    i = src.index(f"void {kernel}(")
+    j = src.index("\n}\n", i)
+    return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
 
 
 def stored_traffic(workload: str):
@@ -106,7 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--s", type=float, default=None)
-    ap.add_argument("--cpu-passes", type=int, default=2)
+    ap.add_argument("--cpu-passes", type=int, default=8, help="oracle passes over the workload (about 10-15 s)")
     ap.add_argument("--pool", type=int, default=32, help="distinct gradient sets cycled through (HBM: 4 B/value each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-bandwidth yardstick")
