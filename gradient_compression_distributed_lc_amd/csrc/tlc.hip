@@ -385,6 +385,7 @@ __device__ uint32_t find_segment(const Seg* segs, uint32_t lo, uint32_t hi, uint
 __global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, uint64_t N, const float* __restrict__ x,
                                                         float* __restrict__ err, float* __restrict__ pmax,
                                                         uint64_t* __restrict__ span_flags, uint64_t spans,
+                                                        uint32_t* __restrict__ span_tickets,
                                                         uint32_t* __restrict__ ctrl, int* __restrict__ status) {
     __shared__ float sm[kWaves];
     __shared__ uint32_t s_part[kFTile];  // per-tensor maxima of a tile that spans tensors
@@ -438,8 +439,9 @@ __global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, uint64_t N,
     // look-back state of k_emit starts empty on every call
     for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < spans; i += (uint64_t)gridDim.x * kThreads)
         span_flags[i] = 0;
+    for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < g.count; i += (uint64_t)gridDim.x * kThreads)
+        span_tickets[i] = 0;
     if (t == 0 && threadIdx.x == 0) {
-        ctrl[0] = 0;  // k_emit tickets
         ctrl[1] = 0;  // listed encode tiles
         *status = TLC_OK;
     }
@@ -463,16 +465,15 @@ __global__ __launch_bounds__(kScaleThreads) void k_seg_scale(GroupView g, float 
     const Seg sg = load_seg(g, gi);
     const uint64_t tf = sg.elem_off / kFTile, tl = (sg.elem_off + sg.n - 1) / kFTile;
     const float* pm = pmax + gi;
-    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+    float mm[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     uint64_t t = tf + threadIdx.x;
-    for (; t + 3 * kScaleThreads <= tl; t += 4 * kScaleThreads) {  // four independent loads in flight
-        m0 = fmaxf(m0, pm[t]);
-        m1 = fmaxf(m1, pm[t + kScaleThreads]);
-        m2 = fmaxf(m2, pm[t + 2 * kScaleThreads]);
-        m3 = fmaxf(m3, pm[t + 3 * kScaleThreads]);
+    for (; t + 7 * kScaleThreads <= tl; t += 8 * kScaleThreads) {  // eight independent loads in flight
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mm[k] = fmaxf(mm[k], pm[t + k * kScaleThreads]);
     }
-    for (; t <= tl; t += kScaleThreads) m0 = fmaxf(m0, pm[t]);
-    float m = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+    for (; t <= tl; t += kScaleThreads) mm[0] = fmaxf(mm[0], pm[t]);
+    float m = wave_max(fmaxf(fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3])),
+                             fmaxf(fmaxf(mm[4], mm[5]), fmaxf(mm[6], mm[7]))));
     if (lane == 0) sm[w] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -746,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __r
 
 __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* __restrict__ etile_agg,
                                                    const uint8_t* __restrict__ staging,
-                                                   uint64_t* __restrict__ flags, uint32_t* __restrict__ ctrl,
+                                                   uint64_t* __restrict__ flags, uint32_t* __restrict__ tickets,
                                                    uint8_t* __restrict__ out, uint64_t* __restrict__ out_lens,
                                                    int* __restrict__ status) {
     __shared__ uint64_t s_sm[kWaves];
@@ -757,15 +758,21 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     __shared__ uint16_t s_kint[kThreads];     // staged bytes after the lead (and remainder code)
     __shared__ uint8_t s_rem[kThreads];       // remainder code after the 255s, or 0
     __shared__ uint8_t s_fin[kThreads];       // closing remainder code of the tensor's last tile, or 0
+    __shared__ uint32_t s_wpre[kThreads + 1];  // prefix of staged 4-byte words over the span's tiles
     __shared__ uint32_t s_span, s_E, s_r, s_ok;
 
-    if (threadIdx.x == 0) s_span = atomicAdd(ctrl, 1u);
-    __syncthreads();
-    const uint32_t sp = s_span;
-    const uint32_t gi = g.segs ? g.span_seg[sp] : 0u;
+    // Block b belongs to the tensor of span b.  A tensor with several spans
+    // hands them out in ticket order from its own counter, so that the
+    // look-back only ever waits for blocks that already hold a smaller
+    // ticket; a single-span tensor needs no ticket.
+    const uint32_t gi = g.segs ? g.span_seg[blockIdx.x] : 0u;
     const Seg sg = load_seg(g, gi);
     const uint32_t B = quartic_len(sg.n), ne = etiles_of(sg.n);
-    const uint32_t lsp = sp - sg.span0;
+    const uint32_t nsp = (ne + kSpan - 1) / kSpan;
+    if (threadIdx.x == 0) s_span = nsp > 1 ? atomicAdd(tickets + gi, 1u) : 0u;
+    __syncthreads();
+    const uint32_t lsp = s_span;
+    const uint32_t sp = sg.span0 + lsp;
     const uint32_t j = lsp * kSpan + threadIdx.x;  // tensor-relative encode tile
     const bool valid = j < ne;
     const uint32_t nb = valid ? min(kETileBytes, B - j * kETileBytes) : 0u;
@@ -852,9 +859,11 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 
     // The span's tiles are consecutive in one tensor, so its output is the
     // contiguous stream range [D, D + tot_len), D = stream position of tile 0.
-    // Lanes take 16-byte aligned chunks of it: one owner search per chunk,
-    // then the owning tile advances byte by byte; whole chunks are stored with
-    // one 16-byte store, the two partial end chunks byte by byte.
+    // Pass A writes 255 over all of it with aligned 16-byte stores (the two
+    // partial end chunks byte by byte).  Pass B, after a barrier, overwrites
+    // the few other bytes: each tile's remainder code after its leading
+    // 255s, its staged bytes (copied a word at a time, all lanes in
+    // parallel), and the tensor's closing remainder code.
     const uint32_t D = s_dst[0];
     const uint32_t end = min(tot_len, B - min(B, D));  // never past the tensor's slot
     uint8_t* const o = out + sg.stream_off + D;
@@ -863,40 +872,40 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     const uint32_t nchunks = end ? (mis + end + 15) / 16 : 0u;
     for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
         const int64_t p0 = (int64_t)c * 16 - mis;  // span byte of the chunk's first byte
-        const uint32_t pb = (uint32_t)max<int64_t>(p0, 0), pe = (uint32_t)min<int64_t>(p0 + 16, end);
-        uint32_t k = 0, hi2 = kThreads;  // last tile whose offset is <= pb
+        uint8_t* const dst = o + p0;
+        if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(~0u, ~0u, ~0u, ~0u);
+        } else {
+            for (int64_t i = 0; i < 16; ++i)
+                if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = 255;
+        }
+    }
+    // staged words of this lane's tile, and their prefix over the span
+    const uint32_t my_words = (kint + 3) / 4;
+    uint32_t tot_words;
+    const uint32_t wpre = block_excl_sum(my_words, s_u, &tot_words);
+    s_wpre[threadIdx.x] = wpre;
+    if (threadIdx.x == 0) s_wpre[kThreads] = tot_words;
+    __syncthreads();  // pass A done; s_wpre visible
+    {
+        const uint32_t t_off = s_off[threadIdx.x];
+        if (rem && t_off + lead < end) o[t_off + lead] = (uint8_t)rem;
+        if (fin && t_off + len - 1 < end) o[t_off + len - 1] = (uint8_t)fin;
+    }
+    for (uint32_t wv = threadIdx.x; wv < tot_words; wv += kThreads) {
+        uint32_t k = 0, hi2 = kThreads;  // tile owning staged word wv
         while (hi2 - k > 1) {
             const uint32_t mid = (k + hi2) >> 1;
-            if (s_off[mid] <= pb) k = mid;
+            if (s_wpre[mid] <= wv) k = mid;
             else hi2 = mid;
         }
-        uint32_t word[4] = {0, 0, 0, 0};
+        const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
+        const uint32_t val = reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
+        const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
+        const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
 #pragma unroll
-        for (uint32_t i = 0; i < 16; ++i) {
-            const int64_t p = p0 + i;
-            if (p >= (int64_t)pb && p < (int64_t)pe) {
-                while (s_off[k + 1] <= (uint32_t)p) ++k;
-                const uint32_t u = (uint32_t)p - s_off[k];
-                const uint32_t ld = s_lead[k], rm = s_rem[k];
-                uint32_t byte;
-                if (u < ld) {
-                    byte = 255;
-                } else if (rm && u == ld) {
-                    byte = rm;
-                } else {
-                    const uint32_t w = u - ld - (rm ? 1u : 0u);
-                    byte = (w < s_kint[k]) ? stg[(uint64_t)k * kETileBytes + w] : s_fin[k];
-                }
-                word[i >> 2] |= byte << (8 * (i & 3));
-            }
-        }
-        uint8_t* const dst = o + p0;
-        if (pb == p0 && pe == p0 + 16) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(word[0], word[1], word[2], word[3]);
-        } else {
-            for (uint32_t i = 0; i < 16; ++i)
-                if (p0 + i >= pb && p0 + i < pe) dst[i] = (uint8_t)(word[i >> 2] >> (8 * (i & 3)));
-        }
+        for (uint32_t i = 0; i < 4; ++i)
+            if (i < nbw && sbase + i < end) o[sbase + i] = (uint8_t)(val >> (8 * i));
     }
 }
 
@@ -910,7 +919,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
                                                    const uint64_t* __restrict__ in_lens,
                                                    uint64_t* __restrict__ flags, uint64_t nflags,
                                                    uint32_t* __restrict__ dec_map, uint32_t* __restrict__ dec_first,
-                                                   uint32_t* __restrict__ ctrl, int* __restrict__ status) {
+                                                   uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
+                                                   int* __restrict__ status) {
     __shared__ uint32_t s_u[kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -934,12 +944,12 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
             const uint32_t first = carry + block_excl_sum(rc, s_u, &tot);
             if (gi < g.count) {
                 dec_first[gi] = first;
+                tickets[gi] = 0;
                 for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = gi;
             }
             carry += tot;
         }
         if (threadIdx.x == 0) {
-            ctrl[2] = 0;      // decoder tickets
             ctrl[3] = carry;  // decoder chunks
             *status = TLC_OK;
         }
@@ -952,27 +962,29 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                                                      float* __restrict__ y, uint64_t* __restrict__ flags,
                                                      const uint32_t* __restrict__ dec_map,
                                                      const uint32_t* __restrict__ dec_first,
-                                                     uint32_t* __restrict__ ctrl, int* __restrict__ status,
-                                                     int accumulate) {
+                                                     uint32_t* __restrict__ tickets, const uint32_t* __restrict__ ctrl,
+                                                     int* __restrict__ status, int accumulate) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_chunk, s_ok;
     __shared__ uint64_t s_base;
 
     if (blockIdx.x >= ctrl[3]) return;  // the grid is sized for the largest possible streams
-    if (threadIdx.x == 0) s_chunk = atomicAdd(ctrl + 2, 1u);
-    __syncthreads();
-    const uint32_t c = s_chunk;
-    const uint32_t gi = dec_map[c];
+    // Block b belongs to the tensor of chunk b.  A tensor with several chunks
+    // hands them out in ticket order from its own counter, so that the
+    // look-back only ever waits for blocks that already hold a smaller ticket.
+    const uint32_t gi = dec_map[blockIdx.x];
     const uint32_t c0 = dec_first[gi];
-    const uint32_t lc = c - c0;
     const Seg sg = load_seg(g, gi);
     const uint32_t n = sg.n;
     const uint64_t B = quartic_len(n);
-    uint64_t L = in_lens[gi];
-    if (L > B) {
-        if (lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
-        L = B;
-    }
+    const uint64_t L_in = in_lens[gi];
+    const uint64_t L = min(L_in, B);
+    const uint32_t nch = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
+    if (threadIdx.x == 0) s_chunk = nch > 1 ? atomicAdd(tickets + gi, 1u) : 0u;
+    __syncthreads();
+    const uint32_t lc = s_chunk;
+    const uint32_t c = c0 + lc;
+    if (L_in > B && lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
     const uint64_t start = (uint64_t)lc * kChunk;
     if (start >= L) {
         // only an empty stream gets here (chunk 0 of a tensor with L == 0),
@@ -1120,7 +1132,7 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, active, span_flags, staging, dec_flags, dec_map, dec_first,
+    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
         total;
 };
 
@@ -1139,6 +1151,8 @@ Layout ws_layout(const Dims& d) {
     l.etile_agg = take(d.etiles * sizeof(uint64_t));
     l.active = take(d.etiles * sizeof(uint64_t));
     l.span_flags = take(d.spans * sizeof(uint64_t));
+    l.span_tickets = take(d.count * sizeof(uint32_t));
+    l.chunk_tickets = take(d.count * sizeof(uint32_t));
     l.staging = take(d.etiles * kETileBytes);
     l.dec_flags = take(d.chunks * sizeof(uint64_t));
     l.dec_map = take(d.chunks * sizeof(uint32_t));
@@ -1220,13 +1234,15 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     uint64_t* etile_agg = reinterpret_cast<uint64_t*>(w + l.etile_agg);
     uint64_t* active = reinterpret_cast<uint64_t*>(w + l.active);
     uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
+    uint32_t* span_tickets = reinterpret_cast<uint32_t*>(w + l.span_tickets);
     uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
     const GroupView g = p.g;
     const uint64_t N = p.d.total;
     const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<ftiles, kThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, ctrl, status);
+        k_accum_max<<<ftiles, kThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, span_tickets, ctrl,
+                                                 status);
     });
     if (rc) return rc;
     rc = launch("tlc_seg_scale", st, [&] {
@@ -1238,7 +1254,7 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     });
     if (rc) return rc;
     return launch("tlc_emit", st, [&] {
-        k_emit<<<spans, kThreads, 0, st>>>(g, etile_agg, staging, span_flags, ctrl, out, out_lens, status);
+        k_emit<<<spans, kThreads, 0, st>>>(g, etile_agg, staging, span_flags, span_tickets, out, out_lens, status);
     });
 }
 
@@ -1254,6 +1270,7 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     uint64_t* flags = reinterpret_cast<uint64_t*>(w + l.dec_flags);
     uint32_t* dec_map = reinterpret_cast<uint32_t*>(w + l.dec_map);
     uint32_t* dec_first = reinterpret_cast<uint32_t*>(w + l.dec_first);
+    uint32_t* chunk_tickets = reinterpret_cast<uint32_t*>(w + l.chunk_tickets);
     const GroupView g = p.g;
     const uint64_t chunks = p.d.chunks;
     const uint64_t n_fill = accumulate ? 0 : p.d.total;
@@ -1262,12 +1279,13 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     blocks = std::max<uint64_t>(blocks, 1);
     const uint32_t grid = (uint32_t)std::min<uint64_t>(blocks, 1u << 20);
     rc = launch(accumulate ? "tlc_prep" : "tlc_prep_fill", st, [&] {
-        k_prep<<<grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, dec_map, dec_first, ctrl, status);
+        k_prep<<<grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, dec_map, dec_first, chunk_tickets,
+                                          ctrl, status);
     });
     if (rc) return rc;
     return launch("tlc_decode", st, [&] {
         k_decode<<<(uint32_t)chunks, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, flags, dec_map, dec_first,
-                                                         ctrl, status, accumulate);
+                                                         chunk_tickets, ctrl, status, accumulate);
     });
 }
 
