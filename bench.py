@@ -211,7 +211,7 @@ def main():
         n, ms = table.get(name, (0, 0.0))
         return ms / n if n else 0.0
 
-    comp_ms = sum(per_launch(k, kt_all) for k in ("tlc_accum_max", "tlc_seg_scale", "tlc_quant_pack", "tlc_emit"))
+    comp_ms = sum(per_launch(k, kt_all) for k in ("tlc_accum_max", "tlc_tile_max", "tlc_tile_activity", "tlc_quant_pack", "tlc_emit"))
     dec_ms = sum(per_launch(k, kt_all) for k in ("tlc_prep_fill", "tlc_decode"))
     dom_ms = per_launch(DOMINANT, kt)
     achieved = DOMINANT_BYTES_PER_ELEM * N / (dom_ms * 1e-3) / 1e9 if dom_ms else 0.0

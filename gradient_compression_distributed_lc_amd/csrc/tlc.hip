@@ -8,31 +8,36 @@
 // byte, and the reverse path.  The page's implementation is vectorised CPU
 // code; here every step runs in the kernels below, laid out for CDNA4.
 //
-// compress (four launches):
+// compress (five launches):
 //   k_accum_max   the one full HBM pass: v = x + err written back to err, and
 //                 the max |v| of every 1024-element flat tile (256 lanes x one
 //                 16-byte load each: many small blocks keep the most bytes in
 //                 flight).  A tile that spans tensors keeps one partial max per
 //                 tensor, in slot tile + tensor.  12 bytes per element.
-//   k_seg_scale   one block per tensor: M = max of its partial maxima, M*s,
-//                 the exact fp32 selection threshold (select_threshold), and
-//                 the list of encode tiles (5120 elements = 1024 quartic
-//                 bytes) whose partial maxima reach it.  Every other encode
-//                 tile holds only zero codes and is summarised as a run of
-//                 byte 121 without touching err again.
+//   k_tile_max    one thread per encode tile (5120 elements = 1024 quartic
+//                 bytes): the tile's max from the partial maxima under it,
+//                 and every tensor's M through a segmented wave max and one
+//                 atomic per tensor and wave.
+//   k_tile_activity  per tensor M*s and the exact fp32 selection threshold
+//                 (select_threshold); per encode tile, the list of tiles whose
+//                 max reaches it.  Every other tile holds only zero codes and
+//                 is summarised as a run of byte 121 without touching err.
 //   k_quant_pack  one wavefront per listed tile: re-read v only in flat tiles
 //                 whose max reaches the threshold, write err = v - q*M*s where
 //                 q != 0, pack quartic bytes through LDS and zero-run encode
 //                 them from the tile's first literal on into a staging slot
 //                 (wave-level scans, no block barriers).
 //   k_emit        spans of 256 encode tiles: block scan of the tiles' carry
-//                 summaries, decoupled look-back across spans for the span's
-//                 input state, then the span's stream bytes are written
-//                 cooperatively (255 runs, remainder codes, staged bytes).
-// decompress: k_prep (zero fill of y, decoder state, list of stream chunks)
-//             -> k_decode (one block per 16 KiB of stream bytes: expansion
-//             scan + look-back for the quartic byte index, then only literal
-//             bytes are decoded and their nonzero codes written or added).
+//                 summaries, decoupled look-back across the tensor's spans for
+//                 the span's input state, then the span's stream bytes: 255
+//                 runs written densely first, remainder codes and staged
+//                 literal bytes over them.
+// decompress: k_prep (zero fill of y, one 16-byte store per lane; decoder
+//             state; list of stream chunks)
+//             -> k_decode (one block per 2 KiB of stream bytes: expansion
+//             scan + look-back across the tensor's chunks for the quartic
+//             byte index, then only literal bytes are decoded and their
+//             nonzero codes written or added).
 //
 // No matrix-core work exists on this path: it is bound by HBM bandwidth.
 
@@ -386,6 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, uint64_t N,
                                                         float* __restrict__ err, float* __restrict__ pmax,
                                                         uint64_t* __restrict__ span_flags, uint64_t spans,
                                                         uint32_t* __restrict__ span_tickets,
+                                                        uint32_t* __restrict__ mbits,
                                                         uint32_t* __restrict__ ctrl, int* __restrict__ status) {
     __shared__ float sm[kWaves];
     __shared__ uint32_t s_part[kFTile];  // per-tensor maxima of a tile that spans tensors
@@ -439,101 +445,106 @@ __global__ __launch_bounds__(kThreads) void k_accum_max(GroupView g, uint64_t N,
     // look-back state of k_emit starts empty on every call
     for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < spans; i += (uint64_t)gridDim.x * kThreads)
         span_flags[i] = 0;
-    for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < g.count; i += (uint64_t)gridDim.x * kThreads)
+    for (uint64_t i = (uint64_t)t * kThreads + threadIdx.x; i < g.count; i += (uint64_t)gridDim.x * kThreads) {
         span_tickets[i] = 0;
+        mbits[i] = 0;  // M of tensor i, raised by k_tile_max
+    }
     if (t == 0 && threadIdx.x == 0) {
         ctrl[1] = 0;  // listed encode tiles
         *status = TLC_OK;
     }
 }
 
-constexpr int kScaleThreads = 1024;
-constexpr int kActBatch = 8;  // encode tiles per thread per activity batch
+constexpr int kActPerThread = 4;  // encode tiles per thread in k_tile_activity
 
-__global__ __launch_bounds__(kScaleThreads) void k_seg_scale(GroupView g, float s, const float* __restrict__ pmax,
-                                                             float* __restrict__ scales, float* __restrict__ seg_thr,
-                                                             float* __restrict__ seg_ms,
-                                                             uint64_t* __restrict__ etile_agg,
-                                                             uint64_t* __restrict__ active,
-                                                             uint32_t* __restrict__ ctrl) {
-    __shared__ float sm[kScaleThreads / 64];
-    __shared__ uint32_t s_u[kScaleThreads / 64];
-    __shared__ float s_thr;
+__device__ __forceinline__ uint32_t etile_owner(const GroupView& g, uint32_t e) { return g.etile_seg ? g.etile_seg[e] : 0u; }
+
+// max over the flat-tile partial maxima under encode tile j of a tensor
+__device__ __forceinline__ float etile_max(const float* pm, const Seg& sg, uint32_t j) {
+    const uint64_t a = sg.elem_off + (uint64_t)j * kETile;
+    const uint64_t b = sg.elem_off + min((uint64_t)sg.n, (uint64_t)(j + 1) * kETile) - 1;
+    const uint64_t t0 = a / kFTile, t1 = b / kFTile;  // at most 6 flat tiles
+    float mx = 0.0f;
+#pragma unroll
+    for (uint64_t k = 0; k < 6; ++k)
+        if (t0 + k <= t1) mx = fmaxf(mx, pm[t0 + k]);
+    return mx;
+}
+
+// One thread per encode tile of the group: the tile's maximum |x+err| from
+// the flat-tile partial maxima under it, and every tensor's M as the max over
+// its tiles.  Tiles of one tensor are contiguous, so a segmented max over the
+// wave leaves one atomic per tensor and wave; M (zeroed by k_accum_max) is
+// kept as float bits, whose unsigned order is that of non-negative floats.
+__global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t etiles, const float* __restrict__ pmax,
+                                                       float* __restrict__ etmax, uint32_t* __restrict__ mbits) {
+    const uint32_t e = blockIdx.x * kThreads + threadIdx.x;
+    const int lane = lane_id();
+    const bool ok = e < etiles;
+    const uint32_t gi = ok ? etile_owner(g, e) : 0xFFFFFFFFu;
+    float mx = 0.0f;
+    if (ok) {
+        const Seg sg = load_seg(g, gi);
+        mx = etile_max(pmax + gi, sg, e - sg.etile0);  // flat tile t of tensor gi: slot t + gi
+        etmax[e] = mx;
+    }
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(mx, d, 64);
+        const uint32_t og = __shfl_up(gi, d, 64);
+        if (lane >= d && og == gi) mx = fmaxf(mx, o);
+    }
+    const uint32_t next = __shfl_down(gi, 1, 64);
+    if (ok && (lane == 63 || next != gi)) atomicMax(mbits + gi, __float_as_uint(mx));
+}
+
+// Per tensor: s*M and the quantisation threshold (written by the thread of
+// its first encode tile).  Per encode tile: a tile whose maximum reaches the
+// threshold can hold nonzero codes and is listed for k_quant_pack; any other
+// holds only zero codes and is summarised here as a run of byte 121.
+__global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_t etiles, float s,
+                                                            const float* __restrict__ etmax,
+                                                            const float* __restrict__ scales,
+                                                            float* __restrict__ seg_thr, float* __restrict__ seg_ms,
+                                                            uint64_t* __restrict__ etile_agg,
+                                                            uint64_t* __restrict__ active, uint32_t* __restrict__ ctrl) {
+    __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_base;
-    const uint32_t gi = blockIdx.x;
-    const int lane = lane_id(), w = wave_id();
-    const Seg sg = load_seg(g, gi);
-    const uint64_t tf = sg.elem_off / kFTile, tl = (sg.elem_off + sg.n - 1) / kFTile;
-    const float* pm = pmax + gi;
-    float mm[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    uint64_t t = tf + threadIdx.x;
-    for (; t + 7 * kScaleThreads <= tl; t += 8 * kScaleThreads) {  // eight independent loads in flight
+    const uint32_t base = blockIdx.x * (kThreads * kActPerThread);
+    uint32_t mask = 0, own[kActPerThread];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) mm[k] = fmaxf(mm[k], pm[t + k * kScaleThreads]);
-    }
-    for (; t <= tl; t += kScaleThreads) mm[0] = fmaxf(mm[0], pm[t]);
-    float m = wave_max(fmaxf(fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3])),
-                             fmaxf(fmaxf(mm[4], mm[5]), fmaxf(mm[6], mm[7]))));
-    if (lane == 0) sm[w] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int i = 0; i < kScaleThreads / 64; ++i) m = fmaxf(m, sm[i]);
-        const float ms = m * s;
-        const float thr = select_threshold(m, ms);
-        scales[gi] = m;
-        seg_ms[gi] = ms;
-        seg_thr[gi] = thr;
-        s_thr = thr;
-    }
-    __syncthreads();
-    const float thr = s_thr;
-
-    // Encode tiles whose partial maxima reach the threshold can hold nonzero
-    // codes: list them for k_quant_pack.  The others hold only zero codes
-    // and are summarised here as runs of byte 121.
-    const uint32_t B = quartic_len(sg.n), ne = etiles_of(sg.n);
-    for (uint32_t base = 0; base < ne; base += kScaleThreads * kActBatch) {
-        uint32_t mask = 0;
-#pragma unroll
-        for (int r = 0; r < kActBatch; ++r) {
-            const uint32_t j = base + r * kScaleThreads + threadIdx.x;
-            if (j < ne) {
-                const uint64_t a = sg.elem_off + (uint64_t)j * kETile;
-                const uint64_t b = sg.elem_off + min((uint64_t)sg.n, (uint64_t)(j + 1) * kETile) - 1;
-                const uint64_t t0 = a / kFTile, t1 = b / kFTile;  // at most 6 flat tiles
-                float mx = 0.0f;
-#pragma unroll
-                for (uint64_t k = 0; k < 6; ++k)
-                    if (t0 + k <= t1) mx = fmaxf(mx, pm[t0 + k]);
-                if (mx >= thr) mask |= 1u << r;
-                else etile_agg[sg.etile0 + j] = carry_pack(carry_run(min(kETileBytes, B - j * kETileBytes)));
+    for (int r = 0; r < kActPerThread; ++r) {
+        const uint32_t e = base + r * kThreads + threadIdx.x;
+        own[r] = 0;
+        if (e < etiles) {
+            const uint32_t gi = etile_owner(g, e);
+            const Seg sg = load_seg(g, gi);
+            const float m = scales[gi];
+            const float ms = m * s;
+            const float thr = select_threshold(m, ms);
+            const uint32_t j = e - sg.etile0;
+            if (j == 0) {
+                seg_ms[gi] = ms;
+                seg_thr[gi] = thr;
+            }
+            own[r] = gi;
+            if (etmax[e] >= thr) {
+                mask |= 1u << r;
+            } else {
+                const uint32_t B = quartic_len(sg.n);
+                etile_agg[e] = carry_pack(carry_run(min(kETileBytes, B - j * kETileBytes)));
             }
         }
-        // compaction: one atomic per block and batch
-        const uint32_t cnt = __popc(mask);
-        uint32_t inc = cnt;
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(inc, d, 64);
-            if (lane >= d) inc += o;
-        }
-        if (lane == 63) s_u[w] = inc;
-        __syncthreads();
-        uint32_t before = 0, total = 0;
-        for (int i = 0; i < kScaleThreads / 64; ++i) {
-            before += (i < w) ? s_u[i] : 0u;
-            total += s_u[i];
-        }
-        if (total) {
-            if (threadIdx.x == 0) s_base = atomicAdd(ctrl + 1, total);
-            __syncthreads();
-            uint32_t pos = s_base + before + inc - cnt;
-#pragma unroll
-            for (int r = 0; r < kActBatch; ++r)
-                if (mask & (1u << r))
-                    active[pos++] = ((uint64_t)gi << 32) | (sg.etile0 + base + r * kScaleThreads + threadIdx.x);
-        }
-        __syncthreads();  // s_u and s_base are reused by the next batch
     }
+    // compaction: one atomic per block
+    uint32_t tot;
+    const uint32_t before = block_excl_sum(__popc(mask), s_u, &tot);
+    if (tot == 0) return;
+    if (threadIdx.x == 0) s_base = atomicAdd(ctrl + 1, tot);
+    __syncthreads();
+    uint32_t pos = s_base + before;
+#pragma unroll
+    for (int r = 0; r < kActPerThread; ++r)
+        if (mask & (1u << r)) active[pos++] = ((uint64_t)own[r] << 32) | (base + r * kThreads + threadIdx.x);
 }
 
 // LDS writes of one lane visible to the other lanes of its wave
@@ -1162,7 +1173,7 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
+    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, etmax, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
         total;
 };
 
@@ -1179,6 +1190,7 @@ Layout ws_layout(const Dims& d) {
     l.seg_thr = take(d.count * sizeof(float));
     l.seg_ms = take(d.count * sizeof(float));
     l.etile_agg = take(d.etiles * sizeof(uint64_t));
+    l.etmax = take(d.etiles * sizeof(float));
     l.active = take(d.etiles * sizeof(uint64_t));
     l.span_flags = take(d.spans * sizeof(uint64_t));
     l.span_tickets = take(d.count * sizeof(uint32_t));
@@ -1262,6 +1274,7 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     float* thr = reinterpret_cast<float*>(w + l.seg_thr);
     float* ms = reinterpret_cast<float*>(w + l.seg_ms);
     uint64_t* etile_agg = reinterpret_cast<uint64_t*>(w + l.etile_agg);
+    float* etmax = reinterpret_cast<float*>(w + l.etmax);
     uint64_t* active = reinterpret_cast<uint64_t*>(w + l.active);
     uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
     uint32_t* span_tickets = reinterpret_cast<uint32_t*>(w + l.span_tickets);
@@ -1271,12 +1284,20 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<ftiles, kThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, span_tickets, ctrl,
-                                                 status);
+        k_accum_max<<<ftiles, kThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, span_tickets,
+                                                 reinterpret_cast<uint32_t*>(scales), ctrl, status);
     });
     if (rc) return rc;
-    rc = launch("tlc_seg_scale", st, [&] {
-        k_seg_scale<<<count, kScaleThreads, 0, st>>>(g, s, pmax, scales, thr, ms, etile_agg, active, ctrl);
+    const uint32_t etiles = (uint32_t)p.d.etiles;
+    rc = launch("tlc_tile_max", st, [&] {
+        k_tile_max<<<(etiles + kThreads - 1) / kThreads, kThreads, 0, st>>>(g, etiles, pmax, etmax,
+                                                                           reinterpret_cast<uint32_t*>(scales));
+    });
+    if (rc) return rc;
+    rc = launch("tlc_tile_activity", st, [&] {
+        constexpr uint32_t per_block = kThreads * kActPerThread;
+        k_tile_activity<<<(etiles + per_block - 1) / per_block, kThreads, 0, st>>>(g, etiles, s, etmax, scales, thr, ms,
+                                                                                 etile_agg, active, ctrl);
     });
     if (rc) return rc;
     rc = launch("tlc_quant_pack", st, [&] {
@@ -1304,8 +1325,10 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     const GroupView g = p.g;
     const uint64_t chunks = p.d.chunks;
     const uint64_t n_fill = accumulate ? 0 : p.d.total;
-    uint64_t blocks = std::max<uint64_t>((n_fill / 4 + kThreads * 8 - 1) / (kThreads * 8),
-                                         (chunks + kThreads - 1) / kThreads);
+    // one float4 of the fill per thread: a grid of many short blocks is the
+    // fastest fill measured on MI355X (~6.9 TB/s against ~5.7 TB/s with eight
+    // stores per thread in a grid-stride loop)
+    uint64_t blocks = std::max<uint64_t>((n_fill / 4 + kThreads - 1) / kThreads, (chunks + kThreads - 1) / kThreads);
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
     rc = launch(accumulate ? "tlc_prep" : "tlc_prep_fill", st, [&] {
         k_prep<<<prep_grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, dec_map, dec_first, chunk_tickets,
