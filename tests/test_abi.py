@@ -45,8 +45,10 @@ def test_workspace_size():
     assert tlc.workspace_size(2 ** 32) == 0
     small, big = tlc.workspace_size(1), tlc.workspace_size(335_000_000)
     assert 0 < small <= 8192 and small % 256 == 0
-    # staging for the zero-run bytes of tiles with nonzero codes (ceil(n/5)) plus a few bytes per tile
-    assert big < 335_000_000 // 5 + 4_000_000
+    # staging for the zero-run bytes of tiles with nonzero codes (ceil(n/5)), one partial max per
+    # 512-element flat tile, a few words per 5120-element encode tile, and small per-call state
+    n = 335_000_000
+    assert big < n // 5 + 4 * (n // 512) + 32 * (n // 5120) + 1_000_000
     assert big % 256 == 0
 
 
@@ -59,7 +61,7 @@ def test_group_plan_layout():
     etiles = sum(-(-n // 5120) for n in sizes)
     spans = sum(-(-(-(-n // 5120)) // 256) for n in sizes)
     chunks = sum(max(1, -(-(-(-n // 5)) // 2048)) for n in sizes)
-    ftiles = -(-N // 1024)
+    ftiles = -(-N // 512)
     assert info.tiles == etiles and info.chunks == chunks and info.spans == spans
     assert len(table) == info.table_bytes
     # stream slots: 16-byte aligned, in order, each ceil(n/5) long, inside the buffer
@@ -85,7 +87,7 @@ def test_group_plan_layout():
     info_arr = np.frombuffer(table[fi_at:fi_at + 4 * ftiles], dtype=np.uint32)
     seg_of = np.searchsorted(np.cumsum(sizes), np.arange(N), side="right")
     for t in range(ftiles):
-        first, last = t * 1024, min(N, (t + 1) * 1024) - 1
+        first, last = t * 512, min(N, (t + 1) * 512) - 1
         want = int(seg_of[first]) | (0x80000000 if seg_of[last] != seg_of[first] else 0)
         assert int(info_arr[t]) == want, t
 
