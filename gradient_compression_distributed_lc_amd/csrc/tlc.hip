@@ -69,6 +69,9 @@ constexpr uint32_t kRunMax = 14;                  // codes 243..255 = runs of 2.
 constexpr uint32_t kRunBase = 241;
 constexpr uint64_t kMaxN = 0xFFFFFFFFull;
 constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (about a second)
+// s_waitcnt operand that waits for every outstanding vector memory access
+// and nothing else (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmem = 0x0F70;
 constexpr uint32_t kPackGrid = 2048;              // blocks of k_quant_pack
 
 // look-back word: 2 status bits | 62 payload bits
@@ -104,6 +107,19 @@ struct GroupView {
 };
 
 __device__ __forceinline__ Seg load_seg(const GroupView& g, uint32_t i) { return g.segs ? g.segs[i] : g.one; }
+
+// One encode tile that can hold nonzero codes, with everything k_quant_pack
+// needs to process it (written by k_tile_activity).
+struct PackJob {
+    uint64_t e0;     // group element offset of the tile's first element
+    uint32_t et;     // encode tile index in the group (carry word, staging slot)
+    uint32_t nel;    // elements in the tile
+    uint32_t fmask;  // bit k: flat tile e0 / kFTile + k holds |v| >= thr
+    float thr;       // selection threshold of the tensor
+    float ms;        // M * s of the tensor
+    uint32_t gi;     // tensor
+};
+static_assert(sizeof(PackJob) == 32, "job layout");
 
 __device__ __forceinline__ uint32_t quartic_len(uint32_t n) { return (uint32_t)(((uint64_t)n + 4) / 5); }
 __device__ __forceinline__ uint32_t etiles_of(uint32_t n) {
@@ -506,43 +522,83 @@ __global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t eti
     if (ok && (lane == 63 || next != gi)) atomicMax(mbits + gi, __float_as_uint(mx));
 }
 
-// Per tensor: s*M and the quantisation threshold (written by the thread of
-// its first encode tile).  Per encode tile: a tile whose maximum reaches the
-// threshold can hold nonzero codes and is listed for k_quant_pack; any other
-// holds only zero codes and is summarised here as a run of byte 121.
+// Per encode tile: M*s and the exact selection threshold of its tensor; a
+// tile whose maximum reaches the threshold can hold nonzero codes and is
+// listed for k_quant_pack, with the flat tiles under it that reach it; any
+// other tile holds only zero codes and is summarised here as a run of byte
+// 121.
 __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_t etiles, float s,
+                                                            const float* __restrict__ pmax,
                                                             const float* __restrict__ etmax,
                                                             const float* __restrict__ scales,
-                                                            float* __restrict__ seg_thr, float* __restrict__ seg_ms,
                                                             uint64_t* __restrict__ etile_agg,
-                                                            uint64_t* __restrict__ active, uint32_t* __restrict__ ctrl) {
+                                                            PackJob* __restrict__ jobs, uint32_t* __restrict__ ctrl) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_base;
     const uint32_t base = blockIdx.x * (kThreads * kActPerThread);
-    uint32_t mask = 0, own[kActPerThread];
+    // the thread's tiles go through each dependent load step together
+    uint32_t gis[kActPerThread];
 #pragma unroll
     for (int r = 0; r < kActPerThread; ++r) {
         const uint32_t e = base + r * kThreads + threadIdx.x;
-        own[r] = 0;
+        gis[r] = e < etiles ? etile_owner(g, e) : 0u;
+    }
+    Seg sgs[kActPerThread];
+    float ms_[kActPerThread], tmax[kActPerThread];
+#pragma unroll
+    for (int r = 0; r < kActPerThread; ++r) {
+        const uint32_t e = base + r * kThreads + threadIdx.x;
+        sgs[r] = load_seg(g, gis[r]);
+        ms_[r] = scales[gis[r]];
+        tmax[r] = e < etiles ? etmax[e] : 0.0f;
+    }
+    uint32_t mask = 0;
+    PackJob jb[kActPerThread] = {};
+#pragma unroll
+    for (int r = 0; r < kActPerThread; ++r) {
+        const uint32_t e = base + r * kThreads + threadIdx.x;
         if (e < etiles) {
-            const uint32_t gi = etile_owner(g, e);
-            const Seg sg = load_seg(g, gi);
-            const float m = scales[gi];
+            const Seg& sg = sgs[r];
+            const float m = ms_[r];
             const float ms = m * s;
             const float thr = select_threshold(m, ms);
             const uint32_t j = e - sg.etile0;
-            if (j == 0) {
-                seg_ms[gi] = ms;
-                seg_thr[gi] = thr;
-            }
-            own[r] = gi;
-            if (etmax[e] >= thr) {
+            if (tmax[r] >= thr) {
                 mask |= 1u << r;
+                jb[r].e0 = sg.elem_off + (uint64_t)j * kETile;
+                jb[r].et = e;
+                jb[r].nel = min(kETile, sg.n - j * kETile);
+                jb[r].thr = thr;
+                jb[r].ms = ms;
+                jb[r].gi = gis[r];
             } else {
                 const uint32_t B = quartic_len(sg.n);
                 etile_agg[e] = carry_pack(carry_run(min(kETileBytes, B - j * kETileBytes)));
             }
         }
+    }
+    // which flat tiles under a listed tile reach the threshold: every load
+    // is issued before the first compare
+    constexpr int kSub = kETile / kFTile + 1;  // flat tiles an encode tile can touch
+    float pv[kActPerThread][kSub];
+#pragma unroll
+    for (int r = 0; r < kActPerThread; ++r) {
+        const bool act = (mask >> r) & 1;
+        const uint64_t t0 = act ? jb[r].e0 / kFTile : 0, t1 = act ? (jb[r].e0 + jb[r].nel - 1) / kFTile : 0;
+        const float* pm = pmax + (act ? jb[r].gi : 0u) + t0;  // flat tile t of tensor gi: slot t + gi
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) {
+            pv[r][k] = -1.0f;
+            if (act && t0 + k <= t1) pv[r][k] = pm[k];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+#pragma unroll
+    for (int r = 0; r < kActPerThread; ++r) {
+        uint32_t fm = 0;
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) fm |= (uint32_t)(pv[r][k] >= jb[r].thr) << k;
+        jb[r].fmask = fm;
     }
     // compaction: one atomic per block
     uint32_t tot;
@@ -553,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_
     uint32_t pos = s_base + before;
 #pragma unroll
     for (int r = 0; r < kActPerThread; ++r)
-        if (mask & (1u << r)) active[pos++] = ((uint64_t)own[r] << 32) | (base + r * kThreads + threadIdx.x);
+        if (mask & (1u << r)) jobs[pos++] = jb[r];
 }
 
 // LDS writes of one lane visible to the other lanes of its wave
@@ -592,86 +648,104 @@ __device__ __forceinline__ int wave_min(int v) {
 }
 
 // One wavefront quantizes, packs and zero-run encodes one encode tile.  Only
-// the flat tiles (1024 elements) whose max reaches the threshold are read
+// the flat tiles (512 elements) whose max reaches the threshold are read
 // again: every other element has code 0 and err = v already, so it needs no
 // HBM traffic.  Codes go through this wave's LDS slice so that the loads stay
-// coalesced (lane l, slot l + 64k) while lane l then owns the contiguous tile
-// bytes 16l..16l+15 (codes 80l..80l+79).
-__device__ void pack_tile(const GroupView& g, uint64_t entry, float* __restrict__ err,
-                          const float* __restrict__ pmax, const float* __restrict__ seg_thr,
-                          const float* __restrict__ seg_ms, uint64_t* __restrict__ etile_agg,
+// coalesced (lane l, elements 4l..4l+3 of each 256) while lane l then owns the
+// contiguous tile bytes 16l..16l+15 (codes 80l..80l+79).  The job comes in
+// scalar registers, so the tile's first vector loads are its error values.
+__device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* __restrict__ etile_agg,
                           uint8_t* __restrict__ staging, int8_t* q) {
     const int lane = lane_id();
-    const uint32_t gi = (uint32_t)(entry >> 32), et = (uint32_t)entry;
-    const Seg sg = load_seg(g, gi);
-    const uint32_t j = et - sg.etile0;
-    const uint32_t nbytes = min(kETileBytes, quartic_len(sg.n) - j * kETileBytes);
-    const uint32_t nel = min(kETile, sg.n - j * kETile);
-    const uint64_t e0 = sg.elem_off + (uint64_t)j * kETile;
-    const float thr = seg_thr[gi];
-    const float ms = seg_ms[gi];
+    const uint64_t e0 = jb.e0;
+    const uint32_t et = jb.et, nel = jb.nel;
+    const uint32_t nbytes = (nel + 4) / 5;
+    const float thr = jb.thr, ms = jb.ms;
 
-    // which of the (at most 11) flat tiles under this encode tile can hold a nonzero code
-    const uint64_t ta0 = e0 / kFTile;
-    const uint32_t nft = (uint32_t)((e0 + nel - 1) / kFTile - ta0) + 1;
-    const uint64_t fmask = __ballot(lane < (int)nft && pmax[ta0 + lane + gi] >= thr);
-
-    if ((e0 & 3) == 0) {
-        float4* const es = reinterpret_cast<float4*>(err + e0);
-        uint32_t* const q4 = reinterpret_cast<uint32_t*>(q);
-        // five groups of four slots of 256 elements; with an aligned tile start
-        // a slot lies in one flat tile.  A group's loads are all issued before
-        // any of its error writes (the writes go to the same array).
-#pragma unroll 1
-        for (int grp = 0; grp < 5; ++grp) {
-            float vv[4][4];
-            bool act[4];
+    // every code starts at 0, pad codes past the tensor end included
+    uint4* const q16 = reinterpret_cast<uint4*>(q);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t slot = lane + 64 * (4 * grp + k);
-                const uint32_t u = 4 * slot;  // tile element of the slot's first code
-                act[k] = u < nel && ((fmask >> ((e0 + u) / kFTile - ta0)) & 1);
-                float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (act[k]) {
-                    if (u + 4 <= nel) {
-                        v = es[slot];
-                    } else {
-                        v.x = err[e0 + u];
-                        if (u + 1 < nel) v.y = err[e0 + u + 1];
-                        if (u + 2 < nel) v.z = err[e0 + u + 2];
-                    }
+    for (int k = 0; k < kETile / 1024; ++k) q16[lane + 64 * k] = make_uint4(0u, 0u, 0u, 0u);
+
+    const uint64_t ta0 = e0 / kFTile;
+    if ((e0 & 3) == 0) {
+        // Active flat tiles, two at a time.  A batch issues all its loads
+        // (each one predicated, no branch writes a register another branch
+        // loads into), waits for them once, and only then computes and
+        // writes: so no wait inside the tile can fall on a store.  Four
+        // consecutive elements never straddle two encode tiles here, so every
+        // float4 inside the tile is written back whole (unchanged where
+        // q = 0); only the last float4 of a tensor whose size is not a
+        // multiple of 4 is partial.
+        uint32_t m = jb.fmask;
+        uint32_t* const q4 = reinterpret_cast<uint32_t*>(q);
+        while (m) {
+            int64_t u[4];
+            bool full[4], part[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int f = m ? __builtin_ctz(m) : -1;
+                if (m) m &= m - 1;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int slot = 2 * h + k;
+                    u[slot] = f < 0 ? -1 : (int64_t)((ta0 + f) * kFTile) - (int64_t)e0 + 4 * lane + 256 * k;
+                    full[slot] = u[slot] >= 0 && u[slot] + 4 <= (int64_t)nel;
+                    part[slot] = u[slot] >= 0 && u[slot] < (int64_t)nel && !full[slot];
                 }
-                vv[k][0] = v.x;
-                vv[k][1] = v.y;
-                vv[k][2] = v.z;
-                vv[k][3] = v.w;
+            }
+            f4 v[4];
+            float p0[4], p1[4], p2[4];
+#pragma unroll
+            for (int slot = 0; slot < 4; ++slot) {
+                v[slot] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                p0[slot] = p1[slot] = p2[slot] = 0.0f;
+                const float* const a = err + e0 + u[slot];
+                if (full[slot]) v[slot] = *reinterpret_cast<const f4*>(a);
+                if (part[slot]) {
+                    p0[slot] = a[0];
+                    if (u[slot] + 1 < (int64_t)nel) p1[slot] = a[1];
+                    if (u[slot] + 2 < (int64_t)nel) p2[slot] = a[2];
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmem);
+            f4 nv[4];
+            int qs[4][4];
+#pragma unroll
+            for (int slot = 0; slot < 4; ++slot) {
+                if (part[slot]) v[slot] = f4{p0[slot], p1[slot], p2[slot], 0.0f};
+                qs[slot][0] = ternary(v[slot].x, thr);
+                qs[slot][1] = ternary(v[slot].y, thr);
+                qs[slot][2] = ternary(v[slot].z, thr);
+                qs[slot][3] = ternary(v[slot].w, thr);  // 0 past the tensor end (v = 0)
+                nv[slot] = f4{v[slot].x - (float)qs[slot][0] * ms, v[slot].y - (float)qs[slot][1] * ms,
+                              v[slot].z - (float)qs[slot][2] * ms, v[slot].w - (float)qs[slot][3] * ms};
+                if (full[slot] || part[slot])
+                    q4[u[slot] >> 2] = (uint32_t)(uint8_t)(int8_t)qs[slot][0] |
+                                       (uint32_t)(uint8_t)(int8_t)qs[slot][1] << 8 |
+                                       (uint32_t)(uint8_t)(int8_t)qs[slot][2] << 16 |
+                                       (uint32_t)(uint8_t)(int8_t)qs[slot][3] << 24;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t slot = lane + 64 * (4 * grp + k);
-                const uint32_t u = 4 * slot;
-                uint32_t packed = 0;
-                if (act[k]) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int qq = ternary(vv[k][jj], thr);  // 0 past the tensor end (v = 0)
-                        if (qq) err[e0 + u + jj] = vv[k][jj] - (float)qq * ms;
-                        packed |= (uint32_t)(uint8_t)(int8_t)qq << (8 * jj);
-                    }
+            for (int slot = 0; slot < 4; ++slot) {
+                float* const a = err + e0 + u[slot];
+                if (full[slot]) *reinterpret_cast<f4*>(a) = nv[slot];
+                if (part[slot]) {
+                    if (qs[slot][0]) a[0] = nv[slot].x;
+                    if (qs[slot][1]) a[1] = nv[slot].y;
+                    if (qs[slot][2]) a[2] = nv[slot].z;
                 }
-                q4[slot] = packed;  // zeros also cover the pad codes past the tensor
             }
         }
     } else {
         // a tensor that starts off a 16-byte boundary: element by element
-        for (uint32_t u = lane; u < 5 * nbytes; u += 64) {
-            int qq = 0;
-            if (u < nel && ((fmask >> ((e0 + u) / kFTile - ta0)) & 1)) {
+        for (uint32_t u = lane; u < nel; u += 64) {
+            if ((jb.fmask >> ((e0 + u) / kFTile - ta0)) & 1) {
                 const float vv = err[e0 + u];
-                qq = ternary(vv, thr);
+                const int qq = ternary(vv, thr);
                 if (qq) err[e0 + u] = vv - (float)qq * ms;
+                q[u] = (int8_t)qq;
             }
-            q[u] = (int8_t)qq;
         }
     }
     wave_sync();
@@ -738,7 +812,7 @@ __device__ void pack_tile(const GroupView& g, uint64_t entry, float* __restrict_
             }
         }
         uint32_t pos = wave_excl_sum(te, &k_int);
-        uint8_t* const st = staging + (uint64_t)et * kETileBytes;
+        uint8_t* const st = reinterpret_cast<uint8_t*>(q);  // the codes are in registers now
         prev = prev_excl;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
@@ -757,6 +831,11 @@ __device__ void pack_tile(const GroupView& g, uint64_t entry, float* __restrict_
                 }
             }
         }
+        // the staged bytes (at most one per quartic byte) leave in one
+        // 16-byte store per lane
+        wave_sync();
+        if (16u * lane < k_int)
+            reinterpret_cast<uint4*>(staging + (uint64_t)et * kETileBytes)[lane] = reinterpret_cast<const uint4*>(q)[lane];
         agg.lit = 1;
         agg.p = (uint32_t)first % kRunMax;
         agg.K = (uint32_t)first / kRunMax + k_int;
@@ -766,19 +845,16 @@ __device__ void pack_tile(const GroupView& g, uint64_t entry, float* __restrict_
     wave_sync();  // the LDS slice is rewritten by the wave's next tile
 }
 
-__global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __restrict__ err,
-                                                         const float* __restrict__ pmax,
-                                                         const float* __restrict__ seg_thr,
-                                                         const float* __restrict__ seg_ms,
-                                                         const uint64_t* __restrict__ active,
+__global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err, const PackJob* __restrict__ jobs,
                                                          const uint32_t* __restrict__ ctrl,
                                                          uint64_t* __restrict__ etile_agg,
                                                          uint8_t* __restrict__ staging) {
     __shared__ __align__(16) int8_t s_q[kWaves * kETile];
     const uint32_t na = ctrl[1];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
     const uint32_t waves = gridDim.x * kWaves;
-    for (uint32_t i = blockIdx.x * kWaves + wave_id(); i < na; i += waves)
-        pack_tile(g, active[i], err, pmax, seg_thr, seg_ms, etile_agg, staging, s_q + wave_id() * kETile);
+    for (uint32_t i = blockIdx.x * kWaves + wave; i < na; i += waves)
+        pack_tile(jobs[i], err, etile_agg, staging, s_q + wave * kETile);
 }
 
 __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* __restrict__ etile_agg,
@@ -1185,7 +1261,7 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, seg_thr, seg_ms, etile_agg, etmax, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
+    size_t ctrl, pmax, etile_agg, etmax, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
         total;
 };
 
@@ -1199,11 +1275,9 @@ Layout ws_layout(const Dims& d) {
     };
     l.ctrl = take(256);
     l.pmax = take((d.ftiles + d.count) * sizeof(float));
-    l.seg_thr = take(d.count * sizeof(float));
-    l.seg_ms = take(d.count * sizeof(float));
     l.etile_agg = take(d.etiles * sizeof(uint64_t));
     l.etmax = take(d.etiles * sizeof(float));
-    l.active = take(d.etiles * sizeof(uint64_t));
+    l.active = take(d.etiles * sizeof(PackJob));
     l.span_flags = take(d.spans * sizeof(uint64_t));
     l.span_tickets = take(d.count * sizeof(uint32_t));
     l.chunk_tickets = take(d.count * sizeof(uint32_t));
@@ -1283,11 +1357,9 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     char* w = static_cast<char*>(ws);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
     float* pmax = reinterpret_cast<float*>(w + l.pmax);
-    float* thr = reinterpret_cast<float*>(w + l.seg_thr);
-    float* ms = reinterpret_cast<float*>(w + l.seg_ms);
     uint64_t* etile_agg = reinterpret_cast<uint64_t*>(w + l.etile_agg);
     float* etmax = reinterpret_cast<float*>(w + l.etmax);
-    uint64_t* active = reinterpret_cast<uint64_t*>(w + l.active);
+    PackJob* jobs = reinterpret_cast<PackJob*>(w + l.active);
     uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
     uint32_t* span_tickets = reinterpret_cast<uint32_t*>(w + l.span_tickets);
     uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
@@ -1308,12 +1380,12 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     if (rc) return rc;
     rc = launch("tlc_tile_activity", st, [&] {
         constexpr uint32_t per_block = kThreads * kActPerThread;
-        k_tile_activity<<<(etiles + per_block - 1) / per_block, kThreads, 0, st>>>(g, etiles, s, etmax, scales, thr, ms,
-                                                                                 etile_agg, active, ctrl);
+        k_tile_activity<<<(etiles + per_block - 1) / per_block, kThreads, 0, st>>>(g, etiles, s, pmax, etmax, scales,
+                                                                                 etile_agg, jobs, ctrl);
     });
     if (rc) return rc;
     rc = launch("tlc_quant_pack", st, [&] {
-        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(g, err, pmax, thr, ms, active, ctrl, etile_agg, staging);
+        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging);
     });
     if (rc) return rc;
     return launch("tlc_emit", st, [&] {

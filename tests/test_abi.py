@@ -46,9 +46,10 @@ def test_workspace_size():
     small, big = tlc.workspace_size(1), tlc.workspace_size(335_000_000)
     assert 0 < small <= 8192 and small % 256 == 0
     # staging for the zero-run bytes of tiles with nonzero codes (ceil(n/5)), one partial max per
-    # 512-element flat tile, a few words per 5120-element encode tile, and small per-call state
+    # 512-element flat tile, a carry word, a max and a 32-byte job per 5120-element encode tile,
+    # and small per-call state
     n = 335_000_000
-    assert big < n // 5 + 4 * (n // 512) + 32 * (n // 5120) + 1_000_000
+    assert big < n // 5 + 4 * (n // 512) + 48 * (n // 5120) + 1_000_000
     assert big % 256 == 0
 
 
