@@ -647,25 +647,48 @@ __device__ __forceinline__ int wave_min(int v) {
     return v;
 }
 
+// Per-wave LDS slice of k_quant_pack: the tile's codes (one int8 per element),
+// its staged stream bytes, and a bitmap of its literal quartic bytes.
+constexpr uint32_t kSliceStage = kETile;                      // offset of the staged bytes
+constexpr uint32_t kSliceBits = kSliceStage + kETileBytes;    // offset of the bitmap
+constexpr uint32_t kSlice = kSliceBits + kETileBytes / 8;     // bytes per wave
+
+// Marks the quartic bytes of tile elements u..u+3 that hold a nonzero code
+// (four elements touch at most two bytes).
+__device__ __forceinline__ void mark_literals(uint32_t* lit, uint32_t u, int q0, int q1, int q2, int q3) {
+    const uint32_t b0 = u / 5, split = 5 * (b0 + 1) - u;  // elements d < split lie in byte b0
+    const bool f0 = q0 || (q1 && split > 1) || (q2 && split > 2) || (q3 && split > 3);
+    const bool f1 = (q1 && split <= 1) || (q2 && split <= 2) || (q3 && split <= 3);
+    if (f0) atomicOr(lit + (b0 >> 5), 1u << (b0 & 31));
+    if (f1) atomicOr(lit + ((b0 + 1) >> 5), 1u << ((b0 + 1) & 31));
+}
+
 // One wavefront quantizes, packs and zero-run encodes one encode tile.  Only
 // the flat tiles (512 elements) whose max reaches the threshold are read
 // again: every other element has code 0 and err = v already, so it needs no
-// HBM traffic.  Codes go through this wave's LDS slice so that the loads stay
-// coalesced (lane l, elements 4l..4l+3 of each 256) while lane l then owns the
-// contiguous tile bytes 16l..16l+15 (codes 80l..80l+79).  The job comes in
-// scalar registers, so the tile's first vector loads are its error values.
+// HBM traffic.  The job comes in scalar registers, so the tile's first vector
+// loads are its error values.  Codes go to this wave's LDS slice, and every
+// quartic byte that holds a nonzero code (a literal) is marked in a bitmap;
+// the zero-run encoding then works literal by literal (64 per round), which
+// costs nothing for the runs of byte 121 that make up most of a tile.
 __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* __restrict__ etile_agg,
-                          uint8_t* __restrict__ staging, int8_t* q) {
+                          uint8_t* __restrict__ staging, int8_t* slice) {
     const int lane = lane_id();
     const uint64_t e0 = jb.e0;
     const uint32_t et = jb.et, nel = jb.nel;
     const uint32_t nbytes = (nel + 4) / 5;
     const float thr = jb.thr, ms = jb.ms;
+    int8_t* const q = slice;
+    uint8_t* const stage = reinterpret_cast<uint8_t*>(slice + kSliceStage);
+    uint32_t* const lit = reinterpret_cast<uint32_t*>(slice + kSliceBits);
 
-    // every code starts at 0, pad codes past the tensor end included
-    uint4* const q16 = reinterpret_cast<uint4*>(q);
+    // every code starts at 0 (pad codes past the tensor end included), no
+    // byte is marked, and the staged bytes start as 255 (a full 14-run), so
+    // only remainder codes and literals are written there later
 #pragma unroll
-    for (int k = 0; k < kETile / 1024; ++k) q16[lane + 64 * k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < kETile / 1024; ++k) reinterpret_cast<uint4*>(q)[lane + 64 * k] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(stage)[lane] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (lane < 32) lit[lane] = 0u;
 
     const uint64_t ta0 = e0 / kFTile;
     if ((e0 & 3) == 0) {
@@ -720,11 +743,13 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
                 qs[slot][3] = ternary(v[slot].w, thr);  // 0 past the tensor end (v = 0)
                 nv[slot] = f4{v[slot].x - (float)qs[slot][0] * ms, v[slot].y - (float)qs[slot][1] * ms,
                               v[slot].z - (float)qs[slot][2] * ms, v[slot].w - (float)qs[slot][3] * ms};
-                if (full[slot] || part[slot])
+                if (full[slot] || part[slot]) {
                     q4[u[slot] >> 2] = (uint32_t)(uint8_t)(int8_t)qs[slot][0] |
                                        (uint32_t)(uint8_t)(int8_t)qs[slot][1] << 8 |
                                        (uint32_t)(uint8_t)(int8_t)qs[slot][2] << 16 |
                                        (uint32_t)(uint8_t)(int8_t)qs[slot][3] << 24;
+                    mark_literals(lit, (uint32_t)u[slot], qs[slot][0], qs[slot][1], qs[slot][2], qs[slot][3]);
+                }
             }
 #pragma unroll
             for (int slot = 0; slot < 4; ++slot) {
@@ -743,103 +768,86 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
             if ((jb.fmask >> ((e0 + u) / kFTile - ta0)) & 1) {
                 const float vv = err[e0 + u];
                 const int qq = ternary(vv, thr);
-                if (qq) err[e0 + u] = vv - (float)qq * ms;
+                if (qq) {
+                    err[e0 + u] = vv - (float)qq * ms;
+                    atomicOr(lit + ((u / 5) >> 5), 1u << ((u / 5) & 31));
+                }
                 q[u] = (int8_t)qq;
             }
         }
     }
     wave_sync();
 
-    uint32_t bw[4];  // the lane's 16 quartic bytes, 4 per word
-    {
-        uint32_t words[20];
-#pragma unroll
-        for (int i = 0; i < 20; ++i) words[i] = reinterpret_cast<const uint32_t*>(q)[20 * lane + i];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                uint32_t byte = 0, w3 = 1;
-#pragma unroll
-                for (int d = 0; d < 5; ++d) {
-                    const int idx = 20 * gq + 5 * jj + d;
-                    const int qq = (int)(int8_t)(words[idx >> 2] >> (8 * (idx & 3)));
-                    byte += (uint32_t)(qq + 1) * w3;
-                    w3 *= 3;
-                }
-                word |= byte << (8 * jj);
-            }
-            bw[gq] = word;
-        }
-    }
-
-    // bytes past the tile end count as 121 (they are never emitted)
-    int tfirst = INT_MAX, tlast = -1;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-        const uint32_t k = 16u * lane + jj;
-        const uint32_t byte = (bw[jj >> 2] >> (8 * (jj & 3))) & 255u;
-        if (k < nbytes && byte != kZero) {
-            tfirst = min(tfirst, (int)k);
-            tlast = (int)k;
-        }
-    }
-    int last;
-    const int prev_excl = wave_excl_max(tlast, &last);
-    const int first = wave_min(tfirst);
-
+    // Literal n of the tile (in byte order) is found by rank: lanes 0..31
+    // hold the bitmap words, a prefix sum of their popcounts gives each
+    // word's first rank.  Each literal emits, after the previous literal at
+    // distance g + 1: g / 14 bytes 255, the remainder code of g mod 14 (if
+    // not 0) and itself; the first literal emits only itself (the run before
+    // it is part of the carry summary).
+    const uint32_t w = lane < 32 ? lit[lane] : 0u;
+    uint32_t L;
+    const uint32_t wpre = wave_excl_sum((uint32_t)__popc(w), &L);
     Carry agg = carry_run(nbytes);
     uint32_t k_int = 0;
-    if (last >= 0) {
-        // stream bytes from the first literal on: a literal emits the
-        // remainder code of the run before it (if any) and itself; a 121 emits
-        // a 255 when it completes a 14-byte chunk of its run
-        const int kb = 16 * lane;
-        uint32_t te = 0;
-        int prev = prev_excl;
+    if (L) {
+        uint32_t out_base = 0;  // staged bytes of earlier rounds
+        int prev_last = 0, first = 0;
+        for (uint32_t c0 = 0; c0 < L; c0 += 64) {
+            const uint32_t n = c0 + lane;
+            const bool has = n < L;
+            int wi = 0;  // last bitmap word whose first rank is <= n
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int k = kb + jj;
-            const uint32_t byte = (bw[jj >> 2] >> (8 * (jj & 3))) & 255u;
-            if (k < (int)nbytes && k >= first) {
-                if (byte != kZero) {
-                    te += (k == first) ? 1u : 1u + (((uint32_t)(k - prev - 1) % kRunMax) != 0);
-                    prev = k;
-                } else {
-                    te += ((uint32_t)(k - prev) % kRunMax) == 0;
+            for (int step = 16; step >= 1; step >>= 1) {
+                const uint32_t pc = __shfl(wpre, wi + step, 64);
+                if (pc <= n) wi += step;
+            }
+            uint32_t x = __shfl(w, wi, 64);
+            uint32_t r = n - __shfl(wpre, wi, 64);  // rank inside the word
+            int pos = 0;
+#pragma unroll
+            for (int step = 16; step >= 1; step >>= 1) {
+                const uint32_t c = (uint32_t)__popc(x & ((1u << step) - 1u));
+                if (r >= c) {
+                    r -= c;
+                    x >>= step;
+                    pos += step;
                 }
             }
-        }
-        uint32_t pos = wave_excl_sum(te, &k_int);
-        uint8_t* const st = reinterpret_cast<uint8_t*>(q);  // the codes are in registers now
-        prev = prev_excl;
+            const int k = has ? 32 * wi + pos : 0;  // quartic byte index of literal n
+            uint32_t val = 0;
+            if (has) {
+                uint32_t w3 = 1;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int k = kb + jj;
-            const uint32_t byte = (bw[jj >> 2] >> (8 * (jj & 3))) & 255u;
-            if (k < (int)nbytes && k >= first) {
-                if (byte != kZero) {
-                    if (k != first) {
-                        const uint32_t gap = (uint32_t)(k - prev - 1) % kRunMax;
-                        if (gap) st[pos++] = remainder_code(gap);
-                    }
-                    st[pos++] = (uint8_t)byte;
-                    prev = k;
-                } else if (((uint32_t)(k - prev) % kRunMax) == 0) {
-                    st[pos++] = 255;
+                for (int d = 0; d < 5; ++d) {
+                    val += (uint32_t)((int)q[5 * k + d] + 1) * w3;
+                    w3 *= 3;
                 }
             }
+            int pk = __shfl_up(k, 1, 64);
+            if (lane == 0) pk = prev_last;
+            const uint32_t g = (uint32_t)(k - pk - 1);
+            const uint32_t len = !has ? 0u : (n == 0 ? 1u : g / kRunMax + (g % kRunMax != 0) + 1u);
+            uint32_t tot;
+            const uint32_t ex = wave_excl_sum(len, &tot);
+            if (has) {
+                const uint32_t end = out_base + ex + len;  // one past this literal's bytes
+                stage[end - 1] = (uint8_t)val;
+                if (n != 0 && g % kRunMax) stage[end - 2] = remainder_code(g % kRunMax);
+            }
+            out_base += tot;
+            if (c0 == 0) first = __shfl(k, 0, 64);
+            prev_last = __shfl(k, (int)min(64u, L - c0) - 1, 64);
         }
-        // the staged bytes (at most one per quartic byte) leave in one
-        // 16-byte store per lane
+        const uint32_t t = nbytes - 1 - (uint32_t)prev_last;  // zero bytes after the last literal
+        k_int = out_base + t / kRunMax;                       // their full runs stay 255
         wave_sync();
         if (16u * lane < k_int)
-            reinterpret_cast<uint4*>(staging + (uint64_t)et * kETileBytes)[lane] = reinterpret_cast<const uint4*>(q)[lane];
+            reinterpret_cast<uint4*>(staging + (uint64_t)et * kETileBytes)[lane] =
+                reinterpret_cast<const uint4*>(stage)[lane];
         agg.lit = 1;
         agg.p = (uint32_t)first % kRunMax;
         agg.K = (uint32_t)first / kRunMax + k_int;
-        agg.c = (nbytes - 1 - (uint32_t)last) % kRunMax;
+        agg.c = t % kRunMax;
     }
     if (lane == 0) etile_agg[et] = carry_pack(agg) | ((uint64_t)k_int << 32);
     wave_sync();  // the LDS slice is rewritten by the wave's next tile
@@ -849,12 +857,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err
                                                          const uint32_t* __restrict__ ctrl,
                                                          uint64_t* __restrict__ etile_agg,
                                                          uint8_t* __restrict__ staging) {
-    __shared__ __align__(16) int8_t s_q[kWaves * kETile];
+    __shared__ __align__(16) int8_t s_q[kWaves * kSlice];
     const uint32_t na = ctrl[1];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
     const uint32_t waves = gridDim.x * kWaves;
     for (uint32_t i = blockIdx.x * kWaves + wave; i < na; i += waves)
-        pack_tile(jobs[i], err, etile_agg, staging, s_q + wave * kETile);
+        pack_tile(jobs[i], err, etile_agg, staging, s_q + wave * kSlice);
 }
 
 __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* __restrict__ etile_agg,
