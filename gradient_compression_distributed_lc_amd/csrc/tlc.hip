@@ -34,7 +34,7 @@
 //                 literal bytes over them.
 // decompress: k_prep (zero fill of y, one 16-byte store per lane; decoder
 //             state; list of stream chunks)
-//             -> k_decode (one block per 2 KiB of stream bytes: expansion
+//             -> k_decode (one block per 4 KiB of stream bytes: expansion
 //             scan + look-back across the tensor's chunks for the quartic
 //             byte index, then only literal bytes are decoded and their
 //             nonzero codes written or added).
@@ -63,7 +63,7 @@ constexpr int kAccThreads = kFTile / 4;            // lanes per k_accum_max bloc
 constexpr uint32_t kETile = 5120;                 // encode tile: elements
 constexpr uint32_t kETileBytes = kETile / 5;      // 1024 quartic bytes = 4 per lane
 constexpr uint32_t kSpan = 256;                   // encode tiles per k_emit block (one per lane)
-constexpr uint32_t kChunk = 2048;                 // decoder stream bytes per chunk = 8 per lane
+constexpr uint32_t kChunk = 4096;                 // decoder stream bytes per chunk = 16 per lane
 constexpr uint32_t kZero = 121;                   // quartic byte of five zero codes
 constexpr uint32_t kRunMax = 14;                  // codes 243..255 = runs of 2..14
 constexpr uint32_t kRunBase = 241;
@@ -73,6 +73,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (abo
 // and nothing else (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmem = 0x0F70;
 constexpr uint32_t kPackGrid = 2048;              // blocks of k_quant_pack
+constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (about what is resident at once)
 
 // look-back word: 2 status bits | 62 payload bits
 constexpr uint64_t kInvalid = 0, kAggregate = 1, kPrefix = 2, kPoison = 3;
@@ -865,6 +866,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err
         pack_tile(jobs[i], err, etile_agg, staging, s_q + wave * kSlice);
 }
 
+// Largest span output assembled in LDS by k_emit (an all-zero span of 256
+// encode tiles needs ~18.7 KB); larger spans take the two-pass path.
+constexpr uint32_t kEmitLds = 24576;
+
+// One block per span of 256 encode tiles of a tensor: block scan of the
+// tiles' carry summaries, decoupled look-back across the tensor's spans for
+// the span's input state, then the span's stream bytes.
 __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* __restrict__ etile_agg,
                                                    const uint8_t* __restrict__ staging,
                                                    uint64_t* __restrict__ flags, uint32_t* __restrict__ tickets,
@@ -879,6 +887,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     __shared__ uint8_t s_rem[kThreads];       // remainder code after the 255s, or 0
     __shared__ uint8_t s_fin[kThreads];       // closing remainder code of the tensor's last tile, or 0
     __shared__ uint32_t s_wpre[kThreads + 1];  // prefix of staged 4-byte words over the span's tiles
+    __shared__ __align__(16) uint8_t s_out[kEmitLds + 16];  // the span's bytes, shifted by the store misalignment
     __shared__ uint32_t s_span, s_E, s_r, s_ok;
 
     // Block b belongs to the tensor of span b.  A tensor with several spans
@@ -899,8 +908,31 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     const uint64_t word = valid ? etile_agg[sg.etile0 + j] : 0ull;
     const Carry a = carry_unpack(word);
     uint32_t kint = (uint32_t)(word >> 32) & 0x7FFu;
+    if (!a.lit) kint = 0;
     uint64_t total;
     const uint64_t excl = block_excl_scan(carry_pack(a), 0ull, CarryCompose(), s_sm, &total);
+
+    // The staged words of the span's tiles do not depend on the look-back:
+    // the first 256 of them are loaded before it.
+    const uint8_t* const stg = staging + (uint64_t)(sg.etile0 + lsp * kSpan) * kETileBytes;
+    uint32_t tot_words;
+    s_wpre[threadIdx.x] = block_excl_sum((kint + 3) / 4, s_u, &tot_words);
+    if (threadIdx.x == 0) s_wpre[kThreads] = tot_words;
+    __syncthreads();
+    auto word_owner = [&](uint32_t wv) {  // tile holding staged word wv of the span
+        uint32_t k = 0, hi2 = kThreads;
+        while (hi2 - k > 1) {
+            const uint32_t mid = (k + hi2) >> 1;
+            if (s_wpre[mid] <= wv) k = mid;
+            else hi2 = mid;
+        }
+        return k;
+    };
+    uint32_t k0 = 0, val0 = 0;
+    if (threadIdx.x < tot_words) {
+        k0 = word_owner(threadIdx.x);
+        val0 = reinterpret_cast<const uint32_t*>(stg + (uint64_t)k0 * kETileBytes)[threadIdx.x - s_wpre[k0]];
+    }
 
     if (threadIdx.x < 64) {
         uint32_t E = 0, r = 0, ok = 1;
@@ -945,7 +977,6 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
         if (!a.lit) {
             const uint32_t t = r_in + nb;
             lead = t / kRunMax;
-            kint = 0;
             E_out = E_in + lead;
             r_out = t % kRunMax;
         } else {
@@ -978,20 +1009,56 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     __syncthreads();
 
     // The span's tiles are consecutive in one tensor, so its output is the
-    // contiguous stream range [D, D + tot_len), D = stream position of tile 0.
-    // Pass A writes 255 over all of it with aligned 16-byte stores (the two
-    // partial end chunks byte by byte).  Pass B, after a barrier, overwrites
-    // the few other bytes: each tile's remainder code after its leading
-    // 255s, its staged bytes (copied a word at a time, all lanes in
-    // parallel), and the tensor's closing remainder code.
+    // contiguous stream range [D, D + tot_len), D = stream position of tile 0:
+    // byte 255 except for each tile's remainder code after its leading 255s,
+    // its staged bytes, and the tensor's closing remainder code.
     const uint32_t D = s_dst[0];
     const uint32_t end = min(tot_len, B - min(B, D));  // never past the tensor's slot
     uint8_t* const o = out + sg.stream_off + D;
-    const uint8_t* const stg = staging + (uint64_t)(sg.etile0 + lsp * kSpan) * kETileBytes;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(o) & 15);
     const uint32_t nchunks = end ? (mis + end + 15) / 16 : 0u;
+    if (end <= kEmitLds) {
+        // Assembled in LDS (byte p of the span at s_out[mis + p]): 255 fill,
+        // then the exceptions, then one aligned 16-byte store per chunk, so
+        // every stream byte is written once and no barrier waits on HBM.
+        for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads)
+            reinterpret_cast<uint4*>(s_out)[c] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        __syncthreads();
+        {
+            const uint32_t t_off = s_off[threadIdx.x];
+            if (rem && t_off + lead < end) s_out[mis + t_off + lead] = (uint8_t)rem;
+            if (fin && t_off + len - 1 < end) s_out[mis + t_off + len - 1] = (uint8_t)fin;
+        }
+        for (uint32_t wv = threadIdx.x; wv < tot_words; wv += kThreads) {
+            const uint32_t k = wv == threadIdx.x ? k0 : word_owner(wv);
+            const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
+            const uint32_t val =
+                wv == threadIdx.x ? val0 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
+            const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
+            const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i)
+                if (i < nbw && sbase + i < end) s_out[mis + sbase + i] = (uint8_t)(val >> (8 * i));
+        }
+        __syncthreads();
+        for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
+            const int64_t p0 = (int64_t)c * 16 - mis;  // span byte of the chunk's first byte
+            uint8_t* const dst = o + p0;
+            if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
+                *reinterpret_cast<uint4*>(dst) = reinterpret_cast<const uint4*>(s_out)[c];
+            } else {
+                for (int64_t i = 0; i < 16; ++i)
+                    if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = s_out[c * 16 + i];
+            }
+        }
+        return;
+    }
+
+    // Two passes straight to HBM: pass A writes 255 over all of the span
+    // with aligned 16-byte stores (the two partial end chunks byte by byte);
+    // pass B, after a barrier, overwrites the exceptions.
     for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
-        const int64_t p0 = (int64_t)c * 16 - mis;  // span byte of the chunk's first byte
+        const int64_t p0 = (int64_t)c * 16 - mis;
         uint8_t* const dst = o + p0;
         if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
             *reinterpret_cast<uint4*>(dst) = make_uint4(~0u, ~0u, ~0u, ~0u);
@@ -1000,27 +1067,17 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
                 if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = 255;
         }
     }
-    // staged words of this lane's tile, and their prefix over the span
-    const uint32_t my_words = (kint + 3) / 4;
-    uint32_t tot_words;
-    const uint32_t wpre = block_excl_sum(my_words, s_u, &tot_words);
-    s_wpre[threadIdx.x] = wpre;
-    if (threadIdx.x == 0) s_wpre[kThreads] = tot_words;
-    __syncthreads();  // pass A done; s_wpre visible
+    __syncthreads();  // pass A done
     {
         const uint32_t t_off = s_off[threadIdx.x];
         if (rem && t_off + lead < end) o[t_off + lead] = (uint8_t)rem;
         if (fin && t_off + len - 1 < end) o[t_off + len - 1] = (uint8_t)fin;
     }
     for (uint32_t wv = threadIdx.x; wv < tot_words; wv += kThreads) {
-        uint32_t k = 0, hi2 = kThreads;  // tile owning staged word wv
-        while (hi2 - k > 1) {
-            const uint32_t mid = (k + hi2) >> 1;
-            if (s_wpre[mid] <= wv) k = mid;
-            else hi2 = mid;
-        }
-        const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
-        const uint32_t val = reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
+        const uint32_t k = wv == threadIdx.x ? k0 : word_owner(wv);
+        const uint32_t w4 = wv - s_wpre[k];
+        const uint32_t val =
+            wv == threadIdx.x ? val0 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
         const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
         const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
 #pragma unroll
@@ -1079,7 +1136,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
     }
 }
 
-// One block per stream chunk (kChunk bytes, 8 per lane): expansion lengths,
+// One block per stream chunk (kChunk bytes, 16 per lane): expansion lengths,
 // block scan, look-back across the tensor's chunks for the quartic byte index
 // of the chunk, then the nonzero codes of its literal bytes are written
 // (decompress, over the zero fill of k_prep) or added (accumulate).
@@ -1094,9 +1151,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_chunk, s_ok;
     __shared__ uint64_t s_base;
-    // one chunk per block: the grid is sized for the largest possible streams
-    // and blocks past the real chunk count leave at once (a persistent loop
-    // would give some blocks two chunks' worth of zero fill)
+    // The real chunk count is only known on the device: the grid is capped
+    // near what the GPU holds at once and blocks loop over the chunks.
     for (uint32_t slot = blockIdx.x; slot < ctrl[3]; slot += gridDim.x) {
         // A tensor with several chunks hands them out in ticket order from its
         // own counter, so that the look-back only ever waits for blocks that
@@ -1125,24 +1181,22 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
         }
         const uint32_t cnt = (uint32_t)min((uint64_t)kChunk, L - start);
         const uint8_t* p = in + sg.stream_off + start;
-        const uint32_t off = 8u * threadIdx.x;
-        const uint32_t nv = cnt > off ? min(8u, cnt - off) : 0u;
-        uint32_t w0 = 0, w1 = 0;
-        if (nv == 8 && ((reinterpret_cast<uintptr_t>(p + off) & 7) == 0)) {
-            const uint2 v = *reinterpret_cast<const uint2*>(p + off);
-            w0 = v.x;
-            w1 = v.y;
+        const uint32_t off = 16u * threadIdx.x;
+        const uint32_t nv = cnt > off ? min(16u, cnt - off) : 0u;
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+        if (nv == 16 && ((reinterpret_cast<uintptr_t>(p + off) & 15) == 0)) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p + off);
+            wd[0] = v.x;
+            wd[1] = v.y;
+            wd[2] = v.z;
+            wd[3] = v.w;
         } else {
-            for (uint32_t i = 0; i < nv; ++i) {
-                const uint32_t b = (uint32_t)p[off + i] << (8 * (i & 3));
-                if (i < 4) w0 |= b;
-                else w1 |= b;
-            }
+            for (uint32_t i = 0; i < nv; ++i) wd[i >> 2] |= (uint32_t)p[off + i] << (8 * (i & 3));
         }
         uint32_t tsum = 0, nlit = 0;
 #pragma unroll
-        for (uint32_t i = 0; i < 8; ++i) {
-            const uint32_t byte = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 255u;
+        for (uint32_t i = 0; i < 16; ++i) {
+            const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
             const bool inr = i < nv;
             tsum += inr ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
             nlit += (inr && byte < 243u && byte != kZero) ? 1u : 0u;
@@ -1178,8 +1232,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             uint64_t pos = base + texcl;
             bool bad = false;
 #pragma unroll
-            for (uint32_t i = 0; i < 8; ++i) {
-                const uint32_t byte = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 255u;
+            for (uint32_t i = 0; i < 16; ++i) {
+                const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
                 if (i < nv) {
                     if (byte < 243u) {
                         if (pos >= B) {
@@ -1427,7 +1481,7 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
                                                ctrl, status);
     });
     if (rc) return rc;
-    const uint32_t grid = (uint32_t)chunks;
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(chunks, kDecodeGrid);
     return launch("tlc_decode", st, [&] {
         k_decode<<<grid, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, flags, dec_map, dec_first, chunk_tickets,
                                             ctrl, status, accumulate);

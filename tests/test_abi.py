@@ -61,7 +61,7 @@ def test_group_plan_layout():
     assert info.total_elems == N
     etiles = sum(-(-n // 5120) for n in sizes)
     spans = sum(-(-(-(-n // 5120)) // 256) for n in sizes)
-    chunks = sum(max(1, -(-(-(-n // 5)) // 2048)) for n in sizes)
+    chunks = sum(max(1, -(-(-(-n // 5)) // 4096)) for n in sizes)
     ftiles = -(-N // 512)
     assert info.tiles == etiles and info.chunks == chunks and info.spans == spans
     assert len(table) == info.table_bytes
