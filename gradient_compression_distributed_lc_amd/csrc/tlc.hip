@@ -97,6 +97,7 @@ struct TableHeader {
 static_assert(sizeof(TableHeader) == 64, "table layout");
 constexpr uint64_t kMagic = 0x32434c5433ull;  // "3TLC2"
 constexpr uint32_t kStraddle = 0x80000000u;   // ftile_info flag: the flat tile spans tensors
+constexpr uint32_t kMulti = 0x80000000u;      // span_seg / dec_map flag: the tensor has several spans / chunks
 
 struct GroupView {
     const Seg* segs;            // device table, or nullptr for one tensor
@@ -894,11 +895,11 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     // hands them out in ticket order from its own counter, so that the
     // look-back only ever waits for blocks that already hold a smaller
     // ticket; a single-span tensor needs no ticket.
-    const uint32_t gi = g.segs ? g.span_seg[blockIdx.x] : 0u;
+    const uint32_t ent = g.segs ? g.span_seg[blockIdx.x] : (etiles_of(g.one.n) > kSpan ? kMulti : 0u);
+    const uint32_t gi = ent & ~kMulti;
+    if (threadIdx.x == 0) s_span = (ent & kMulti) ? atomicAdd(tickets + gi, 1u) : 0u;  // in flight with the record
     const Seg sg = load_seg(g, gi);
     const uint32_t B = quartic_len(sg.n), ne = etiles_of(sg.n);
-    const uint32_t nsp = (ne + kSpan - 1) / kSpan;
-    if (threadIdx.x == 0) s_span = nsp > 1 ? atomicAdd(tickets + gi, 1u) : 0u;
     __syncthreads();
     const uint32_t lsp = s_span;
     const uint32_t sp = sg.span0 + lsp;
@@ -1125,7 +1126,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
             if (gi < g.count) {
                 dec_first[gi] = first;
                 tickets[gi] = 0;
-                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = gi;
+                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = gi | (rc > 1 ? kMulti : 0u);
             }
             carry += tot;
         }
@@ -1154,10 +1155,13 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
     // The real chunk count is only known on the device: the grid is capped
     // near what the GPU holds at once and blocks loop over the chunks.
     for (uint32_t slot = blockIdx.x; slot < ctrl[3]; slot += gridDim.x) {
+        if (slot != blockIdx.x) __syncthreads();  // s_chunk / s_base of the previous chunk are read
         // A tensor with several chunks hands them out in ticket order from its
         // own counter, so that the look-back only ever waits for blocks that
         // already hold a smaller ticket (and are working on that chunk).
-        const uint32_t gi = dec_map[slot];
+        const uint32_t ent = dec_map[slot];
+        const uint32_t gi = ent & ~kMulti;
+        if (threadIdx.x == 0) s_chunk = (ent & kMulti) ? atomicAdd(tickets + gi, 1u) : 0u;  // in flight with the loads
         const uint32_t c0 = dec_first[gi];
         const float msc = scales[gi];
         const Seg sg = load_seg(g, gi);
@@ -1165,8 +1169,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
         const uint64_t B = quartic_len(n);
         const uint64_t L_in = in_lens[gi];
         const uint64_t L = min(L_in, B);
-        const uint32_t nch = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
-        if (threadIdx.x == 0) s_chunk = nch > 1 ? atomicAdd(tickets + gi, 1u) : 0u;
         __syncthreads();
         const uint32_t lc = s_chunk;
         const uint32_t c = c0 + lc;
@@ -1176,7 +1178,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             // only an empty stream gets here (chunk 0 of a tensor with L == 0),
             // which is corrupt because ceil(n/5) >= 1
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
-            __syncthreads();
             continue;
         }
         const uint32_t cnt = (uint32_t)min((uint64_t)kChunk, L - start);
@@ -1223,7 +1224,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
         const uint64_t base = s_base;
         if (!s_ok) {
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_INTERNAL);
-            __syncthreads();
             continue;
         }
         float* const yy = y + sg.elem_off;
@@ -1260,7 +1260,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             if (bad) raise_status(status, TLC_ERR_CORRUPT);
         }
         if (threadIdx.x == 0 && start + cnt == L && base + csum != B) raise_status(status, TLC_ERR_CORRUPT);
-        __syncthreads();  // s_chunk / s_base are reused by the next chunk
     }
 }
 
@@ -1388,7 +1387,7 @@ Dims dims_of(const tlc_group_info* info) {
 }
 
 int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
-    if (!info || !d_table || !aligned16(d_table) || info->count == 0 || info->count > 0xFFFFFFFFull)
+    if (!info || !d_table || !aligned16(d_table) || info->count == 0 || info->count > 0x7FFFFFFFull)
         return TLC_ERR_INVALID_ARG;
     p->d = dims_of(info);
     const TableLayout t = table_layout(p->d);
@@ -1592,7 +1591,7 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
             sg.span0 = (uint32_t)span;
             sg.chunk0 = (uint32_t)chunk;
             memcpy(base + t.segs + i * sizeof(Seg), &sg, sizeof(Seg));
-            for (uint64_t k = 0; k < spans_host(n); ++k) span_seg[span + k] = (uint32_t)i;
+            for (uint64_t k = 0; k < spans_host(n); ++k) span_seg[span + k] = (uint32_t)i | (spans_host(n) > 1 ? kMulti : 0u);
             for (uint64_t k = 0; k < etiles_host(n); ++k) etile_seg[etile + k] = (uint32_t)i;
             // flat tiles whose first element lies in this tensor
             const uint64_t end = eoff + n;
