@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "tlco_compress": (ctypes.c_int, [P, P, U64, F, P, U64, P, P]),
             "tlco_decompress": (ctypes.c_int, [P, U64, F, U64, F, P]),
             "tlco_decompress_accumulate": (ctypes.c_int, [P, U64, F, U64, F, P]),
+            "tlco_server_compress": (ctypes.c_int, [P, ctypes.c_uint32, P, U64, F, P, U64, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -180,6 +181,20 @@ def decompress_accumulate(stream, M, n: int, s: float, acc: np.ndarray) -> np.nd
     _check(lib().tlco_decompress_accumulate(_ptr(stream), stream.size, float(M), n, s, _ptr(acc)),
            "decompress_accumulate")
     return acc
+
+
+def server_compress(acc, workers: int, err, s: float):
+    """Model-delta direction: compress of acc / workers with the server's error buffer.
+    Returns (stream uint8[L], M float32, err_new float32[n]); inputs are not modified."""
+    acc = _f32(acc)
+    e = _f32(err).copy()
+    cap = quartic_len(acc.size)
+    out = np.empty(max(cap, 1), dtype=np.uint8)
+    L = ctypes.c_uint64()
+    M = ctypes.c_float()
+    _check(lib().tlco_server_compress(_ptr(acc), workers, _ptr(e), acc.size, s, _ptr(out), cap,
+                                      ctypes.byref(L), ctypes.byref(M)), "server_compress")
+    return out[: L.value].copy(), np.float32(M.value), e
 
 
 def rc_of(fn_name: str, *args) -> int:

@@ -206,3 +206,16 @@ int tlco_decompress_accumulate(const uint8_t* in, uint64_t L, float M, uint64_t 
     free(q);
     return rc;
 }
+
+int tlco_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s,
+                         uint8_t* out, uint64_t cap, uint64_t* L, float* M)
+{
+    if (!acc || workers == 0 || n == 0) return TLCO_ERR_INVALID_ARG;
+    float* avg = (float*)malloc(n * sizeof(float));
+    if (!avg) return TLCO_ERR_NOMEM;
+    const float w = (float)workers;
+    for (uint64_t i = 0; i < n; ++i) avg[i] = acc[i] / w;  /* the mean of the workers' state changes */
+    int rc = tlco_compress(avg, err, n, s, out, cap, L, M);
+    free(avg);
+    return rc;
+}

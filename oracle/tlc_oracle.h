@@ -84,6 +84,16 @@ int tlco_decompress(const uint8_t* in, uint64_t L, float M, uint64_t n, float s,
 int tlco_decompress_accumulate(const uint8_t* in, uint64_t L, float M, uint64_t n, float s,
                                float* acc);
 
+/* Model-delta direction (the 3LC page, "Proposed method", fourth item: the
+ * same pipeline compresses model deltas as well as gradients).  The server's
+ * state change is the mean of the workers' decoded payloads: acc holds their
+ * fp32 sum (tlco_decompress_accumulate in worker order) and
+ *   avg_i = acc_i / workers                     (fp32 IEEE divide)
+ * is compressed exactly as tlco_compress does, with the server's own error
+ * buffer err.  workers >= 1; workers == 1 is tlco_compress on acc. */
+int tlco_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s,
+                         uint8_t* out, uint64_t cap, uint64_t* L, float* M);
+
 #ifdef __cplusplus
 }
 #endif
