@@ -16,7 +16,10 @@ Printed: one JSON line with the whole-job throughput in GB/s of fp32 input
 (4 bytes x values / (compress + decompress time)), the roofline of the
 dominant kernel (the 12-byte/element pass over x and err) measured with HIP
 events inside the timed region, bits per value, and the CPU oracle timed on
-the host over the same workload.
+the host over the same workload.  Also reported, outside the timed steps:
+compress and decompress timed apart, the 8-payload accumulate, and the
+model-delta direction's server step (the workers' sum, then the compress of
+their mean with the server's error buffer).
 
     python bench.py [--steps K] [--warmup W] [--workload bert_large] [--no-cpu]
 """
@@ -193,8 +196,25 @@ def main():
     kt = tlc.profile_read()
     last_bits = 8.0 * float(lens.sum().item()) / N
 
+    # phase times: compress calls alone, then decompress calls alone, each
+    # bracketed as a whole (the error buffer keeps evolving; inputs rotate)
+    kp = min(args.steps, 10)
+    p0, p1, p2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    p0.record()
+    for _ in range(kp):
+        group.compress(xs[counter[0] % pool], ed, s, out=out, out_lens=lens, scales=scales, workspace=ws,
+                       status=st_c)
+        counter[0] += 1
+    p1.record()
+    for _ in range(kp):
+        group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d)
+    p2.record()
+    torch.cuda.synchronize()
+    comp_ms = p0.elapsed_time(p1) / kp
+    dec_ms = p1.elapsed_time(p2) / kp
+
     # per-kernel breakdown: a separate, shorter pass with every kernel bracketed
-    # (events add a small gap around each kernel, so this pass is not the step time)
+    # (events add a small gap around each kernel, so short kernels read long)
     tlc.profile_only(None)
     tlc.profile_enable(True)
     for _ in range(min(args.steps, 5)):
@@ -211,8 +231,6 @@ def main():
         n, ms = table.get(name, (0, 0.0))
         return ms / n if n else 0.0
 
-    comp_ms = sum(per_launch(k, kt_all) for k in ("tlc_accum_max", "tlc_tile_max", "tlc_tile_activity", "tlc_quant_pack", "tlc_emit"))
-    dec_ms = sum(per_launch(k, kt_all) for k in ("tlc_prep_fill", "tlc_decode"))
     dom_ms = per_launch(DOMINANT, kt)
     achieved = DOMINANT_BYTES_PER_ELEM * N / (dom_ms * 1e-3) / 1e9 if dom_ms else 0.0
 
@@ -228,6 +246,41 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     acc_ms = a0.elapsed_time(a1) / 8
+
+    # model-delta direction, server side: the workers' sum (the payload decoded
+    # densely into acc, then accumulated 7 more times), then the server's
+    # compress of the 8-worker mean with its own error buffer (carried)
+    err_srv = torch.zeros(N, dtype=torch.float32, device=dev)
+    out_srv = torch.empty(group.stream_bytes, dtype=torch.uint8, device=dev)
+    lens_srv = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+    scales_srv = torch.empty(len(sizes), dtype=torch.float32, device=dev)
+    st_s = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def server_step():
+        group.decompress(out, lens, scales, s, y=acc, workspace=ws, status=st_a)
+        for _ in range(7):
+            group.decompress_accumulate(out, lens, scales, s, acc, workspace=ws, status=st_a)
+        group.server_compress(acc, 8, err_srv, s, out=out_srv, out_lens=lens_srv, scales=scales_srv,
+                              workspace=ws, status=st_s)
+
+    server_step()
+    torch.cuda.synchronize()
+    ks = 5
+    s0, s1, s2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    s0.record()
+    for _ in range(ks):
+        server_step()
+    s1.record()
+    for _ in range(ks):
+        group.server_compress(acc, 8, err_srv, s, out=out_srv, out_lens=lens_srv, scales=scales_srv,
+                              workspace=ws, status=st_s)
+    s2.record()
+    torch.cuda.synchronize()
+    if int(st_a.item()) != 0 or int(st_s.item()) != 0:
+        raise SystemExit(f"device status not ok in the server step: {int(st_a.item())} / {int(st_s.item())}")
+    srv_step_ms = s0.elapsed_time(s1) / ks
+    srv_comp_ms = s1.elapsed_time(s2) / ks
+    L_srv = int(lens_srv.sum().item())
 
     # copy yardstick: what a plain streaming copy reaches on this GPU
     copy_gbps = None
@@ -251,6 +304,10 @@ def main():
     bits_hdr = 8.0 * (L_total + 4 * len(sizes)) / N
     alg_bytes_comp = 12.0 * N + L_total + 4 * len(sizes)
     alg_bytes_dec = 4.0 * N + L_total
+    # server step: dense decode of the first payload (4 B/value + stream), 7
+    # sparse accumulates (stream + 8 B per nonzero code), the mean's compress
+    nnz_bytes = 0.0  # the nonzero codes are a few thousand here: below rounding
+    alg_bytes_srv = (4.0 * N + L_total) + 7 * (L_total + nnz_bytes) + (12.0 * N + L_srv + 4 * len(sizes))
     gbps = 4.0 * N / (ms_per_step * 1e-3) / 1e9
 
     cpu = None
@@ -301,12 +358,20 @@ def main():
                                     4),
         "compress_roofline_frac": round(alg_bytes_comp / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         if comp_ms else None,
+        "compress_roofline_frac_nominal_12p3B": round(12.3 * N / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if comp_ms else None,
         "decompress_roofline_frac": round(alg_bytes_dec / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         if dec_ms else None,
         "accumulate_ms_per_payload": round(acc_ms, 4),
+        "server_step_ms": round(srv_step_ms, 4),
+        "server_step_roofline_frac": round(alg_bytes_srv / (srv_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "server_compress_ms": round(srv_comp_ms, 4),
+        "server_compress_roofline_frac": round((12.0 * N + L_srv + 4 * len(sizes)) / (srv_comp_ms * 1e-3) / 1e9
+                                               / HBM_PEAK_GBPS, 4),
+        "server_bits_per_value": round(8.0 * L_srv / N, 4),
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
-        "kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
+        "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "wall_s_timed": round(wall, 3),
         "kernel_source": kernel_source_hash(),
     }

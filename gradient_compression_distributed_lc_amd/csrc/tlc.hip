@@ -73,6 +73,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (abo
 // and nothing else (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmem = 0x0F70;
 constexpr uint32_t kPackGrid = 2048;              // blocks of k_quant_pack
+constexpr int kPackSlots = 4;                     // float4 loads per lane in one k_quant_pack batch (two flat tiles)
 constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (about what is resident at once)
 
 // look-back word: 2 status bits | 62 payload bits
@@ -407,7 +408,8 @@ __device__ uint32_t find_segment(const Seg* segs, uint32_t lo, uint32_t hi, uint
 // compress kernels
 
 __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t N, const float* __restrict__ x,
-                                                        float* __restrict__ err, float* __restrict__ pmax,
+                                                        float x_div, float* __restrict__ err,
+                                                        float* __restrict__ pmax,
                                                         uint64_t* __restrict__ span_flags, uint64_t spans,
                                                         uint32_t* __restrict__ span_tickets,
                                                         uint32_t* __restrict__ mbits,
@@ -424,8 +426,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
         // x is read once and err is not read again on most tiles: stream all
         // three accesses past the caches (measured ~10% faster on MI355X
         // than plain loads and stores)
-        const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x) + i4);
+        f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(x) + i4);
         const f4 b = __builtin_nontemporal_load(reinterpret_cast<const f4*>(err) + i4);
+        if (x_div != 1.0f) a = a / x_div;  // the workers' mean (server direction); IEEE divide
         const f4 r = a + b;
         __builtin_nontemporal_store(r, reinterpret_cast<f4*>(err) + i4);
         v[0] = r.x;
@@ -435,7 +438,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
     } else {
         for (int j = 0; j < 4; ++j) {
             if (el + j < N) {
-                v[j] = x[el + j] + err[el + j];
+                const float xj = x_div != 1.0f ? x[el + j] / x_div : x[el + j];
+                v[j] = xj + err[el + j];
                 err[el + j] = v[j];
             }
         }
@@ -694,21 +698,20 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
 
     const uint64_t ta0 = e0 / kFTile;
     if ((e0 & 3) == 0) {
-        // Active flat tiles, two at a time.  A batch issues all its loads
+        // Active flat tiles, kPackSlots / 2 at a time.  A batch issues all its loads
         // (each one predicated, no branch writes a register another branch
         // loads into), waits for them once, and only then computes and
         // writes: so no wait inside the tile can fall on a store.  Four
-        // consecutive elements never straddle two encode tiles here, so every
-        // float4 inside the tile is written back whole (unchanged where
-        // q = 0); only the last float4 of a tensor whose size is not a
-        // multiple of 4 is partial.
+        // consecutive elements never straddle two encode tiles here; only
+        // the last float4 of a tensor whose size is not a multiple of 4 is
+        // partial.
         uint32_t m = jb.fmask;
         uint32_t* const q4 = reinterpret_cast<uint32_t*>(q);
         while (m) {
-            int64_t u[4];
-            bool full[4], part[4];
+            int64_t u[kPackSlots];
+            bool full[kPackSlots], part[kPackSlots];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < kPackSlots / 2; ++h) {
                 const int f = m ? __builtin_ctz(m) : -1;
                 if (m) m &= m - 1;
 #pragma unroll
@@ -719,10 +722,10 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
                     part[slot] = u[slot] >= 0 && u[slot] < (int64_t)nel && !full[slot];
                 }
             }
-            f4 v[4];
-            float p0[4], p1[4], p2[4];
+            f4 v[kPackSlots];
+            float p0[kPackSlots], p1[kPackSlots], p2[kPackSlots];
 #pragma unroll
-            for (int slot = 0; slot < 4; ++slot) {
+            for (int slot = 0; slot < kPackSlots; ++slot) {
                 v[slot] = f4{0.0f, 0.0f, 0.0f, 0.0f};
                 p0[slot] = p1[slot] = p2[slot] = 0.0f;
                 const float* const a = err + e0 + u[slot];
@@ -734,10 +737,10 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
                 }
             }
             __builtin_amdgcn_s_waitcnt(kWaitVmem);
-            f4 nv[4];
-            int qs[4][4];
+            f4 nv[kPackSlots];
+            int qs[kPackSlots][4];
 #pragma unroll
-            for (int slot = 0; slot < 4; ++slot) {
+            for (int slot = 0; slot < kPackSlots; ++slot) {
                 if (part[slot]) v[slot] = f4{p0[slot], p1[slot], p2[slot], 0.0f};
                 qs[slot][0] = ternary(v[slot].x, thr);
                 qs[slot][1] = ternary(v[slot].y, thr);
@@ -753,14 +756,17 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
                     mark_literals(lit, (uint32_t)u[slot], qs[slot][0], qs[slot][1], qs[slot][2], qs[slot][3]);
                 }
             }
+            // only the elements with a nonzero code change (err = v already
+            // holds for the others): partial writes cost less HBM time than
+            // writing the flat tiles back whole once most tiles are active
 #pragma unroll
-            for (int slot = 0; slot < 4; ++slot) {
+            for (int slot = 0; slot < kPackSlots; ++slot) {
                 float* const a = err + e0 + u[slot];
-                if (full[slot]) *reinterpret_cast<f4*>(a) = nv[slot];
-                if (part[slot]) {
+                if (full[slot] || part[slot]) {
                     if (qs[slot][0]) a[0] = nv[slot].x;
                     if (qs[slot][1]) a[1] = nv[slot].y;
                     if (qs[slot][2]) a[2] = nv[slot].z;
+                    if (qs[slot][3]) a[3] = nv[slot].w;  // 0 for a partial float4
                 }
             }
         }
@@ -1408,7 +1414,7 @@ int check_ws(const Plan& p, void* ws, size_t ws_bytes, Layout* l) {
     return TLC_OK;
 }
 
-int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* out, uint64_t* out_lens,
+int run_compress(const Plan& p, const float* x, float x_div, float* err, float s, uint8_t* out, uint64_t* out_lens,
                  float* scales, void* ws, size_t ws_bytes, int* status, hipStream_t st) {
     if (!x || !err || !out || !out_lens || !scales || !status) return TLC_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(err) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
@@ -1429,7 +1435,7 @@ int run_compress(const Plan& p, const float* x, float* err, float s, uint8_t* ou
     const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, err, pmax, span_flags, p.d.spans, span_tickets,
+        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, span_flags, p.d.spans, span_tickets,
                                                  reinterpret_cast<uint32_t*>(scales), ctrl, status);
     });
     if (rc) return rc;
@@ -1521,8 +1527,17 @@ int tlc_compress(const float* x, float* err, uint64_t n, float s, uint8_t* out, 
                  tlc_stream_t stream) {
     if (n == 0 || n > kMaxN) return TLC_ERR_INVALID_ARG;
     if (out_capacity < tlc_compress_bound(n)) return TLC_ERR_CAPACITY;
-    return run_compress(single_plan(n), x, err, s, out, out_len, scale, workspace, workspace_bytes, status,
+    return run_compress(single_plan(n), x, 1.0f, err, s, out, out_len, scale, workspace, workspace_bytes, status,
                         static_cast<hipStream_t>(stream));
+}
+
+int tlc_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s, uint8_t* out,
+                        uint64_t out_capacity, uint64_t* out_len, float* scale, void* workspace,
+                        size_t workspace_bytes, int* status, tlc_stream_t stream) {
+    if (n == 0 || n > kMaxN || workers == 0) return TLC_ERR_INVALID_ARG;
+    if (out_capacity < tlc_compress_bound(n)) return TLC_ERR_CAPACITY;
+    return run_compress(single_plan(n), acc, (float)workers, err, s, out, out_len, scale, workspace,
+                        workspace_bytes, status, static_cast<hipStream_t>(stream));
 }
 
 int tlc_decompress(const uint8_t* in, const uint64_t* in_len, const float* scale, uint64_t n, float s, float* y,
@@ -1615,7 +1630,18 @@ int tlc_compress_group(const tlc_group_info* info, const void* d_table, const fl
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_compress(p, x, err, s, out, out_lens, scales, workspace, workspace_bytes, status,
+    return run_compress(p, x, 1.0f, err, s, out, out_lens, scales, workspace, workspace_bytes, status,
+                        static_cast<hipStream_t>(stream));
+}
+
+int tlc_server_compress_group(const tlc_group_info* info, const void* d_table, const float* acc, uint32_t workers,
+                              float* err, float s, uint8_t* out, uint64_t* out_lens, float* scales, void* workspace,
+                              size_t workspace_bytes, int* status, tlc_stream_t stream) {
+    if (workers == 0) return TLC_ERR_INVALID_ARG;
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_compress(p, acc, (float)workers, err, s, out, out_lens, scales, workspace, workspace_bytes, status,
                         static_cast<hipStream_t>(stream));
 }
 

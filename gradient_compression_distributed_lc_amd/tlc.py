@@ -49,6 +49,7 @@ _U64 = ctypes.c_uint64
 _F = ctypes.c_float
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
+_U32 = ctypes.c_uint32
 
 _SIGS = {
     "tlc_status_string": (ctypes.c_char_p, [_I]),
@@ -56,10 +57,13 @@ _SIGS = {
     "tlc_compress_bound": (_U64, [_U64]),
     "tlc_workspace_size": (_SZ, [_U64]),
     "tlc_compress": (_I, [_P, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_server_compress": (_I, [_P, _U32, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
     "tlc_decompress": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
     "tlc_decompress_accumulate": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
     "tlc_group_plan": (_I, [_P, _U64, ctypes.POINTER(GroupInfo), _P, _SZ, _P]),
     "tlc_compress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_server_compress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U32, _P, _F, _P, _P, _P, _P, _SZ,
+                                       _P, _P]),
     "tlc_decompress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ, _P, _P]),
     "tlc_decompress_accumulate_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ,
                                              _P, _P]),
@@ -172,6 +176,28 @@ def compress(x: torch.Tensor, err: torch.Tensor, s: float, *, out=None, out_len=
     return Compressed(out, out_len, scale, status, n, s)
 
 
+def server_compress(acc: torch.Tensor, workers: int, err: torch.Tensor, s: float, *, out=None, out_len=None,
+                    scale=None, workspace=None, status=None, stream=None) -> Compressed:
+    """Model-delta direction: compress the workers' mean acc / workers with the
+    server's error buffer err (updated in place)."""
+    n = acc.numel()
+    dev = acc.device
+    if err.numel() != n:
+        raise ValueError("err must have as many elements as acc")
+    out = out if out is not None else torch.empty(max(compress_bound(n), 1), dtype=torch.uint8, device=dev)
+    out_len = out_len if out_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace_size(n), dev, workspace)
+    rc = lib().tlc_server_compress(_ptr(acc, torch.float32, "acc"), workers, _ptr(err, torch.float32, "err"), n,
+                                   s, _ptr(out, torch.uint8, "out"), out.numel(),
+                                   _ptr(out_len, torch.int64, "out_len"), _ptr(scale, torch.float32, "scale"),
+                                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                   _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_server_compress")
+    return Compressed(out, out_len, scale, status, n, s)
+
+
 def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float, *, y=None,
                workspace=None, status=None, stream=None):
     """Returns (y, status)."""
@@ -255,6 +281,28 @@ class Group:
                                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                       _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_compress_group")
+        return out, out_lens, scales, status
+
+    def server_compress(self, acc, workers, err, s, *, out=None, out_lens=None, scales=None, workspace=None,
+                        status=None, stream=None):
+        """Model-delta direction: per tensor, compress acc / workers with the
+        server's error buffer err.  Returns (out, out_lens, scales, status)."""
+        if acc.numel() != self.total or err.numel() != self.total:
+            raise ValueError("acc and err must hold the whole group")
+        dev = self.device
+        out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
+        out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
+        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        workspace = workspace if workspace is not None else self.workspace()
+        rc = lib().tlc_server_compress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                             _ptr(acc, torch.float32, "acc"), workers,
+                                             _ptr(err, torch.float32, "err"), s, _ptr(out, torch.uint8, "out"),
+                                             _ptr(out_lens, torch.int64, "out_lens"),
+                                             _ptr(scales, torch.float32, "scales"),
+                                             _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                             _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_server_compress_group")
         return out, out_lens, scales, status
 
     def decompress(self, inp, in_lens, scales, s, *, y=None, workspace=None, status=None, stream=None):

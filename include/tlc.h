@@ -94,6 +94,20 @@ int tlc_compress(const float* x, float* err, uint64_t n, float s,
                  uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
                  void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
 
+/* Model-delta direction, server side (3LC page, "Proposed method", fourth
+ * item: the same pipeline compresses model deltas as well as gradients).
+ * acc[n] holds the fp32 sum of the workers' decoded payloads (for example
+ * `workers` calls of tlc_decompress_accumulate on a zeroed buffer); the
+ * server's state change is their mean, acc[i] / workers (fp32 IEEE divide),
+ * and it is compressed exactly as tlc_compress does, with the server's own
+ * error buffer err[n].  workers >= 1 (TLC_ERR_INVALID_ARG otherwise);
+ * workers == 1 is tlc_compress on acc.  acc is read only; every other
+ * argument is as for tlc_compress.  The divide is fused into the pass that
+ * reads acc and err, so the step moves the same bytes as a compress. */
+int tlc_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s,
+                        uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
+                        void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
 /* Decompress one tensor: y[i] = q_i * (M*s) for i < n, with q decoded from
  * the stream in[0 .. *in_len) (device length, so no host round trip is
  * needed after tlc_compress).  `in` must be readable for *in_len bytes.
@@ -145,6 +159,13 @@ int tlc_compress_group(const tlc_group_info* info, const void* d_table,
                        const float* x, float* err, float s,
                        uint8_t* out, uint64_t* out_lens, float* scales,
                        void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* Grouped tlc_server_compress: acc/err flat fp32[info->total_elems], per
+ * tensor mean acc / workers compressed with the server's error buffer. */
+int tlc_server_compress_group(const tlc_group_info* info, const void* d_table,
+                              const float* acc, uint32_t workers, float* err, float s,
+                              uint8_t* out, uint64_t* out_lens, float* scales,
+                              void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
 
 /* Grouped decompress into flat y[info->total_elems].  in: the grouped stream
  * buffer laid out as by tlc_compress_group; in_lens: device uint64[count];

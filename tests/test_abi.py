@@ -130,6 +130,15 @@ def test_argument_errors_return_before_any_launch():
     assert L.tlc_decompress(fake, None, fake, 10, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_accumulate(fake, fake, fake, 10, 1.99, fake, ws, 1, fake, None) == tlc.ERR_WORKSPACE
     assert L.tlc_copy_probe(fake, fake, 17, None) == tlc.ERR_INVALID_ARG
+    # server compress: no workers, no elements, capacity, s out of range
+    assert L.tlc_server_compress(fake, 0, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, fake,
+                                 None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_server_compress(fake, 8, fake, 0, 1.5, fake, 10, fake, fake, ws, 4096, fake,
+                                 None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_server_compress(fake, 8, fake, 11, 1.5, fake, 2, fake, fake, ws, 4096, fake,
+                                 None) == tlc.ERR_CAPACITY
+    assert L.tlc_server_compress(fake, 8, fake, 10, 2.0, fake, 10, fake, fake, ws, 4096, fake,
+                                 None) == tlc.ERR_INVALID_ARG
     # grouped calls: the info/table pair must be consistent
     info, _, _ = tlc.group_plan([100, 200])
     bad = tlc.GroupInfo.from_buffer_copy(info)
@@ -140,6 +149,8 @@ def test_argument_errors_return_before_any_launch():
                                 None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_group(ctypes.byref(info), fake, fake, fake, fake, 1.5, fake, ws, 16, fake,
                                   None) == tlc.ERR_WORKSPACE
+    assert L.tlc_server_compress_group(ctypes.byref(info), fake, fake, 0, fake, 1.5, fake, fake, fake, ws,
+                                       1 << 20, fake, None) == tlc.ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -7,7 +7,7 @@ benchmark uses (grouped calls over the whole gradient set):
 * resnet50     161 tensors, s in {1.0, 1.5, 1.9}, error reset for each s
 * bert_large   391 tensors, workers 0..7 (seed 500+w) each compressed from a
                zero error buffer, then the 8 payloads decompress-accumulated in
-               order into one fp32 sum
+               order into one fp32 sum, and the server's compress of their mean
 
 Everything is compared bit for bit with the CPU oracle: every tensor's stream
 and length, M, the error buffer, the decompressed values and the sum."""
@@ -100,3 +100,20 @@ def test_bert_large_eight_workers_accumulate():
         del out, lens, scales
     say("case bert_large: 8-payload sum")
     assert np.array_equal(bits(acc_d.cpu().numpy()), bits(acc_h))
+    # model-delta direction: the server compresses the workers' mean with its
+    # own (zero) error buffer; every tensor's stream, M and error bit for bit
+    say("case bert_large: server compress of the 8-worker mean")
+    err_d = torch.zeros(N, dtype=torch.float32, device="cuda:0")
+    out, lens, scales, st = g.server_compress(acc_d, 8, err_d, s, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got_out, got_lens, got_M = out.cpu().numpy(), lens.cpu().numpy(), scales.cpu().numpy()
+    got_err = bits(err_d.cpu().numpy())
+    off = 0
+    for t, n in enumerate(sizes):
+        want_st, want_M, want_e = oracle.server_compress(acc_h[off:off + n], 8, np.zeros(n, np.float32), s)
+        o, L = g.offsets[t], int(got_lens[t])
+        assert got_M[t] == want_M, t
+        assert L == want_st.size and np.array_equal(got_out[o:o + L], want_st), t
+        assert np.array_equal(got_err[off:off + n], bits(want_e)), t
+        off += n
