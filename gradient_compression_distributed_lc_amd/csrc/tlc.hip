@@ -74,6 +74,13 @@ constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (abo
 constexpr int kWaitVmem = 0x0F70;
 constexpr uint32_t kPackGrid = 2048;              // blocks of k_quant_pack
 constexpr int kPackSlots = 4;                     // float4 loads per lane in one k_quant_pack batch (two flat tiles)
+// Candidate lists: the first pass keeps, per flat tile, the elements that can
+// still reach the threshold (see cand_bound), so that the second pass need
+// not read the flat tile again.
+constexpr uint32_t kCand = 64;                    // list slots per flat tile
+constexpr float kCandFrac = 0.475f;               // candidate bound = hint * s * kCandFrac
+constexpr uint16_t kCandNone = 0xFFFF;            // count of a flat tile without a usable list
+constexpr uint32_t kCandOk = 0x80000000u;         // PackJob.fmask flag: the tensor's lists are complete
 constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (about what is resident at once)
 
 // look-back word: 2 status bits | 62 payload bits
@@ -117,7 +124,7 @@ struct PackJob {
     uint64_t e0;     // group element offset of the tile's first element
     uint32_t et;     // encode tile index in the group (carry word, staging slot)
     uint32_t nel;    // elements in the tile
-    uint32_t fmask;  // bit k: flat tile e0 / kFTile + k holds |v| >= thr
+    uint32_t fmask;  // bit k: flat tile e0 / kFTile + k holds |v| >= thr; kCandOk: lists complete
     float thr;       // selection threshold of the tensor
     float ms;        // M * s of the tensor
     uint32_t gi;     // tensor
@@ -138,6 +145,17 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ float wave_max(float v) {
     for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
     return v;
+}
+
+__device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t* total) {
+    const int lane = lane_id();
+    uint32_t inc = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    *total = __shfl(inc, 63, 64);
+    return inc - v;
 }
 
 __device__ float block_max(float v, float* sm) {
@@ -373,6 +391,19 @@ __device__ __forceinline__ uint8_t remainder_code(uint32_t m) {  // m = 1..13
     return (uint8_t)(m == 1 ? kZero : kRunBase + m);
 }
 
+// Candidate bound of a tensor from a hint of its M (normally the previous
+// step's): an element with |v| below it has q = 0 whenever the threshold of
+// this step is at least the bound, which the second pass checks before it
+// relies on the lists.  Any hint is allowed: a missing or wrong one only
+// sends tensors or flat tiles down the full re-read.  kCandFrac = 0.95 of
+// the threshold M*s/2 at M = hint: a step whose M is within 5% below the
+// hint still uses the lists (measured on the BERT-large set under error
+// feedback: 5% keeps ~90% of the tensors, and the lists hold ~5% of the
+// elements; 10% doubles the lists for few more tensors).
+__device__ __forceinline__ float cand_bound(float hint, float s) {
+    return (hint > 0.0f && hint <= FLT_MAX) ? hint * s * kCandFrac : INFINITY;
+}
+
 // Smallest float a with |v| >= a  <=>  rint(v / Ms) != 0 for fp32 v, where
 // v / Ms is the correctly rounded fp32 quotient.  For |v| <= M <= Ms the
 // quotient rounds to a value > 0.5 exactly when the real quotient exceeds the
@@ -409,12 +440,16 @@ __device__ uint32_t find_segment(const Seg* segs, uint32_t lo, uint32_t hi, uint
 
 __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t N, const float* __restrict__ x,
                                                         float x_div, float* __restrict__ err,
-                                                        float* __restrict__ pmax,
+                                                        float* __restrict__ pmax, const float* __restrict__ hint,
+                                                        float s, uint16_t* __restrict__ cand_cnt,
+                                                        uint16_t* __restrict__ cand_idx,
+                                                        float* __restrict__ cand_val,
                                                         uint64_t* __restrict__ span_flags, uint64_t spans,
                                                         uint32_t* __restrict__ span_tickets,
                                                         uint32_t* __restrict__ mbits,
                                                         uint32_t* __restrict__ ctrl, int* __restrict__ status) {
     __shared__ float sm[kAccThreads / 64];
+    __shared__ uint32_t s_cc[kAccThreads / 64];
     __shared__ uint32_t s_part[kFTile];  // per-tensor maxima of a tile that spans tensors
     __shared__ uint32_t s_last;
     const uint32_t t = blockIdx.x;
@@ -446,7 +481,18 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
     }
     if (!(info & kStraddle)) {
         const float m = wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-        if (lane_id() == 0) sm[wave_id()] = m;
+        // the tile's candidate list (elements with |v| >= the tensor's bound)
+        const float cb = cand_bound(hint[info], s);
+        uint32_t cm = 0, cex = 0, ctot = 0;
+        if (cb != INFINITY) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cm |= (uint32_t)(fabsf(v[j]) >= cb) << j;
+            if (__ballot(cm != 0)) cex = wave_excl_sum((uint32_t)__popc(cm), &ctot);  // most waves have none
+        }
+        if (lane_id() == 0) {
+            sm[wave_id()] = m;
+            s_cc[wave_id()] = ctot;
+        }
         __syncthreads();
         if (threadIdx.x == 0) {
             float r = sm[0];
@@ -454,6 +500,24 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
             for (int k = 1; k < kAccThreads / 64; ++k) r = fmaxf(r, sm[k]);
             pmax[t + info] = r;
         }
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < kAccThreads / 64; ++k) {
+            before += k < wave_id() ? s_cc[k] : 0u;
+            total += s_cc[k];
+        }
+        if (cb != INFINITY && total <= kCand) {
+            uint64_t pos = (uint64_t)t * kCand + before + cex;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if ((cm >> j) & 1) {
+                    cand_idx[pos] = (uint16_t)(4 * threadIdx.x + j);
+                    cand_val[pos] = v[j];
+                    ++pos;
+                }
+            }
+        }
+        if (threadIdx.x == 0) cand_cnt[t] = (cb != INFINITY && total <= kCand) ? (uint16_t)total : kCandNone;
     } else {
         // the tile spans tensors g0..g1: one partial max per tensor, in slot t + g
         const uint32_t g0 = info & ~kStraddle;
@@ -472,6 +536,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
         }
         __syncthreads();
         for (uint32_t k = threadIdx.x; k <= s_last - g0; k += kAccThreads) pmax[t + g0 + k] = __uint_as_float(s_part[k]);
+        if (threadIdx.x == 0) cand_cnt[t] = kCandNone;  // a tile shared by tensors is read again in full
     }
     // look-back state of k_emit starts empty on every call
     for (uint64_t i = (uint64_t)t * kAccThreads + threadIdx.x; i < spans; i += (uint64_t)gridDim.x * kAccThreads)
@@ -508,7 +573,9 @@ __device__ __forceinline__ float etile_max(const float* pm, const Seg& sg, uint3
 // wave leaves one atomic per tensor and wave; M (zeroed by k_accum_max) is
 // kept as float bits, whose unsigned order is that of non-negative floats.
 __global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t etiles, const float* __restrict__ pmax,
-                                                       float* __restrict__ etmax, uint32_t* __restrict__ mbits) {
+                                                       float* __restrict__ etmax, uint32_t* __restrict__ mbits,
+                                                       const float* __restrict__ hint, float s,
+                                                       float* __restrict__ seg_cb) {
     const uint32_t e = blockIdx.x * kThreads + threadIdx.x;
     const int lane = lane_id();
     const bool ok = e < etiles;
@@ -518,6 +585,9 @@ __global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t eti
         const Seg sg = load_seg(g, gi);
         mx = etile_max(pmax + gi, sg, e - sg.etile0);  // flat tile t of tensor gi: slot t + gi
         etmax[e] = mx;
+        // the bound the first pass used for the tensor's candidate lists (the
+        // hint is the caller's M buffer, rewritten only by k_tile_activity)
+        if (e == sg.etile0) seg_cb[gi] = cand_bound(hint[gi], s);
     }
     for (int d = 1; d < 64; d <<= 1) {
         const float o = __shfl_up(mx, d, 64);
@@ -536,7 +606,9 @@ __global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t eti
 __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_t etiles, float s,
                                                             const float* __restrict__ pmax,
                                                             const float* __restrict__ etmax,
-                                                            const float* __restrict__ scales,
+                                                            const uint32_t* __restrict__ mbits,
+                                                            const float* __restrict__ seg_cb,
+                                                            float* __restrict__ scales,
                                                             uint64_t* __restrict__ etile_agg,
                                                             PackJob* __restrict__ jobs, uint32_t* __restrict__ ctrl) {
     __shared__ uint32_t s_u[kWaves];
@@ -550,12 +622,13 @@ __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_
         gis[r] = e < etiles ? etile_owner(g, e) : 0u;
     }
     Seg sgs[kActPerThread];
-    float ms_[kActPerThread], tmax[kActPerThread];
+    float ms_[kActPerThread], tmax[kActPerThread], cbs[kActPerThread];
 #pragma unroll
     for (int r = 0; r < kActPerThread; ++r) {
         const uint32_t e = base + r * kThreads + threadIdx.x;
         sgs[r] = load_seg(g, gis[r]);
-        ms_[r] = scales[gis[r]];
+        ms_[r] = __uint_as_float(mbits[gis[r]]);
+        cbs[r] = seg_cb[gis[r]];
         tmax[r] = e < etiles ? etmax[e] : 0.0f;
     }
     uint32_t mask = 0;
@@ -569,6 +642,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_
             const float ms = m * s;
             const float thr = select_threshold(m, ms);
             const uint32_t j = e - sg.etile0;
+            if (j == 0) scales[gis[r]] = m;  // the caller's M (it held the hint until now)
             if (tmax[r] >= thr) {
                 mask |= 1u << r;
                 jb[r].e0 = sg.elem_off + (uint64_t)j * kETile;
@@ -604,6 +678,9 @@ __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_
         uint32_t fm = 0;
 #pragma unroll
         for (int k = 0; k < kSub; ++k) fm |= (uint32_t)(pv[r][k] >= jb[r].thr) << k;
+        // every element with a nonzero code is on its flat tile's list when
+        // the threshold is at least the bound the lists were cut at
+        if (jb[r].thr >= cbs[r] && (jb[r].e0 & 3) == 0) fm |= kCandOk;
         jb[r].fmask = fm;
     }
     // compaction: one atomic per block
@@ -623,17 +700,6 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t* total) {
-    const int lane = lane_id();
-    uint32_t inc = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += o;
-    }
-    *total = __shfl(inc, 63, 64);
-    return inc - v;
 }
 
 __device__ __forceinline__ int wave_excl_max(int v, int* total) {
@@ -678,7 +744,9 @@ __device__ __forceinline__ void mark_literals(uint32_t* lit, uint32_t u, int q0,
 // the zero-run encoding then works literal by literal (64 per round), which
 // costs nothing for the runs of byte 121 that make up most of a tile.
 __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* __restrict__ etile_agg,
-                          uint8_t* __restrict__ staging, int8_t* slice) {
+                          uint8_t* __restrict__ staging, const uint16_t* __restrict__ cand_cnt,
+                          const uint16_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
+                          int8_t* slice) {
     const int lane = lane_id();
     const uint64_t e0 = jb.e0;
     const uint32_t et = jb.et, nel = jb.nel;
@@ -697,6 +765,62 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
     if (lane < 32) lit[lane] = 0u;
 
     const uint64_t ta0 = e0 / kFTile;
+    uint32_t m = jb.fmask & ~kCandOk;  // active flat tiles still to be read in full
+    if (jb.fmask & kCandOk) {
+        // Flat tiles with a list: every element with a nonzero code is on it,
+        // with its v, so only the list is read.  Lane f < 11 holds flat tile
+        // ta0 + f; the lists are taken 4 x 64 candidates per round.
+        const uint32_t nft = (uint32_t)((e0 + nel - 1) / kFTile - ta0) + 1;
+        const bool act = (uint32_t)lane < nft && ((m >> lane) & 1);
+        const uint32_t c = act ? cand_cnt[ta0 + lane] : 0u;
+        const uint32_t ovf = (uint32_t)__ballot(act && c == kCandNone);
+        uint32_t C;
+        const uint32_t pre = wave_excl_sum(act && c != kCandNone ? c : 0u, &C);
+        uint32_t pres[kETile / kFTile + 1];  // first candidate number of each flat tile
+#pragma unroll
+        for (int f = 0; f <= (int)(kETile / kFTile); ++f) pres[f] = __shfl(pre, f, 64);
+        for (uint32_t base = 0; base < C; base += 4 * 64) {
+            uint64_t at[4];
+            uint32_t idx[4];
+            float val[4];
+            bool ok[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t k = base + 64 * r + lane;
+                ok[r] = k < C;
+                int f = 0;      // last flat tile whose first candidate number is <= k
+                uint32_t pf = 0;
+#pragma unroll
+                for (int j = 1; j <= (int)(kETile / kFTile); ++j) {
+                    const bool le = pres[j] <= k && (uint32_t)j < nft;
+                    f = le ? j : f;
+                    pf = le ? pres[j] : pf;
+                }
+                at[r] = (ta0 + f) * kCand + (k - pf);
+                idx[r] = 0;
+                val[r] = 0.0f;
+                if (ok[r]) {
+                    idx[r] = cand_idx[at[r]];
+                    val[r] = cand_val[at[r]];
+                }
+                at[r] = (ta0 + f) * kFTile;  // the flat tile's first element
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmem);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t u = (int64_t)(at[r] + idx[r]) - (int64_t)e0;  // tile element
+                if (ok[r] && u >= 0 && u < (int64_t)nel) {
+                    const int qq = ternary(val[r], thr);
+                    if (qq) {
+                        err[e0 + u] = val[r] - (float)qq * ms;
+                        q[u] = (int8_t)qq;
+                        atomicOr(lit + (((uint32_t)u / 5) >> 5), 1u << (((uint32_t)u / 5) & 31));
+                    }
+                }
+            }
+        }
+        m = ovf;
+    }
     if ((e0 & 3) == 0) {
         // Active flat tiles, kPackSlots / 2 at a time.  A batch issues all its loads
         // (each one predicated, no branch writes a register another branch
@@ -705,7 +829,6 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
         // consecutive elements never straddle two encode tiles here; only
         // the last float4 of a tensor whose size is not a multiple of 4 is
         // partial.
-        uint32_t m = jb.fmask;
         uint32_t* const q4 = reinterpret_cast<uint32_t*>(q);
         while (m) {
             int64_t u[kPackSlots];
@@ -773,7 +896,7 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
     } else {
         // a tensor that starts off a 16-byte boundary: element by element
         for (uint32_t u = lane; u < nel; u += 64) {
-            if ((jb.fmask >> ((e0 + u) / kFTile - ta0)) & 1) {
+            if ((m >> ((e0 + u) / kFTile - ta0)) & 1) {
                 const float vv = err[e0 + u];
                 const int qq = ternary(vv, thr);
                 if (qq) {
@@ -864,13 +987,16 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
 __global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err, const PackJob* __restrict__ jobs,
                                                          const uint32_t* __restrict__ ctrl,
                                                          uint64_t* __restrict__ etile_agg,
-                                                         uint8_t* __restrict__ staging) {
+                                                         uint8_t* __restrict__ staging,
+                                                         const uint16_t* __restrict__ cand_cnt,
+                                                         const uint16_t* __restrict__ cand_idx,
+                                                         const float* __restrict__ cand_val) {
     __shared__ __align__(16) int8_t s_q[kWaves * kSlice];
     const uint32_t na = ctrl[1];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
     const uint32_t waves = gridDim.x * kWaves;
     for (uint32_t i = blockIdx.x * kWaves + wave; i < na; i += waves)
-        pack_tile(jobs[i], err, etile_agg, staging, s_q + wave * kSlice);
+        pack_tile(jobs[i], err, etile_agg, staging, cand_cnt, cand_idx, cand_val, s_q + wave * kSlice);
 }
 
 // Largest span output assembled in LDS by k_emit (an all-zero span of 256
@@ -1328,7 +1454,7 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, etile_agg, etmax, active, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
+    size_t ctrl, pmax, etile_agg, etmax, active, mbits, seg_cb, cand_cnt, cand_idx, cand_val, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
         total;
 };
 
@@ -1345,6 +1471,11 @@ Layout ws_layout(const Dims& d) {
     l.etile_agg = take(d.etiles * sizeof(uint64_t));
     l.etmax = take(d.etiles * sizeof(float));
     l.active = take(d.etiles * sizeof(PackJob));
+    l.mbits = take(d.count * sizeof(uint32_t));
+    l.seg_cb = take(d.count * sizeof(float));
+    l.cand_cnt = take(d.ftiles * sizeof(uint16_t));
+    l.cand_idx = take(d.ftiles * kCand * sizeof(uint16_t));
+    l.cand_val = take(d.ftiles * kCand * sizeof(float));
     l.span_flags = take(d.spans * sizeof(uint64_t));
     l.span_tickets = take(d.count * sizeof(uint32_t));
     l.chunk_tickets = take(d.count * sizeof(uint32_t));
@@ -1427,6 +1558,11 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     uint64_t* etile_agg = reinterpret_cast<uint64_t*>(w + l.etile_agg);
     float* etmax = reinterpret_cast<float*>(w + l.etmax);
     PackJob* jobs = reinterpret_cast<PackJob*>(w + l.active);
+    uint32_t* mbits = reinterpret_cast<uint32_t*>(w + l.mbits);
+    float* seg_cb = reinterpret_cast<float*>(w + l.seg_cb);
+    uint16_t* cand_cnt = reinterpret_cast<uint16_t*>(w + l.cand_cnt);
+    uint16_t* cand_idx = reinterpret_cast<uint16_t*>(w + l.cand_idx);
+    float* cand_val = reinterpret_cast<float*>(w + l.cand_val);
     uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
     uint32_t* span_tickets = reinterpret_cast<uint32_t*>(w + l.span_tickets);
     uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
@@ -1435,24 +1571,27 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, span_flags, p.d.spans, span_tickets,
-                                                 reinterpret_cast<uint32_t*>(scales), ctrl, status);
+        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, scales, s, cand_cnt, cand_idx,
+                                                 cand_val, span_flags, p.d.spans, span_tickets, mbits, ctrl,
+                                                 status);
     });
     if (rc) return rc;
     const uint32_t etiles = (uint32_t)p.d.etiles;
     rc = launch("tlc_tile_max", st, [&] {
-        k_tile_max<<<(etiles + kThreads - 1) / kThreads, kThreads, 0, st>>>(g, etiles, pmax, etmax,
-                                                                           reinterpret_cast<uint32_t*>(scales));
+        k_tile_max<<<(etiles + kThreads - 1) / kThreads, kThreads, 0, st>>>(g, etiles, pmax, etmax, mbits,
+                                                                           scales, s, seg_cb);
     });
     if (rc) return rc;
     rc = launch("tlc_tile_activity", st, [&] {
         constexpr uint32_t per_block = kThreads * kActPerThread;
-        k_tile_activity<<<(etiles + per_block - 1) / per_block, kThreads, 0, st>>>(g, etiles, s, pmax, etmax, scales,
-                                                                                 etile_agg, jobs, ctrl);
+        k_tile_activity<<<(etiles + per_block - 1) / per_block, kThreads, 0, st>>>(g, etiles, s, pmax, etmax, mbits,
+                                                                                 seg_cb, scales, etile_agg, jobs,
+                                                                                 ctrl);
     });
     if (rc) return rc;
     rc = launch("tlc_quant_pack", st, [&] {
-        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging);
+        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging, cand_cnt, cand_idx,
+                                                     cand_val);
     });
     if (rc) return rc;
     return launch("tlc_emit", st, [&] {

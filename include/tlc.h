@@ -88,7 +88,12 @@ size_t tlc_workspace_size(uint64_t n);
  *   s           sparsity multiplier, 1 <= s < 2.
  *   out         stream bytes, capacity out_capacity >= tlc_compress_bound(n).
  *   out_len     (device uint64) receives the stream length L <= ceil(n/5).
- *   scale       (device fp32) receives M = max|x+err|.
+ *   scale       (device fp32) receives M = max|x+err|.  On entry it is read as
+ *               a hint: when it still holds the previous step's M (the same
+ *               buffer passed every step), the second pass reads only short
+ *               per-tile lists of the values that can reach the threshold
+ *               instead of the error buffer.  Any content is allowed: a
+ *               missing or stale hint only costs speed, never changes a bit.
  *   status      (device int), see above. */
 int tlc_compress(const float* x, float* err, uint64_t n, float s,
                  uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
@@ -154,7 +159,8 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info,
 
 /* Grouped compress.  x/err: flat fp32[info->total_elems]; out: bytes
  * [info->stream_bytes]; out_lens: device uint64[count]; scales: device
- * fp32[count]. */
+ * fp32[count], read on entry as per-tensor hints exactly as `scale` is in
+ * tlc_compress. */
 int tlc_compress_group(const tlc_group_info* info, const void* d_table,
                        const float* x, float* err, float s,
                        uint8_t* out, uint64_t* out_lens, float* scales,

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 
-from gpu_util import bits, check_group, check_single, say, to_dev
+from gpu_util import bits, check_group, check_single, oracle_group_compress, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -259,3 +259,56 @@ def test_group_of_tiny_tensors():
     for s in (1.0, 1.9):
         say(f"case tiny tensors s={s}")
         check_group(g, x, e, s, label=f"tiny s={s}")
+
+
+def test_hint_paths_give_identical_results():
+    # The M buffer is read on entry as a hint for the second pass's candidate
+    # lists.  Exact, too-large (lists rejected), too-small (lists overflow),
+    # and invalid hints must all give the oracle's bits; so must the steady
+    # case where each call's M is the next call's hint.
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(5)
+    sizes = [3 * TILE + 1, 17, 40_000, 5, 2 * TILE, 100_003]
+    g = tlc.Group(sizes)
+    N = sum(sizes)
+    for dense in (False, True):
+        x = (rng.standard_normal(N) * 1e-3).astype(np.float32)
+        if dense:
+            x = np.clip((rng.standard_cauchy(N) * 1e-3).astype(np.float32), -1, 1)
+        e = (rng.standard_normal(N) * 3e-4).astype(np.float32)
+        streams, Ms, e_new = oracle_group_compress(x, e, sizes, 1.5)
+        hints = {"exact": Ms, "double": Ms * 2, "half": Ms * 0.5, "zero": np.zeros_like(Ms),
+                 "nan": np.full_like(Ms, np.nan), "inf": np.full_like(Ms, np.inf), "neg": -Ms,
+                 "denormal": np.full_like(Ms, 1e-40)}
+        for name, h in hints.items():
+            say(f"case hint {name} dense={dense}")
+            ed = to_dev(e)
+            scales = to_dev(h.astype(np.float32))
+            out, lens, sc, st = g.compress(to_dev(x), ed, 1.5, scales=scales)
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0, name
+            assert np.array_equal(bits(sc.cpu().numpy()), bits(Ms)), name
+            got = out.cpu().numpy()
+            for t, n in enumerate(sizes):
+                L = int(lens[t].item())
+                assert L == streams[t].size and np.array_equal(got[g.offsets[t]:g.offsets[t] + L], streams[t]), (
+                    name, dense, t)
+            assert np.array_equal(bits(ed.cpu().numpy()), bits(e_new)), (name, dense)
+    # steady: the same M buffer every step, error carried
+    ed = torch.zeros(N, dtype=torch.float32, device="cuda:0")
+    scales = torch.zeros(len(sizes), dtype=torch.float32, device="cuda:0")
+    e_cpu = np.zeros(N, np.float32)
+    for step in range(8):
+        say(f"case hint steady step {step}")
+        x = (rng.standard_normal(N) * 1e-3).astype(np.float32)
+        streams, Ms, e_cpu = oracle_group_compress(x, e_cpu, sizes, 1.75)
+        out, lens, sc, st = g.compress(to_dev(x), ed, 1.75, scales=scales)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert np.array_equal(bits(scales.cpu().numpy()), bits(Ms)), step
+        got = out.cpu().numpy()
+        for t, n in enumerate(sizes):
+            L = int(lens[t].item())
+            assert L == streams[t].size and np.array_equal(got[g.offsets[t]:g.offsets[t] + L], streams[t]), (step, t)
+        assert np.array_equal(bits(ed.cpu().numpy()), bits(e_cpu)), step
