@@ -17,9 +17,11 @@ Printed: one JSON line with the whole-job throughput in GB/s of fp32 input
 dominant kernel (the 12-byte/element pass over x and err) measured with HIP
 events inside the timed region, bits per value, and the CPU oracle timed on
 the host over the same workload.  Also reported, outside the timed steps:
-compress and decompress timed apart, the 8-payload accumulate, and the
-model-delta direction's server step (the workers' sum, then the compress of
-their mean with the server's error buffer).
+compress and decompress timed apart, the 8-payload accumulate, the same
+step after --steady-steps steps of error feedback (the error buffer then
+keeps every encode tile active and the streams are about twice as dense),
+and the model-delta direction's server step (the workers' sum, then the
+compress of their mean with the server's error buffer).
 
     python bench.py [--steps K] [--warmup W] [--workload bert_large] [--no-cpu]
 """
@@ -119,6 +121,8 @@ def main():
     ap.add_argument("--pool", type=int, default=32, help="distinct gradient sets cycled through (HBM: 4 B/value each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-bandwidth yardstick")
+    ap.add_argument("--steady-steps", type=int, default=150,
+                    help="error-feedback steps before the steady-state figure (0: skip it)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -282,6 +286,27 @@ def main():
     srv_comp_ms = s1.elapsed_time(s2) / ks
     L_srv = int(lens_srv.sum().item())
 
+    # steady state of error feedback: the same step continued until the error
+    # buffer has filled (every encode tile active, denser streams), then timed
+    steady = None
+    if args.steady_steps > 0:
+        while counter[0] < args.steady_steps:
+            step()
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record()
+        for _ in range(10):
+            step()
+        q1.record()
+        torch.cuda.synchronize()
+        st_ms = q0.elapsed_time(q1) / 10
+        if (int(st_c.item()), int(st_d.item())) != (0, 0):
+            raise SystemExit("device status not ok in the steady-state steps")
+        steady = {"after_steps": counter[0] - 10, "ms_per_step": round(st_ms, 4),
+                  "GBps_fp32_in": round(4.0 * N / (st_ms * 1e-3) / 1e9, 1),
+                  "bits_per_value": round(8.0 * float(lens.sum().item()) / N, 4)}
+
+
     # copy yardstick: what a plain streaming copy reaches on this GPU
     copy_gbps = None
     if not args.no_copy:
@@ -371,6 +396,7 @@ def main():
         "server_bits_per_value": round(8.0 * L_srv / N, 4),
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
+        "steady_state": steady,
         "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "wall_s_timed": round(wall, 3),
         "kernel_source": kernel_source_hash(),
