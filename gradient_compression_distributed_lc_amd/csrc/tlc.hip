@@ -442,8 +442,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
                                                         float x_div, float* __restrict__ err,
                                                         float* __restrict__ pmax, const float* __restrict__ hint,
                                                         float s, uint16_t* __restrict__ cand_cnt,
-                                                        uint16_t* __restrict__ cand_idx,
-                                                        float* __restrict__ cand_val,
+                                                        uint2* __restrict__ cand,
                                                         uint64_t* __restrict__ span_flags, uint64_t spans,
                                                         uint32_t* __restrict__ span_tickets,
                                                         uint32_t* __restrict__ mbits,
@@ -483,11 +482,21 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
         const float m = wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
         // the tile's candidate list (elements with |v| >= the tensor's bound)
         const float cb = cand_bound(hint[info], s);
-        uint32_t cm = 0, cex = 0, ctot = 0;
+        // a list is in no particular order: component j of every lane, lane by
+        // lane, after components 0..j-1; positions come from the ballots
+        uint32_t cm = 0, ctot = 0, cpos[4] = {0u, 0u, 0u, 0u};
         if (cb != INFINITY) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) cm |= (uint32_t)(fabsf(v[j]) >= cb) << j;
-            if (__ballot(cm != 0)) cex = wave_excl_sum((uint32_t)__popc(cm), &ctot);  // most waves have none
+            if (__ballot(cm != 0)) {  // most waves have none
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint64_t b = __ballot((cm >> j) & 1);
+                    cpos[j] = ctot + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                    ctot += (uint32_t)__popcll(b);
+                }
+            }
         }
         if (lane_id() == 0) {
             sm[wave_id()] = m;
@@ -507,15 +516,10 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
             total += s_cc[k];
         }
         if (cb != INFINITY && total <= kCand) {
-            uint64_t pos = (uint64_t)t * kCand + before + cex;
+            uint2* const lst = cand + (uint64_t)t * kCand + before;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if ((cm >> j) & 1) {
-                    cand_idx[pos] = (uint16_t)(4 * threadIdx.x + j);
-                    cand_val[pos] = v[j];
-                    ++pos;
-                }
-            }
+            for (int j = 0; j < 4; ++j)
+                if ((cm >> j) & 1) lst[cpos[j]] = make_uint2(4 * threadIdx.x + j, __float_as_uint(v[j]));
         }
         if (threadIdx.x == 0) cand_cnt[t] = (cb != INFINITY && total <= kCand) ? (uint16_t)total : kCandNone;
     } else {
@@ -745,7 +749,7 @@ __device__ __forceinline__ void mark_literals(uint32_t* lit, uint32_t u, int q0,
 // costs nothing for the runs of byte 121 that make up most of a tile.
 __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* __restrict__ etile_agg,
                           uint8_t* __restrict__ staging, const uint16_t* __restrict__ cand_cnt,
-                          const uint16_t* __restrict__ cand_idx, const float* __restrict__ cand_val,
+                          const uint2* __restrict__ cand,
                           int8_t* slice) {
     const int lane = lane_id();
     const uint64_t e0 = jb.e0;
@@ -800,8 +804,9 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
                 idx[r] = 0;
                 val[r] = 0.0f;
                 if (ok[r]) {
-                    idx[r] = cand_idx[at[r]];
-                    val[r] = cand_val[at[r]];
+                    const uint2 c2 = cand[at[r]];
+                    idx[r] = c2.x;
+                    val[r] = __uint_as_float(c2.y);
                 }
                 at[r] = (ta0 + f) * kFTile;  // the flat tile's first element
             }
@@ -989,19 +994,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err
                                                          uint64_t* __restrict__ etile_agg,
                                                          uint8_t* __restrict__ staging,
                                                          const uint16_t* __restrict__ cand_cnt,
-                                                         const uint16_t* __restrict__ cand_idx,
-                                                         const float* __restrict__ cand_val) {
+                                                         const uint2* __restrict__ cand) {
     __shared__ __align__(16) int8_t s_q[kWaves * kSlice];
     const uint32_t na = ctrl[1];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
     const uint32_t waves = gridDim.x * kWaves;
     for (uint32_t i = blockIdx.x * kWaves + wave; i < na; i += waves)
-        pack_tile(jobs[i], err, etile_agg, staging, cand_cnt, cand_idx, cand_val, s_q + wave * kSlice);
+        pack_tile(jobs[i], err, etile_agg, staging, cand_cnt, cand, s_q + wave * kSlice);
 }
 
 // Largest span output assembled in LDS by k_emit (an all-zero span of 256
-// encode tiles needs ~18.7 KB); larger spans take the two-pass path.
-constexpr uint32_t kEmitLds = 24576;
+// encode tiles needs ~18.7 KB, a span of the BERT-large set after many
+// error-feedback steps ~39 KB); larger spans take the two-pass path.
+constexpr uint32_t kEmitLds = 49152;
 
 // One block per span of 256 encode tiles of a tensor: block scan of the
 // tiles' carry summaries, decoupled look-back across the tensor's spans for
@@ -1454,7 +1459,7 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, etile_agg, etmax, active, mbits, seg_cb, cand_cnt, cand_idx, cand_val, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
+    size_t ctrl, pmax, etile_agg, etmax, active, mbits, seg_cb, cand_cnt, cand, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
         total;
 };
 
@@ -1474,8 +1479,7 @@ Layout ws_layout(const Dims& d) {
     l.mbits = take(d.count * sizeof(uint32_t));
     l.seg_cb = take(d.count * sizeof(float));
     l.cand_cnt = take(d.ftiles * sizeof(uint16_t));
-    l.cand_idx = take(d.ftiles * kCand * sizeof(uint16_t));
-    l.cand_val = take(d.ftiles * kCand * sizeof(float));
+    l.cand = take(d.ftiles * kCand * sizeof(uint2));
     l.span_flags = take(d.spans * sizeof(uint64_t));
     l.span_tickets = take(d.count * sizeof(uint32_t));
     l.chunk_tickets = take(d.count * sizeof(uint32_t));
@@ -1561,8 +1565,7 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     uint32_t* mbits = reinterpret_cast<uint32_t*>(w + l.mbits);
     float* seg_cb = reinterpret_cast<float*>(w + l.seg_cb);
     uint16_t* cand_cnt = reinterpret_cast<uint16_t*>(w + l.cand_cnt);
-    uint16_t* cand_idx = reinterpret_cast<uint16_t*>(w + l.cand_idx);
-    float* cand_val = reinterpret_cast<float*>(w + l.cand_val);
+    uint2* cand = reinterpret_cast<uint2*>(w + l.cand);
     uint64_t* span_flags = reinterpret_cast<uint64_t*>(w + l.span_flags);
     uint32_t* span_tickets = reinterpret_cast<uint32_t*>(w + l.span_tickets);
     uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
@@ -1571,8 +1574,8 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
     rc = launch("tlc_accum_max", st, [&] {
-        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, scales, s, cand_cnt, cand_idx,
-                                                 cand_val, span_flags, p.d.spans, span_tickets, mbits, ctrl,
+        k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, scales, s, cand_cnt, cand,
+                                                 span_flags, p.d.spans, span_tickets, mbits, ctrl,
                                                  status);
     });
     if (rc) return rc;
@@ -1590,8 +1593,7 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     });
     if (rc) return rc;
     rc = launch("tlc_quant_pack", st, [&] {
-        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging, cand_cnt, cand_idx,
-                                                     cand_val);
+        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging, cand_cnt, cand);
     });
     if (rc) return rc;
     return launch("tlc_emit", st, [&] {

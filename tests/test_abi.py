@@ -46,10 +46,10 @@ def test_workspace_size():
     small, big = tlc.workspace_size(1), tlc.workspace_size(335_000_000)
     assert 0 < small <= 8192 and small % 256 == 0
     # staging for the zero-run bytes of tiles with nonzero codes (ceil(n/5)); per 512-element flat
-    # tile a partial max and a candidate list (count + 64 x (u16 index, f32 value)); a carry
+    # tile a partial max and a candidate list (count + 64 x (u32 index, f32 value)); a carry
     # word, a max and a 32-byte job per 5120-element encode tile; small per-call state
     n = 335_000_000
-    assert big < n // 5 + (4 + 2 + 64 * 6) * (n // 512) + 48 * (n // 5120) + 1_000_000
+    assert big < n // 5 + (4 + 2 + 64 * 8) * (n // 512) + 48 * (n // 5120) + 1_000_000
     assert big % 256 == 0
 
 
