@@ -1005,8 +1005,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err
 
 // Largest span output assembled in LDS by k_emit (an all-zero span of 256
 // encode tiles needs ~18.7 KB, a span of the BERT-large set after many
-// error-feedback steps ~39 KB); larger spans take the two-pass path.
-constexpr uint32_t kEmitLds = 49152;
+// error-feedback steps ~39 KB); larger spans take the two-pass path.  With
+// the block's other arrays this keeps three blocks per CU (160 KB of LDS),
+// so the ~560 spans of a 340M-value set are resident at once.
+constexpr uint32_t kEmitLds = 40960;
 
 // One block per span of 256 encode tiles of a tensor: block scan of the
 // tiles' carry summaries, decoupled look-back across the tensor's spans for
