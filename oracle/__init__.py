@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
             "tlco_decompress": (ctypes.c_int, [P, U64, F, U64, F, P]),
             "tlco_decompress_accumulate": (ctypes.c_int, [P, U64, F, U64, F, P]),
             "tlco_server_compress": (ctypes.c_int, [P, ctypes.c_uint32, P, U64, F, P, U64, P, P]),
+            "tlco_fixed_len": (U64, [U64, ctypes.c_int]),
+            "tlco_pack_fixed": (ctypes.c_int, [P, U64, ctypes.c_int, P]),
+            "tlco_unpack_fixed": (ctypes.c_int, [P, U64, ctypes.c_int, P]),
+            "tlco_compress_fixed": (ctypes.c_int, [P, P, U64, F, ctypes.c_int, P, U64, P]),
+            "tlco_decompress_fixed": (ctypes.c_int, [P, F, U64, F, ctypes.c_int, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -195,6 +200,50 @@ def server_compress(acc, workers: int, err, s: float):
     _check(lib().tlco_server_compress(_ptr(acc), workers, _ptr(e), acc.size, s, _ptr(out), cap,
                                       ctypes.byref(L), ctypes.byref(M)), "server_compress")
     return out[: L.value].copy(), np.float32(M.value), e
+
+
+ENC_QUARTIC = 1  # quartic bytes without zero-run encoding
+ENC_TWOBIT = 2   # 2-bit fields, four values per byte
+
+
+def fixed_len(n: int, encoding: int) -> int:
+    return int(lib().tlco_fixed_len(n, encoding))
+
+
+def pack_fixed(q, encoding: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    out = np.empty(max(fixed_len(q.size, encoding), 1), dtype=np.uint8)
+    _check(lib().tlco_pack_fixed(_ptr(q), q.size, encoding, _ptr(out)), "pack_fixed")
+    return out[: fixed_len(q.size, encoding)].copy()
+
+
+def unpack_fixed(b, n: int, encoding: int) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    q = np.empty(max(n, 1), dtype=np.int8)
+    _check(lib().tlco_unpack_fixed(_ptr(b), n, encoding, _ptr(q)), "unpack_fixed")
+    return q[:n].copy()
+
+
+def compress_fixed(x, err, s: float, encoding: int):
+    """Fixed-length encoding of the quantized codes (no zero-run encoding).
+    Returns (bytes uint8[fixed_len], M float32, err_new float32[n])."""
+    x = _f32(x)
+    e = _f32(err).copy()
+    nb = fixed_len(x.size, encoding)
+    out = np.empty(max(nb, 1), dtype=np.uint8)
+    M = ctypes.c_float()
+    _check(lib().tlco_compress_fixed(_ptr(x), _ptr(e), x.size, s, encoding, _ptr(out), nb, ctypes.byref(M)),
+           "compress_fixed")
+    return out[:nb].copy(), np.float32(M.value), e
+
+
+def decompress_fixed(stream, M, n: int, s: float, encoding: int) -> np.ndarray:
+    stream = np.ascontiguousarray(stream, dtype=np.uint8)
+    if stream.size < fixed_len(n, encoding):
+        raise ValueError("stream shorter than the fixed length")
+    y = np.empty(n, dtype=np.float32)
+    _check(lib().tlco_decompress_fixed(_ptr(stream), float(M), n, s, encoding, _ptr(y)), "decompress_fixed")
+    return y
 
 
 def rc_of(fn_name: str, *args) -> int:

@@ -219,3 +219,74 @@ int tlco_server_compress(const float* acc, uint32_t workers, float* err, uint64_
     free(avg);
     return rc;
 }
+
+uint64_t tlco_fixed_len(uint64_t n, int encoding)
+{
+    if (encoding == TLCO_ENC_QUARTIC) return tlco_quartic_len(n);
+    if (encoding == TLCO_ENC_TWOBIT) return (n + 3u) / 4u;
+    return 0;
+}
+
+int tlco_pack_fixed(const int8_t* q, uint64_t n, int encoding, uint8_t* out)
+{
+    if (!q || !out) return TLCO_ERR_INVALID_ARG;
+    if (encoding == TLCO_ENC_QUARTIC) return tlco_quartic_pack(q, n, out);
+    if (encoding != TLCO_ENC_TWOBIT) return TLCO_ERR_INVALID_ARG;
+    uint64_t nb = tlco_fixed_len(n, encoding);
+    for (uint64_t k = 0; k < nb; ++k) {
+        unsigned byte = 0;
+        for (unsigned j = 0; j < 4; ++j) {
+            uint64_t i = 4u * k + j;
+            int c = i < n ? q[i] : 0;
+            byte |= (unsigned)(c + 1) << (2u * j);
+        }
+        out[k] = (uint8_t)byte;
+    }
+    return TLCO_OK;
+}
+
+int tlco_unpack_fixed(const uint8_t* in, uint64_t n, int encoding, int8_t* q)
+{
+    if (!in || !q) return TLCO_ERR_INVALID_ARG;
+    if (encoding == TLCO_ENC_QUARTIC) return tlco_quartic_unpack(in, n, q);
+    if (encoding != TLCO_ENC_TWOBIT) return TLCO_ERR_INVALID_ARG;
+    uint64_t nb = tlco_fixed_len(n, encoding);
+    for (uint64_t k = 0; k < nb; ++k) {
+        for (unsigned j = 0; j < 4; ++j) {
+            unsigned f = (in[k] >> (2u * j)) & 3u;
+            if (f == 3u) return TLCO_ERR_CORRUPT;
+            uint64_t i = 4u * k + j;
+            if (i < n) q[i] = (int8_t)((int)f - 1);
+        }
+    }
+    return TLCO_OK;
+}
+
+int tlco_compress_fixed(const float* x, float* err, uint64_t n, float s, int encoding,
+                        uint8_t* out, uint64_t cap, float* M)
+{
+    if (!x || !err || !out || !M || n == 0) return TLCO_ERR_INVALID_ARG;
+    uint64_t nb = tlco_fixed_len(n, encoding);
+    if (nb == 0) return TLCO_ERR_INVALID_ARG;
+    if (cap < nb) return TLCO_ERR_CAPACITY;
+    int8_t* q = (int8_t*)malloc(n);
+    if (!q) return TLCO_ERR_NOMEM;
+    int rc = tlco_quantize(x, err, n, s, q, M);
+    if (rc == TLCO_OK) rc = tlco_pack_fixed(q, n, encoding, out);
+    free(q);
+    return rc;
+}
+
+int tlco_decompress_fixed(const uint8_t* in, float M, uint64_t n, float s, int encoding, float* y)
+{
+    if (!in || !y || n == 0 || !valid_s(s) || tlco_fixed_len(n, encoding) == 0) return TLCO_ERR_INVALID_ARG;
+    int8_t* q = (int8_t*)malloc(n);
+    if (!q) return TLCO_ERR_NOMEM;
+    int rc = tlco_unpack_fixed(in, n, encoding, q);
+    if (rc == TLCO_OK) {
+        float Ms = M * s;
+        for (uint64_t i = 0; i < n; ++i) y[i] = (float)q[i] * Ms;
+    }
+    free(q);
+    return rc;
+}

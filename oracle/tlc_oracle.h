@@ -84,6 +84,23 @@ int tlco_decompress(const uint8_t* in, uint64_t L, float M, uint64_t n, float s,
 int tlco_decompress_accumulate(const uint8_t* in, uint64_t L, float M, uint64_t n, float s,
                                float* acc);
 
+/* Fixed-length encodings (no zero-run encoding), the ablations of the 3LC
+ * page's "Proposed method" second and third items: the same quantized codes
+ * written as
+ *   TLCO_ENC_QUARTIC  the quartic bytes alone, ceil(n/5) bytes (1.6 bits/value);
+ *   TLCO_ENC_TWOBIT   the 2-bit encoding the page compares quartic encoding
+ *                     with: element i is bits 2*(i%4)..2*(i%4)+1 of byte i/4,
+ *                     holding q_i + 1 (0, 1 or 2), ceil(n/4) bytes (2 bits/value);
+ *                     missing trailing fields hold 1 (code 0).
+ * Decoding rejects a quartic byte > 242 or a 2-bit field of 3 (TLCO_ERR_CORRUPT). */
+enum { TLCO_ENC_QUARTIC = 1, TLCO_ENC_TWOBIT = 2 };
+uint64_t tlco_fixed_len(uint64_t n, int encoding);
+int tlco_pack_fixed(const int8_t* q, uint64_t n, int encoding, uint8_t* out);
+int tlco_unpack_fixed(const uint8_t* in, uint64_t n, int encoding, int8_t* q);
+int tlco_compress_fixed(const float* x, float* err, uint64_t n, float s, int encoding,
+                        uint8_t* out, uint64_t cap, float* M);
+int tlco_decompress_fixed(const uint8_t* in, float M, uint64_t n, float s, int encoding, float* y);
+
 /* Model-delta direction (the 3LC page, "Proposed method", fourth item: the
  * same pipeline compresses model deltas as well as gradients).  The server's
  * state change is the mean of the workers' decoded payloads: acc holds their
