@@ -20,8 +20,10 @@ the host over the same workload.  Also reported, outside the timed steps:
 compress and decompress timed apart, the 8-payload accumulate, the same
 step after --steady-steps steps of error feedback (the error buffer then
 keeps every encode tile active and the streams are about twice as dense),
-and the model-delta direction's server step (the workers' sum, then the
-compress of their mean with the server's error buffer).
+the model-delta direction's server step (the workers' sum, then the
+compress of their mean with the server's error buffer), and the ablations:
+the same codes as quartic bytes only and as 2-bit fields (no zero-run
+encoding), with the zero-run gain of the first step.
 
     python bench.py [--steps K] [--warmup W] [--workload bert_large] [--no-cpu]
 """
@@ -286,6 +288,49 @@ def main():
     srv_comp_ms = s1.elapsed_time(s2) / ks
     L_srv = int(lens_srv.sum().item())
 
+    # ablations (3LC page, method items two and three): the same quantization
+    # with the codes written as quartic bytes only, or as 2-bit fields; each
+    # from a zero error buffer, 5 timed compress calls on rotating inputs (the
+    # error carried, as in the main steps), then 5 timed decompress calls
+    ablations = {}
+    err_fx = torch.empty(N, dtype=torch.float32, device=dev)
+    for name, enc in (("quartic_only", tlc.ENC_QUARTIC), ("two_bit", tlc.ENC_TWOBIT)):
+        offs_h, offs_d, total_b = group.fixed_offsets(enc)
+        out_fx = torch.empty(total_b, dtype=torch.uint8, device=dev)
+        sc_fx = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+        y_fx = torch.empty(N, dtype=torch.float32, device=dev)
+        err_fx.zero_()
+        for k in range(3):
+            group.compress_fixed(xs[k % pool], err_fx, s, enc, out_fx, offs_d, scales=sc_fx, workspace=ws,
+                                 status=st_c)
+        group.decompress_fixed(out_fx, offs_d, sc_fx, s, enc, y=y_fx, status=st_d)
+        torch.cuda.synchronize()
+        f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        f0.record()
+        for k in range(3, 8):
+            group.compress_fixed(xs[k % pool], err_fx, s, enc, out_fx, offs_d, scales=sc_fx, workspace=ws,
+                                 status=st_c)
+        f1.record()
+        for _ in range(5):
+            group.decompress_fixed(out_fx, offs_d, sc_fx, s, enc, y=y_fx, status=st_d)
+        f2.record()
+        torch.cuda.synchronize()
+        if (int(st_c.item()), int(st_d.item())) != (0, 0):
+            raise SystemExit(f"device status not ok in the {name} ablation")
+        nbytes = sum(tlc.fixed_len(n, enc) for n in sizes)
+        c_ms = f0.elapsed_time(f1) / 5
+        d_ms = f1.elapsed_time(f2) / 5
+        ablations[name] = {"bits_per_value": round(8.0 * nbytes / N, 4), "compress_ms": round(c_ms, 4),
+                           "decompress_ms": round(d_ms, 4),
+                           "compress_roofline_frac": round((12.0 * N + nbytes) / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                                           4),
+                           "decompress_roofline_frac": round((4.0 * N + nbytes) / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                                             4)}
+        del out_fx, y_fx
+    del err_fx
+    B_total = sum(-(-n // 5) for n in sizes)
+    ablations["zero_run_gain_first_step"] = round(B_total / int(first["lens"].sum()), 2)
+
     # steady state of error feedback: the same step continued until the error
     # buffer has filled (every encode tile active, denser streams), then timed
     steady = None
@@ -397,6 +442,7 @@ def main():
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
         "steady_state": steady,
+        "ablations": ablations,
         "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "wall_s_timed": round(wall, 3),
         "kernel_source": kernel_source_hash(),

@@ -131,6 +131,21 @@ struct PackJob {
 };
 static_assert(sizeof(PackJob) == 32, "job layout");
 
+// Fixed-length encodings (no zero-run encoding): the quartic bytes alone, or
+// 2-bit fields (four values per byte, q+1 in bits 2*(i%4) of byte i/4).  An
+// encode tile (5120 values) is kFixedTile bytes of either, at a fixed place.
+struct FixedOut {
+    int enc;                // 0: the 3LC stream; TLC_ENC_QUARTIC or TLC_ENC_TWOBIT
+    uint8_t* out;           // compress: tensor t's bytes at out + offs[t] (offset 0 for one tensor)
+    const uint64_t* offs;   // device, count entries, or nullptr for one tensor
+};
+
+__host__ __device__ __forceinline__ uint32_t fixed_tile_bytes(int enc) { return enc == TLC_ENC_TWOBIT ? 1280u : 1024u; }
+__host__ __device__ __forceinline__ uint64_t fixed_len_of(uint64_t n, int enc) {
+    return enc == TLC_ENC_TWOBIT ? (n + 3) / 4 : (n + 4) / 5;
+}
+__host__ __device__ __forceinline__ uint8_t fixed_zero_byte(int enc) { return enc == TLC_ENC_TWOBIT ? 0x55 : 121; }
+
 __device__ __forceinline__ uint32_t quartic_len(uint32_t n) { return (uint32_t)(((uint64_t)n + 4) / 5); }
 __device__ __forceinline__ uint32_t etiles_of(uint32_t n) {
     return (uint32_t)(((uint64_t)n + kETile - 1) / kETile);
@@ -747,9 +762,9 @@ __device__ __forceinline__ void mark_literals(uint32_t* lit, uint32_t u, int q0,
 // quartic byte that holds a nonzero code (a literal) is marked in a bitmap;
 // the zero-run encoding then works literal by literal (64 per round), which
 // costs nothing for the runs of byte 121 that make up most of a tile.
-__device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* __restrict__ etile_agg,
-                          uint8_t* __restrict__ staging, const uint16_t* __restrict__ cand_cnt,
-                          const uint2* __restrict__ cand,
+__device__ void pack_tile(const GroupView& g, const PackJob& jb, float* __restrict__ err,
+                          uint64_t* __restrict__ etile_agg, uint8_t* __restrict__ staging,
+                          const uint16_t* __restrict__ cand_cnt, const uint2* __restrict__ cand, const FixedOut& fo,
                           int8_t* slice) {
     const int lane = lane_id();
     const uint64_t e0 = jb.e0;
@@ -914,6 +929,66 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
     }
     wave_sync();
 
+    if (fo.enc) {
+        // fixed-length encodings: lane l packs codes 80l..80l+79 (20 words of
+        // LDS) into its 16 quartic bytes or 20 two-bit bytes at a fixed place
+        const Seg sg = load_seg(g, jb.gi);
+        const uint32_t TB = fixed_tile_bytes(fo.enc);
+        const uint64_t j = et - sg.etile0;
+        const uint32_t nb = (uint32_t)min((uint64_t)TB, fixed_len_of(sg.n, fo.enc) - j * TB);
+        uint8_t* const dst = fo.out + (fo.offs ? fo.offs[jb.gi] : 0ull) + j * TB;
+        uint32_t words[20];
+#pragma unroll
+        for (int i = 0; i < 20; ++i) words[i] = reinterpret_cast<const uint32_t*>(q)[20 * lane + i];
+        uint32_t ob[5];  // up to 20 output bytes, 4 per word
+        uint32_t nout;
+        if (fo.enc == TLC_ENC_QUARTIC) {
+            nout = 16;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    uint32_t byte = 0, w3 = 1;
+#pragma unroll
+                    for (int d = 0; d < 5; ++d) {
+                        const int idx = 20 * gq + 5 * jj + d;
+                        const int qq = (int)(int8_t)(words[idx >> 2] >> (8 * (idx & 3)));
+                        byte += (uint32_t)(qq + 1) * w3;
+                        w3 *= 3;
+                    }
+                    word |= byte << (8 * jj);
+                }
+                ob[gq] = word;
+            }
+            ob[4] = 0;
+        } else {
+            nout = 20;
+#pragma unroll
+            for (int b = 0; b < 20; ++b) {
+                uint32_t byte = 0;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) byte |= ((((words[b] >> (8 * d)) & 0xFFu) + 1u) & 3u) << (2 * d);
+                if ((b & 3) == 0) ob[b >> 2] = 0;
+                ob[b >> 2] |= byte << (8 * (b & 3));
+            }
+        }
+        const uint32_t o0 = nout * lane;
+        if (o0 + nout <= nb && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            if (nout == 16) {
+                *reinterpret_cast<uint4*>(dst + o0) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 5; ++k) reinterpret_cast<uint32_t*>(dst + o0)[k] = ob[k];
+            }
+        } else {
+            for (uint32_t b = 0; b < nout; ++b)
+                if (o0 + b < nb) dst[o0 + b] = (uint8_t)(ob[b >> 2] >> (8 * (b & 3)));
+        }
+        wave_sync();  // the LDS slice is rewritten by the wave's next tile
+        return;
+    }
+
     // Literal n of the tile (in byte order) is found by rank: lanes 0..31
     // hold the bitmap words, a prefix sum of their popcounts gives each
     // word's first rank.  Each literal emits, after the previous literal at
@@ -989,18 +1064,19 @@ __device__ void pack_tile(const PackJob& jb, float* __restrict__ err, uint64_t* 
     wave_sync();  // the LDS slice is rewritten by the wave's next tile
 }
 
-__global__ __launch_bounds__(kThreads) void k_quant_pack(float* __restrict__ err, const PackJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __restrict__ err,
+                                                         const PackJob* __restrict__ jobs,
                                                          const uint32_t* __restrict__ ctrl,
                                                          uint64_t* __restrict__ etile_agg,
                                                          uint8_t* __restrict__ staging,
                                                          const uint16_t* __restrict__ cand_cnt,
-                                                         const uint2* __restrict__ cand) {
+                                                         const uint2* __restrict__ cand, FixedOut fo) {
     __shared__ __align__(16) int8_t s_q[kWaves * kSlice];
     const uint32_t na = ctrl[1];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
     const uint32_t waves = gridDim.x * kWaves;
     for (uint32_t i = blockIdx.x * kWaves + wave; i < na; i += waves)
-        pack_tile(jobs[i], err, etile_agg, staging, cand_cnt, cand, s_q + wave * kSlice);
+        pack_tile(g, jobs[i], err, etile_agg, staging, cand_cnt, cand, fo, s_q + wave * kSlice);
 }
 
 // Largest span output assembled in LDS by k_emit (an all-zero span of 256
@@ -1403,6 +1479,108 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
 }
 
 // ---------------------------------------------------------------------------
+// fixed-length encodings (the ablations without zero-run encoding)
+
+// Every encode tile's output bytes set to the encoding's byte of zero codes;
+// k_quant_pack then overwrites the tiles that hold a nonzero code.  One
+// wavefront per encode tile, 16 bytes per lane.
+__global__ __launch_bounds__(64) void k_fixed_fill(GroupView g, uint32_t etiles, FixedOut fo) {
+    const uint32_t e = blockIdx.x;
+    const uint32_t gi = etile_owner(g, e);
+    const Seg sg = load_seg(g, gi);
+    const uint32_t TB = fixed_tile_bytes(fo.enc);
+    const uint64_t j = e - sg.etile0;
+    const uint32_t nb = (uint32_t)min((uint64_t)TB, fixed_len_of(sg.n, fo.enc) - j * TB);
+    uint8_t* const dst = fo.out + (fo.offs ? fo.offs[gi] : 0ull) + j * TB;
+    const uint8_t z = fixed_zero_byte(fo.enc);
+    const uint32_t z4 = 0x01010101u * z;
+    const bool al = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    for (uint32_t c = threadIdx.x; 16 * c < nb; c += 64) {
+        if (al && 16 * c + 16 <= nb) {
+            *reinterpret_cast<uint4*>(dst + 16 * c) = make_uint4(z4, z4, z4, z4);
+        } else {
+            for (uint32_t b = 16 * c; b < min(nb, 16 * c + 16); ++b) dst[b] = z;
+        }
+    }
+}
+
+__global__ void k_status_ok(int* __restrict__ status) { *status = TLC_OK; }
+
+// Decode of a fixed-length encoding: one wavefront per encode tile; lane l
+// decodes codes 80l..80l+79 into LDS, then y is written with coalesced
+// 16-byte stores, y_i = q_i * (M*s).  A quartic byte above 242 or a 2-bit
+// field of 3 sets *status = TLC_ERR_CORRUPT.
+__global__ __launch_bounds__(64) void k_fixed_decode(GroupView g, int enc, const uint8_t* __restrict__ in,
+                                                     const uint64_t* __restrict__ offs,
+                                                     const float* __restrict__ scales, float s,
+                                                     float* __restrict__ y, int* __restrict__ status) {
+    __shared__ __align__(16) int8_t sq[kETile];
+    const uint32_t e = blockIdx.x;
+    const int lane = threadIdx.x;
+    const uint32_t gi = etile_owner(g, e);
+    const Seg sg = load_seg(g, gi);
+    const uint32_t TB = fixed_tile_bytes(enc);
+    const uint64_t j = e - sg.etile0;
+    const uint32_t nb = (uint32_t)min((uint64_t)TB, fixed_len_of(sg.n, enc) - j * TB);
+    const uint32_t nel = min(kETile, sg.n - (uint32_t)j * kETile);
+    const uint8_t* const src = in + (offs ? offs[gi] : 0ull) + j * TB;
+    const float ms = scales[gi] * s;
+    bool bad = false;
+    const uint32_t nin = enc == TLC_ENC_TWOBIT ? 20u : 16u;  // bytes per lane
+    const uint32_t o0 = nin * lane;
+    uint32_t codes[20];  // 4 codes per word, as int8
+#pragma unroll
+    for (int i = 0; i < 20; ++i) codes[i] = 0;
+    if (enc == TLC_ENC_QUARTIC) {
+#pragma unroll
+        for (uint32_t b = 0; b < 16; ++b) {
+            const uint32_t byte = o0 + b < nb ? src[o0 + b] : kZero;
+            bad |= byte > 242u;
+            uint32_t rest = byte;
+#pragma unroll
+            for (uint32_t d = 0; d < 5; ++d) {
+                const uint32_t c = 5 * b + d;
+                codes[c >> 2] |= ((rest % 3u - 1u) & 0xFFu) << (8 * (c & 3));
+                rest /= 3u;
+            }
+        }
+    } else {
+#pragma unroll
+        for (uint32_t b = 0; b < 20; ++b) {
+            const uint32_t byte = o0 + b < nb ? src[o0 + b] : 0x55u;
+#pragma unroll
+            for (uint32_t d = 0; d < 4; ++d) {
+                const uint32_t f = (byte >> (2 * d)) & 3u;
+                bad |= f == 3u;
+                codes[b] |= ((f - 1u) & 0xFFu) << (8 * d);
+            }
+        }
+    }
+    if (bad) raise_status(status, TLC_ERR_CORRUPT);
+#pragma unroll
+    for (int i = 0; i < 20; ++i) reinterpret_cast<uint32_t*>(sq)[20 * lane + i] = codes[i];
+    __syncthreads();
+    float* const yy = y + sg.elem_off + j * kETile;
+    const bool al = ((sg.elem_off + j * kETile) & 3) == 0;
+    for (uint32_t u = 4 * lane; u < nel; u += 256) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(sq)[u >> 2];
+        float4 v;
+        v.x = (float)(int)(int8_t)(w) * ms;
+        v.y = (float)(int)(int8_t)(w >> 8) * ms;
+        v.z = (float)(int)(int8_t)(w >> 16) * ms;
+        v.w = (float)(int)(int8_t)(w >> 24) * ms;
+        if (al && u + 4 <= nel) {
+            *reinterpret_cast<float4*>(yy + u) = v;
+        } else {
+            yy[u] = v.x;
+            if (u + 1 < nel) yy[u + 1] = v.y;
+            if (u + 2 < nel) yy[u + 2] = v.z;
+            if (u + 3 < nel) yy[u + 3] = v.w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bandwidth yardstick: one 16-byte load and store per lane, many small blocks,
 // both streamed past the caches like the codec's own streaming accesses
 
@@ -1551,9 +1729,13 @@ int check_ws(const Plan& p, void* ws, size_t ws_bytes, Layout* l) {
     return TLC_OK;
 }
 
+// fo.enc == 0: the 3LC stream into out/out_lens; otherwise a fixed-length
+// encoding into fo (out and out_lens unused)
 int run_compress(const Plan& p, const float* x, float x_div, float* err, float s, uint8_t* out, uint64_t* out_lens,
-                 float* scales, void* ws, size_t ws_bytes, int* status, hipStream_t st) {
-    if (!x || !err || !out || !out_lens || !scales || !status) return TLC_ERR_INVALID_ARG;
+                 float* scales, void* ws, size_t ws_bytes, int* status, hipStream_t st,
+                 const FixedOut& fo = FixedOut{0, nullptr, nullptr}) {
+    if (!x || !err || !scales || !status) return TLC_ERR_INVALID_ARG;
+    if (fo.enc ? !fo.out : (!out || !out_lens)) return TLC_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(err) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
     Layout l;
     int rc = check_ws(p, ws, ws_bytes, &l);
@@ -1594,10 +1776,14 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
                                                                                  ctrl);
     });
     if (rc) return rc;
+    if (fo.enc) {
+        rc = launch("tlc_fixed_fill", st, [&] { k_fixed_fill<<<etiles, 64, 0, st>>>(g, etiles, fo); });
+        if (rc) return rc;
+    }
     rc = launch("tlc_quant_pack", st, [&] {
-        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(err, jobs, ctrl, etile_agg, staging, cand_cnt, cand);
+        k_quant_pack<<<pack_grid, kThreads, 0, st>>>(g, err, jobs, ctrl, etile_agg, staging, cand_cnt, cand, fo);
     });
-    if (rc) return rc;
+    if (rc || fo.enc) return rc;
     return launch("tlc_emit", st, [&] {
         k_emit<<<spans, kThreads, 0, st>>>(g, etile_agg, staging, span_flags, span_tickets, out, out_lens, status);
     });
@@ -1636,6 +1822,19 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     });
 }
 
+int run_decompress_fixed(const Plan& p, int enc, const uint8_t* in, const uint64_t* offs, const float* scales,
+                         float s, float* y, int* status, hipStream_t st) {
+    if (!in || !scales || !y || !status) return TLC_ERR_INVALID_ARG;
+    if (!valid_s(s)) return TLC_ERR_INVALID_ARG;
+    int rc = launch("tlc_status_ok", st, [&] { k_status_ok<<<1, 1, 0, st>>>(status); });
+    if (rc) return rc;
+    return launch("tlc_fixed_decode", st, [&] {
+        k_fixed_decode<<<(uint32_t)p.d.etiles, 64, 0, st>>>(p.g, enc, in, offs, scales, s, y, status);
+    });
+}
+
+bool valid_enc(int enc) { return enc == TLC_ENC_QUARTIC || enc == TLC_ENC_TWOBIT; }
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1672,6 +1871,27 @@ int tlc_compress(const float* x, float* err, uint64_t n, float s, uint8_t* out, 
     if (out_capacity < tlc_compress_bound(n)) return TLC_ERR_CAPACITY;
     return run_compress(single_plan(n), x, 1.0f, err, s, out, out_len, scale, workspace, workspace_bytes, status,
                         static_cast<hipStream_t>(stream));
+}
+
+uint64_t tlc_fixed_len(uint64_t n, int encoding) {
+    if (n == 0 || n > kMaxN || !valid_enc(encoding)) return 0;
+    return fixed_len_of(n, encoding);
+}
+
+int tlc_compress_fixed(const float* x, float* err, uint64_t n, float s, int encoding, uint8_t* out,
+                       uint64_t out_capacity, float* scale, void* workspace, size_t workspace_bytes, int* status,
+                       tlc_stream_t stream) {
+    if (n == 0 || n > kMaxN || !valid_enc(encoding)) return TLC_ERR_INVALID_ARG;
+    if (out_capacity < fixed_len_of(n, encoding)) return TLC_ERR_CAPACITY;
+    return run_compress(single_plan(n), x, 1.0f, err, s, nullptr, nullptr, scale, workspace, workspace_bytes, status,
+                        static_cast<hipStream_t>(stream), FixedOut{encoding, out, nullptr});
+}
+
+int tlc_decompress_fixed(const uint8_t* in, const float* scale, uint64_t n, float s, int encoding, float* y,
+                         int* status, tlc_stream_t stream) {
+    if (n == 0 || n > kMaxN || !valid_enc(encoding)) return TLC_ERR_INVALID_ARG;
+    return run_decompress_fixed(single_plan(n), encoding, in, nullptr, scale, s, y, status,
+                                static_cast<hipStream_t>(stream));
 }
 
 int tlc_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s, uint8_t* out,
@@ -1775,6 +1995,27 @@ int tlc_compress_group(const tlc_group_info* info, const void* d_table, const fl
     if (rc) return rc;
     return run_compress(p, x, 1.0f, err, s, out, out_lens, scales, workspace, workspace_bytes, status,
                         static_cast<hipStream_t>(stream));
+}
+
+int tlc_compress_fixed_group(const tlc_group_info* info, const void* d_table, int encoding, const float* x,
+                             float* err, float s, uint8_t* out, const uint64_t* out_offsets, float* scales,
+                             void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream) {
+    if (!valid_enc(encoding) || !out_offsets) return TLC_ERR_INVALID_ARG;
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_compress(p, x, 1.0f, err, s, nullptr, nullptr, scales, workspace, workspace_bytes, status,
+                        static_cast<hipStream_t>(stream), FixedOut{encoding, out, out_offsets});
+}
+
+int tlc_decompress_fixed_group(const tlc_group_info* info, const void* d_table, int encoding, const uint8_t* in,
+                               const uint64_t* in_offsets, const float* scales, float s, float* y, int* status,
+                               tlc_stream_t stream) {
+    if (!valid_enc(encoding) || !in_offsets) return TLC_ERR_INVALID_ARG;
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_decompress_fixed(p, encoding, in, in_offsets, scales, s, y, status, static_cast<hipStream_t>(stream));
 }
 
 int tlc_server_compress_group(const tlc_group_info* info, const void* d_table, const float* acc, uint32_t workers,

@@ -58,6 +58,11 @@ _SIGS = {
     "tlc_workspace_size": (_SZ, [_U64]),
     "tlc_compress": (_I, [_P, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
     "tlc_server_compress": (_I, [_P, _U32, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_fixed_len": (_U64, [_U64, _I]),
+    "tlc_compress_fixed": (_I, [_P, _P, _U64, _F, _I, _P, _U64, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_fixed": (_I, [_P, _P, _U64, _F, _I, _P, _P, _P]),
+    "tlc_compress_fixed_group": (_I, [ctypes.POINTER(GroupInfo), _P, _I, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_fixed_group": (_I, [ctypes.POINTER(GroupInfo), _P, _I, _P, _P, _P, _F, _P, _P, _P]),
     "tlc_decompress": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
     "tlc_decompress_accumulate": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
     "tlc_group_plan": (_I, [_P, _U64, ctypes.POINTER(GroupInfo), _P, _SZ, _P]),
@@ -198,6 +203,49 @@ def server_compress(acc: torch.Tensor, workers: int, err: torch.Tensor, s: float
     return Compressed(out, out_len, scale, status, n, s)
 
 
+ENC_QUARTIC = 1  # quartic bytes without zero-run encoding, ceil(n/5) bytes
+ENC_TWOBIT = 2   # 2-bit fields, four values per byte, ceil(n/4) bytes
+
+
+def fixed_len(n: int, encoding: int) -> int:
+    return int(lib().tlc_fixed_len(n, encoding))
+
+
+def compress_fixed(x: torch.Tensor, err: torch.Tensor, s: float, encoding: int, *, out=None, scale=None,
+                   workspace=None, status=None, stream=None):
+    """Fixed-length encoding of the codes (no zero-run encoding).  Returns (out, scale, status)."""
+    n = x.numel()
+    dev = x.device
+    if err.numel() != n:
+        raise ValueError("err must have as many elements as x")
+    nb = fixed_len(n, encoding)
+    if nb == 0:
+        raise ValueError("bad size or encoding")
+    out = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace(workspace_size(n), dev, workspace)
+    rc = lib().tlc_compress_fixed(_ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), n, s, encoding,
+                                  _ptr(out, torch.uint8, "out"), out.numel(), _ptr(scale, torch.float32, "scale"),
+                                  _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                  _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_compress_fixed")
+    return out, scale, status
+
+
+def decompress_fixed(inp: torch.Tensor, scale: torch.Tensor, n: int, s: float, encoding: int, *, y=None,
+                     status=None, stream=None):
+    """Returns (y, status)."""
+    dev = inp.device
+    y = y if y is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    rc = lib().tlc_decompress_fixed(_ptr(inp, torch.uint8, "in"), _ptr(scale, torch.float32, "scale"), n, s,
+                                    encoding, _ptr(y, torch.float32, "y"), _ptr(status, torch.int32, "status"),
+                                    _stream(stream))
+    _check(rc, "tlc_decompress_fixed")
+    return y, status
+
+
 def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float, *, y=None,
                workspace=None, status=None, stream=None):
     """Returns (y, status)."""
@@ -304,6 +352,47 @@ class Group:
                                              _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_server_compress_group")
         return out, out_lens, scales, status
+
+    def fixed_offsets(self, encoding: int):
+        """(host offsets, device uint64 offsets, total bytes) of a fixed-length
+        encoding: tensors back to back, 16-byte aligned."""
+        offs, at = [], 0
+        for n in self.sizes:
+            offs.append(at)
+            at += -(-fixed_len(n, encoding) // 16) * 16
+        d = torch.tensor(offs, dtype=torch.int64, device=self.device)
+        return offs, d, at
+
+    def compress_fixed(self, x, err, s, encoding, out, d_offsets, *, scales=None, workspace=None, status=None,
+                       stream=None):
+        """Codes of every tensor in a fixed-length encoding at out[d_offsets[t]].  Returns (scales, status)."""
+        if x.numel() != self.total or err.numel() != self.total:
+            raise ValueError("x and err must hold the whole group")
+        dev = self.device
+        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        workspace = workspace if workspace is not None else self.workspace()
+        rc = lib().tlc_compress_fixed_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                            encoding, _ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"),
+                                            s, _ptr(out, torch.uint8, "out"), _ptr(d_offsets, torch.int64, "offsets"),
+                                            _ptr(scales, torch.float32, "scales"),
+                                            _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                            _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_compress_fixed_group")
+        return scales, status
+
+    def decompress_fixed(self, inp, d_offsets, scales, s, encoding, *, y=None, status=None, stream=None):
+        """Returns (y, status)."""
+        dev = self.device
+        y = y if y is not None else torch.empty(self.total, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        rc = lib().tlc_decompress_fixed_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                              encoding, _ptr(inp, torch.uint8, "in"),
+                                              _ptr(d_offsets, torch.int64, "offsets"),
+                                              _ptr(scales, torch.float32, "scales"), s, _ptr(y, torch.float32, "y"),
+                                              _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_decompress_fixed_group")
+        return y, status
 
     def decompress(self, inp, in_lens, scales, s, *, y=None, workspace=None, status=None, stream=None):
         """Returns (y, status)."""

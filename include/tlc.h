@@ -99,6 +99,35 @@ int tlc_compress(const float* x, float* err, uint64_t n, float s,
                  uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
                  void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
 
+/* ---- fixed-length encodings (ablations) ------------------------------------
+ * The same quantization (error buffer, M, codes) written without zero-run
+ * encoding, as the 3LC page's "Proposed method" items two and three are
+ * measured against each other:
+ *   TLC_ENC_QUARTIC  the quartic bytes alone: byte k = sum_j (q_{5k+j}+1)*3^j,
+ *                    ceil(n/5) bytes (1.6 bits per value);
+ *   TLC_ENC_TWOBIT   2-bit fields, the page's point of comparison: element i
+ *                    in bits 2*(i%4), 2*(i%4)+1 of byte i/4 holding q_i+1,
+ *                    missing trailing fields 1, ceil(n/4) bytes (2 bits/value).
+ * The length is fixed by n, so no length is returned or passed.  Decoding a
+ * quartic byte above 242 or a 2-bit field of 3 sets *status =
+ * TLC_ERR_CORRUPT. */
+enum tlc_encoding { TLC_ENC_QUARTIC = 1, TLC_ENC_TWOBIT = 2 };
+
+/* Bytes of a fixed-length encoding of n values; host only; 0 for n == 0,
+ * n > 2^32-1 or an unknown encoding. */
+uint64_t tlc_fixed_len(uint64_t n, int encoding);
+
+/* As tlc_compress (same x, err, s, scale-as-hint, workspace, status), with
+ * the codes written in `encoding` to out[0 .. tlc_fixed_len(n, encoding)). */
+int tlc_compress_fixed(const float* x, float* err, uint64_t n, float s, int encoding,
+                       uint8_t* out, uint64_t out_capacity, float* scale,
+                       void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* y[i] = q_i * (M*s) decoded from in[0 .. tlc_fixed_len(n, encoding)).  No
+ * workspace. */
+int tlc_decompress_fixed(const uint8_t* in, const float* scale, uint64_t n, float s, int encoding,
+                         float* y, int* status, tlc_stream_t stream);
+
 /* Model-delta direction, server side (3LC page, "Proposed method", fourth
  * item: the same pipeline compresses model deltas as well as gradients).
  * acc[n] holds the fp32 sum of the workers' decoded payloads (for example
@@ -165,6 +194,18 @@ int tlc_compress_group(const tlc_group_info* info, const void* d_table,
                        const float* x, float* err, float s,
                        uint8_t* out, uint64_t* out_lens, float* scales,
                        void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* Grouped fixed-length encodings: tensor t's bytes at out[out_offsets[t]]
+ * (device uint64[count], 16-byte aligned offsets recommended, ranges of
+ * tlc_fixed_len(n_t, encoding) bytes that do not overlap); scales as in
+ * tlc_compress_group. */
+int tlc_compress_fixed_group(const tlc_group_info* info, const void* d_table, int encoding,
+                             const float* x, float* err, float s, uint8_t* out,
+                             const uint64_t* out_offsets, float* scales,
+                             void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+int tlc_decompress_fixed_group(const tlc_group_info* info, const void* d_table, int encoding,
+                               const uint8_t* in, const uint64_t* in_offsets, const float* scales, float s,
+                               float* y, int* status, tlc_stream_t stream);
 
 /* Grouped tlc_server_compress: acc/err flat fp32[info->total_elems], per
  * tensor mean acc / workers compressed with the server's error buffer. */

@@ -130,6 +130,15 @@ def test_argument_errors_return_before_any_launch():
     assert L.tlc_decompress(fake, None, fake, 10, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_accumulate(fake, fake, fake, 10, 1.99, fake, ws, 1, fake, None) == tlc.ERR_WORKSPACE
     assert L.tlc_copy_probe(fake, fake, 17, None) == tlc.ERR_INVALID_ARG
+    # fixed-length encodings: lengths, unknown encodings, capacity
+    assert tlc.fixed_len(10, tlc.ENC_QUARTIC) == 2 and tlc.fixed_len(10, tlc.ENC_TWOBIT) == 3
+    assert tlc.fixed_len(10, 3) == 0 and tlc.fixed_len(0, tlc.ENC_TWOBIT) == 0
+    assert tlc.fixed_len(2 ** 32 - 1, tlc.ENC_TWOBIT) == 2 ** 30 and tlc.fixed_len(2 ** 32, tlc.ENC_QUARTIC) == 0
+    assert L.tlc_compress_fixed(fake, fake, 10, 1.5, 3, fake, 10, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress_fixed(fake, fake, 10, 1.5, tlc.ENC_TWOBIT, fake, 2, fake, ws, 4096, fake,
+                                None) == tlc.ERR_CAPACITY
+    assert L.tlc_decompress_fixed(fake, fake, 10, 1.5, 0, fake, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_fixed(fake, fake, 10, 2.5, tlc.ENC_QUARTIC, fake, fake, None) == tlc.ERR_INVALID_ARG
     # server compress: no workers, no elements, capacity, s out of range
     assert L.tlc_server_compress(fake, 0, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, fake,
                                  None) == tlc.ERR_INVALID_ARG
@@ -151,6 +160,10 @@ def test_argument_errors_return_before_any_launch():
                                   None) == tlc.ERR_WORKSPACE
     assert L.tlc_server_compress_group(ctypes.byref(info), fake, fake, 0, fake, 1.5, fake, fake, fake, ws,
                                        1 << 20, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress_fixed_group(ctypes.byref(info), fake, tlc.ENC_QUARTIC, fake, fake, 1.5, fake, None,
+                                      fake, ws, 1 << 20, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_fixed_group(ctypes.byref(info), fake, 7, fake, fake, fake, 1.5, fake, fake,
+                                        None) == tlc.ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
