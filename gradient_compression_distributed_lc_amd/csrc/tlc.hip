@@ -13,31 +13,41 @@
 //                 the max |v| of every 512-element flat tile (128 lanes x one
 //                 16-byte load each: many small blocks keep the most bytes in
 //                 flight).  A tile that spans tensors keeps one partial max per
-//                 tensor, in slot tile + tensor.  12 bytes per element.
+//                 tensor, in slot tile + tensor.  12 bytes per element.  Per
+//                 flat tile it also keeps a short list of the elements that can
+//                 reach the threshold, cut at a bound from the caller's M
+//                 buffer (normally last step's M).  In the model-delta
+//                 direction x is the workers' sum and is divided by their count.
 //   k_tile_max    one thread per encode tile (5120 elements = 1024 quartic
 //                 bytes): the tile's max from the partial maxima under it,
 //                 and every tensor's M through a segmented wave max and one
 //                 atomic per tensor and wave.
-//   k_tile_activity  per tensor M*s and the exact fp32 selection threshold
-//                 (select_threshold); per encode tile, the list of tiles whose
-//                 max reaches it.  Every other tile holds only zero codes and
-//                 is summarised as a run of byte 121 without touching err.
-//   k_quant_pack  one wavefront per listed tile: re-read v only in flat tiles
-//                 whose max reaches the threshold, write err = v - q*M*s where
-//                 q != 0, pack quartic bytes through LDS and zero-run encode
-//                 them from the tile's first literal on into a staging slot
-//                 (wave-level scans, no block barriers).
+//   k_tile_activity  per tensor M (to the caller), M*s and the exact fp32
+//                 selection threshold (select_threshold); per encode tile whose
+//                 max reaches it a 32-byte job for k_quant_pack (which flat
+//                 tiles reach it, whether the lists are complete).  Every other
+//                 tile holds only zero codes and is summarised as a run of
+//                 byte 121 without touching err.
+//   k_quant_pack  one wavefront per job: codes from the lists, or from v read
+//                 again in the flat tiles whose max reaches the threshold;
+//                 err = v - q*M*s where q != 0; codes and a bitmap of literal
+//                 bytes in LDS; zero-run encoding literal by literal into a
+//                 staging slot (wave-level scans, no block barriers).
 //   k_emit        spans of 256 encode tiles: block scan of the tiles' carry
 //                 summaries, decoupled look-back across the tensor's spans for
-//                 the span's input state, then the span's stream bytes: 255
-//                 runs written densely first, remainder codes and staged
-//                 literal bytes over them.
+//                 the span's input state, then the span's stream bytes (255
+//                 runs, remainder codes, staged literals) assembled in LDS and
+//                 written once.
 // decompress: k_prep (zero fill of y, one 16-byte store per lane; decoder
 //             state; list of stream chunks)
 //             -> k_decode (one block per 4 KiB of stream bytes: expansion
 //             scan + look-back across the tensor's chunks for the quartic
 //             byte index, then only literal bytes are decoded and their
 //             nonzero codes written or added).
+// fixed-length encodings (ablations: quartic bytes alone, 2-bit fields): the
+//             compress kernels up to k_quant_pack, which writes each tile's
+//             bytes at a fixed place over k_fixed_fill's zero-code bytes;
+//             k_fixed_decode decodes one encode tile per wavefront.
 //
 // No matrix-core work exists on this path: it is bound by HBM bandwidth.
 
@@ -133,7 +143,7 @@ static_assert(sizeof(PackJob) == 32, "job layout");
 
 // Fixed-length encodings (no zero-run encoding): the quartic bytes alone, or
 // 2-bit fields (four values per byte, q+1 in bits 2*(i%4) of byte i/4).  An
-// encode tile (5120 values) is kFixedTile bytes of either, at a fixed place.
+// encode tile (5120 values) is fixed_tile_bytes(enc) bytes of either, at a fixed place.
 struct FixedOut {
     int enc;                // 0: the 3LC stream; TLC_ENC_QUARTIC or TLC_ENC_TWOBIT
     uint8_t* out;           // compress: tensor t's bytes at out + offs[t] (offset 0 for one tensor)
@@ -173,28 +183,6 @@ __device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t* total) {
     return inc - v;
 }
 
-__device__ float block_max(float v, float* sm) {
-    v = wave_max(v);
-    if (lane_id() == 0) sm[wave_id()] = v;
-    __syncthreads();
-    float r = sm[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sm[i]);
-    __syncthreads();
-    return r;
-}
-
-__device__ int block_min_int(int v, int* sm) {
-    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
-    if (lane_id() == 0) sm[wave_id()] = v;
-    __syncthreads();
-    int r = sm[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = min(r, sm[i]);
-    __syncthreads();
-    return r;
-}
-
 // exclusive prefix sum over the block; *total receives the block sum
 __device__ uint32_t block_excl_sum(uint32_t v, uint32_t* sm, uint32_t* total) {
     const int lane = lane_id(), w = wave_id();
@@ -215,30 +203,6 @@ __device__ uint32_t block_excl_sum(uint32_t v, uint32_t* sm, uint32_t* total) {
     __syncthreads();
     *total = tot;
     return before + inc - v;
-}
-
-// exclusive prefix max over the block (identity -1); *total receives the block max
-__device__ int block_excl_max(int v, int* sm, int* total) {
-    const int lane = lane_id(), w = wave_id();
-    int inc = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = max(inc, o);
-    }
-    int prev = __shfl_up(inc, 1, 64);
-    if (lane == 0) prev = -1;
-    if (lane == 63) sm[w] = inc;
-    __syncthreads();
-    int before = -1, tot = -1;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        int t = sm[i];
-        if (i < w) before = max(before, t);
-        tot = max(tot, t);
-    }
-    __syncthreads();
-    *total = tot;
-    return max(before, prev);
 }
 
 // exclusive scan of 62-bit payloads under an associative (not necessarily
@@ -617,9 +581,11 @@ __global__ __launch_bounds__(kThreads) void k_tile_max(GroupView g, uint32_t eti
     if (ok && (lane == 63 || next != gi)) atomicMax(mbits + gi, __float_as_uint(mx));
 }
 
-// Per encode tile: M*s and the exact selection threshold of its tensor; a
-// tile whose maximum reaches the threshold can hold nonzero codes and is
-// listed for k_quant_pack, with the flat tiles under it that reach it; any
+// Per encode tile: M*s and the exact selection threshold of its tensor (the
+// thread of a tensor's first tile writes M to the caller's buffer, which held
+// the hint until now); a tile whose maximum reaches the threshold can hold
+// nonzero codes and is listed for k_quant_pack, with the flat tiles under it
+// that reach it and whether the tensor's candidate lists are complete; any
 // other tile holds only zero codes and is summarised here as a run of byte
 // 121.
 __global__ __launch_bounds__(kThreads) void k_tile_activity(GroupView g, uint32_t etiles, float s,
@@ -721,23 +687,6 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int wave_excl_max(int v, int* total) {
-    const int lane = lane_id();
-    int inc = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = max(inc, o);
-    }
-    *total = __shfl(inc, 63, 64);
-    const int prev = __shfl_up(inc, 1, 64);
-    return lane == 0 ? -1 : prev;
-}
-
-__device__ __forceinline__ int wave_min(int v) {
-    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
-    return v;
-}
-
 // Per-wave LDS slice of k_quant_pack: the tile's codes (one int8 per element),
 // its staged stream bytes, and a bitmap of its literal quartic bytes.
 constexpr uint32_t kSliceStage = kETile;                      // offset of the staged bytes
@@ -755,10 +704,11 @@ __device__ __forceinline__ void mark_literals(uint32_t* lit, uint32_t u, int q0,
 }
 
 // One wavefront quantizes, packs and zero-run encodes one encode tile.  Only
-// the flat tiles (512 elements) whose max reaches the threshold are read
-// again: every other element has code 0 and err = v already, so it needs no
-// HBM traffic.  The job comes in scalar registers, so the tile's first vector
-// loads are its error values.  Codes go to this wave's LDS slice, and every
+// the flat tiles (512 elements) whose max reaches the threshold are read: from
+// their candidate lists when the tensor's lists are complete (and the tile's
+// did not overflow), else from err again.  Every other element has code 0 and
+// err = v already, so it needs no HBM traffic.  The job comes in scalar
+// registers, so the tile's first vector loads are its data.  Codes go to this wave's LDS slice, and every
 // quartic byte that holds a nonzero code (a literal) is marked in a bitmap;
 // the zero-run encoding then works literal by literal (64 per round), which
 // costs nothing for the runs of byte 121 that make up most of a tile.
