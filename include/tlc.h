@@ -31,8 +31,9 @@
  *   - The library never allocates, frees or synchronises device memory; the
  *     caller owns every buffer.  Scratch memory is the caller's `workspace`
  *     (device, 256-byte aligned, at least the size the *_workspace_size call
- *     returns).  Calls that may run at the same time need separate
- *     workspaces and separate status words.
+ *     returns; its contents need not survive between calls).  Calls that may
+ *     run at the same time need separate workspaces and separate status
+ *     words.
  *   - fp32 buffers (x, err, y, acc) must be 16-byte aligned and must not
  *     alias each other or the byte streams.
  *   - Return value: TLC_OK, or a synchronous error (invalid argument, too
@@ -63,7 +64,8 @@ enum tlc_status {
     TLC_ERR_CAPACITY = 2,    /* output capacity below tlc_compress_bound(n) */
     TLC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
     TLC_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
-    TLC_ERR_CORRUPT = 5,     /* (device status) stream does not expand to exactly ceil(n/5) bytes */
+    TLC_ERR_CORRUPT = 5,     /* (device status) stream does not expand to exactly ceil(n/5) bytes, or a
+                                fixed-length encoding holds a byte that is no valid code */
     TLC_ERR_INTERNAL = 6     /* (device status) a bounded inter-block wait expired */
 };
 
