@@ -1183,6 +1183,39 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     uint8_t* const o = out + sg.stream_off + D;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(o) & 15);
     const uint32_t nchunks = end ? (mis + end + 15) / 16 : 0u;
+    // The staged words of the span, 8 per thread and round with every load
+    // issued before the first byte is placed (the first word was loaded
+    // before the look-back); put(p, b) writes span byte p.
+    auto copy_staged = [&](auto put) {
+        for (uint32_t base = 0; base < tot_words; base += 8 * kThreads) {
+            uint32_t kk[8], val[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t wv = base + r * kThreads + threadIdx.x;
+                kk[r] = 0;
+                val[r] = 0;
+                if (wv < tot_words) {
+                    kk[r] = wv == threadIdx.x ? k0 : word_owner(wv);
+                    val[r] = wv == threadIdx.x
+                                 ? val0
+                                 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)kk[r] * kETileBytes)[wv - s_wpre[kk[r]]];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t wv = base + r * kThreads + threadIdx.x;
+                if (wv < tot_words) {
+                    const uint32_t k = kk[r];
+                    const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
+                    const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
+                    const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
+#pragma unroll
+                    for (uint32_t i = 0; i < 4; ++i)
+                        if (i < nbw && sbase + i < end) put(sbase + i, (uint8_t)(val[r] >> (8 * i)));
+                }
+            }
+        }
+    };
     if (end <= kEmitLds) {
         // Assembled in LDS (byte p of the span at s_out[mis + p]): 255 fill,
         // then the exceptions, then one aligned 16-byte store per chunk, so
@@ -1195,17 +1228,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
             if (rem && t_off + lead < end) s_out[mis + t_off + lead] = (uint8_t)rem;
             if (fin && t_off + len - 1 < end) s_out[mis + t_off + len - 1] = (uint8_t)fin;
         }
-        for (uint32_t wv = threadIdx.x; wv < tot_words; wv += kThreads) {
-            const uint32_t k = wv == threadIdx.x ? k0 : word_owner(wv);
-            const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
-            const uint32_t val =
-                wv == threadIdx.x ? val0 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
-            const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
-            const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
-#pragma unroll
-            for (uint32_t i = 0; i < 4; ++i)
-                if (i < nbw && sbase + i < end) s_out[mis + sbase + i] = (uint8_t)(val >> (8 * i));
-        }
+        copy_staged([&](uint32_t p, uint8_t b) { s_out[mis + p] = b; });
         __syncthreads();
         for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
             const int64_t p0 = (int64_t)c * 16 - mis;  // span byte of the chunk's first byte
@@ -1239,17 +1262,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
         if (rem && t_off + lead < end) o[t_off + lead] = (uint8_t)rem;
         if (fin && t_off + len - 1 < end) o[t_off + len - 1] = (uint8_t)fin;
     }
-    for (uint32_t wv = threadIdx.x; wv < tot_words; wv += kThreads) {
-        const uint32_t k = wv == threadIdx.x ? k0 : word_owner(wv);
-        const uint32_t w4 = wv - s_wpre[k];
-        const uint32_t val =
-            wv == threadIdx.x ? val0 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)k * kETileBytes)[w4];
-        const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
-        const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
-#pragma unroll
-        for (uint32_t i = 0; i < 4; ++i)
-            if (i < nbw && sbase + i < end) o[sbase + i] = (uint8_t)(val >> (8 * i));
-    }
+    copy_staged([&](uint32_t p, uint8_t b) { o[p] = b; });
 }
 
 // ---------------------------------------------------------------------------
