@@ -59,6 +59,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -82,7 +83,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;         // bounded look-back wait (abo
 // s_waitcnt operand that waits for every outstanding vector memory access
 // and nothing else (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmem = 0x0F70;
-constexpr uint32_t kPackGrid = 2048;              // blocks of k_quant_pack
+constexpr uint32_t kPackGrid = 2048;              // most blocks of k_quant_pack
 constexpr int kPackSlots = 4;                     // float4 loads per lane in one k_quant_pack batch (two flat tiles)
 // Candidate lists: the first pass keeps, per flat tile, the elements that can
 // still reach the threshold (see cand_bound), so that the second pass need
@@ -1268,36 +1269,60 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 // ---------------------------------------------------------------------------
 // decompress kernels
 
-// Zero fill of y (decompress only; every code 0 dequantizes to +0.0), the
-// decoder state reset, and the list of stream chunks: tensor i has
+// Where k_decode found encode tile j of a tensor to begin (decompress only):
+// the stream byte, counted from the tensor's first, whose expansion holds
+// quartic byte 1024 j, and how many quartic bytes of that expansion come
+// before it (a run byte can straddle two tiles).
+constexpr uint64_t kNoStart = ~0ull;
+__device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { return byte | skip << 32; }
+
+// A decompress whose streams hold more than one byte per kDenseFrac quartic
+// bytes is expected to have nonzero codes in most encode tiles.
+constexpr uint64_t kDenseFrac = 8;
+
+// Decoder state reset and set-up.  Sparse decompress (n_fill > 0): zero fill
+// of y, one 16-byte store per lane (the fastest fill measured on MI355X; any
+// load before the store, or more stores per lane, slows it by 10-40%).  Dense
+// decompress (tstart set): the tile starts and literal flags are reset.
+// Always: the look-back flags, and the list of stream chunks: tensor i has
 // max(1, ceil(min(L_i, B_i) / kChunk)) chunks, numbered dec_first[i] ...;
-// chunk r belongs to tensor dec_map[r]; ctrl[3] = number of chunks.  A
-// dedicated grid-stride fill sweeps HBM faster than fills spread over the
-// decoding blocks (measured ~6.5 vs ~5.6 TB/s).
+// chunk r belongs to tensor dec_map[r]; ctrl[3] = number of chunks.  Block 0
+// also writes the density of the streams to *hint (when set): 1 if dense.
 __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restrict__ y, uint64_t n_fill,
                                                    const uint64_t* __restrict__ in_lens,
                                                    uint64_t* __restrict__ flags, uint64_t nflags,
+                                                   uint64_t* __restrict__ tstart, uint32_t* __restrict__ tlit,
+                                                   uint64_t ntiles,
                                                    uint32_t* __restrict__ dec_map, uint32_t* __restrict__ dec_first,
                                                    uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
-                                                   int* __restrict__ status) {
+                                                   int* __restrict__ status, uint32_t* hint) {
     __shared__ uint32_t s_u[kWaves];
+    __shared__ uint64_t s_d[2][kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
     const uint64_t n4 = n_fill >> 2;
-    float4* y4 = reinterpret_cast<float4*>(y);
-    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (uint64_t i = tid; i < n4; i += stride) y4[i] = z;
+    float4* const y4 = reinterpret_cast<float4*>(y);
+    for (uint64_t i = tid; i < n4; i += stride) y4[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (tid < (n_fill & 3)) y[(n4 << 2) + tid] = 0.0f;
     for (uint64_t i = tid; i < nflags; i += stride) flags[i] = 0;
+    if (tstart)
+        for (uint64_t i = tid; i < ntiles; i += stride) {
+            tstart[i] = kNoStart;
+            tlit[i] = 0;
+        }
     if (blockIdx.x == 0) {
         uint32_t carry = 0;
+        uint64_t sum_l = 0, sum_b = 0;
         for (uint32_t base = 0; base < g.count; base += kThreads) {
             const uint32_t gi = base + threadIdx.x;
             uint32_t rc = 0;
             if (gi < g.count) {
                 const Seg sg = load_seg(g, gi);
-                const uint64_t L = min(in_lens[gi], (uint64_t)quartic_len(sg.n));
+                const uint64_t B = quartic_len(sg.n);
+                const uint64_t L = min(in_lens[gi], B);
                 rc = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
+                sum_l += L;
+                sum_b += B;
             }
             uint32_t tot;
             const uint32_t first = carry + block_excl_sum(rc, s_u, &tot);
@@ -1308,6 +1333,25 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
             }
             carry += tot;
         }
+        if (hint) {
+            for (int d = 32; d >= 1; d >>= 1) {
+                sum_l += __shfl_xor(sum_l, d, 64);
+                sum_b += __shfl_xor(sum_b, d, 64);
+            }
+            if (lane_id() == 0) {
+                s_d[0][wave_id()] = sum_l;
+                s_d[1][wave_id()] = sum_b;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                uint64_t tl = 0, tb = 0;
+                for (int w = 0; w < kWaves; ++w) {
+                    tl += s_d[0][w];
+                    tb += s_d[1][w];
+                }
+                *hint = kDenseFrac * tl > tb ? 1u : 0u;
+            }
+        }
         if (threadIdx.x == 0) {
             ctrl[3] = carry;  // decoder chunks
             *status = TLC_OK;
@@ -1315,18 +1359,27 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
     }
 }
 
+// What k_decode does with a chunk once it knows where the chunk's bytes land.
+enum DecodeMode {
+    kDecodeWrite = 0,   // sparse decompress: nonzero codes written over k_prep's zero fill
+    kDecodeAdd = 1,     // accumulate: nonzero codes added to y in place
+    kDecodeRecord = 2,  // dense decompress: tile starts and literal flags for k_expand
+};
+
 // One block per stream chunk (kChunk bytes, 16 per lane): expansion lengths,
 // block scan, look-back across the tensor's chunks for the quartic byte index
-// of the chunk, then the nonzero codes of its literal bytes are written
-// (decompress, over the zero fill of k_prep) or added (accumulate).
+// of the chunk, then the work of Mode (one instantiation each, so that each
+// keeps only its own registers).
+template <int Mode>
 __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t* __restrict__ in,
                                                      const uint64_t* __restrict__ in_lens,
                                                      const float* __restrict__ scales, float s,
-                                                     float* __restrict__ y, uint64_t* __restrict__ flags,
+                                                     float* __restrict__ y, uint64_t* __restrict__ tstart,
+                                                     uint32_t* __restrict__ tlit, uint64_t* __restrict__ flags,
                                                      const uint32_t* __restrict__ dec_map,
                                                      const uint32_t* __restrict__ dec_first,
                                                      uint32_t* __restrict__ tickets, const uint32_t* __restrict__ ctrl,
-                                                     int* __restrict__ status, int accumulate) {
+                                                     int* __restrict__ status) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_chunk, s_ok;
     __shared__ uint64_t s_base;
@@ -1404,8 +1457,44 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_INTERNAL);
             continue;
         }
-        float* const yy = y + sg.elem_off;
-        if (nlit) {
+        if (Mode == kDecodeRecord) {
+            // A lane's 16 bytes expand to at most 224 quartic bytes, so at
+            // most one tile boundary (a multiple of 1024) falls inside them,
+            // d quartic bytes after the lane's first; the lane's literal bytes
+            // lie in the tiles before and after it.
+            const uint64_t p0 = base + texcl;
+            const uint32_t d = (uint32_t)((kETileBytes - p0 % kETileBytes) % kETileBytes);
+            const uint32_t lim = (uint32_t)min<uint64_t>(B - min(B, p0), 1u << 16);  // quartic bytes left in the tensor
+            uint32_t rel = 0, bi = 16, bskip = 0;
+            bool lit_lo = false, lit_hi = false, bad = false;
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) {
+                const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
+                if (i < nv) {
+                    const uint32_t len = byte < 243u ? 1u : byte - kRunBase;
+                    if (d >= rel && d < rel + len) {
+                        bi = i;
+                        bskip = d - rel;
+                    }
+                    if (byte < 243u) {
+                        bad |= rel >= lim;
+                        if (byte != kZero) {
+                            lit_lo |= rel < d;
+                            lit_hi |= rel >= d;
+                        }
+                    }
+                    rel += len;
+                }
+            }
+            if (bi < 16 && d < lim) tstart[sg.etile0 + (p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
+            if (bad) {
+                raise_status(status, TLC_ERR_CORRUPT);
+            } else {
+                if (lit_lo) tlit[sg.etile0 + p0 / kETileBytes] = 1u;
+                if (lit_hi) tlit[sg.etile0 + (p0 + d) / kETileBytes] = 1u;
+            }
+        } else if (nlit) {
+            float* const yy = y + sg.elem_off;
             const float ms = msc * s;
             uint64_t pos = base + texcl;
             bool bad = false;
@@ -1425,7 +1514,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                                 const uint64_t e = 5u * pos + d;
                                 if (digit != 1u && e < n) {
                                     const float val = (float)((int)digit - 1) * ms;
-                                    yy[e] = accumulate ? yy[e] + val : val;
+                                    yy[e] = Mode == kDecodeAdd ? yy[e] + val : val;
                                 }
                             }
                         }
@@ -1438,6 +1527,144 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             if (bad) raise_status(status, TLC_ERR_CORRUPT);
         }
         if (threadIdx.x == 0 && start + cnt == L && base + csum != B) raise_status(status, TLC_ERR_CORRUPT);
+    }
+}
+
+// Unit handled by block b of a grid of 8 * ceil(units / 8) blocks (a result
+// >= units means none).  Blocks are dispatched round-robin over the 8 XCDs,
+// so this gives each XCD a contiguous eighth of the units: large per-block
+// stores then reach ~6.2 TB/s on MI355X, against ~5.5 TB/s in plain order.
+__device__ __forceinline__ uint32_t xcd_unit(uint32_t b, uint32_t units) {
+    const uint32_t q = (units + 7) / 8;
+    return (b % 8) * q + b / 8;
+}
+uint32_t xcd_grid(uint64_t units) { return (uint32_t)((units + 7) / 8 * 8); }
+
+// One wavefront per encode tile (5120 elements, 1024 quartic bytes), four per
+// block, with no block barrier: every element of the tile is written once,
+// y = q * (M*s), with 16-byte stores, so decompress writes each line of y
+// once (a zero fill with the nonzero values scattered over it afterwards wrote
+// every line that holds a nonzero code twice).  A tile k_decode found no
+// nonzero code in is written without reading the stream.  Otherwise its
+// stream bytes, from the start k_decode recorded, are staged in LDS with
+// aligned 16-byte loads, re-read 16 per lane in stream order, and expanded
+// into the tile's codes (one int8 per element, same LDS slice).
+__global__ __launch_bounds__(kThreads) void k_expand(GroupView g, uint32_t etiles, const uint8_t* __restrict__ in,
+                                                     const uint64_t* __restrict__ in_lens,
+                                                     const float* __restrict__ scales, float s,
+                                                     const uint64_t* __restrict__ tstart,
+                                                     const uint32_t* __restrict__ tlit, float* __restrict__ y,
+                                                     int* __restrict__ status) {
+    __shared__ __align__(16) int8_t s_codes[kWaves * kETile];
+    const int lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const uint32_t e = xcd_unit(blockIdx.x, (etiles + kWaves - 1) / kWaves) * kWaves + wave;
+    if (e >= etiles) return;
+    int8_t* const sq = s_codes + wave * kETile;
+    const uint32_t gi = etile_owner(g, e);
+    const uint64_t ts = tstart[e];
+    const uint64_t tn = e + 1 < etiles ? tstart[e + 1] : kNoStart;
+    const bool has_lit = tlit[e] != 0u;
+    const Seg sg = load_seg(g, gi);
+    const float ms = scales[gi] * s;
+    const uint64_t L_in = in_lens[gi];
+    if (ts == kNoStart) {  // the stream never reached this tile
+        if (lane == 0) raise_status(status, TLC_ERR_CORRUPT);
+        return;
+    }
+    const uint32_t j = e - sg.etile0;
+    const uint32_t nel = min(kETile, sg.n - j * kETile);
+    if (has_lit) {
+        const uint64_t B = quartic_len(sg.n);
+        const uint32_t need = (uint32_t)min((uint64_t)kETileBytes, B - (uint64_t)j * kETileBytes);
+        const uint64_t sb = ts & 0xFFFFFFFFull, skip = ts >> 32;
+        // bytes sb .. eb-1: at most 1024 (each covers at least one quartic
+        // byte), none past the byte where the tensor's next tile begins
+        uint64_t eb = min(min(L_in, B), sb + kETileBytes);
+        if ((uint64_t)(j + 1) * kETileBytes < B && tn != kNoStart) eb = min(eb, (tn & 0xFFFFFFFFull) + 1);
+        // 16-byte chunks c = 0..64 from the one holding byte sb; each one
+        // loaded holds a byte of the tile, so it lies in a readable page
+        const uint8_t* const p = in + sg.stream_off + sb;
+        const uint8_t* const pend = in + sg.stream_off + eb;
+        const uint4* const a16 = reinterpret_cast<const uint4*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)15);
+        const uint32_t o = (uint32_t)(p - reinterpret_cast<const uint8_t*>(a16));  // 0..15, wave-uniform
+        uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
+        if (reinterpret_cast<const uint8_t*>(a16 + lane) < pend) c0 = a16[lane];
+        if (lane == 0 && reinterpret_cast<const uint8_t*>(a16 + 64) < pend) c1 = a16[64];
+        uint4* const st16 = reinterpret_cast<uint4*>(sq);
+        st16[lane] = c0;
+        if (lane == 0) st16[64] = c1;
+        wave_sync();
+        // this lane's bytes sb + 16 lane .. + 15, from dwords 4 lane + o/4 ..
+        const uint32_t* const st32 = reinterpret_cast<const uint32_t*>(sq) + 4 * lane + (o >> 2);
+        uint32_t w5[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) w5[i] = st32[i];
+        uint32_t wd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[i] = __builtin_amdgcn_alignbyte(w5[i + 1], w5[i], o & 3u);
+        const uint64_t have = eb - sb;
+        const uint32_t nv = (uint32_t)min<uint64_t>(16u, have > 16u * lane ? have - 16u * lane : 0u);
+        uint32_t tsum = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < 16; ++i) {
+            const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
+            uint32_t len = i < nv ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
+            if (lane == 0 && i == 0) len = len > skip ? len - (uint32_t)skip : 0u;
+            tsum += len;
+        }
+        uint32_t tot;
+        uint32_t pos = wave_excl_sum(tsum, &tot);  // tile quartic byte of this lane's first byte
+        if (tot < need && lane == 0) raise_status(status, TLC_ERR_CORRUPT);
+        wave_sync();  // every lane has read the staged bytes
+        uint4* const q16 = reinterpret_cast<uint4*>(sq);
+#pragma unroll
+        for (uint32_t k = 0; k < kETile / 16 / 64; ++k) q16[lane + 64 * k] = make_uint4(0u, 0u, 0u, 0u);
+        wave_sync();
+#pragma unroll
+        for (uint32_t i = 0; i < 16; ++i) {
+            const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
+            uint32_t len = i < nv ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
+            if (lane == 0 && i == 0) len = len > skip ? len - (uint32_t)skip : 0u;
+            if (len && byte < 243u && byte != kZero && pos < need) {
+                uint32_t rest = byte;
+#pragma unroll
+                for (uint32_t d = 0; d < 5; ++d) {
+                    sq[5 * pos + d] = (int8_t)((int)(rest % 3u) - 1);
+                    rest /= 3u;
+                }
+            }
+            pos += len;
+        }
+        wave_sync();
+    }
+    // float4 group h holds tile elements 4h - mis .. 4h - mis + 3, aligned in y
+    const uint64_t a = sg.elem_off + (uint64_t)j * kETile;
+    const int32_t mis = (int32_t)(a & 3);
+    float* const yt = y + a;
+    const int32_t ng = (mis + (int32_t)nel + 3) / 4;
+    for (int32_t h = lane; h < ng; h += 64) {
+        const int32_t u0 = 4 * h - mis;
+        int q[4] = {0, 0, 0, 0};
+        if (has_lit) {
+            if (mis == 0) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(sq)[h];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = (int)(int8_t)(w >> (8 * i));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = u0 + i >= 0 && u0 + i < (int32_t)nel ? sq[u0 + i] : 0;
+            }
+        }
+        const float4 v = make_float4((float)q[0] * ms, (float)q[1] * ms, (float)q[2] * ms, (float)q[3] * ms);
+        if (u0 >= 0 && u0 + 4 <= (int32_t)nel) {
+            *reinterpret_cast<float4*>(yt + u0) = v;
+        } else {
+            if (u0 >= 0 && u0 < (int32_t)nel) yt[u0] = v.x;
+            if (u0 + 1 >= 0 && u0 + 1 < (int32_t)nel) yt[u0 + 1] = v.y;
+            if (u0 + 2 >= 0 && u0 + 2 < (int32_t)nel) yt[u0 + 2] = v.z;
+            if (u0 + 3 < (int32_t)nel) yt[u0 + 3] = v.w;
+        }
     }
 }
 
@@ -1589,6 +1816,32 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
     return TLC_OK;
 }
 
+// Blocks of a grid-looping kernel that are resident on the current device at
+// once (occupancy per CU times the CU count, at most `cap`), queried once per
+// device.  Such kernels hand work to their blocks or waves round-robin, so a
+// grid larger than this leaves a second, partial round of blocks running
+// alone at the end.
+enum GridKind { kGridPack, kGridDecode, kGridDecodeAdd, kGridDecodeRecord, kGridKinds };
+uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap) {
+    static std::mutex mu;
+    static std::vector<uint32_t> per_dev;  // kGridKinds entries per device, 0 = not queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return cap;
+    std::lock_guard<std::mutex> lk(mu);
+    const size_t at = (size_t)dev * kGridKinds + kind;
+    if (at >= per_dev.size()) per_dev.resize(at + 1, 0);
+    if (!per_dev[at]) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) == hipSuccess && cus > 0 &&
+            per_cu > 0)
+            per_dev[at] = (uint32_t)std::min<int64_t>((int64_t)cus * per_cu, cap);
+        else
+            per_dev[at] = cap, (void)hipGetLastError();  // a failed query leaves no error behind
+    }
+    return per_dev[at];
+}
+
 constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 uint64_t ftiles_of(uint64_t total) { return (total + kFTile - 1) / kFTile; }
@@ -1718,8 +1971,9 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     uint8_t* staging = reinterpret_cast<uint8_t*>(w + l.staging);
     const GroupView g = p.g;
     const uint64_t N = p.d.total;
-    const uint32_t ftiles = (uint32_t)p.d.ftiles, count = (uint32_t)p.d.count, spans = (uint32_t)p.d.spans;
-    const uint32_t pack_grid = (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, kPackGrid);
+    const uint32_t ftiles = (uint32_t)p.d.ftiles, spans = (uint32_t)p.d.spans;
+    const uint32_t pack_grid =
+        (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, resident_grid(kGridPack, reinterpret_cast<const void*>(k_quant_pack), kPackGrid));
     rc = launch("tlc_accum_max", st, [&] {
         k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, scales, s, cand_cnt, cand,
                                                  span_flags, p.d.spans, span_tickets, mbits, ctrl,
@@ -1752,6 +2006,51 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     });
 }
 
+// Decompress takes one of two launch sequences, both giving the same y.
+// Sparse: k_prep zero-fills y, then k_decode writes the nonzero codes over
+// the fill.  Dense: k_decode records where each encode tile begins and
+// k_expand writes every tile once.  The sparse path is faster while few tiles
+// hold a nonzero code (the fill is the fastest way to write y, and few lines
+// are written twice); the dense path once most tiles do (the scattered writes
+// then land on lines the fill has already written).  The host cannot see the
+// stream lengths without a synchronisation, so under TLC_DECODE_AUTO it
+// follows the density that the previous decompress on the same workspace
+// found: k_prep writes it to a slot of pinned host memory.
+std::atomic<int> g_decode_policy{TLC_DECODE_AUTO};
+constexpr uint32_t kHintSlots = 64;
+
+struct HintSlots {
+    bool tried = false;
+    uint32_t* host = nullptr;  // kHintSlots words of pinned host memory
+    uint32_t* dev = nullptr;   // the same words as the device addresses them
+};
+
+HintSlots hint_slots() {
+    static std::mutex mu;
+    static std::vector<HintSlots> per_dev;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return HintSlots{};
+    std::lock_guard<std::mutex> lk(mu);
+    if ((size_t)dev >= per_dev.size()) per_dev.resize(dev + 1);
+    HintSlots& h = per_dev[dev];
+    if (!h.tried) {
+        h.tried = true;
+        void* hp = nullptr;
+        void* dp = nullptr;
+        if (hipHostMalloc(&hp, kHintSlots * sizeof(uint32_t), hipHostMallocDefault) == hipSuccess) {
+            memset(hp, 0, kHintSlots * sizeof(uint32_t));
+            if (hipHostGetDevicePointer(&dp, hp, 0) == hipSuccess) {
+                h.host = static_cast<uint32_t*>(hp);
+                h.dev = static_cast<uint32_t*>(dp);
+            } else {
+                (void)hipHostFree(hp);
+            }
+        }
+        (void)hipGetLastError();  // a failed set-up leaves no error behind; AUTO then stays sparse
+    }
+    return h;
+}
+
 int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, const float* scales, float s,
                    float* y, void* ws, size_t ws_bytes, int* status, hipStream_t st, int accumulate) {
     if (!in || !in_lens || !scales || !y || !status) return TLC_ERR_INVALID_ARG;
@@ -1765,23 +2064,45 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     uint32_t* dec_map = reinterpret_cast<uint32_t*>(w + l.dec_map);
     uint32_t* dec_first = reinterpret_cast<uint32_t*>(w + l.dec_first);
     uint32_t* chunk_tickets = reinterpret_cast<uint32_t*>(w + l.chunk_tickets);
+    bool dense = false;
+    uint32_t* hint = nullptr;
+    if (!accumulate) {
+        const int policy = g_decode_policy.load(std::memory_order_relaxed);
+        const HintSlots h = hint_slots();
+        const uint32_t slot = (uint32_t)((reinterpret_cast<uintptr_t>(ws) >> 8) % kHintSlots);
+        if (h.host) hint = h.dev + slot;
+        dense = policy == TLC_DECODE_DENSE ||
+                (policy == TLC_DECODE_AUTO && h.host && reinterpret_cast<volatile uint32_t*>(h.host)[slot] != 0u);
+    }
+    // dense decompress: the compressor's per-tile summaries and maxima are not
+    // needed here, so their slots hold the tile starts and literal flags
+    uint64_t* tstart = dense ? reinterpret_cast<uint64_t*>(w + l.etile_agg) : nullptr;
+    uint32_t* tlit = reinterpret_cast<uint32_t*>(w + l.etmax);
     const GroupView g = p.g;
-    const uint64_t chunks = p.d.chunks;
-    const uint64_t n_fill = accumulate ? 0 : p.d.total;
-    // one float4 of the fill per thread: a grid of many short blocks is the
-    // fastest fill measured on MI355X (~6.9 TB/s against ~5.7 TB/s with eight
-    // stores per thread in a grid-stride loop)
-    uint64_t blocks = std::max<uint64_t>((n_fill / 4 + kThreads - 1) / kThreads, (chunks + kThreads - 1) / kThreads);
+    const uint64_t chunks = p.d.chunks, etiles = p.d.etiles;
+    const uint64_t n_fill = accumulate || dense ? 0 : p.d.total;
+    const uint64_t blocks =
+        std::max((n_fill / 4 + kThreads - 1) / kThreads, (std::max(chunks, etiles) + kThreads - 1) / kThreads);
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
-    rc = launch(accumulate ? "tlc_prep" : "tlc_prep_fill", st, [&] {
-        k_prep<<<prep_grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, dec_map, dec_first, chunk_tickets,
-                                               ctrl, status);
+    rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
+        k_prep<<<prep_grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, tstart, tlit, etiles, dec_map,
+                                               dec_first, chunk_tickets, ctrl, status, hint);
     });
     if (rc) return rc;
-    const uint32_t grid = (uint32_t)std::min<uint64_t>(chunks, kDecodeGrid);
-    return launch("tlc_decode", st, [&] {
-        k_decode<<<grid, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, flags, dec_map, dec_first, chunk_tickets,
-                                            ctrl, status, accumulate);
+    const int mode = accumulate ? kDecodeAdd : dense ? kDecodeRecord : kDecodeWrite;
+    auto kern = mode == kDecodeAdd ? k_decode<kDecodeAdd> : mode == kDecodeRecord ? k_decode<kDecodeRecord>
+                                                                                  : k_decode<kDecodeWrite>;
+    const GridKind gk = mode == kDecodeAdd ? kGridDecodeAdd : mode == kDecodeRecord ? kGridDecodeRecord : kGridDecode;
+    const uint32_t grid =
+        (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
+    rc = launch("tlc_decode", st, [&] {
+        kern<<<grid, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, tstart, tlit, flags, dec_map, dec_first,
+                                        chunk_tickets, ctrl, status);
+    });
+    if (rc || !dense) return rc;
+    return launch("tlc_expand", st, [&] {
+        k_expand<<<xcd_grid((etiles + kWaves - 1) / kWaves), kThreads, 0, st>>>(g, (uint32_t)etiles, in, in_lens,
+                                                                                 scales, s, tstart, tlit, y, status);
     });
 }
 
@@ -2028,6 +2349,13 @@ int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stre
 int tlc_profile_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_on = enable != 0;
+    return TLC_OK;
+}
+
+int tlc_set_decode_policy(int policy) {
+    if (policy != TLC_DECODE_AUTO && policy != TLC_DECODE_SPARSE && policy != TLC_DECODE_DENSE)
+        return TLC_ERR_INVALID_ARG;
+    g_decode_policy.store(policy, std::memory_order_relaxed);
     return TLC_OK;
 }
 

@@ -76,6 +76,7 @@ _SIGS = {
     "tlc_profile_enable": (_I, [_I]),
     "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
     "tlc_profile_only": (_I, [ctypes.c_char_p]),
+    "tlc_set_decode_policy": (_I, [_I]),
 }
 
 
@@ -428,6 +429,15 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
 
 def profile_enable(on: bool = True):
     _check(lib().tlc_profile_enable(1 if on else 0), "tlc_profile_enable")
+
+
+DECODE_AUTO, DECODE_SPARSE, DECODE_DENSE = 0, 1, 2
+
+
+def set_decode_policy(policy: int):
+    """Decompress launch sequence (tlc_set_decode_policy): DECODE_AUTO, or
+    DECODE_SPARSE / DECODE_DENSE to force one; the output is the same."""
+    _check(lib().tlc_set_decode_policy(int(policy)), "tlc_set_decode_policy")
 
 
 def profile_only(kernel_name: str | None):

@@ -29,7 +29,10 @@
  *     device memory (out_len, scale, status, ...) are valid once the stream
  *     reaches that point.
  *   - The library never allocates, frees or synchronises device memory; the
- *     caller owns every buffer.  Scratch memory is the caller's `workspace`
+ *     caller owns every buffer.  (Its one allocation is 256 bytes of pinned
+ *     host memory per device, made at the first decompress on that device
+ *     and kept until the process ends: the decode-path hints of
+ *     tlc_set_decode_policy.)  Scratch memory is the caller's `workspace`
  *     (device, 256-byte aligned, at least the size the *_workspace_size call
  *     returns; its contents need not survive between calls).  Calls that may
  *     run at the same time need separate workspaces and separate status
@@ -236,6 +239,24 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
 /* Streaming copy of `bytes` bytes (a multiple of 16, both pointers 16-byte
  * aligned): the achievable-HBM-bandwidth yardstick for the codec kernels. */
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream);
+
+/* Which of two launch sequences decompress (not accumulate) uses; both give
+ * the same y, bit for bit, so this is a performance setting only.
+ *   TLC_DECODE_SPARSE  zero fill of y, then the nonzero codes written over it:
+ *                      fastest while few encode tiles hold a nonzero code.
+ *   TLC_DECODE_DENSE   every encode tile decoded in LDS and written once:
+ *                      fastest once most tiles do (streams longer than about
+ *                      one byte per 8 quartic bytes, as after many steps of
+ *                      error feedback).
+ *   TLC_DECODE_AUTO    (default) the host cannot see the stream lengths
+ *                      without a synchronisation, so it takes the path that
+ *                      suits the streams of the previous decompress on the
+ *                      same workspace (the device leaves that density in a
+ *                      word of pinned host memory, one of 64 per device
+ *                      chosen by the workspace address); sparse at first.
+ * Process-wide, host only; returns TLC_ERR_INVALID_ARG for another value. */
+enum tlc_decode_policy { TLC_DECODE_AUTO = 0, TLC_DECODE_SPARSE = 1, TLC_DECODE_DENSE = 2 };
+int tlc_set_decode_policy(int policy);
 
 /* Kernel timing with HIP events.  While enabled, every kernel the library
  * launches is bracketed by two events recorded on the same stream.

@@ -171,3 +171,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tlc, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         tlc.lib()
+
+
+def test_decode_policy_argument_check():
+    for p in (tlc.DECODE_SPARSE, tlc.DECODE_DENSE, tlc.DECODE_AUTO):
+        tlc.set_decode_policy(p)
+    for bad in (-1, 3, 99):
+        assert tlc.lib().tlc_set_decode_policy(bad) == tlc.ERR_INVALID_ARG
+    tlc.set_decode_policy(tlc.DECODE_AUTO)
