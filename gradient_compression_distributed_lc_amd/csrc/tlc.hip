@@ -38,12 +38,16 @@
 //                 the span's input state, then the span's stream bytes (255
 //                 runs, remainder codes, staged literals) assembled in LDS and
 //                 written once.
-// decompress: k_prep (zero fill of y, one 16-byte store per lane; decoder
-//             state; list of stream chunks)
+// decompress: k_prep (decoder state; list of stream chunks; for sparse
+//             streams also the zero fill of y, one 16-byte store per lane)
 //             -> k_decode (one block per 4 KiB of stream bytes: expansion
 //             scan + look-back across the tensor's chunks for the quartic
-//             byte index, then only literal bytes are decoded and their
-//             nonzero codes written or added).
+//             byte index; then for sparse streams only literal bytes are
+//             decoded and their nonzero codes written (or, to accumulate,
+//             added); for dense streams the start of every encode tile is
+//             recorded)
+//             -> k_expand (dense streams: one wavefront per encode tile
+//             decodes it in LDS and writes it once).
 // fixed-length encodings (ablations: quartic bytes alone, 2-bit fields): the
 //             compress kernels up to k_quant_pack, which writes each tile's
 //             bytes at a fixed place over k_fixed_fill's zero-code bytes;
@@ -89,7 +93,7 @@ constexpr int kPackSlots = 4;                     // float4 loads per lane in on
 // still reach the threshold (see cand_bound), so that the second pass need
 // not read the flat tile again.
 constexpr uint32_t kCand = 64;                    // list slots per flat tile
-constexpr float kCandFrac = 0.475f;               // candidate bound = hint * s * kCandFrac
+constexpr float kCandFrac = 0.485f;               // candidate bound = hint * s * kCandFrac
 constexpr uint16_t kCandNone = 0xFFFF;            // count of a flat tile without a usable list
 constexpr uint32_t kCandOk = 0x80000000u;         // PackJob.fmask flag: the tensor's lists are complete
 constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (about what is resident at once)
@@ -375,11 +379,13 @@ __device__ __forceinline__ uint8_t remainder_code(uint32_t m) {  // m = 1..13
 // step's): an element with |v| below it has q = 0 whenever the threshold of
 // this step is at least the bound, which the second pass checks before it
 // relies on the lists.  Any hint is allowed: a missing or wrong one only
-// sends tensors or flat tiles down the full re-read.  kCandFrac = 0.95 of
-// the threshold M*s/2 at M = hint: a step whose M is within 5% below the
-// hint still uses the lists (measured on the BERT-large set under error
-// feedback: 5% keeps ~90% of the tensors, and the lists hold ~5% of the
-// elements; 10% doubles the lists for few more tensors).
+// sends tensors or flat tiles down the full re-read.  kCandFrac = 0.97 of
+// the threshold M*s/2 at M = hint: a step whose M is within 3% below the
+// hint still uses the lists.  Measured on the BERT-large set after 150 steps
+// of error feedback: margins of 2-3% give the fastest step (the lists are
+// written by the first pass and read by the second, so shorter lists save
+// in both); 5% writes ~25% more list entries; 1% and less sends so many
+// tensors down the full re-read that the second pass slows by 25-50%.
 __device__ __forceinline__ float cand_bound(float hint, float s) {
     return (hint > 0.0f && hint <= FLT_MAX) ? hint * s * kCandFrac : INFINITY;
 }
@@ -742,7 +748,19 @@ __device__ void pack_tile(const GroupView& g, const PackJob& jb, float* __restri
         // ta0 + f; the lists are taken 4 x 64 candidates per round.
         const uint32_t nft = (uint32_t)((e0 + nel - 1) / kFTile - ta0) + 1;
         const bool act = (uint32_t)lane < nft && ((m >> lane) & 1);
-        const uint32_t c = act ? cand_cnt[ta0 + lane] : 0u;
+        // The counts of flat tiles ta0 .. ta0 + 10 lie in 7 aligned words from
+        // word ta0 / 2 (read past the last count stays inside the workspace).
+        // The address is wave-uniform, so these are scalar loads, which do not
+        // wait behind the vector stores of the wave's previous tile.
+        const uint32_t* const cw = reinterpret_cast<const uint32_t*>(cand_cnt) + (ta0 >> 1);
+        uint32_t cwords[7];
+#pragma unroll
+        for (int k = 0; k < 7; ++k) cwords[k] = cw[k];
+        const uint32_t hw = (uint32_t)(ta0 & 1) + (uint32_t)lane;  // half-word holding flat tile ta0 + lane
+        uint32_t wsel = 0;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) wsel = (hw >> 1) == (uint32_t)k ? cwords[k] : wsel;
+        const uint32_t c = act ? ((hw & 1) ? wsel >> 16 : wsel & 0xFFFFu) : 0u;
         const uint32_t ovf = (uint32_t)__ballot(act && c == kCandNone);
         uint32_t C;
         const uint32_t pre = wave_excl_sum(act && c != kCandNone ? c : 0u, &C);
@@ -1276,9 +1294,11 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 constexpr uint64_t kNoStart = ~0ull;
 __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { return byte | skip << 32; }
 
-// A decompress whose streams hold more than one byte per kDenseFrac quartic
-// bytes is expected to have nonzero codes in most encode tiles.
-constexpr uint64_t kDenseFrac = 8;
+// Stream density (bytes per quartic byte) above which the dense decompress
+// path is faster: 81/1000, measured on MI355X over error-feedback runs of the
+// BERT-large set (the two paths cross at 0.081-0.082 with cycled and with
+// fresh inputs).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
+constexpr uint64_t kDenseNum = 81, kDenseDen = 1000;
 
 // Decoder state reset and set-up.  Sparse decompress (n_fill > 0): zero fill
 // of y, one 16-byte store per lane (the fastest fill measured on MI355X; any
@@ -1349,7 +1369,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
                     tl += s_d[0][w];
                     tb += s_d[1][w];
                 }
-                *hint = kDenseFrac * tl > tb ? 1u : 0u;
+                *hint = kDenseDen * tl > kDenseNum * tb ? 1u : 0u;
             }
         }
         if (threadIdx.x == 0) {
