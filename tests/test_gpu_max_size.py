@@ -1,5 +1,6 @@
 """GPU parity at the largest tensor the library takes: n = 2^32 - 1 fp32
-values (16 GiB), one compress + decompress + accumulate through the C ABI.
+values (16 GiB), one compress, a decompress on each of the two decode paths
+and an accumulate, through the C ABI.
 
 The input is a zero tensor with seeded spikes (first and last element
 included), so the oracle's results are computed exactly without holding the
@@ -79,8 +80,21 @@ def test_max_size_tensor():
     want_y = oracle.decompress(small, M, val.size, s)
     assert np.array_equal(bits(y[ti].cpu().numpy()), bits(want_y))
     assert int(torch.count_nonzero(y).item()) == int(nz.sum())
+    # the dense path on the same stream (its tile records hold 32-bit byte
+    # offsets within the tensor, largest here): the same y
+    say("case max size: decompress ok, dense path")
+    y.fill_(1.0)
+    tlc.set_decode_policy(tlc.DECODE_DENSE)
+    try:
+        y, st = tlc.decompress(c.out, c.out_len, c.scale, n, s, y=y)
+        torch.cuda.synchronize()
+    finally:
+        tlc.set_decode_policy(tlc.DECODE_AUTO)
+    assert int(st.item()) == 0
+    assert np.array_equal(bits(y[ti].cpu().numpy()), bits(want_y))
+    assert int(torch.count_nonzero(y).item()) == int(nz.sum())
     del y
-    say("case max size: decompress ok, accumulate")
+    say("case max size: dense decompress ok, accumulate")
 
     acc = err  # reuse the 16 GiB buffer: acc starts as the new error
     _, st = tlc.decompress_accumulate(c.out, c.out_len, c.scale, n, s, acc)
