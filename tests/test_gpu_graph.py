@@ -1,0 +1,99 @@
+"""A compress + decompress step captured in a HIP graph (torch.cuda.CUDAGraph)
+and replayed: every replay, with fresh inputs copied in eagerly between
+replays and the error buffer carried, must give the same stream bytes,
+lengths, M, error buffer and y as the same calls made eagerly on a second set
+of buffers, and the last replay must match the CPU oracle.  The library
+launches only kernels on the caller's stream (no memset nodes, no host
+synchronisation), so the captured step is the eager one."""
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import bits, oracle_group_compress, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager_and_oracle():
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(123)
+    sizes = [int(v) for v in rng.integers(1, 60_000, 40)] + [5120, 3, 200_001]
+    N = sum(sizes)
+    s = 1.5
+    dev = torch.device("cuda:0")
+
+    def buffers(g):
+        return dict(x=torch.zeros(N, dtype=torch.float32, device=dev),
+                    err=torch.zeros(N, dtype=torch.float32, device=dev),
+                    y=torch.empty(N, dtype=torch.float32, device=dev),
+                    out=torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev),
+                    lens=torch.empty(len(sizes), dtype=torch.int64, device=dev),
+                    scales=torch.zeros(len(sizes), dtype=torch.float32, device=dev),
+                    st_c=torch.empty(1, dtype=torch.int32, device=dev),
+                    st_d=torch.empty(1, dtype=torch.int32, device=dev),
+                    ws=g.workspace())
+
+    def step(g, b):  # on torch's current stream
+        g.compress(b["x"], b["err"], s, out=b["out"], out_lens=b["lens"], scales=b["scales"], workspace=b["ws"],
+                   status=b["st_c"])
+        g.decompress(b["out"], b["lens"], b["scales"], s, y=b["y"], workspace=b["ws"], status=b["st_d"])
+
+    g = tlc.Group(sizes)
+    gb, eb = buffers(g), buffers(g)
+    inputs = []
+    for k in range(5):
+        x = (rng.standard_normal(N) * 1e-3).astype(np.float32)
+        x[rng.random(N) < 0.3] = 0
+        inputs.append(x)
+    # warm-up outside capture (one-time set-up: occupancy queries, decode-path hint memory)
+    step(g, gb)
+    torch.cuda.synchronize()
+    gb["err"].zero_()
+    gb["scales"].zero_()
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(g, gb)
+    torch.cuda.synchronize()
+    # capture ran nothing: start both copies from the same zero state
+    gb["err"].zero_()
+    gb["scales"].zero_()
+    torch.cuda.synchronize()
+
+    err_h = np.zeros(N, np.float32)
+    for k, x in enumerate(inputs):
+        say(f"case graph replay {k}")
+        xd = to_dev(x)
+        gb["x"].copy_(xd)
+        eb["x"].copy_(xd)
+        torch.cuda.synchronize()
+        graph.replay()
+        step(g, eb)
+        torch.cuda.synchronize()
+        for b in (gb, eb):
+            assert int(b["st_c"].item()) == 0 and int(b["st_d"].item()) == 0, k
+        assert torch.equal(gb["lens"], eb["lens"]), k
+        assert torch.equal(gb["scales"].view(torch.int32), eb["scales"].view(torch.int32)), k
+        assert torch.equal(gb["err"].view(torch.int32), eb["err"].view(torch.int32)), k
+        assert torch.equal(gb["y"].view(torch.int32), eb["y"].view(torch.int32)), k
+        lens = gb["lens"].cpu().numpy()
+        out_g, out_e = gb["out"].cpu().numpy(), eb["out"].cpu().numpy()
+        for t in range(len(sizes)):
+            o = g.offsets[t]
+            assert np.array_equal(out_g[o:o + lens[t]], out_e[o:o + lens[t]]), (k, t)
+        # the oracle on the same chain of inputs
+        streams, Ms, err_h = oracle_group_compress(x, err_h, sizes, s)
+        if k == len(inputs) - 1:
+            assert np.array_equal(bits(gb["scales"].cpu().numpy()), bits(Ms))
+            assert np.array_equal(bits(gb["err"].cpu().numpy()), bits(err_h))
+            want_y = np.concatenate([oracle.decompress(streams[t], Ms[t], n, s) for t, n in enumerate(sizes)])
+            assert np.array_equal(bits(gb["y"].cpu().numpy()), bits(want_y))
+            for t in range(len(sizes)):
+                o = g.offsets[t]
+                assert lens[t] == streams[t].size and np.array_equal(out_g[o:o + lens[t]], streams[t]), t
