@@ -51,7 +51,8 @@
 // fixed-length encodings (ablations: quartic bytes alone, 2-bit fields): the
 //             compress kernels up to k_quant_pack, which writes each tile's
 //             bytes at a fixed place over k_fixed_fill's zero-code bytes;
-//             k_fixed_decode decodes one encode tile per wavefront.
+//             k_fixed_decode decodes one encode tile per wavefront, four per
+//             block.
 //
 // No matrix-core work exists on this path: it is bound by HBM bandwidth.
 
@@ -1716,76 +1717,118 @@ __global__ __launch_bounds__(64) void k_fixed_fill(GroupView g, uint32_t etiles,
 
 __global__ void k_status_ok(int* __restrict__ status) { *status = TLC_OK; }
 
-// Decode of a fixed-length encoding: one wavefront per encode tile; lane l
-// decodes codes 80l..80l+79 into LDS, then y is written with coalesced
-// 16-byte stores, y_i = q_i * (M*s).  A quartic byte above 242 or a 2-bit
-// field of 3 sets *status = TLC_ERR_CORRUPT.
-__global__ __launch_bounds__(64) void k_fixed_decode(GroupView g, int enc, const uint8_t* __restrict__ in,
-                                                     const uint64_t* __restrict__ offs,
-                                                     const float* __restrict__ scales, float s,
-                                                     float* __restrict__ y, int* __restrict__ status) {
-    __shared__ __align__(16) int8_t sq[kETile];
-    const uint32_t e = blockIdx.x;
-    const int lane = threadIdx.x;
+// Decode of a fixed-length encoding: one wavefront per encode tile, four per
+// block, tile ranges contiguous per XCD (as in k_expand).  Lane l reads the
+// bytes of codes 80l..80l+79 (16 quartic or 20 two-bit bytes, with aligned
+// vector loads when the tile's bytes start on a 16-byte boundary) and decodes
+// them into LDS; y is then written with 16-byte stores, y_i = q_i * (M*s).  A
+// tile whose bytes all encode zero codes skips the LDS.  A quartic byte above
+// 242 or a 2-bit field of 3 sets *status = TLC_ERR_CORRUPT.
+__global__ __launch_bounds__(kThreads) void k_fixed_decode(GroupView g, uint32_t etiles, int enc,
+                                                           const uint8_t* __restrict__ in,
+                                                           const uint64_t* __restrict__ offs,
+                                                           const float* __restrict__ scales, float s,
+                                                           float* __restrict__ y, int* __restrict__ status) {
+    __shared__ __align__(16) int8_t s_codes[kWaves * kETile];
+    const int lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const uint32_t e = xcd_unit(blockIdx.x, (etiles + kWaves - 1) / kWaves) * kWaves + wave;
+    if (e >= etiles) return;
+    int8_t* const sq = s_codes + wave * kETile;
     const uint32_t gi = etile_owner(g, e);
     const Seg sg = load_seg(g, gi);
     const uint32_t TB = fixed_tile_bytes(enc);
-    const uint64_t j = e - sg.etile0;
-    const uint32_t nb = (uint32_t)min((uint64_t)TB, fixed_len_of(sg.n, enc) - j * TB);
-    const uint32_t nel = min(kETile, sg.n - (uint32_t)j * kETile);
-    const uint8_t* const src = in + (offs ? offs[gi] : 0ull) + j * TB;
+    const uint32_t j = e - sg.etile0;
+    const uint32_t nb = (uint32_t)min((uint64_t)TB, fixed_len_of(sg.n, enc) - (uint64_t)j * TB);
+    const uint32_t nel = min(kETile, sg.n - j * kETile);
+    const uint8_t* const src = in + (offs ? offs[gi] : 0ull) + (uint64_t)j * TB;
     const float ms = scales[gi] * s;
-    bool bad = false;
-    const uint32_t nin = enc == TLC_ENC_TWOBIT ? 20u : 16u;  // bytes per lane
+    const bool two = enc == TLC_ENC_TWOBIT;
+    const uint32_t nin = two ? 20u : 16u;  // bytes per lane
     const uint32_t o0 = nin * lane;
-    uint32_t codes[20];  // 4 codes per word, as int8
+    const uint32_t zb = fixed_zero_byte(enc) * 0x01010101u;  // four zero-code bytes
+    uint32_t wb[5] = {zb, zb, zb, zb, zb};
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && o0 + nin <= nb) {
+        if (!two) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + o0);
+            wb[0] = v.x;
+            wb[1] = v.y;
+            wb[2] = v.z;
+            wb[3] = v.w;
+        } else {
 #pragma unroll
-    for (int i = 0; i < 20; ++i) codes[i] = 0;
-    if (enc == TLC_ENC_QUARTIC) {
-#pragma unroll
-        for (uint32_t b = 0; b < 16; ++b) {
-            const uint32_t byte = o0 + b < nb ? src[o0 + b] : kZero;
-            bad |= byte > 242u;
-            uint32_t rest = byte;
-#pragma unroll
-            for (uint32_t d = 0; d < 5; ++d) {
-                const uint32_t c = 5 * b + d;
-                codes[c >> 2] |= ((rest % 3u - 1u) & 0xFFu) << (8 * (c & 3));
-                rest /= 3u;
-            }
+            for (int k = 0; k < 5; ++k) wb[k] = reinterpret_cast<const uint32_t*>(src + o0)[k];
         }
     } else {
+        for (uint32_t b = 0; b < nin; ++b)
+            if (o0 + b < nb)
+                wb[b >> 2] = (wb[b >> 2] & ~(0xFFu << (8 * (b & 3)))) | (uint32_t)src[o0 + b] << (8 * (b & 3));
+    }
+    bool nz = false;
 #pragma unroll
-        for (uint32_t b = 0; b < 20; ++b) {
-            const uint32_t byte = o0 + b < nb ? src[o0 + b] : 0x55u;
+    for (int k = 0; k < 5; ++k) nz |= wb[k] != zb;
+    const bool any = __ballot(nz) != 0;  // wave-uniform
+    if (any) {
+        bool bad = false;
+        uint32_t codes[20];  // 4 codes per word, as int8
 #pragma unroll
-            for (uint32_t d = 0; d < 4; ++d) {
-                const uint32_t f = (byte >> (2 * d)) & 3u;
-                bad |= f == 3u;
-                codes[b] |= ((f - 1u) & 0xFFu) << (8 * d);
+        for (int i = 0; i < 20; ++i) codes[i] = 0;
+        if (!two) {
+#pragma unroll
+            for (uint32_t b = 0; b < 16; ++b) {
+                const uint32_t byte = (wb[b >> 2] >> (8 * (b & 3))) & 255u;
+                bad |= byte > 242u;
+                uint32_t rest = byte;
+#pragma unroll
+                for (uint32_t d = 0; d < 5; ++d) {
+                    const uint32_t c = 5 * b + d;
+                    codes[c >> 2] |= ((rest % 3u - 1u) & 0xFFu) << (8 * (c & 3));
+                    rest /= 3u;
+                }
+            }
+        } else {
+#pragma unroll
+            for (uint32_t b = 0; b < 20; ++b) {
+                const uint32_t byte = (wb[b >> 2] >> (8 * (b & 3))) & 255u;
+#pragma unroll
+                for (uint32_t d = 0; d < 4; ++d) {
+                    const uint32_t f = (byte >> (2 * d)) & 3u;
+                    bad |= f == 3u;
+                    codes[b] |= ((f - 1u) & 0xFFu) << (8 * d);
+                }
             }
         }
-    }
-    if (bad) raise_status(status, TLC_ERR_CORRUPT);
+        if (bad) raise_status(status, TLC_ERR_CORRUPT);
 #pragma unroll
-    for (int i = 0; i < 20; ++i) reinterpret_cast<uint32_t*>(sq)[20 * lane + i] = codes[i];
-    __syncthreads();
-    float* const yy = y + sg.elem_off + j * kETile;
-    const bool al = ((sg.elem_off + j * kETile) & 3) == 0;
-    for (uint32_t u = 4 * lane; u < nel; u += 256) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(sq)[u >> 2];
-        float4 v;
-        v.x = (float)(int)(int8_t)(w) * ms;
-        v.y = (float)(int)(int8_t)(w >> 8) * ms;
-        v.z = (float)(int)(int8_t)(w >> 16) * ms;
-        v.w = (float)(int)(int8_t)(w >> 24) * ms;
-        if (al && u + 4 <= nel) {
-            *reinterpret_cast<float4*>(yy + u) = v;
+        for (int i = 0; i < 20; ++i) reinterpret_cast<uint32_t*>(sq)[20 * lane + i] = codes[i];
+        wave_sync();
+    }
+    // float4 group h holds tile elements 4h - mis .. 4h - mis + 3, aligned in y
+    const uint64_t a = sg.elem_off + (uint64_t)j * kETile;
+    const int32_t mis = (int32_t)(a & 3);
+    float* const yt = y + a;
+    const int32_t ng = (mis + (int32_t)nel + 3) / 4;
+    for (int32_t h = lane; h < ng; h += 64) {
+        const int32_t u0 = 4 * h - mis;
+        int q[4] = {0, 0, 0, 0};
+        if (any) {
+            if (mis == 0) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(sq)[h];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = (int)(int8_t)(w >> (8 * i));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = u0 + i >= 0 && u0 + i < (int32_t)nel ? sq[u0 + i] : 0;
+            }
+        }
+        const float4 v = make_float4((float)q[0] * ms, (float)q[1] * ms, (float)q[2] * ms, (float)q[3] * ms);
+        if (u0 >= 0 && u0 + 4 <= (int32_t)nel) {
+            *reinterpret_cast<float4*>(yt + u0) = v;
         } else {
-            yy[u] = v.x;
-            if (u + 1 < nel) yy[u + 1] = v.y;
-            if (u + 2 < nel) yy[u + 2] = v.z;
-            if (u + 3 < nel) yy[u + 3] = v.w;
+            if (u0 >= 0 && u0 < (int32_t)nel) yt[u0] = v.x;
+            if (u0 + 1 >= 0 && u0 + 1 < (int32_t)nel) yt[u0 + 1] = v.y;
+            if (u0 + 2 >= 0 && u0 + 2 < (int32_t)nel) yt[u0 + 2] = v.z;
+            if (u0 + 3 < (int32_t)nel) yt[u0 + 3] = v.w;
         }
     }
 }
@@ -2133,7 +2176,8 @@ int run_decompress_fixed(const Plan& p, int enc, const uint8_t* in, const uint64
     int rc = launch("tlc_status_ok", st, [&] { k_status_ok<<<1, 1, 0, st>>>(status); });
     if (rc) return rc;
     return launch("tlc_fixed_decode", st, [&] {
-        k_fixed_decode<<<(uint32_t)p.d.etiles, 64, 0, st>>>(p.g, enc, in, offs, scales, s, y, status);
+        k_fixed_decode<<<xcd_grid((p.d.etiles + kWaves - 1) / kWaves), kThreads, 0, st>>>(
+            p.g, (uint32_t)p.d.etiles, enc, in, offs, scales, s, y, status);
     });
 }
 
