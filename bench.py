@@ -50,15 +50,16 @@ METRIC = "3LC compress+decompress GB/s (fp32 in) and % of HBM roofline; bits/val
 def kernel_source_hash(kernel: str = "k_accum_max") -> str:
     """Hash of one kernel's source text (from its signature to the closing
     brace at column 0), of the candidate-bound helper it calls and of every
-    file-scope constant, so that counters taken on it stay valid while other
-    kernels change, and are dropped once it or a constant changes."""
+    file-scope constant (code only, without comments or spacing), so that
+    counters taken on it stay valid while other kernels change, and are
+    dropped once it or a constant changes."""
     with open(os.path.join(ROOT, "gradient_compression_distributed_lc_amd", "csrc", "tlc.hip")) as f:
         src = f.read()
     parts = []
     for sig in (f"void {kernel}(", "float cand_bound("):
         i = src.index(sig)
         parts.append(src[i:src.index("\n}\n", i)])
-    parts += [ln for ln in src.splitlines() if ln.startswith("constexpr ")]
+    parts += ["".join(ln.split("//")[0].split()) for ln in src.splitlines() if ln.startswith("constexpr ")]
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 

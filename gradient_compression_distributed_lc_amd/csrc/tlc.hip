@@ -97,7 +97,7 @@ constexpr uint32_t kCand = 64;                    // list slots per flat tile
 constexpr float kCandFrac = 0.485f;               // candidate bound = hint * s * kCandFrac
 constexpr uint16_t kCandNone = 0xFFFF;            // count of a flat tile without a usable list
 constexpr uint32_t kCandOk = 0x80000000u;         // PackJob.fmask flag: the tensor's lists are complete
-constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (about what is resident at once)
+constexpr uint32_t kDecodeGrid = 2048;            // most blocks of k_decode (the grid follows the resident count)
 
 // look-back word: 2 status bits | 62 payload bits
 constexpr uint64_t kInvalid = 0, kAggregate = 1, kPrefix = 2, kPoison = 3;
@@ -2036,7 +2036,8 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     const uint64_t N = p.d.total;
     const uint32_t ftiles = (uint32_t)p.d.ftiles, spans = (uint32_t)p.d.spans;
     const uint32_t pack_grid =
-        (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves, resident_grid(kGridPack, reinterpret_cast<const void*>(k_quant_pack), kPackGrid));
+        (uint32_t)std::min<uint64_t>((p.d.etiles + kWaves - 1) / kWaves,
+                                     resident_grid(kGridPack, reinterpret_cast<const void*>(k_quant_pack), kPackGrid));
     rc = launch("tlc_accum_max", st, [&] {
         k_accum_max<<<ftiles, kAccThreads, 0, st>>>(g, N, x, x_div, err, pmax, scales, s, cand_cnt, cand,
                                                  span_flags, p.d.spans, span_tickets, mbits, ctrl,
