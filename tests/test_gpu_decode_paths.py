@@ -127,3 +127,50 @@ def test_auto_follows_density_on_one_workspace():
         y, status = gpu_decompress(st, M, n, 1.25, ws=ws)
         assert status == 0
         assert np.array_equal(bits(y), bits(oracle.decompress(st, M, n, 1.25))), k
+
+
+@pytest.mark.timeout(600)
+def test_bert_large_steady_state_streams_both_paths():
+    # the full 335M-value set after 100 steps of error feedback on the GPU
+    # (inputs cycled through 4 rolled copies): every encode tile holds nonzero
+    # codes, so AUTO takes the dense path.  Both paths decode the final streams
+    # to the oracle's decode of the same streams, tensor by tensor.
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc, workloads
+    w = workloads.get("bert_large")
+    sizes, N, s = w.sizes, w.total, w.s_values[0]
+    g = tlc.Group(sizes)
+    x0 = to_dev(workloads.generate("bert_large"))
+    xs = [x0] + [torch.roll(x0, k * 1_000_003) for k in range(1, 4)]
+    err = torch.zeros(N, dtype=torch.float32, device="cuda:0")
+    ws = g.workspace()
+    out = torch.empty(g.stream_bytes, dtype=torch.uint8, device="cuda:0")
+    lens = torch.empty(len(sizes), dtype=torch.int64, device="cuda:0")
+    scales = torch.zeros(len(sizes), dtype=torch.float32, device="cuda:0")
+    st = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    for k in range(100):
+        g.compress(xs[k % 4], err, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got_out, got_lens, got_M = out.cpu().numpy(), lens.cpu().numpy(), scales.cpu().numpy()
+    B = sum(-(-n // 5) for n in sizes)
+    say(f"case decode path bert_large steady: density {got_lens.sum() / B:.4f}")
+    assert got_lens.sum() / B > 0.081  # the dense regime
+    want = np.empty(N, np.float32)
+    off = 0
+    for t, n in enumerate(sizes):
+        o = g.offsets[t]
+        want[off:off + n] = oracle.decompress(got_out[o:o + got_lens[t]], got_M[t], n, s)
+        off += n
+    y = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    for pol in (tlc.DECODE_DENSE, tlc.DECODE_SPARSE, tlc.DECODE_AUTO, tlc.DECODE_AUTO):
+        say(f"case decode path bert_large steady policy {pol}")
+        tlc.set_decode_policy(pol)
+        try:
+            y.fill_(7.0)
+            _, st_d = g.decompress(out, lens, scales, s, y=y, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            tlc.set_decode_policy(tlc.DECODE_AUTO)
+        assert int(st_d.item()) == 0
+        assert np.array_equal(bits(y.cpu().numpy()), bits(want)), pol
