@@ -445,6 +445,10 @@ def main():
                                                / HBM_PEAK_GBPS, 4),
         "server_bits_per_value": round(8.0 * L_srv / N, 4),
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
+        # the same algorithmic bytes against the measured copy rate instead of the nominal peak
+        "path_copy_ceiling_frac": round((alg_bytes_comp + alg_bytes_dec) / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4)
+        if copy_gbps else None,
+        "dominant_copy_ceiling_frac": round(achieved / copy_gbps, 4) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
         "steady_state": steady,
         "ablations": ablations,
