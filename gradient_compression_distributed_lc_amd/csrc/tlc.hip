@@ -1049,12 +1049,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __r
         pack_tile(g, jobs[i], err, etile_agg, staging, cand_cnt, cand, fo, s_q + wave * kSlice);
 }
 
-// Largest span output assembled in LDS by k_emit (an all-zero span of 256
-// encode tiles needs ~18.7 KB, a span of the BERT-large set after many
-// error-feedback steps ~39 KB); larger spans take the two-pass path.  With
-// the block's other arrays this keeps three blocks per CU (160 KB of LDS),
-// so the ~560 spans of a 340M-value set are resident at once.
+// Bytes of a span's output that k_emit assembles in LDS at a time (an
+// all-zero span of 256 encode tiles needs ~18.7 KB, a span of the BERT-large
+// set after many error-feedback steps ~35-45 KB); a larger output goes out in
+// several windows.  With the block's other arrays this keeps three blocks per
+// CU (160 KB of LDS), so the ~560 spans of a 340M-value set are resident at
+// once.
 constexpr uint32_t kEmitLds = 40960;
+
+__device__ __forceinline__ uint8_t byte_of(const uint4& v, uint32_t i) {  // byte i (0..15) of v
+    const uint32_t w = i < 4 ? v.x : i < 8 ? v.y : i < 12 ? v.z : v.w;
+    return (uint8_t)(w >> (8 * (i & 3)));
+}
 
 // One block per span of 256 encode tiles of a tensor: block scan of the
 // tiles' carry summaries, decoupled look-back across the tensor's spans for
@@ -1072,9 +1078,9 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     __shared__ uint16_t s_kint[kThreads];     // staged bytes after the lead (and remainder code)
     __shared__ uint8_t s_rem[kThreads];       // remainder code after the 255s, or 0
     __shared__ uint8_t s_fin[kThreads];       // closing remainder code of the tensor's last tile, or 0
-    __shared__ uint32_t s_wpre[kThreads + 1];  // prefix of staged 4-byte words over the span's tiles
-    __shared__ __align__(16) uint8_t s_out[kEmitLds + 16];  // the span's bytes, shifted by the store misalignment
-    __shared__ uint32_t s_span, s_E, s_r, s_ok;
+    __shared__ uint32_t s_cpre[kThreads + 1];  // prefix of staged 16-byte chunks over the span's tiles
+    __shared__ __align__(16) uint32_t s_out[(kEmitLds + 16) / 4];  // the span's bytes, inverted and shifted by the store misalignment
+    __shared__ uint32_t s_span, s_E, s_r, s_ok, s_clo, s_chi;
 
     // Block b belongs to the tensor of span b.  A tensor with several spans
     // hands them out in ticket order from its own counter, so that the
@@ -1098,26 +1104,34 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     uint64_t total;
     const uint64_t excl = block_excl_scan(carry_pack(a), 0ull, CarryCompose(), s_sm, &total);
 
-    // The staged words of the span's tiles do not depend on the look-back:
-    // the first 256 of them are loaded before it.
+    // The staged bytes of the span's tiles do not depend on the look-back:
+    // they move in aligned 16-byte chunks (chunk c of a tile holds its staged
+    // bytes 16c .. 16c + 15), and the first 256 chunks are loaded before it.
     const uint8_t* const stg = staging + (uint64_t)(sg.etile0 + lsp * kSpan) * kETileBytes;
-    uint32_t tot_words;
-    s_wpre[threadIdx.x] = block_excl_sum((kint + 3) / 4, s_u, &tot_words);
-    if (threadIdx.x == 0) s_wpre[kThreads] = tot_words;
+    uint32_t tot_chunks;
+    s_cpre[threadIdx.x] = block_excl_sum((kint + 15) / 16, s_u, &tot_chunks);
+    if (threadIdx.x == 0) s_cpre[kThreads] = tot_chunks;
     __syncthreads();
-    auto word_owner = [&](uint32_t wv) {  // tile holding staged word wv of the span
+    auto chunk_owner = [&](uint32_t cv) {  // tile holding staged chunk cv of the span
         uint32_t k = 0, hi2 = kThreads;
         while (hi2 - k > 1) {
             const uint32_t mid = (k + hi2) >> 1;
-            if (s_wpre[mid] <= wv) k = mid;
+            if (s_cpre[mid] <= cv) k = mid;
             else hi2 = mid;
         }
         return k;
     };
-    uint32_t k0 = 0, val0 = 0;
-    if (threadIdx.x < tot_words) {
-        k0 = word_owner(threadIdx.x);
-        val0 = reinterpret_cast<const uint32_t*>(stg + (uint64_t)k0 * kETileBytes)[threadIdx.x - s_wpre[k0]];
+    auto load_chunk = [&](uint32_t k, uint32_t cv) {
+        return reinterpret_cast<const uint4*>(stg + (uint64_t)k * kETileBytes)[cv - s_cpre[k]];
+    };
+    uint32_t k0 = 0, v0x = 0, v0y = 0, v0z = 0, v0w = 0;  // (held in registers across the look-back)
+    if (threadIdx.x < tot_chunks) {
+        k0 = chunk_owner(threadIdx.x);
+        const uint4 c = load_chunk(k0, threadIdx.x);
+        v0x = c.x;
+        v0y = c.y;
+        v0z = c.z;
+        v0w = c.w;
     }
 
     if (threadIdx.x < 64) {
@@ -1203,86 +1217,118 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     uint8_t* const o = out + sg.stream_off + D;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(o) & 15);
     const uint32_t nchunks = end ? (mis + end + 15) / 16 : 0u;
-    // The staged words of the span, 8 per thread and round with every load
-    // issued before the first byte is placed (the first word was loaded
-    // before the look-back); put(p, b) writes span byte p.
-    auto copy_staged = [&](auto put) {
-        for (uint32_t base = 0; base < tot_words; base += 8 * kThreads) {
-            uint32_t kk[8], val[8];
+    // Staged chunks cv_lo .. cv_hi - 1 of the span, 4 per thread and round
+    // with every load issued before the first byte is placed (chunk t was
+    // loaded by thread t before the look-back); put(p, nb, v) places the
+    // first nb bytes of v (nb >= 1) at span bytes p .. p + nb - 1.
+    auto copy_staged = [&](uint32_t cv_lo, uint32_t cv_hi, auto put) {
+        for (uint32_t base = cv_lo; base < cv_hi; base += 4 * kThreads) {
+            uint32_t kk[4];
+            uint4 val[4];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t wv = base + r * kThreads + threadIdx.x;
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t cv = base + r * kThreads + threadIdx.x;
                 kk[r] = 0;
-                val[r] = 0;
-                if (wv < tot_words) {
-                    kk[r] = wv == threadIdx.x ? k0 : word_owner(wv);
-                    val[r] = wv == threadIdx.x
-                                 ? val0
-                                 : reinterpret_cast<const uint32_t*>(stg + (uint64_t)kk[r] * kETileBytes)[wv - s_wpre[kk[r]]];
+                val[r] = make_uint4(0u, 0u, 0u, 0u);
+                if (cv < cv_hi) {
+                    kk[r] = cv == threadIdx.x ? k0 : chunk_owner(cv);
+                    val[r] = cv == threadIdx.x ? make_uint4(v0x, v0y, v0z, v0w) : load_chunk(kk[r], cv);
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t wv = base + r * kThreads + threadIdx.x;
-                if (wv < tot_words) {
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t cv = base + r * kThreads + threadIdx.x;
+                if (cv < cv_hi) {
                     const uint32_t k = kk[r];
-                    const uint32_t w4 = wv - s_wpre[k];  // word within the tile's staged bytes
-                    const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + 4 * w4;
-                    const uint32_t nbw = min(4u, (uint32_t)s_kint[k] - 4 * w4);
-#pragma unroll
-                    for (uint32_t i = 0; i < 4; ++i)
-                        if (i < nbw && sbase + i < end) put(sbase + i, (uint8_t)(val[r] >> (8 * i)));
+                    const uint32_t c16 = 16 * (cv - s_cpre[k]);  // first staged byte of the chunk
+                    const uint32_t sbase = s_off[k] + s_lead[k] + (s_rem[k] ? 1u : 0u) + c16;
+                    if (sbase < end) put(sbase, min(min(16u, (uint32_t)s_kint[k] - c16), end - sbase), val[r]);
                 }
             }
         }
     };
-    if (end <= kEmitLds) {
-        // Assembled in LDS (byte p of the span at s_out[mis + p]): 255 fill,
-        // then the exceptions, then one aligned 16-byte store per chunk, so
-        // every stream byte is written once and no barrier waits on HBM.
-        for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads)
-            reinterpret_cast<uint4*>(s_out)[c] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        __syncthreads();
-        {
-            const uint32_t t_off = s_off[threadIdx.x];
-            if (rem && t_off + lead < end) s_out[mis + t_off + lead] = (uint8_t)rem;
-            if (fin && t_off + len - 1 < end) s_out[mis + t_off + len - 1] = (uint8_t)fin;
+
+    // The output goes out in windows of kEmitLds bytes (one window for all
+    // but the densest spans).  A window is assembled in LDS, where span byte
+    // p is byte p - lo of s_out (lo: the span byte of the window's first
+    // aligned 16-byte store chunk) and holds the stream byte inverted: the
+    // buffer starts at zero (all bytes 255) and every exception byte is OR-ed
+    // in, so neighbouring tiles' bytes that share a word need no ordering.
+    // Then one aligned 16-byte store per chunk, inverted back: every stream
+    // byte is written once and no barrier waits on HBM.
+    constexpr uint32_t kWin = kEmitLds / 16;  // store chunks per window
+    const uint32_t so = s_off[threadIdx.x] + lead + (rem ? 1u : 0u);  // span byte of this tile's first staged byte
+    for (uint32_t w0 = 0; w0 < nchunks; w0 += kWin) {
+        const uint32_t wn = min(kWin, nchunks - w0);
+        const int32_t lo = (int32_t)(16 * w0) - (int32_t)mis;
+        const int32_t hi = lo + (int32_t)(16 * wn);
+        if (threadIdx.x == 0) {
+            s_clo = ~0u;
+            s_chi = 0u;
         }
-        copy_staged([&](uint32_t p, uint8_t b) { s_out[mis + p] = b; });
+        for (uint32_t c = threadIdx.x; c < wn; c += kThreads)
+            reinterpret_cast<uint4*>(s_out)[c] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-        for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
-            const int64_t p0 = (int64_t)c * 16 - mis;  // span byte of the chunk's first byte
-            uint8_t* const dst = o + p0;
-            if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
-                *reinterpret_cast<uint4*>(dst) = reinterpret_cast<const uint4*>(s_out)[c];
-            } else {
-                for (int64_t i = 0; i < 16; ++i)
-                    if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = s_out[c * 16 + i];
+        // the staged chunks that meet the window are consecutive: their range
+        // is the min and max over the tiles
+        if (kint) {
+            const int32_t a = max(lo - (int32_t)so, 0), b = min(hi - (int32_t)so, (int32_t)kint);
+            if (a < b) {
+                atomicMin(&s_clo, s_cpre[threadIdx.x] + (uint32_t)a / 16);
+                atomicMax(&s_chi, s_cpre[threadIdx.x] + ((uint32_t)b + 15) / 16);
             }
         }
-        return;
-    }
-
-    // Two passes straight to HBM: pass A writes 255 over all of the span
-    // with aligned 16-byte stores (the two partial end chunks byte by byte);
-    // pass B, after a barrier, overwrites the exceptions.
-    for (uint32_t c = threadIdx.x; c < nchunks; c += kThreads) {
-        const int64_t p0 = (int64_t)c * 16 - mis;
-        uint8_t* const dst = o + p0;
-        if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(~0u, ~0u, ~0u, ~0u);
-        } else {
-            for (int64_t i = 0; i < 16; ++i)
-                if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = 255;
+        auto or_byte = [&](int32_t p, uint32_t b) {  // span byte p in [lo, hi)
+            const uint32_t pos = (uint32_t)(p - lo);
+            atomicOr(s_out + (pos >> 2), (~b & 0xFFu) << (8 * (pos & 3)));
+        };
+        {
+            const int32_t pr = (int32_t)(s_off[threadIdx.x] + lead), pf = (int32_t)(s_off[threadIdx.x] + len) - 1;
+            if (rem && pr < (int32_t)end && pr >= lo && pr < hi) or_byte(pr, rem);
+            if (fin && pf < (int32_t)end && pf >= lo && pf < hi) or_byte(pf, fin);
         }
+        __syncthreads();
+        copy_staged(s_clo, s_chi, [&](uint32_t p, uint32_t nb, uint4 v) {
+            // bytes j of the chunk with j < nb and lo <= p + j < hi, inverted
+            // (the others zeroed), shifted to the byte offset of p - lo in its
+            // word, into the five words of s_out they meet
+            const int32_t dst = (int32_t)p - lo;
+            const int32_t jlo = max(-dst, 0), jhi = min((int32_t)nb, (int32_t)(16 * wn) - dst);
+            auto inv = [&](uint32_t w, int32_t b0) {  // chunk bytes b0 .. b0 + 3
+                const int32_t x = max(jlo - b0, 0), y = min(jhi - b0, 4);
+                const uint32_t keep = y <= x ? 0u
+                                             : (uint32_t)((((uint64_t)1 << (8 * (y - x))) - 1u) << (8 * x));
+                return ~w & keep;
+            };
+            const uint32_t i0 = inv(v.x, 0), i1 = inv(v.y, 4), i2 = inv(v.z, 8), i3 = inv(v.w, 12);
+            const uint32_t m = (uint32_t)dst & 3u;
+            const int32_t wb = (dst - (int32_t)m) / 4;  // word of s_out holding byte dst (may be -1..-4)
+            auto put_word = [&](int32_t i, uint32_t cur, uint32_t prev) {
+                const uint32_t o = m == 0 ? cur : __builtin_amdgcn_alignbyte(cur, prev, 4u - m);
+                if (o) atomicOr(s_out + (wb + i), o);  // o != 0 only for a word inside the window
+            };
+            put_word(0, i0, 0u);
+            put_word(1, i1, i0);
+            put_word(2, i2, i1);
+            put_word(3, i3, i2);
+            put_word(4, 0u, i3);
+        });
+        __syncthreads();
+        for (uint32_t c = threadIdx.x; c < wn; c += kThreads) {
+            const int64_t p0 = (int64_t)(w0 + c) * 16 - mis;  // span byte of the chunk's first byte
+            uint8_t* const dst = o + p0;
+            uint4 v = reinterpret_cast<const uint4*>(s_out)[c];
+            v = make_uint4(~v.x, ~v.y, ~v.z, ~v.w);
+            if (p0 >= 0 && p0 + 16 <= (int64_t)end) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (p0 + i >= 0 && p0 + i < (int64_t)end) dst[i] = byte_of(v, (uint32_t)i);
+            }
+        }
+        __syncthreads();  // s_out is cleared for the next window
     }
-    __syncthreads();  // pass A done
-    {
-        const uint32_t t_off = s_off[threadIdx.x];
-        if (rem && t_off + lead < end) o[t_off + lead] = (uint8_t)rem;
-        if (fin && t_off + len - 1 < end) o[t_off + len - 1] = (uint8_t)fin;
-    }
-    copy_staged([&](uint32_t p, uint8_t b) { o[p] = b; });
 }
 
 // ---------------------------------------------------------------------------

@@ -91,6 +91,28 @@ def test_dense_codes():
         check_single(x, np.zeros(n, np.float32), s, label=f"dense s={s}")
 
 
+def test_dense_spans_with_long_outputs():
+    # The stream of a span of 256 encode tiles is assembled on chip 40 KB at
+    # a time.  Dense codes make each span's output several windows long; the
+    # mid-density case puts it just past one window; the third case is dense
+    # in the first span only.  Tensors of two spans and a ragged tail, so that
+    # later spans start at unaligned stream offsets.
+    span = 256 * TILE
+    n = 2 * span + 777
+    rng = np.random.default_rng(21)
+    dense = rng.uniform(-1.0, 1.0, n).astype(np.float32)
+    mid = np.where(rng.random(n) < 0.02, rng.choice([-0.8, 0.8], n), 0.0).astype(np.float32)
+    mid[n // 2] = 1.0
+    half = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    half[:span] = rng.uniform(-1.0, 1.0, span).astype(np.float32)
+    for name, x, s in (("dense", dense, 1.0), ("mid", mid, 1.0), ("dense-first-span", half, 1.2)):
+        say(f"case long span outputs {name}")
+        got = check_single(x, np.zeros(n, np.float32), s, label=name)
+        say(f"  stream {got['L']} bytes over {-(-n // span)} spans")
+        if name == "mid":  # each full span's output lies between one and two windows
+            assert 2 * 40960 < got["L"] < 4 * 40960, got["L"]
+
+
 def test_runs_end_at_every_phase_across_tile_boundaries():
     # spikes put literal bytes at tile-boundary offsets -14..+14 so that runs
     # end at every phase of the 14-chunk cycle on both sides of a boundary
