@@ -16,7 +16,8 @@ Printed: one JSON line with the whole-job throughput in GB/s of fp32 input
 (4 bytes x values / (compress + decompress time)), the roofline of the
 dominant kernel (the 12-byte/element pass over x and err) measured with HIP
 events inside the timed region, bits per value, and the CPU oracle timed on
-the host over the same workload.  Also reported, outside the timed steps:
+the host over the same workload (single-threaded, and as independent
+per-tensor calls over up to 16 host cores).  Also reported, outside the timed steps:
 compress and decompress timed apart, the 8-payload accumulate, the same
 step after --steady-steps steps of error feedback (the error buffer then
 keeps every encode tile active and the streams are about twice as dense),
@@ -115,6 +116,59 @@ def cpu_baseline(x: np.ndarray, sizes, s: float, passes: int):
         "compress_s": round(tc / passes, 3),
         "decompress_s": round(td / passes, 3),
     }, streams, Ms, err0
+
+
+def cpu_baseline_all_cores(x: np.ndarray, sizes, s: float, passes: int):
+    """The same oracle, untouched, as independent per-tensor units spread over
+    the host's cores (a thread pool; each call into the C oracle runs outside
+    the interpreter lock).  Largest tensors are started first."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from gradient_compression_distributed_lc_amd import workloads
+    offs = workloads.offsets(sizes)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(avail, 16))
+    order = sorted(range(len(sizes)), key=lambda t: -sizes[t])
+    oracle.lib()  # built and loaded before the clock starts
+    outs = [np.empty(-(-n // 5), dtype=np.uint8) for n in sizes]
+    ys = [np.empty(n, dtype=np.float32) for n in sizes]
+
+    def unit(t, err):
+        a, b = offs[t], offs[t + 1]
+        L, M = oracle.compress_inplace(x[a:b], err[a:b], s, outs[t])
+        oracle.decompress(outs[t][:L], M, sizes[t], s, out=ys[t])
+
+    total = 0.0
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for _ in range(passes):
+            err = np.zeros(x.size, dtype=np.float32)
+            t0 = time.perf_counter()
+            list(pool.map(lambda t: unit(t, err), order))
+            total += time.perf_counter() - t0
+    return {
+        "value": round(4.0 * passes * x.size / total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"whole workload, {passes} pass(es) of compress+decompress, one oracle call per tensor "
+                  f"on a pool of {threads} threads ({avail} cores available)",
+        "host_cpu": host_cpu_model(),
+    }
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -385,7 +439,7 @@ def main():
     alg_bytes_srv = (4.0 * N + L_total) + 7 * (L_total + nnz_bytes) + (12.0 * N + L_srv + 4 * len(sizes))
     gbps = 4.0 * N / (ms_per_step * 1e-3) / 1e9
 
-    cpu = None
+    cpu = cpu_all = None
     parity = "not checked (--no-cpu)"
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -399,6 +453,9 @@ def main():
         parity = "bit-exact vs oracle (streams, M, error buffer; first step)" if ok else "MISMATCH"
         if not ok:
             print("[bench] PARITY MISMATCH", file=sys.stderr, flush=True)
+        cpu["host_cpu"] = host_cpu_model()
+        print("[bench] timing the CPU oracle on all cores", file=sys.stderr, flush=True)
+        cpu_all = cpu_baseline_all_cores(x_host, sizes, s, args.cpu_passes)
 
     traffic = stored_traffic(args.workload)
     result = {
@@ -421,6 +478,7 @@ def main():
                      "traffic": traffic, "bytes_per_elem": DOMINANT_BYTES_PER_ELEM,
                      "avg_ms": round(dom_ms, 4)},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "parity": parity,
         "bits_per_value": round(bits, 4),
         "bits_per_value_with_scale": round(bits_hdr, 4),
