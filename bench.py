@@ -334,7 +334,7 @@ def main():
     pipe_ms = pa.elapsed_time(pb) / args.steps
     ed.copy_(e_keep)
     counter[0] = c_keep
-    del pay, ws_d, e_keep
+    del e_keep
     torch.cuda.synchronize()
 
     # per-kernel breakdown: a separate, shorter pass with every kernel bracketed
@@ -468,6 +468,18 @@ def main():
         steady = {"after_steps": counter[0] - 10, "ms_per_step": round(st_ms, 4),
                   "GBps_fp32_in": round(4.0 * N / (st_ms * 1e-3) / 1e9, 1),
                   "bits_per_value": round(8.0 * float(lens.sum().item()) / N, 4)}
+        # the same state pipelined over the two streams (10 more steps)
+        for b in range(2):
+            pay[b][2].copy_(scales)
+        torch.cuda.synchronize()
+        pa.record(sA)
+        pipeline(10, counter[0])
+        pb.record(sB)
+        torch.cuda.synchronize()
+        if (int(st_pc.item()), int(st_pd.item())) != (0, 0):
+            raise SystemExit("device status not ok in the pipelined steady-state steps")
+        steady["pipelined_ms_per_step"] = round(pa.elapsed_time(pb) / 10, 4)
+    del pay, ws_d
 
 
     # copy yardstick: what a plain streaming copy reaches on this GPU
