@@ -1349,7 +1349,10 @@ constexpr uint64_t kDenseNum = 81, kDenseDen = 1000;
 
 // Decoder state reset and set-up.  Sparse decompress (n_fill > 0): zero fill
 // of y, one 16-byte store per lane (the fastest fill measured on MI355X; any
-// load before the store, or more stores per lane, slows it by 10-40%).  Dense
+// load before the store, or more stores per lane, slows it by 10-40%), with a
+// nontemporal hint: y is not read again here, and the kernels that follow
+// (the caller's next compress) run faster when the caches do not hold y's
+// dirty lines.  Dense
 // decompress (tstart set): the tile starts and literal flags are reset.
 // Always: the look-back flags, and the list of stream chunks: tensor i has
 // max(1, ceil(min(L_i, B_i) / kChunk)) chunks, numbered dec_first[i] ...;
@@ -1369,7 +1372,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
     const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
     const uint64_t n4 = n_fill >> 2;
     float4* const y4 = reinterpret_cast<float4*>(y);
-    for (uint64_t i = tid; i < n4; i += stride) y4[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (uint64_t i = tid; i < n4; i += stride)
+        __builtin_nontemporal_store(f4{0.0f, 0.0f, 0.0f, 0.0f}, reinterpret_cast<f4*>(y4 + i));
     if (tid < (n_fill & 3)) y[(n4 << 2) + tid] = 0.0f;
     for (uint64_t i = tid; i < nflags; i += stride) flags[i] = 0;
     if (tstart)
@@ -1609,9 +1613,10 @@ uint32_t xcd_grid(uint64_t units) { return (uint32_t)((units + 7) / 8 * 8); }
 
 // One wavefront per encode tile (5120 elements, 1024 quartic bytes), four per
 // block, with no block barrier: every element of the tile is written once,
-// y = q * (M*s), with 16-byte stores, so decompress writes each line of y
-// once (a zero fill with the nonzero values scattered over it afterwards wrote
-// every line that holds a nonzero code twice).  A tile k_decode found no
+// y = q * (M*s), with nontemporal 16-byte stores (as the zero fill), so
+// decompress writes each line of y once (a zero fill with the nonzero values
+// scattered over it afterwards wrote every line that holds a nonzero code
+// twice).  A tile k_decode found no
 // nonzero code in is written without reading the stream.  Otherwise its
 // stream bytes, from the start k_decode recorded, are staged in LDS with
 // aligned 16-byte loads, re-read 16 per lane in stream order, and expanded
@@ -1725,7 +1730,7 @@ __global__ __launch_bounds__(kThreads) void k_expand(GroupView g, uint32_t etile
         }
         const float4 v = make_float4((float)q[0] * ms, (float)q[1] * ms, (float)q[2] * ms, (float)q[3] * ms);
         if (u0 >= 0 && u0 + 4 <= (int32_t)nel) {
-            *reinterpret_cast<float4*>(yt + u0) = v;
+            __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4*>(yt + u0));
         } else {
             if (u0 >= 0 && u0 < (int32_t)nel) yt[u0] = v.x;
             if (u0 + 1 >= 0 && u0 + 1 < (int32_t)nel) yt[u0 + 1] = v.y;
@@ -1869,7 +1874,7 @@ __global__ __launch_bounds__(kThreads) void k_fixed_decode(GroupView g, uint32_t
         }
         const float4 v = make_float4((float)q[0] * ms, (float)q[1] * ms, (float)q[2] * ms, (float)q[3] * ms);
         if (u0 >= 0 && u0 + 4 <= (int32_t)nel) {
-            *reinterpret_cast<float4*>(yt + u0) = v;
+            __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4*>(yt + u0));
         } else {
             if (u0 >= 0 && u0 < (int32_t)nel) yt[u0] = v.x;
             if (u0 + 1 >= 0 && u0 + 1 < (int32_t)nel) yt[u0 + 1] = v.y;
