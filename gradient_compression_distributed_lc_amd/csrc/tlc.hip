@@ -1342,10 +1342,11 @@ constexpr uint64_t kNoStart = ~0ull;
 __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { return byte | skip << 32; }
 
 // Stream density (bytes per quartic byte) above which the dense decompress
-// path is faster: 81/1000, measured on MI355X over error-feedback runs of the
-// BERT-large set (the two paths cross at 0.081-0.082 with cycled and with
-// fresh inputs).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
-constexpr uint64_t kDenseNum = 81, kDenseDen = 1000;
+// path is faster: 104/1000, measured on MI355X over error-feedback runs of
+// the BERT-large set, as the time of whole compress+decompress steps with
+// each path forced (sparse ahead by 24 us at 0.094, dense ahead by 13 us at
+// 0.109).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
+constexpr uint64_t kDenseNum = 104, kDenseDen = 1000;
 
 // Decoder state reset and set-up.  Sparse decompress (n_fill > 0): zero fill
 // of y, one 16-byte store per lane (the fastest fill measured on MI355X; any

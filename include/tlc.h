@@ -246,7 +246,7 @@ int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stre
  *                      fastest while few encode tiles hold a nonzero code.
  *   TLC_DECODE_DENSE   every encode tile decoded in LDS and written once:
  *                      fastest once most tiles do (streams longer than about
- *                      0.081 bytes per quartic byte, where runs of zeros
+ *                      0.104 bytes per quartic byte, where runs of zeros
  *                      alone give 1/14 = 0.071; reached after some tens of
  *                      steps of error feedback).
  *   TLC_DECODE_AUTO    (default) the host cannot see the stream lengths

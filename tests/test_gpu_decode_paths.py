@@ -131,7 +131,7 @@ def test_auto_follows_density_on_one_workspace():
 
 @pytest.mark.timeout(600)
 def test_bert_large_steady_state_streams_both_paths():
-    # the full 335M-value set after 100 steps of error feedback on the GPU
+    # the full 335M-value set after 150 steps of error feedback on the GPU
     # (inputs cycled through 4 rolled copies): every encode tile holds nonzero
     # codes, so AUTO takes the dense path.  Both paths decode the final streams
     # to the oracle's decode of the same streams, tensor by tensor.
@@ -148,14 +148,14 @@ def test_bert_large_steady_state_streams_both_paths():
     lens = torch.empty(len(sizes), dtype=torch.int64, device="cuda:0")
     scales = torch.zeros(len(sizes), dtype=torch.float32, device="cuda:0")
     st = torch.empty(1, dtype=torch.int32, device="cuda:0")
-    for k in range(100):
+    for k in range(150):
         g.compress(xs[k % 4], err, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     got_out, got_lens, got_M = out.cpu().numpy(), lens.cpu().numpy(), scales.cpu().numpy()
     B = sum(-(-n // 5) for n in sizes)
     say(f"case decode path bert_large steady: density {got_lens.sum() / B:.4f}")
-    assert got_lens.sum() / B > 0.081  # the dense regime
+    assert got_lens.sum() / B > 0.104  # the dense regime
     want = np.empty(N, np.float32)
     off = 0
     for t, n in enumerate(sizes):
