@@ -1353,8 +1353,8 @@ constexpr uint64_t kDenseNum = 104, kDenseDen = 1000;
 // load before the store, or more stores per lane, slows it by 10-40%), with a
 // nontemporal hint: y is not read again here, and the kernels that follow
 // (the caller's next compress) run faster when the caches do not hold y's
-// dirty lines.  Dense
-// decompress (tstart set): the tile starts and literal flags are reset.
+// dirty lines.  Dense decompress (tstart set): the tile starts and literal
+// flags are reset.
 // Always: the look-back flags, and the list of stream chunks: tensor i has
 // max(1, ceil(min(L_i, B_i) / kChunk)) chunks, numbered dec_first[i] ...;
 // chunk r belongs to tensor dec_map[r]; ctrl[3] = number of chunks.  Block 0
@@ -1617,11 +1617,11 @@ uint32_t xcd_grid(uint64_t units) { return (uint32_t)((units + 7) / 8 * 8); }
 // y = q * (M*s), with nontemporal 16-byte stores (as the zero fill), so
 // decompress writes each line of y once (a zero fill with the nonzero values
 // scattered over it afterwards wrote every line that holds a nonzero code
-// twice).  A tile k_decode found no
-// nonzero code in is written without reading the stream.  Otherwise its
-// stream bytes, from the start k_decode recorded, are staged in LDS with
-// aligned 16-byte loads, re-read 16 per lane in stream order, and expanded
-// into the tile's codes (one int8 per element, same LDS slice).
+// twice).  A tile k_decode found no nonzero code in is written without
+// reading the stream.  Otherwise its stream bytes, from the start k_decode
+// recorded, are staged in LDS with aligned 16-byte loads, re-read 16 per lane
+// in stream order, and expanded into the tile's codes (one int8 per element,
+// same LDS slice).
 __global__ __launch_bounds__(kThreads) void k_expand(GroupView g, uint32_t etiles, const uint8_t* __restrict__ in,
                                                      const uint64_t* __restrict__ in_lens,
                                                      const float* __restrict__ scales, float s,
