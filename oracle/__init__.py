@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
             "tlco_unpack_fixed": (ctypes.c_int, [P, U64, ctypes.c_int, P]),
             "tlco_compress_fixed": (ctypes.c_int, [P, P, U64, F, ctypes.c_int, P, U64, P]),
             "tlco_decompress_fixed": (ctypes.c_int, [P, F, U64, F, ctypes.c_int, P]),
+            "tlco_quartic_pack_planes": (ctypes.c_int, [P, U64, P]),
+            "tlco_quartic_unpack_planes": (ctypes.c_int, [P, U64, P]),
+            "tlco_compress_planes": (ctypes.c_int, [P, P, U64, F, P, U64, P, P]),
+            "tlco_decompress_planes": (ctypes.c_int, [P, U64, F, U64, F, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -249,3 +253,42 @@ def decompress_fixed(stream, M, n: int, s: float, encoding: int) -> np.ndarray:
 def rc_of(fn_name: str, *args) -> int:
     """Raw return code of an oracle entry point (for error-path tests)."""
     return int(getattr(lib(), fn_name)(*args))
+
+
+# Five-plane layout (the other reading of which five values share a byte):
+# byte k holds elements k + j*B, j = 0..4, as digit j; B = ceil(n/5).
+
+def quartic_pack_planes(q) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    b = np.empty(quartic_len(q.size), dtype=np.uint8)
+    _check(lib().tlco_quartic_pack_planes(_ptr(q), q.size, _ptr(b)), "quartic_pack_planes")
+    return b
+
+
+def quartic_unpack_planes(b, n: int) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    if b.size < quartic_len(n):
+        raise ValueError("byte array shorter than ceil(n/5)")
+    q = np.empty(n, dtype=np.int8)
+    _check(lib().tlco_quartic_unpack_planes(_ptr(b), n, _ptr(q)), "quartic_unpack_planes")
+    return q
+
+
+def compress_planes(x, err, s: float):
+    """As compress, with the five-plane byte layout.  Returns (stream, M, err_new)."""
+    x = _f32(x)
+    e = _f32(err).copy()
+    cap = quartic_len(x.size)
+    out = np.empty(max(cap, 1), dtype=np.uint8)
+    L = ctypes.c_uint64()
+    M = ctypes.c_float()
+    _check(lib().tlco_compress_planes(_ptr(x), _ptr(e), x.size, s, _ptr(out), cap,
+                                      ctypes.byref(L), ctypes.byref(M)), "compress_planes")
+    return out[: L.value].copy(), np.float32(M.value), e
+
+
+def decompress_planes(stream, M, n: int, s: float) -> np.ndarray:
+    stream = np.ascontiguousarray(stream, dtype=np.uint8)
+    y = np.empty(n, dtype=np.float32)
+    _check(lib().tlco_decompress_planes(_ptr(stream), stream.size, float(M), n, s, _ptr(y)), "decompress_planes")
+    return y

@@ -290,3 +290,72 @@ int tlco_decompress_fixed(const uint8_t* in, float M, uint64_t n, float s, int e
     free(q);
     return rc;
 }
+
+/* Five-plane layout: byte k holds elements k + j*B, j = 0..4, as digit j. */
+int tlco_quartic_pack_planes(const int8_t* q, uint64_t n, uint8_t* b)
+{
+    if (!q || !b) return TLCO_ERR_INVALID_ARG;
+    uint64_t B = tlco_quartic_len(n);
+    for (uint64_t k = 0; k < B; ++k) {
+        unsigned byte = 0;
+        for (unsigned j = 0; j < 5; ++j) {
+            uint64_t i = k + (uint64_t)j * B;
+            int t = (i < n) ? q[i] : 0;
+            if (t < -1 || t > 1) return TLCO_ERR_RANGE;
+            byte += (unsigned)(t + 1) * POW3[j];
+        }
+        b[k] = (uint8_t)byte;
+    }
+    return TLCO_OK;
+}
+
+int tlco_quartic_unpack_planes(const uint8_t* b, uint64_t n, int8_t* q)
+{
+    if (!b || !q) return TLCO_ERR_INVALID_ARG;
+    uint64_t B = tlco_quartic_len(n);
+    for (uint64_t i = 0; i < n; ++i) {
+        unsigned byte = b[i % B];
+        if (byte > 242u) return TLCO_ERR_CORRUPT;
+        unsigned digit = (byte / POW3[i / B]) % 3u;
+        q[i] = (int8_t)((int)digit - 1);
+    }
+    return TLCO_OK;
+}
+
+int tlco_compress_planes(const float* x, float* err, uint64_t n, float s,
+                         uint8_t* out, uint64_t cap, uint64_t* L, float* M)
+{
+    if (!x || !err || !out || !L || !M || n == 0 || !valid_s(s)) return TLCO_ERR_INVALID_ARG;
+    uint64_t B = tlco_quartic_len(n);
+    int8_t* q = (int8_t*)malloc(n);
+    uint8_t* bytes = (uint8_t*)malloc(B);
+    int rc = TLCO_ERR_NOMEM;
+    if (q && bytes) {
+        rc = tlco_quantize(x, err, n, s, q, M);
+        if (rc == TLCO_OK) rc = tlco_quartic_pack_planes(q, n, bytes);
+        if (rc == TLCO_OK) rc = tlco_zre_encode(bytes, B, out, cap, L);
+    }
+    free(q);
+    free(bytes);
+    return rc;
+}
+
+int tlco_decompress_planes(const uint8_t* in, uint64_t L, float M, uint64_t n, float s, float* y)
+{
+    if (!y || n == 0 || !valid_s(s)) return TLCO_ERR_INVALID_ARG;
+    uint64_t B = tlco_quartic_len(n);
+    int8_t* q = (int8_t*)malloc(n);
+    uint8_t* bytes = (uint8_t*)malloc(B);
+    int rc = TLCO_ERR_NOMEM;
+    if (q && bytes) {
+        rc = tlco_zre_decode(in, L, bytes, B);
+        if (rc == TLCO_OK) rc = tlco_quartic_unpack_planes(bytes, n, q);
+        if (rc == TLCO_OK) {
+            float Ms = M * s;
+            for (uint64_t i = 0; i < n; ++i) y[i] = (float)q[i] * Ms;
+        }
+    }
+    free(q);
+    free(bytes);
+    return rc;
+}

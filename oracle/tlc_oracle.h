@@ -111,6 +111,19 @@ int tlco_decompress_fixed(const uint8_t* in, float M, uint64_t n, float s, int e
 int tlco_server_compress(const float* acc, uint32_t workers, float* err, uint64_t n, float s,
                          uint8_t* out, uint64_t cap, uint64_t* L, float* M);
 
+/* The other reading of which five values share a quartic byte (the 3LC page,
+ * "Proposed method", second item, does not say): five planes of B = ceil(n/5)
+ * consecutive elements, byte k holding elements k, k+B, k+2B, k+3B, k+4B,
+ * element k + j*B as digit j (weight 3^j); elements past n are zero codes.
+ * Quantization and zero-run encoding are those of tlco_compress.  Parity
+ * unpinned by the page (a convention); pinned by the worked example in
+ * tests/golden. */
+int tlco_quartic_pack_planes(const int8_t* q, uint64_t n, uint8_t* b);
+int tlco_quartic_unpack_planes(const uint8_t* b, uint64_t n, int8_t* q);
+int tlco_compress_planes(const float* x, float* err, uint64_t n, float s,
+                         uint8_t* out, uint64_t cap, uint64_t* L, float* M);
+int tlco_decompress_planes(const uint8_t* in, uint64_t L, float M, uint64_t n, float s, float* y);
+
 #ifdef __cplusplus
 }
 #endif
