@@ -1889,6 +1889,31 @@ __global__ __launch_bounds__(kThreads) void k_fixed_decode(GroupView g, uint32_t
 // bandwidth yardstick: one 16-byte load and store per lane, many small blocks,
 // both streamed past the caches like the codec's own streaming accesses
 
+// Five-plane layout helpers: tensor t (blockIdx.y) between its natural order
+// (n values) and the order p = 5k + j <- element k + jB (B = ceil(n/5), 5B
+// positions, zeros at the pads).  Gather walks the 5B positions and scatter
+// the n elements, each in its destination's order, so every store is
+// contiguous; a block strides over the tensor.
+template <bool kGather>
+__global__ __launch_bounds__(kThreads) void k_planes(const float* __restrict__ src, const uint64_t* __restrict__ src_off,
+                                                     float* __restrict__ dst, const uint64_t* __restrict__ dst_off,
+                                                     const uint64_t* __restrict__ nv) {
+    const uint32_t t = blockIdx.y;
+    const uint64_t n = nv[t], B = (n + 4) / 5;
+    const float* const s = src + src_off[t];
+    float* const d = dst + dst_off[t];
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    if (kGather) {
+        for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < 5 * B; p += stride) {
+            const uint64_t i = p / 5 + (p % 5) * B;
+            d[p] = i < n ? s[i] : 0.0f;
+        }
+    } else {
+        for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+            d[i] = s[5 * (i % B) + i / B];
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ src, float4* __restrict__ dst,
                                                    uint64_t n4) {
     const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -2236,6 +2261,19 @@ int run_decompress_fixed(const Plan& p, int enc, const uint8_t* in, const uint64
 
 bool valid_enc(int enc) { return enc == TLC_ENC_QUARTIC || enc == TLC_ENC_TWOBIT; }
 
+int run_planes(bool gather, const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
+               const uint64_t* n, uint32_t count, uint64_t max_n, hipStream_t st) {
+    if (!src || !src_off || !dst || !dst_off || !n || count == 0 || count > 65535 || max_n == 0 || max_n > kMaxN)
+        return TLC_ERR_INVALID_ARG;  // one grid row per tensor: at most 65535
+    const uint64_t span = gather ? 5 * ((max_n + 4) / 5) : max_n;
+    const dim3 grid((uint32_t)std::min<uint64_t>((span + kThreads - 1) / kThreads, 1024), count);
+    return launch(gather ? "tlc_planes_gather" : "tlc_planes_scatter", st, [&] {
+        if (gather)
+            k_planes<true><<<grid, kThreads, 0, st>>>(src, src_off, dst, dst_off, n);
+        else
+            k_planes<false><<<grid, kThreads, 0, st>>>(src, src_off, dst, dst_off, n);
+    });
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2461,6 +2499,16 @@ int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stre
         k_copy<<<(uint32_t)blocks, kThreads, 0, st>>>(static_cast<const float4*>(src), static_cast<float4*>(dst),
                                                        n4);
     });
+}
+
+int tlc_planes_gather(const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
+                      const uint64_t* n, uint32_t count, uint64_t max_n, tlc_stream_t stream) {
+    return run_planes(true, src, src_off, dst, dst_off, n, count, max_n, static_cast<hipStream_t>(stream));
+}
+
+int tlc_planes_scatter(const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
+                       const uint64_t* n, uint32_t count, uint64_t max_n, tlc_stream_t stream) {
+    return run_planes(false, src, src_off, dst, dst_off, n, count, max_n, static_cast<hipStream_t>(stream));
 }
 
 int tlc_profile_enable(int enable) {

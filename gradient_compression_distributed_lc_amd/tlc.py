@@ -72,6 +72,8 @@ _SIGS = {
     "tlc_decompress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ, _P, _P]),
     "tlc_decompress_accumulate_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ,
                                              _P, _P]),
+    "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
+    "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_copy_probe": (_I, [_P, _P, _U64, _P]),
     "tlc_profile_enable": (_I, [_I]),
     "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
@@ -421,6 +423,25 @@ class Group:
             _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_decompress_accumulate_group")
         return acc, status
+
+
+def planes_gather(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, dst_off: torch.Tensor,
+                  n: torch.Tensor, max_n: int, stream=None):
+    """tlc_planes_gather: each tensor's values into the five-plane order
+    (offsets and sizes are device int64 tensors, one entry per tensor)."""
+    _check(lib().tlc_planes_gather(_ptr(src, torch.float32, "src"), _ptr(src_off, torch.int64, "src_off"),
+                                   _ptr(dst, torch.float32, "dst"), _ptr(dst_off, torch.int64, "dst_off"),
+                                   _ptr(n, torch.int64, "n"), n.numel(), int(max_n), _stream(stream)),
+           "tlc_planes_gather")
+
+
+def planes_scatter(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, dst_off: torch.Tensor,
+                   n: torch.Tensor, max_n: int, stream=None):
+    """tlc_planes_scatter: each tensor's values back from the five-plane order."""
+    _check(lib().tlc_planes_scatter(_ptr(src, torch.float32, "src"), _ptr(src_off, torch.int64, "src_off"),
+                                    _ptr(dst, torch.float32, "dst"), _ptr(dst_off, torch.int64, "dst_off"),
+                                    _ptr(n, torch.int64, "n"), n.numel(), int(max_n), _stream(stream)),
+           "tlc_planes_scatter")
 
 
 def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):

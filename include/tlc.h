@@ -234,6 +234,34 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
                                     void* workspace, size_t workspace_bytes, int* status,
                                     tlc_stream_t stream);
 
+/* ---- five-plane byte layout (ablation) --------------------------------------
+ * The 3LC page ("Proposed method", second item) packs five ternary values per
+ * byte without saying which five.  The codec above takes five consecutive
+ * elements.  The other reading is five planes: byte k of a tensor of n values
+ * holds elements k, k+B, k+2B, k+3B, k+4B (B = ceil(n/5)) as digits 0..4.
+ * That is the codec's consecutive layout applied to the tensor's elements in
+ * the order p = 5k + j <- element k + jB, with zeros where k + jB >= n.  These
+ * two calls move fp32 data between the two orders, tensor by tensor, so that
+ * the five-plane codec is:
+ *   compress:   gather(x), gather(err), tlc_compress_group on the plan of
+ *               sizes 5*ceil(n_t/5), scatter(err);
+ *   decompress: tlc_decompress_group on that plan, scatter(y).
+ * (Zero pads change neither M nor the stream, and their error stays zero.)
+ * Arguments: count tensors; device arrays src_off, dst_off and n of count
+ * uint64 each: tensor t has n[t] >= 1 values; its data is read at
+ * src + src_off[t] and written at dst + dst_off[t], element offsets;
+ * max_n >= every n[t] (host, sizes the launch).
+ *   tlc_planes_gather:  reads n[t] values, writes 5*ceil(n[t]/5) (pads 0).
+ *   tlc_planes_scatter: reads 5*ceil(n[t]/5) values, writes n[t].
+ * src and dst must not overlap.  Asynchronous on `stream`; no allocation.
+ * Returns TLC_ERR_INVALID_ARG for a null pointer, count == 0 or above 65535,
+ * or max_n == 0 or above 2^32 - 1 (an n[t] above max_n is not checked on the
+ * device and is undefined), TLC_ERR_HIP for a failed launch. */
+int tlc_planes_gather(const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
+                      const uint64_t* n, uint32_t count, uint64_t max_n, tlc_stream_t stream);
+int tlc_planes_scatter(const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
+                       const uint64_t* n, uint32_t count, uint64_t max_n, tlc_stream_t stream);
+
 /* ---- measurement helpers (not part of the codec) -------------------------- */
 
 /* Streaming copy of `bytes` bytes (a multiple of 16, both pointers 16-byte

@@ -105,6 +105,19 @@ def test_group_plan_rejects_bad_sizes():
     assert tlc.lib().tlc_group_plan(arr, 1, ctypes.byref(info), small, 8, None) == tlc.ERR_CAPACITY
 
 
+def test_planes_argument_errors_return_before_any_launch():
+    L = tlc.lib()
+    V = ctypes.c_void_p
+    f = V(0x10000)  # never dereferenced: every case below fails validation first
+    for fn in (L.tlc_planes_gather, L.tlc_planes_scatter):
+        assert fn(None, f, f, f, f, 3, 100, None) == tlc.ERR_INVALID_ARG
+        assert fn(f, f, f, f, None, 3, 100, None) == tlc.ERR_INVALID_ARG
+        assert fn(f, f, f, f, f, 0, 100, None) == tlc.ERR_INVALID_ARG
+        assert fn(f, f, f, f, f, 65536, 100, None) == tlc.ERR_INVALID_ARG
+        assert fn(f, f, f, f, f, 3, 0, None) == tlc.ERR_INVALID_ARG
+        assert fn(f, f, f, f, f, 3, 1 << 32, None) == tlc.ERR_INVALID_ARG
+
+
 def test_argument_errors_return_before_any_launch():
     L = tlc.lib()
     V = ctypes.c_void_p
