@@ -449,6 +449,64 @@ def main():
     B_total = sum(-(-n // 5) for n in sizes)
     ablations["zero_run_gain_first_step"] = round(B_total / int(first["lens"].sum()), 2)
 
+    # the five-plane byte layout (the other reading of which five values share
+    # a quartic byte): each tensor gathered into the order p = 5k + j <- k + jB,
+    # the grouped codec on the plan of sizes 5*ceil(n/5), the error buffer and
+    # y scattered back; the first step from a zero error buffer on the same
+    # set as the main first step, then 5 timed compress and decompress calls
+    padded = [5 * (-(-n // 5)) for n in sizes]
+    gp = tlc.Group(padded, device=dev)
+    pl_src = torch.tensor(group.elem_offsets[:-1], dtype=torch.int64, device=dev)
+    pl_dst = torch.tensor(gp.elem_offsets[:-1], dtype=torch.int64, device=dev)
+    pl_n = torch.tensor(sizes, dtype=torch.int64, device=dev)
+    max_n = max(sizes)
+    xp = torch.empty(gp.total, dtype=torch.float32, device=dev)
+    ep = torch.empty(gp.total, dtype=torch.float32, device=dev)
+    err_pl = torch.zeros(N, dtype=torch.float32, device=dev)
+    out_pl = torch.empty(gp.stream_bytes, dtype=torch.uint8, device=dev)
+    lens_pl = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+    sc_pl = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+    ws_pl = gp.workspace()
+
+    def pl_compress(k):
+        pl_compress_x(xs[k % pool])
+
+    def pl_compress_x(xk):
+        tlc.planes_gather(xk, pl_src, xp, pl_dst, pl_n, max_n)
+        tlc.planes_gather(err_pl, pl_src, ep, pl_dst, pl_n, max_n)
+        gp.compress(xp, ep, s, out=out_pl, out_lens=lens_pl, scales=sc_pl, workspace=ws_pl, status=st_c)
+        tlc.planes_scatter(ep, pl_dst, err_pl, pl_src, pl_n, max_n)
+
+    def pl_decompress():
+        gp.decompress(out_pl, lens_pl, sc_pl, s, y=xp, workspace=ws_pl, status=st_d)
+        tlc.planes_scatter(xp, pl_dst, yd, pl_src, pl_n, max_n)
+
+    pl_compress(0)
+    torch.cuda.synchronize()
+    L_pl = int(lens_pl.sum().item())
+    for k in range(1, 3):
+        pl_compress(k)
+    pl_decompress()
+    torch.cuda.synchronize()
+    f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    f0.record()
+    for k in range(3, 8):
+        pl_compress(k)
+    f1.record()
+    for _ in range(5):
+        pl_decompress()
+    f2.record()
+    torch.cuda.synchronize()
+    if (int(st_c.item()), int(st_d.item())) != (0, 0):
+        raise SystemExit("device status not ok in the five-plane ablation")
+    ablations["five_plane"] = {
+        "bits_per_value_first_step": round(8.0 * L_pl / N, 4),
+        "consecutive_bits_per_value_first_step": round(8.0 * int(first["lens"].sum()) / N, 4),
+        "compress_ms": round(f0.elapsed_time(f1) / 5, 4),
+        "decompress_ms": round(f1.elapsed_time(f2) / 5, 4),
+        "how": "gather into the five-plane order, the grouped codec on the padded plan, scatter back "
+               "(times include the gather and scatter)"}
+
     # steady state of error feedback: the same step continued until the error
     # buffer has filled (every encode tile active, denser streams), then timed
     steady = None
@@ -479,7 +537,21 @@ def main():
         if (int(st_pc.item()), int(st_pd.item())) != (0, 0):
             raise SystemExit("device status not ok in the pipelined steady-state steps")
         steady["pipelined_ms_per_step"] = round(pa.elapsed_time(pb) / 10, 4)
-    del pay, ws_d
+        # the two byte layouts on the same codes: quantization does not depend
+        # on the layout, so one more step's input and this error state, taken
+        # by each layout on copies of the error buffer
+        xk = xs[counter[0] % pool]
+        e_a = ed.clone()
+        group.compress(xk, e_a, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st_c)
+        err_pl.copy_(ed)
+        pl_compress_x(xk)
+        torch.cuda.synchronize()
+        if int(st_c.item()) != 0:
+            raise SystemExit("device status not ok in the steady-state layout comparison")
+        ablations["five_plane"]["bits_per_value_steady"] = round(8.0 * int(lens_pl.sum().item()) / N, 4)
+        ablations["five_plane"]["consecutive_bits_per_value_steady"] = round(8.0 * int(lens.sum().item()) / N, 4)
+        del e_a
+    del pay, ws_d, gp, xp, ep, err_pl, out_pl, ws_pl
 
 
     # copy yardstick: what a plain streaming copy reaches on this GPU
