@@ -1890,27 +1890,50 @@ __global__ __launch_bounds__(kThreads) void k_fixed_decode(GroupView g, uint32_t
 // both streamed past the caches like the codec's own streaming accesses
 
 // Five-plane layout helpers: tensor t (blockIdx.y) between its natural order
-// (n values) and the order p = 5k + j <- element k + jB (B = ceil(n/5), 5B
-// positions, zeros at the pads).  Gather walks the 5B positions and scatter
-// the n elements, each in its destination's order, so every store is
-// contiguous; a block strides over the tensor.
+// (n values, plane j = elements jB .. jB + B - 1, B = ceil(n/5)) and the order
+// p = 5k + j <- element k + jB (5B positions, zeros at the pads).  A block
+// moves 256 byte positions k at a time through LDS: the five plane segments
+// k0 + jB .. k0 + jB + 255 on one side and the 1280 consecutive positions
+// 5k0 .. 5k0 + 1279 on the other, so every load and store is contiguous
+// (LDS index 5(k - k0) + j: a stride of 5 words, conflict free).
 template <bool kGather>
 __global__ __launch_bounds__(kThreads) void k_planes(const float* __restrict__ src, const uint64_t* __restrict__ src_off,
                                                      float* __restrict__ dst, const uint64_t* __restrict__ dst_off,
                                                      const uint64_t* __restrict__ nv) {
+    __shared__ float s_t[5 * kThreads];
     const uint32_t t = blockIdx.y;
     const uint64_t n = nv[t], B = (n + 4) / 5;
     const float* const s = src + src_off[t];
     float* const d = dst + dst_off[t];
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    if (kGather) {
-        for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < 5 * B; p += stride) {
-            const uint64_t i = p / 5 + (p % 5) * B;
-            d[p] = i < n ? s[i] : 0.0f;
+    const uint32_t tid = threadIdx.x;
+    for (uint64_t k0 = (uint64_t)blockIdx.x * kThreads; k0 < B; k0 += (uint64_t)gridDim.x * kThreads) {
+        const uint32_t kn = (uint32_t)min<uint64_t>(kThreads, B - k0);
+        if (kGather) {
+#pragma unroll
+            for (uint32_t j = 0; j < 5; ++j) {
+                const uint64_t i = k0 + tid + j * B;
+                s_t[5 * tid + j] = (tid < kn && i < n) ? s[i] : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (uint32_t r = 0; r < 5; ++r) {
+                const uint32_t q = tid + kThreads * r;
+                if (q < 5 * kn) d[5 * k0 + q] = s_t[q];
+            }
+        } else {
+#pragma unroll
+            for (uint32_t r = 0; r < 5; ++r) {
+                const uint32_t q = tid + kThreads * r;
+                if (q < 5 * kn) s_t[q] = s[5 * k0 + q];
+            }
+            __syncthreads();
+#pragma unroll
+            for (uint32_t j = 0; j < 5; ++j) {
+                const uint64_t i = k0 + tid + j * B;
+                if (tid < kn && i < n) d[i] = s_t[5 * tid + j];
+            }
         }
-    } else {
-        for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
-            d[i] = s[5 * (i % B) + i / B];
+        __syncthreads();  // s_t is rewritten by the next chunk
     }
 }
 
@@ -2265,8 +2288,8 @@ int run_planes(bool gather, const float* src, const uint64_t* src_off, float* ds
                const uint64_t* n, uint32_t count, uint64_t max_n, hipStream_t st) {
     if (!src || !src_off || !dst || !dst_off || !n || count == 0 || count > 65535 || max_n == 0 || max_n > kMaxN)
         return TLC_ERR_INVALID_ARG;  // one grid row per tensor: at most 65535
-    const uint64_t span = gather ? 5 * ((max_n + 4) / 5) : max_n;
-    const dim3 grid((uint32_t)std::min<uint64_t>((span + kThreads - 1) / kThreads, 1024), count);
+    const uint64_t bmax = (max_n + 4) / 5;  // byte positions of the largest tensor
+    const dim3 grid((uint32_t)std::min<uint64_t>((bmax + kThreads - 1) / kThreads, 256), count);
     return launch(gather ? "tlc_planes_gather" : "tlc_planes_scatter", st, [&] {
         if (gather)
             k_planes<true><<<grid, kThreads, 0, st>>>(src, src_off, dst, dst_off, n);
