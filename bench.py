@@ -534,9 +534,20 @@ def main():
         pipeline(10, counter[0])
         pb.record(sB)
         torch.cuda.synchronize()
+        out_pl_last = pay[(10 - 1) % 2]
         if (int(st_pc.item()), int(st_pd.item())) != (0, 0):
             raise SystemExit("device status not ok in the pipelined steady-state steps")
         steady["pipelined_ms_per_step"] = round(pa.elapsed_time(pb) / 10, 4)
+        # the receive side at this density: the last payload accumulated 8 times
+        a0.record()
+        for _ in range(8):
+            group.decompress_accumulate(out_pl_last[0], out_pl_last[1], out_pl_last[2], s, acc, workspace=ws,
+                                        status=st_a)
+        a1.record()
+        torch.cuda.synchronize()
+        if int(st_a.item()) != 0:
+            raise SystemExit("device status not ok in the steady-state accumulate")
+        steady["accumulate_ms_per_payload"] = round(a0.elapsed_time(a1) / 8, 4)
         # the two byte layouts on the same codes: quantization does not depend
         # on the layout, so one more step's input and this error state, taken
         # by each layout on copies of the error buffer
