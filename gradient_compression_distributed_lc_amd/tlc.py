@@ -126,6 +126,14 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: torch.Tensor | None, count: int, name: str):
+    """Raise unless t holds at least `count` elements (checked before any
+    pointer is handed to the library, so an undersized buffer never reaches a
+    kernel)."""
+    if t is not None and t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {count}")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -173,8 +181,11 @@ def compress(x: torch.Tensor, err: torch.Tensor, s: float, *, out=None, out_len=
         raise ValueError("err must have as many elements as x")
     out = out if out is not None else torch.empty(max(compress_bound(n), 1), dtype=torch.uint8, device=dev)
     out_len = out_len if out_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
-    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    scale = scale if scale is not None else torch.zeros(1, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(out_len, 1, "out_len")
+    _need(scale, 1, "scale")
+    _need(status, 1, "status")
     workspace = _workspace(workspace_size(n), dev, workspace)
     rc = lib().tlc_compress(_ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), n, s,
                             _ptr(out, torch.uint8, "out"), out.numel(), _ptr(out_len, torch.int64, "out_len"),
@@ -194,8 +205,11 @@ def server_compress(acc: torch.Tensor, workers: int, err: torch.Tensor, s: float
         raise ValueError("err must have as many elements as acc")
     out = out if out is not None else torch.empty(max(compress_bound(n), 1), dtype=torch.uint8, device=dev)
     out_len = out_len if out_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
-    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    scale = scale if scale is not None else torch.zeros(1, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(out_len, 1, "out_len")
+    _need(scale, 1, "scale")
+    _need(status, 1, "status")
     workspace = _workspace(workspace_size(n), dev, workspace)
     rc = lib().tlc_server_compress(_ptr(acc, torch.float32, "acc"), workers, _ptr(err, torch.float32, "err"), n,
                                    s, _ptr(out, torch.uint8, "out"), out.numel(),
@@ -225,8 +239,10 @@ def compress_fixed(x: torch.Tensor, err: torch.Tensor, s: float, encoding: int, 
     if nb == 0:
         raise ValueError("bad size or encoding")
     out = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
-    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    scale = scale if scale is not None else torch.zeros(1, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(scale, 1, "scale")
+    _need(status, 1, "status")
     workspace = _workspace(workspace_size(n), dev, workspace)
     rc = lib().tlc_compress_fixed(_ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), n, s, encoding,
                                   _ptr(out, torch.uint8, "out"), out.numel(), _ptr(scale, torch.float32, "scale"),
@@ -242,6 +258,13 @@ def decompress_fixed(inp: torch.Tensor, scale: torch.Tensor, n: int, s: float, e
     dev = inp.device
     y = y if y is not None else torch.empty(n, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    nb = fixed_len(n, encoding)
+    if nb == 0:
+        raise ValueError("bad size or encoding")
+    _need(inp, nb, "in")
+    _need(scale, 1, "scale")
+    _need(y, n, "y")
+    _need(status, 1, "status")
     rc = lib().tlc_decompress_fixed(_ptr(inp, torch.uint8, "in"), _ptr(scale, torch.float32, "scale"), n, s,
                                     encoding, _ptr(y, torch.float32, "y"), _ptr(status, torch.int32, "status"),
                                     _stream(stream))
@@ -251,10 +274,17 @@ def decompress_fixed(inp: torch.Tensor, scale: torch.Tensor, n: int, s: float, e
 
 def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float, *, y=None,
                workspace=None, status=None, stream=None):
-    """Returns (y, status)."""
+    """Returns (y, status).  inp holds at least ceil(n/5) bytes (the capacity
+    tlc_compress writes into), so that no device length can send a read past
+    its end."""
     dev = inp.device
     y = y if y is not None else torch.empty(n, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(inp, compress_bound(n), "in")
+    _need(in_len, 1, "in_len")
+    _need(scale, 1, "scale")
+    _need(y, n, "y")
+    _need(status, 1, "status")
     workspace = _workspace(workspace_size(n), dev, workspace)
     rc = lib().tlc_decompress(_ptr(inp, torch.uint8, "in"), _ptr(in_len, torch.int64, "in_len"),
                               _ptr(scale, torch.float32, "scale"), n, s, _ptr(y, torch.float32, "y"),
@@ -266,9 +296,15 @@ def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: 
 
 def decompress_accumulate(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float,
                           acc: torch.Tensor, *, workspace=None, status=None, stream=None):
-    """acc is updated in place.  Returns (acc, status)."""
+    """acc is updated in place.  Returns (acc, status).  inp holds at least
+    ceil(n/5) bytes, as for decompress."""
     dev = inp.device
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(inp, compress_bound(n), "in")
+    _need(in_len, 1, "in_len")
+    _need(scale, 1, "scale")
+    _need(acc, n, "acc")
+    _need(status, 1, "status")
     workspace = _workspace(workspace_size(n), dev, workspace)
     rc = lib().tlc_decompress_accumulate(_ptr(inp, torch.uint8, "in"), _ptr(in_len, torch.int64, "in_len"),
                                          _ptr(scale, torch.float32, "scale"), n, s,
@@ -322,8 +358,9 @@ class Group:
         dev = self.device
         out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
         out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
-        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        scales = scales if scales is not None else torch.zeros(self.count, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        self._need_out(out, out_lens, scales, status)
         workspace = workspace if workspace is not None else self.workspace()
         rc = lib().tlc_compress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                       _ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), s,
@@ -343,8 +380,9 @@ class Group:
         dev = self.device
         out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
         out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
-        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        scales = scales if scales is not None else torch.zeros(self.count, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        self._need_out(out, out_lens, scales, status)
         workspace = workspace if workspace is not None else self.workspace()
         rc = lib().tlc_server_compress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                              _ptr(acc, torch.float32, "acc"), workers,
@@ -356,24 +394,49 @@ class Group:
         _check(rc, "tlc_server_compress_group")
         return out, out_lens, scales, status
 
-    def fixed_offsets(self, encoding: int):
-        """(host offsets, device uint64 offsets, total bytes) of a fixed-length
-        encoding: tensors back to back, 16-byte aligned."""
+    def _fixed_layout(self, encoding: int):
         offs, at = [], 0
         for n in self.sizes:
             offs.append(at)
-            at += -(-fixed_len(n, encoding) // 16) * 16
+            nb = fixed_len(n, encoding)
+            if nb == 0:
+                raise ValueError("bad size or encoding")
+            at += -(-nb // 16) * 16
+        return offs, at
+
+    def fixed_offsets(self, encoding: int):
+        """(host offsets, device uint64 offsets, total bytes) of a fixed-length
+        encoding: tensors back to back, 16-byte aligned."""
+        offs, at = self._fixed_layout(encoding)
         d = torch.tensor(offs, dtype=torch.int64, device=self.device)
         return offs, d, at
 
+    def _need_out(self, out, out_lens, scales, status):
+        _need(out, self.stream_bytes, "out")
+        _need(out_lens, self.count, "out_lens")
+        _need(scales, self.count, "scales")
+        _need(status, 1, "status")
+
+    def _need_in(self, inp, in_lens, scales, dst, name, status):
+        _need(inp, self.stream_bytes, "in")
+        _need(in_lens, self.count, "in_lens")
+        _need(scales, self.count, "scales")
+        _need(dst, self.total, name)
+        _need(status, 1, "status")
+
     def compress_fixed(self, x, err, s, encoding, out, d_offsets, *, scales=None, workspace=None, status=None,
                        stream=None):
-        """Codes of every tensor in a fixed-length encoding at out[d_offsets[t]].  Returns (scales, status)."""
+        """Codes of every tensor in a fixed-length encoding at out[d_offsets[t]]
+        (d_offsets as fixed_offsets returns them).  Returns (scales, status)."""
         if x.numel() != self.total or err.numel() != self.total:
             raise ValueError("x and err must hold the whole group")
         dev = self.device
-        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        scales = scales if scales is not None else torch.zeros(self.count, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        _need(out, self._fixed_layout(encoding)[1], "out")
+        _need(d_offsets, self.count, "offsets")
+        _need(scales, self.count, "scales")
+        _need(status, 1, "status")
         workspace = workspace if workspace is not None else self.workspace()
         rc = lib().tlc_compress_fixed_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                             encoding, _ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"),
@@ -389,6 +452,11 @@ class Group:
         dev = self.device
         y = y if y is not None else torch.empty(self.total, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        _need(inp, self._fixed_layout(encoding)[1], "in")
+        _need(d_offsets, self.count, "offsets")
+        _need(scales, self.count, "scales")
+        _need(y, self.total, "y")
+        _need(status, 1, "status")
         rc = lib().tlc_decompress_fixed_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                               encoding, _ptr(inp, torch.uint8, "in"),
                                               _ptr(d_offsets, torch.int64, "offsets"),
@@ -402,6 +470,7 @@ class Group:
         dev = self.device
         y = y if y is not None else torch.empty(self.total, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        self._need_in(inp, in_lens, scales, y, "y", status)
         workspace = workspace if workspace is not None else self.workspace()
         rc = lib().tlc_decompress_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                         _ptr(inp, torch.uint8, "in"), _ptr(in_lens, torch.int64, "in_lens"),
@@ -415,6 +484,7 @@ class Group:
         """acc is updated in place.  Returns (acc, status)."""
         dev = self.device
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        self._need_in(inp, in_lens, scales, acc, "acc", status)
         workspace = workspace if workspace is not None else self.workspace()
         rc = lib().tlc_decompress_accumulate_group(
             ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"), _ptr(inp, torch.uint8, "in"),
@@ -429,6 +499,8 @@ def planes_gather(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, d
                   n: torch.Tensor, max_n: int, stream=None):
     """tlc_planes_gather: each tensor's values into the five-plane order
     (offsets and sizes are device int64 tensors, one entry per tensor)."""
+    _need(src_off, n.numel(), "src_off")
+    _need(dst_off, n.numel(), "dst_off")
     _check(lib().tlc_planes_gather(_ptr(src, torch.float32, "src"), _ptr(src_off, torch.int64, "src_off"),
                                    _ptr(dst, torch.float32, "dst"), _ptr(dst_off, torch.int64, "dst_off"),
                                    _ptr(n, torch.int64, "n"), n.numel(), int(max_n), _stream(stream)),
@@ -438,6 +510,8 @@ def planes_gather(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, d
 def planes_scatter(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, dst_off: torch.Tensor,
                    n: torch.Tensor, max_n: int, stream=None):
     """tlc_planes_scatter: each tensor's values back from the five-plane order."""
+    _need(src_off, n.numel(), "src_off")
+    _need(dst_off, n.numel(), "dst_off")
     _check(lib().tlc_planes_scatter(_ptr(src, torch.float32, "src"), _ptr(src_off, torch.int64, "src_off"),
                                     _ptr(dst, torch.float32, "dst"), _ptr(dst_off, torch.int64, "dst_off"),
                                     _ptr(n, torch.int64, "n"), n.numel(), int(max_n), _stream(stream)),
@@ -445,6 +519,9 @@ def planes_scatter(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, 
 
 
 def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
+    for t, name in ((src, "src"), (dst, "dst")):
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, fewer than {nbytes}")
     _check(lib().tlc_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "tlc_copy_probe")
 
 

@@ -28,13 +28,16 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
-def gpu_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None):
-    """Compress, decompress (and accumulate into acc) one tensor on the GPU."""
+def gpu_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None, hint: float = 0.0):
+    """Compress, decompress (and accumulate into acc) one tensor on the GPU.
+    `hint` is what the scale buffer holds on entry: 0 sends the second pass
+    through the full re-read, a value near M through the candidate lists."""
     import torch
     from gradient_compression_distributed_lc_amd import tlc
     n = x.size
     xd, ed = to_dev(x), to_dev(err)
-    c = tlc.compress(xd, ed, s)
+    sc = torch.full((1,), float(hint), dtype=torch.float32, device=dev())
+    c = tlc.compress(xd, ed, s, scale=sc)
     y, st_d = tlc.decompress(c.out, c.out_len, c.scale, n, s)
     res = {}
     if acc is not None:
@@ -55,11 +58,12 @@ def gpu_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None 
     return res
 
 
-def check_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None, label=""):
+def check_single(x: np.ndarray, err: np.ndarray, s: float, acc: np.ndarray | None = None, label="",
+                 hint: float = 0.0):
     n = x.size
     want_stream, want_M, want_err = oracle.compress(x, err, s)
     want_y = oracle.decompress(want_stream, want_M, n, s)
-    got = gpu_single(x, err, s, acc)
+    got = gpu_single(x, err, s, acc, hint=hint)
     assert got["status"] == 0 and got["status_d"] == 0, (label, got["status"], got["status_d"])
     assert got["M"] == want_M, (label, got["M"], want_M)
     assert got["L"] == want_stream.size, (label, got["L"], want_stream.size)
@@ -92,13 +96,17 @@ def oracle_group_compress(x: np.ndarray, err: np.ndarray, sizes, s: float):
     return streams, np.array(Ms, dtype=np.float32), e_new
 
 
-def check_group(group, x: np.ndarray, err: np.ndarray, s: float, label="", want=None):
+def check_group(group, x: np.ndarray, err: np.ndarray, s: float, label="", want=None, hint=None):
     """Grouped compress + decompress on the GPU against the per-tensor oracle.
+    `hint` (per-tensor array, or None for zeros) is what the scale buffer holds
+    on entry, so the caller chooses which second-pass path the test takes.
     Returns the device payload (out, out_lens, scales) for further use."""
     import torch
     sizes = group.sizes
     xd, ed = to_dev(x), to_dev(err)
-    out, lens, scales, st = group.compress(xd, ed, s)
+    h = np.zeros(len(sizes), np.float32) if hint is None else np.asarray(hint, np.float32)
+    assert h.size == len(sizes)
+    out, lens, scales, st = group.compress(xd, ed, s, scales=to_dev(h))
     y, st_d = group.decompress(out, lens, scales, s)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and int(st_d.item()) == 0, (label, int(st.item()), int(st_d.item()))

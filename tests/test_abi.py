@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert tlc.status_string(code)
     assert tlc.status_string(99) == "unknown status"
 
@@ -192,3 +192,78 @@ def test_decode_policy_argument_check():
     for bad in (-1, 3, 99):
         assert tlc.lib().tlc_set_decode_policy(bad) == tlc.ERR_INVALID_ARG
     tlc.set_decode_policy(tlc.DECODE_AUTO)
+
+
+# The binding checks every buffer it is given against the sizes the call
+# needs before any pointer reaches the library: an undersized tensor raises
+# ValueError and nothing is launched.  CPU tensors stand in for device ones
+# (the size checks run before the device check).
+
+def _t(n, dtype):
+    import torch
+    return torch.zeros(max(n, 0), dtype=dtype)
+
+
+def test_binding_rejects_undersized_single_tensor_buffers():
+    import torch
+    n, s = 1000, 1.5
+    B = tlc.compress_bound(n)
+    u8, i64, f32, i32 = torch.uint8, torch.int64, torch.float32, torch.int32
+    ok = dict(inp=_t(B, u8), in_len=_t(1, i64), scale=_t(1, f32))
+    with pytest.raises(ValueError, match="y holds"):
+        tlc.decompress(ok["inp"], ok["in_len"], ok["scale"], n, s, y=_t(n - 1, f32))
+    with pytest.raises(ValueError, match="in holds"):
+        tlc.decompress(_t(B - 1, u8), ok["in_len"], ok["scale"], n, s, y=_t(n, f32))
+    with pytest.raises(ValueError, match="in_len holds"):
+        tlc.decompress(ok["inp"], _t(0, i64), ok["scale"], n, s, y=_t(n, f32))
+    with pytest.raises(ValueError, match="scale holds"):
+        tlc.decompress(ok["inp"], ok["in_len"], _t(0, f32), n, s, y=_t(n, f32))
+    with pytest.raises(ValueError, match="acc holds"):
+        tlc.decompress_accumulate(ok["inp"], ok["in_len"], ok["scale"], n, s, _t(n - 4, f32))
+    with pytest.raises(ValueError, match="status holds"):
+        tlc.decompress_accumulate(ok["inp"], ok["in_len"], ok["scale"], n, s, _t(n, f32), status=_t(0, i32))
+    with pytest.raises(ValueError, match="scale holds"):
+        tlc.compress(_t(n, f32), _t(n, f32), s, scale=_t(0, f32))
+    with pytest.raises(ValueError, match="y holds"):
+        tlc.decompress_fixed(_t(tlc.fixed_len(n, tlc.ENC_QUARTIC), u8), ok["scale"], n, s, tlc.ENC_QUARTIC,
+                             y=_t(n - 1, f32))
+    with pytest.raises(ValueError, match="in holds"):
+        tlc.decompress_fixed(_t(tlc.fixed_len(n, tlc.ENC_TWOBIT) - 1, u8), ok["scale"], n, s, tlc.ENC_TWOBIT,
+                             y=_t(n, f32))
+    with pytest.raises(ValueError, match="dst holds"):
+        tlc.copy_probe(_t(64, u8), _t(32, u8), 64)
+
+
+def test_binding_rejects_undersized_group_buffers():
+    import torch
+    sizes = [10, 5121, 3, 40_000]
+    g = tlc.Group(sizes, device="cpu")
+    N, C, SB = g.total, g.count, g.stream_bytes
+    u8, i64, f32 = torch.uint8, torch.int64, torch.float32
+    x, e = _t(N, f32), _t(N, f32)
+    with pytest.raises(ValueError, match="out holds"):
+        g.compress(x, e, 1.5, out=_t(SB - 1, u8))
+    with pytest.raises(ValueError, match="out_lens holds"):
+        g.compress(x, e, 1.5, out_lens=_t(C - 1, i64))
+    with pytest.raises(ValueError, match="scales holds"):
+        g.compress(x, e, 1.5, scales=_t(C - 1, f32))
+    with pytest.raises(ValueError, match="out holds"):
+        g.server_compress(x, 8, e, 1.5, out=_t(SB - 16, u8))
+    args = (_t(SB, u8), _t(C, i64), _t(C, f32), 1.5)
+    with pytest.raises(ValueError, match="y holds"):
+        g.decompress(*args, y=_t(N - 1, f32))
+    with pytest.raises(ValueError, match="in holds"):
+        g.decompress(_t(SB - 1, u8), *args[1:], y=_t(N, f32))
+    with pytest.raises(ValueError, match="in_lens holds"):
+        g.decompress(args[0], _t(C - 1, i64), *args[2:], y=_t(N, f32))
+    with pytest.raises(ValueError, match="scales holds"):
+        g.decompress(args[0], args[1], _t(C - 1, f32), 1.5, y=_t(N, f32))
+    with pytest.raises(ValueError, match="acc holds"):
+        g.decompress_accumulate(*args, _t(N - 1, f32))
+    total_q = g._fixed_layout(tlc.ENC_QUARTIC)[1]
+    with pytest.raises(ValueError, match="out holds"):
+        g.compress_fixed(x, e, 1.5, tlc.ENC_QUARTIC, _t(total_q - 1, u8), _t(C, i64))
+    with pytest.raises(ValueError, match="offsets holds"):
+        g.decompress_fixed(_t(total_q, u8), _t(C - 1, i64), _t(C, f32), 1.5, tlc.ENC_QUARTIC, y=_t(N, f32))
+    with pytest.raises(ValueError, match="y holds"):
+        g.decompress_fixed(_t(total_q, u8), _t(C, i64), _t(C, f32), 1.5, tlc.ENC_QUARTIC, y=_t(N - 1, f32))

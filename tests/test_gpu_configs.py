@@ -10,7 +10,10 @@ benchmark uses (grouped calls over the whole gradient set):
                order into one fp32 sum, and the server's compress of their mean
 
 Everything is compared bit for bit with the CPU oracle: every tensor's stream
-and length, M, the error buffer, the decompressed values and the sum."""
+and length, M, the error buffer, the decompressed values and the sum.  The
+scale buffer each compress reads as its hint is set on purpose: zeros (the
+second pass reads the error buffer again) or the previous M (the second pass
+reads the first pass's candidate lists), so both paths run at full size."""
 import numpy as np
 import pytest
 
@@ -27,6 +30,8 @@ def test_single_1m():
     say("case single_1m")
     got = check_single(x, np.zeros_like(x), 1.0, acc=np.zeros_like(x), label="single_1m")
     say(f"single_1m bits/value {8 * got['L'] / x.size:.4f}")
+    say("case single_1m, previous-M hint")
+    check_single(x, np.zeros_like(x), 1.0, acc=np.zeros_like(x), label="single_1m hint", hint=float(got["M"]))
 
 
 @pytest.mark.timeout(600)
@@ -37,11 +42,12 @@ def test_single_16m_ten_steps_with_error_feedback():
     n, s = w.total, w.s_values[0]
     e_cpu = np.zeros(n, np.float32)
     ed = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    sc = torch.zeros(1, dtype=torch.float32, device="cuda:0")  # carried: step t reads step t-1's M
     for t in range(10):
         x = workloads.generate("single_16m", step=t)
         say(f"case single_16m step {t}")
         st, M, e_cpu = oracle.compress(x, e_cpu, s)
-        c = tlc.compress(to_dev(x), ed, s)
+        c = tlc.compress(to_dev(x), ed, s, scale=sc)
         y, st_d = tlc.decompress(c.out, c.out_len, c.scale, n, s)
         torch.cuda.synchronize()
         assert int(c.status.item()) == 0 and int(st_d.item()) == 0
@@ -58,7 +64,9 @@ def test_resnet110_group():
     g = tlc.Group(w.sizes)
     x = workloads.generate("resnet110")
     say("case resnet110")
-    check_group(g, x, np.zeros_like(x), w.s_values[0], label="resnet110")
+    _, _, scales, _ = check_group(g, x, np.zeros_like(x), w.s_values[0], label="resnet110")
+    say("case resnet110, previous-M hint")
+    check_group(g, x, np.zeros_like(x), w.s_values[0], label="resnet110 hint", hint=scales.cpu().numpy())
 
 
 @pytest.mark.timeout(600)
@@ -67,9 +75,11 @@ def test_resnet50_group_s_sweep():
     w = workloads.get("resnet50")
     g = tlc.Group(w.sizes)
     x = workloads.generate("resnet50")
+    hint = None  # zeros for the first s, then the M the previous s found (the same x)
     for s in w.s_values:
         say(f"case resnet50 s={s}")
-        check_group(g, x, np.zeros_like(x), s, label=f"resnet50 s={s}")
+        _, _, scales, _ = check_group(g, x, np.zeros_like(x), s, label=f"resnet50 s={s}", hint=hint)
+        hint = scales.cpu().numpy()
 
 
 @pytest.mark.timeout(1200)
@@ -83,13 +93,16 @@ def test_bert_large_eight_workers_accumulate():
     acc_h = np.zeros(N, np.float32)
     x = np.empty(N, np.float32)
     ws = g.workspace()
+    hint = None  # worker 0: zeros; worker w > 0: worker w-1's M
     for wk in range(8):
         say(f"case bert_large worker {wk}: generate")
         workloads.generate("bert_large", worker=wk, out=x)
         zero = np.zeros(N, np.float32)
         want = oracle_group_compress(x, zero, sizes, s)
         say(f"case bert_large worker {wk}: compress/decompress parity")
-        out, lens, scales, (streams, Ms) = check_group(g, x, zero, s, label=f"bert_large worker {wk}", want=want)
+        out, lens, scales, (streams, Ms) = check_group(g, x, zero, s, label=f"bert_large worker {wk}", want=want,
+                                                       hint=hint)
+        hint = Ms
         _, st = g.decompress_accumulate(out, lens, scales, s, acc_d, workspace=ws)
         off = 0
         for t, n in enumerate(sizes):
@@ -104,7 +117,8 @@ def test_bert_large_eight_workers_accumulate():
     # own (zero) error buffer; every tensor's stream, M and error bit for bit
     say("case bert_large: server compress of the 8-worker mean")
     err_d = torch.zeros(N, dtype=torch.float32, device="cuda:0")
-    out, lens, scales, st = g.server_compress(acc_d, 8, err_d, s, workspace=ws)
+    out, lens, scales, st = g.server_compress(acc_d, 8, err_d, s, workspace=ws,
+                                              scales=torch.zeros(len(sizes), dtype=torch.float32, device="cuda:0"))
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     got_out, got_lens, got_M = out.cpu().numpy(), lens.cpu().numpy(), scales.cpu().numpy()

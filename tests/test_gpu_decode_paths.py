@@ -43,9 +43,14 @@ def payload(n, seed, dense, s):
 
 
 def gpu_decompress(st, M, n, s, ws=None):
+    # the stream sits at the start of a buffer of the compress capacity
+    # ceil(n/5) (the binding requires it); the device length says how much of
+    # it is the stream
     import torch
     from gradient_compression_distributed_lc_amd import tlc
-    ind = to_dev(st if st.size else np.zeros(1, np.uint8))
+    buf = np.zeros(max(-(-n // 5), st.size), np.uint8)
+    buf[:st.size] = st
+    ind = to_dev(buf)
     lend = torch.tensor([st.size], dtype=torch.int64, device=ind.device)
     y, status = tlc.decompress(ind, lend, to_dev(np.array([M], np.float32)), n, s, workspace=ws)
     torch.cuda.synchronize()

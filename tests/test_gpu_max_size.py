@@ -59,19 +59,26 @@ def test_max_size_tensor():
     ti = torch.from_numpy(idx).to(dev)
     x[ti] = torch.from_numpy(val).to(dev)
     err = torch.zeros(n, dtype=torch.float32, device=dev)
-    c = tlc.compress(x, err, s)
-    torch.cuda.synchronize()
-    assert int(c.status.item()) == 0
-    assert np.float32(c.scale.item()) == M
-    got = c.stream().cpu().numpy()
-    assert got.size == want_stream.size and np.array_equal(got, want_stream)
+    ws = torch.empty(tlc.workspace_size(n), dtype=torch.uint8, device=dev)
+    # twice from err = 0: a zero hint (the second pass reads err again), then
+    # the exact M as the hint (the second pass reads the candidate lists)
+    for hint in (0.0, float(M)):
+        say(f"case max size: compress, hint {hint}")
+        err.zero_()
+        sc = torch.full((1,), hint, dtype=torch.float32, device=dev)
+        c = tlc.compress(x, err, s, scale=sc, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(c.status.item()) == 0
+        assert np.float32(c.scale.item()) == M
+        got = c.stream().cpu().numpy()
+        assert got.size == want_stream.size and np.array_equal(got, want_stream)
+        assert np.array_equal(bits(err[ti].cpu().numpy()), bits(e_sp))
+        assert int(torch.count_nonzero(err).item()) == int(np.count_nonzero(e_sp))
     nz = q_sp != 0
-    assert np.array_equal(bits(err[ti].cpu().numpy()), bits(e_sp))
-    assert int(torch.count_nonzero(err).item()) == int(np.count_nonzero(e_sp))
     del x
     say("case max size: compress ok, decompress")
 
-    y, st = tlc.decompress(c.out, c.out_len, c.scale, n, s)
+    y, st = tlc.decompress(c.out, c.out_len, c.scale, n, s, workspace=ws)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     # the oracle's decode of the spikes alone (their codes re-encoded as a small
