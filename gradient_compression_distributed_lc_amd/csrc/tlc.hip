@@ -2007,10 +2007,12 @@ uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap) {
 
 constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-uint64_t ftiles_of(uint64_t total) { return (total + kFTile - 1) / kFTile; }
-uint64_t etiles_host(uint64_t n) { return (n + kETile - 1) / kETile; }
-uint64_t spans_host(uint64_t n) { return (etiles_host(n) + kSpan - 1) / kSpan; }
-uint64_t chunks_host(uint64_t n) { return std::max<uint64_t>(1, ((n + 4) / 5 + kChunk - 1) / kChunk); }
+constexpr uint64_t ftiles_of(uint64_t total) { return (total + kFTile - 1) / kFTile; }
+constexpr uint64_t etiles_host(uint64_t n) { return (n + kETile - 1) / kETile; }
+constexpr uint64_t spans_host(uint64_t n) { return (etiles_host(n) + kSpan - 1) / kSpan; }
+constexpr uint64_t chunks_host(uint64_t n) {
+    return ((n + 4) / 5 + kChunk - 1) / kChunk > 1 ? ((n + 4) / 5 + kChunk - 1) / kChunk : 1;
+}
 
 // Sizes of everything a call needs, for one tensor or a group.
 struct Dims {
@@ -2018,11 +2020,12 @@ struct Dims {
 };
 
 struct Layout {
-    size_t ctrl, pmax, etile_agg, etmax, active, mbits, seg_cb, cand_cnt, cand, span_flags, span_tickets, chunk_tickets, staging, dec_flags, dec_map, dec_first,
-        total;
+    size_t ctrl = 0, pmax = 0, etile_agg = 0, etmax = 0, active = 0, mbits = 0, seg_cb = 0, cand_cnt = 0, cand = 0,
+           span_flags = 0, span_tickets = 0, chunk_tickets = 0, staging = 0, dec_flags = 0, dec_map = 0,
+           dec_first = 0, total = 0;
 };
 
-Layout ws_layout(const Dims& d) {
+constexpr Layout ws_layout(const Dims& d) {
     Layout l;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -2050,7 +2053,7 @@ Layout ws_layout(const Dims& d) {
     return l;
 }
 
-Dims single_dims(uint64_t n) { return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n)}; }
+constexpr Dims single_dims(uint64_t n) { return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n)}; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_s(float s) { return s >= 1.0f && s < 2.0f; }  // false for NaN
@@ -2284,6 +2287,39 @@ int run_decompress_fixed(const Plan& p, int enc, const uint8_t* in, const uint64
 
 bool valid_enc(int enc) { return enc == TLC_ENC_QUARTIC || enc == TLC_ENC_TWOBIT; }
 
+// Compress without a caller workspace (tlc_compress_static): its scratch is a
+// fixed device array of the workspace size of the largest tensor it takes.
+// Each device holds its own copy from the first use until the process ends;
+// host code reaches it only through the address hipGetSymbolAddress returns
+// on that device (the array's name is not a device address on the host).
+constexpr uint64_t kStaticMaxN = 1ull << 24;
+constexpr size_t kStaticScratchBytes = ws_layout(single_dims(kStaticMaxN)).total;
+static_assert(kStaticScratchBytes % 256 == 0 && kStaticScratchBytes < (32u << 20), "scratch size");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// The current device's address of `scratch`, looked up once per device (a
+// symbol query, not an allocation); nullptr if the query fails.
+void* static_scratch() {
+    static std::mutex mu;
+    static std::vector<void*> per_dev;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if ((size_t)dev >= per_dev.size()) per_dev.resize(dev + 1, nullptr);
+    if (!per_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        per_dev[dev] = ptr;
+    }
+    return per_dev[dev];
+}
+
 int run_planes(bool gather, const float* src, const uint64_t* src_off, float* dst, const uint64_t* dst_off,
                const uint64_t* n, uint32_t count, uint64_t max_n, hipStream_t st) {
     if (!src || !src_off || !dst || !dst_off || !n || count == 0 || count > 65535 || max_n == 0 || max_n > kMaxN)
@@ -2313,6 +2349,7 @@ const char* tlc_status_string(int code) {
         case TLC_ERR_HIP: return "HIP runtime error";
         case TLC_ERR_CORRUPT: return "corrupt stream";
         case TLC_ERR_INTERNAL: return "internal wait expired";
+        case TLC_ERR_TOO_LARGE: return "n above the largest tensor tlc_compress_static takes";
         default: return "unknown status";
     }
 }
@@ -2332,6 +2369,19 @@ int tlc_compress(const float* x, float* err, uint64_t n, float s, uint8_t* out, 
     if (n == 0 || n > kMaxN) return TLC_ERR_INVALID_ARG;
     if (out_capacity < tlc_compress_bound(n)) return TLC_ERR_CAPACITY;
     return run_compress(single_plan(n), x, 1.0f, err, s, out, out_len, scale, workspace, workspace_bytes, status,
+                        static_cast<hipStream_t>(stream));
+}
+
+uint64_t tlc_compress_static_max_n(void) { return kStaticMaxN; }
+
+int tlc_compress_static(const float* x, float* err, uint64_t n, float s, uint8_t* out, uint64_t out_capacity,
+                        uint64_t* out_len, float* scale, int* status, tlc_stream_t stream) {
+    if (n == 0) return TLC_ERR_INVALID_ARG;
+    if (n > kStaticMaxN) return TLC_ERR_TOO_LARGE;
+    if (out_capacity < tlc_compress_bound(n)) return TLC_ERR_CAPACITY;
+    void* ws = static_scratch();
+    if (!ws) return TLC_ERR_HIP;
+    return run_compress(single_plan(n), x, 1.0f, err, s, out, out_len, scale, ws, kStaticScratchBytes, status,
                         static_cast<hipStream_t>(stream));
 }
 

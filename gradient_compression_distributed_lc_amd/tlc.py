@@ -23,6 +23,7 @@ ERR_WORKSPACE = 3
 ERR_HIP = 4
 ERR_CORRUPT = 5
 ERR_INTERNAL = 6
+ERR_TOO_LARGE = 7
 
 
 class TLCError(RuntimeError):
@@ -57,6 +58,8 @@ _SIGS = {
     "tlc_compress_bound": (_U64, [_U64]),
     "tlc_workspace_size": (_SZ, [_U64]),
     "tlc_compress": (_I, [_P, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_compress_static": (_I, [_P, _P, _U64, _F, _P, _U64, _P, _P, _P, _P]),
+    "tlc_compress_static_max_n": (_U64, []),
     "tlc_server_compress": (_I, [_P, _U32, _P, _U64, _F, _P, _U64, _P, _P, _P, _SZ, _P, _P]),
     "tlc_fixed_len": (_U64, [_U64, _I]),
     "tlc_compress_fixed": (_I, [_P, _P, _U64, _F, _I, _P, _U64, _P, _P, _SZ, _P, _P]),
@@ -192,6 +195,35 @@ def compress(x: torch.Tensor, err: torch.Tensor, s: float, *, out=None, out_len=
                             _ptr(scale, torch.float32, "scale"), _ptr(workspace, torch.uint8, "workspace"),
                             workspace.numel(), _ptr(status, torch.int32, "status"), _stream(stream))
     _check(rc, "tlc_compress")
+    return Compressed(out, out_len, scale, status, n, s)
+
+
+def compress_static_max_n() -> int:
+    return int(lib().tlc_compress_static_max_n())
+
+
+def compress_static(x: torch.Tensor, err: torch.Tensor, s: float, *, out=None, out_len=None, scale=None,
+                    status=None, stream=None) -> Compressed:
+    """tlc_compress_static: tlc_compress with the library's fixed scratch array
+    instead of a workspace (for callers that cannot allocate).  Buffers the
+    caller does not pass are allocated here, by torch; pass them all to keep
+    the call free of allocation."""
+    n = x.numel()
+    dev = x.device
+    if err.numel() != n:
+        raise ValueError("err must have as many elements as x")
+    out = out if out is not None else torch.empty(max(compress_bound(n), 1), dtype=torch.uint8, device=dev)
+    out_len = out_len if out_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    scale = scale if scale is not None else torch.zeros(1, dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    _need(out_len, 1, "out_len")
+    _need(scale, 1, "scale")
+    _need(status, 1, "status")
+    rc = lib().tlc_compress_static(_ptr(x, torch.float32, "x"), _ptr(err, torch.float32, "err"), n, s,
+                                   _ptr(out, torch.uint8, "out"), out.numel(),
+                                   _ptr(out_len, torch.int64, "out_len"), _ptr(scale, torch.float32, "scale"),
+                                   _ptr(status, torch.int32, "status"), _stream(stream))
+    _check(rc, "tlc_compress_static")
     return Compressed(out, out_len, scale, status, n, s)
 
 

@@ -69,7 +69,8 @@ enum tlc_status {
     TLC_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
     TLC_ERR_CORRUPT = 5,     /* (device status) stream does not expand to exactly ceil(n/5) bytes, or a
                                 fixed-length encoding holds a byte that is no valid code */
-    TLC_ERR_INTERNAL = 6     /* (device status) a bounded inter-block wait expired */
+    TLC_ERR_INTERNAL = 6,    /* (device status) a bounded inter-block wait expired */
+    TLC_ERR_TOO_LARGE = 7    /* n above tlc_compress_static_max_n() (tlc_compress_static only) */
 };
 
 /* Human-readable name of a status code.  Host only; never NULL. */
@@ -103,6 +104,23 @@ size_t tlc_workspace_size(uint64_t n);
 int tlc_compress(const float* x, float* err, uint64_t n, float s,
                  uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
                  void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+
+/* Compress for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Exactly tlc_compress, bit for bit, with the same arguments except the
+ * workspace: its scratch memory is a fixed device array inside the library,
+ * sized for n <= tlc_compress_static_max_n() (2^24 values; about 20 MB,
+ * held by each device the library runs on until the process ends).  The call
+ * allocates nothing; its first call on a device looks up that device's
+ * address of the array (a symbol query).  n above the maximum returns
+ * TLC_ERR_TOO_LARGE before anything is enqueued.  Every call on one device
+ * shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing
+ * in the array needs to survive or start at zero between calls. */
+uint64_t tlc_compress_static_max_n(void);
+int tlc_compress_static(const float* x, float* err, uint64_t n, float s,
+                        uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
+                        int* status, tlc_stream_t stream);
 
 /* ---- fixed-length encodings (ablations) ------------------------------------
  * The same quantization (error buffer, M, codes) written without zero-run

@@ -194,6 +194,16 @@ def test_decode_policy_argument_check():
     tlc.set_decode_policy(tlc.DECODE_AUTO)
 
 
+def test_static_compress_rejects_n_above_its_maximum():
+    # checked before any HIP call, so it runs without a GPU
+    L = tlc.lib()
+    assert L.tlc_compress_static_max_n() == 1 << 24
+    assert L.tlc_compress_static(None, None, (1 << 24) + 1, 1.5, None, 1 << 30, None, None, None, None) \
+        == tlc.ERR_TOO_LARGE
+    assert L.tlc_compress_static(None, None, 0, 1.5, None, 1 << 30, None, None, None, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_compress_static(None, None, 100, 1.5, None, 10, None, None, None, None) == tlc.ERR_CAPACITY
+
+
 # The binding checks every buffer it is given against the sizes the call
 # needs before any pointer reaches the library: an undersized tensor raises
 # ValueError and nothing is launched.  CPU tensors stand in for device ones
@@ -224,6 +234,8 @@ def test_binding_rejects_undersized_single_tensor_buffers():
         tlc.decompress_accumulate(ok["inp"], ok["in_len"], ok["scale"], n, s, _t(n, f32), status=_t(0, i32))
     with pytest.raises(ValueError, match="scale holds"):
         tlc.compress(_t(n, f32), _t(n, f32), s, scale=_t(0, f32))
+    with pytest.raises(ValueError, match="out_len holds"):
+        tlc.compress_static(_t(n, f32), _t(n, f32), s, out_len=_t(0, i64))
     with pytest.raises(ValueError, match="y holds"):
         tlc.decompress_fixed(_t(tlc.fixed_len(n, tlc.ENC_QUARTIC), u8), ok["scale"], n, s, tlc.ENC_QUARTIC,
                              y=_t(n - 1, f32))
