@@ -119,15 +119,25 @@ struct TableHeader {
     uint64_t magic, count, ftiles, etiles, spans, chunks, total_elems, stream_bytes;
 };
 static_assert(sizeof(TableHeader) == 64, "table layout");
-constexpr uint64_t kMagic = 0x32434c5433ull;  // "3TLC2"
+constexpr uint64_t kMagic = 0x33434c5433ull;  // "3TLC3"
 constexpr uint32_t kStraddle = 0x80000000u;   // ftile_info flag: the flat tile spans tensors
 constexpr uint32_t kMulti = 0x80000000u;      // span_seg / dec_map flag: the tensor has several spans / chunks
+
+// Per 1024-element block of the group (a "y-block", the unit of the
+// decompress-side streams): where its first element's quartic byte lives.
+struct YRec {
+    uint64_t qoff;  // stream slot offset of the tensor of its first element
+    uint32_t u0;    // that element's index in its tensor
+    uint32_t gi;    // that tensor | kStraddle when the block spans tensors
+};
+static_assert(sizeof(YRec) == 16, "table layout");
 
 struct GroupView {
     const Seg* segs;            // device table, or nullptr for one tensor
     const uint32_t* ftile_info; // per flat tile: tensor of its first element | kStraddle
     const uint32_t* span_seg;   // per k_emit span: tensor
     const uint32_t* etile_seg;  // per encode tile: tensor
+    const YRec* yrec;           // per y-block
     uint32_t count;
     Seg one;
 };
@@ -1333,6 +1343,17 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 
 // ---------------------------------------------------------------------------
 // decompress kernels
+//
+// Decompress takes one of two launch sequences, both giving the same y:
+// sparse streams (few encode tiles with a nonzero code): k_prep zero-fills y
+// and k_decode writes the nonzero codes over the fill; dense streams:
+// k_decode records where every encode tile begins and k_expand decodes each
+// tile in LDS and writes it once.  The accumulate of one payload adds its
+// nonzero codes to acc straight from the stream.  The accumulate of many
+// payloads decodes each payload's quartic bytes into the workspace (laid out
+// like the streams, with one flag byte per 1024-element "y-block" that holds
+// a nonzero code) in one k_decode launch, then k_apply reads and writes acc
+// once, y-block by y-block, applying the payloads in order.
 
 // Where k_decode found encode tile j of a tensor to begin (decompress only):
 // the stream byte, counted from the tensor's first, whose expansion holds
@@ -1348,22 +1369,32 @@ __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { r
 // 0.109).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
 constexpr uint64_t kDenseNum = 104, kDenseDen = 1000;
 
-// Decoder state reset and set-up.  Sparse decompress (n_fill > 0): zero fill
-// of y, one 16-byte store per lane (the fastest fill measured on MI355X; any
-// load before the store, or more stores per lane, slows it by 10-40%), with a
-// nontemporal hint: y is not read again here, and the kernels that follow
-// (the caller's next compress) run faster when the caches do not hold y's
-// dirty lines.  Dense decompress (tstart set): the tile starts and literal
-// flags are reset.
-// Always: the look-back flags, and the list of stream chunks: tensor i has
-// max(1, ceil(min(L_i, B_i) / kChunk)) chunks, numbered dec_first[i] ...;
-// chunk r belongs to tensor dec_map[r]; ctrl[3] = number of chunks.  Block 0
+constexpr uint32_t kYBlock = 1024;            // elements per y-block (256 lanes x 4)
+constexpr uint32_t kMaxPayloads = 64;         // payloads of one accumulate-many call
+
+__host__ __device__ constexpr uint64_t yblocks_of(uint64_t total) { return (total + kYBlock - 1) / kYBlock; }
+// y-block flags of one payload, padded to whole 16-byte rows
+__host__ __device__ constexpr uint64_t yflag_bytes(uint64_t total) { return (yblocks_of(total) + 15) / 16 * 16; }
+
+// Decoder state reset and set-up, for `payloads` payloads of the group (unit
+// u = p * count + t is tensor t of payload p; in_lens and scales are indexed
+// by unit).
+// Sparse decompress (n_fill > 0): zero fill of y, one 16-byte store per lane
+// (the fastest fill measured on MI355X; any load before the store, or more
+// stores per lane, slows it by 10-40%), with a nontemporal hint: y is not
+// read again here, and the kernels that follow (the caller's next compress)
+// run faster when the caches do not hold y's dirty lines.  Dense decompress
+// (tstart set): the tile starts and literal flags are reset.  Accumulate-many
+// (nyfl > 0): the y-block flags are reset.
+// Always: the look-back flags, and the list of stream chunks: unit u has
+// max(1, ceil(min(L_u, B_t) / kChunk)) chunks, numbered dec_first[u] ...;
+// chunk r belongs to unit dec_map[r]; ctrl[3] = number of chunks.  Block 0
 // also writes the density of the streams to *hint (when set): 1 if dense.
-__global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restrict__ y, uint64_t n_fill,
-                                                   const uint64_t* __restrict__ in_lens,
+__global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payloads, float* __restrict__ y,
+                                                   uint64_t n_fill, const uint64_t* __restrict__ in_lens,
                                                    uint64_t* __restrict__ flags, uint64_t nflags,
                                                    uint64_t* __restrict__ tstart, uint32_t* __restrict__ tlit,
-                                                   uint64_t ntiles,
+                                                   uint64_t ntiles, uint8_t* __restrict__ yfl, uint64_t nyfl,
                                                    uint32_t* __restrict__ dec_map, uint32_t* __restrict__ dec_first,
                                                    uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
                                                    int* __restrict__ status, uint32_t* hint) {
@@ -1382,26 +1413,28 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
             tstart[i] = kNoStart;
             tlit[i] = 0;
         }
+    for (uint64_t i = tid; i < nyfl / 16; i += stride) reinterpret_cast<uint4*>(yfl)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (blockIdx.x == 0) {
         uint32_t carry = 0;
         uint64_t sum_l = 0, sum_b = 0;
-        for (uint32_t base = 0; base < g.count; base += kThreads) {
-            const uint32_t gi = base + threadIdx.x;
+        const uint64_t units = (uint64_t)payloads * g.count;
+        for (uint64_t base = 0; base < units; base += kThreads) {
+            const uint64_t u = base + threadIdx.x;
             uint32_t rc = 0;
-            if (gi < g.count) {
-                const Seg sg = load_seg(g, gi);
+            if (u < units) {
+                const Seg sg = load_seg(g, (uint32_t)(u % g.count));
                 const uint64_t B = quartic_len(sg.n);
-                const uint64_t L = min(in_lens[gi], B);
+                const uint64_t L = min(in_lens[u], B);
                 rc = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
                 sum_l += L;
                 sum_b += B;
             }
             uint32_t tot;
             const uint32_t first = carry + block_excl_sum(rc, s_u, &tot);
-            if (gi < g.count) {
-                dec_first[gi] = first;
-                tickets[gi] = 0;
-                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = gi | (rc > 1 ? kMulti : 0u);
+            if (u < units) {
+                dec_first[u] = first;
+                tickets[u] = 0;
+                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = (uint32_t)u | (rc > 1 ? kMulti : 0u);
             }
             carry += tot;
         }
@@ -1433,21 +1466,72 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, float* __restric
 
 // What k_decode does with a chunk once it knows where the chunk's bytes land.
 enum DecodeMode {
-    kDecodeWrite = 0,   // sparse decompress: nonzero codes written over k_prep's zero fill
-    kDecodeAdd = 1,     // accumulate: nonzero codes added to y in place
-    kDecodeRecord = 2,  // dense decompress: tile starts and literal flags for k_expand
+    kDecodeWrite = 0,    // sparse decompress: nonzero codes written over k_prep's zero fill
+    kDecodeAdd = 1,      // accumulate one payload: nonzero codes added to acc in place
+    kDecodeRecord = 2,   // dense decompress: tile starts and literal flags for k_expand
+    kDecodeQuartic = 3,  // accumulate-many: the payload's quartic bytes and y-block flags for k_apply
 };
 
+// The five codes of a quartic byte as 2-bit fields (q & 3), first element
+// lowest.
+__host__ __device__ constexpr uint32_t quartic_fields(uint32_t byte) {
+    uint32_t pat = 0;
+    for (uint32_t d = 0; d < 5; ++d) {
+        const uint32_t digit = byte % 3u;
+        byte /= 3u;
+        pat |= (digit == 1u ? 0u : digit == 2u ? 1u : 3u) << (2 * d);
+    }
+    return pat;
+}
+
+// Elements [a, b) of an array of E-byte elements at `base` set to the
+// pattern v (E = 1: a byte; E = 2: a 16-bit field): aligned 16-byte stores
+// where whole 16-byte pieces lie inside, the largest aligned power-of-two
+// stores at the two ends (pieces shared with another lane are written only
+// where they are this range's).
+template <int E>
+__device__ __forceinline__ void fill_elements(uint8_t* base, uint64_t a, uint64_t b, uint32_t v) {
+    const uint64_t pat = E == 1 ? 0x0101010101010101ull * v : 0x0001000100010001ull * v;
+    uint64_t A = a * E;
+    const uint64_t Z = b * E;
+    auto piece = [&](uint64_t end) {  // [A, end), end - A < 16 or A unaligned
+        while (A < end) {
+            const uint64_t room = end - A;
+            if ((A & 7) == 0 && room >= 8) {
+                *reinterpret_cast<uint64_t*>(base + A) = pat;
+                A += 8;
+            } else if ((A & 3) == 0 && room >= 4) {
+                *reinterpret_cast<uint32_t*>(base + A) = (uint32_t)pat;
+                A += 4;
+            } else if ((A & 1) == 0 && room >= 2) {
+                *reinterpret_cast<uint16_t*>(base + A) = (uint16_t)pat;
+                A += 2;
+            } else {
+                base[A] = (uint8_t)pat;
+                A += 1;
+            }
+        }
+    };
+    piece(min(Z, (A + 15) & ~15ull));
+    const uint4 p4 = make_uint4((uint32_t)pat, (uint32_t)(pat >> 32), (uint32_t)pat, (uint32_t)(pat >> 32));
+    for (; A + 16 <= Z; A += 16) *reinterpret_cast<uint4*>(base + A) = p4;
+    piece(Z);
+}
+
 // One block per stream chunk (kChunk bytes, 16 per lane): expansion lengths,
-// block scan, look-back across the tensor's chunks for the quartic byte index
+// block scan, look-back across the unit's chunks for the quartic byte index
 // of the chunk, then the work of Mode (one instantiation each, so that each
-// keeps only its own registers).
+// keeps only its own registers).  In quartic mode every lane writes the
+// quartic bytes its stream bytes expand to (runs as byte 121) and sets the
+// flag of each y-block that one of its literal bytes reaches.
 template <int Mode>
-__global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t* __restrict__ in,
+__global__ __launch_bounds__(kThreads) void k_decode(GroupView g, uint64_t N, const uint8_t* __restrict__ in,
+                                                     uint64_t in_stride, uint64_t qstride,
                                                      const uint64_t* __restrict__ in_lens,
                                                      const float* __restrict__ scales, float s,
                                                      float* __restrict__ y, uint64_t* __restrict__ tstart,
-                                                     uint32_t* __restrict__ tlit, uint64_t* __restrict__ flags,
+                                                     uint32_t* __restrict__ tlit, uint8_t* __restrict__ qbuf,
+                                                     uint8_t* __restrict__ yfl, uint64_t* __restrict__ flags,
                                                      const uint32_t* __restrict__ dec_map,
                                                      const uint32_t* __restrict__ dec_first,
                                                      uint32_t* __restrict__ tickets, const uint32_t* __restrict__ ctrl,
@@ -1459,43 +1543,45 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
     // near what the GPU holds at once and blocks loop over the chunks.
     for (uint32_t slot = blockIdx.x; slot < ctrl[3]; slot += gridDim.x) {
         if (slot != blockIdx.x) __syncthreads();  // s_chunk / s_base of the previous chunk are read
-        // A tensor with several chunks hands them out in ticket order from its
+        // A unit with several chunks hands them out in ticket order from its
         // own counter, so that the look-back only ever waits for blocks that
         // already hold a smaller ticket (and are working on that chunk).
         const uint32_t ent = dec_map[slot];
-        const uint32_t gi = ent & ~kMulti;
-        if (threadIdx.x == 0) s_chunk = (ent & kMulti) ? atomicAdd(tickets + gi, 1u) : 0u;  // in flight with the loads
-        const uint32_t c0 = dec_first[gi];
-        const float msc = scales[gi];
-        const Seg sg = load_seg(g, gi);
+        const uint32_t u = ent & ~kMulti;
+        const uint32_t t = u % g.count, p = u / g.count;
+        if (threadIdx.x == 0) s_chunk = (ent & kMulti) ? atomicAdd(tickets + u, 1u) : 0u;  // in flight with the loads
+        const uint32_t c0 = dec_first[u];
+        const float msc = scales[u];
+        const Seg sg = load_seg(g, t);
         const uint32_t n = sg.n;
         const uint64_t B = quartic_len(n);
-        const uint64_t L_in = in_lens[gi];
+        const uint64_t L_in = in_lens[u];
         const uint64_t L = min(L_in, B);
+        const uint8_t* const sp = in + (uint64_t)p * in_stride;  // payload p's stream buffer
         __syncthreads();
         const uint32_t lc = s_chunk;
         const uint32_t c = c0 + lc;
         if (L_in > B && lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
         const uint64_t start = (uint64_t)lc * kChunk;
         if (start >= L) {
-            // only an empty stream gets here (chunk 0 of a tensor with L == 0),
+            // only an empty stream gets here (chunk 0 of a unit with L == 0),
             // which is corrupt because ceil(n/5) >= 1
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
             continue;
         }
         const uint32_t cnt = (uint32_t)min((uint64_t)kChunk, L - start);
-        const uint8_t* p = in + sg.stream_off + start;
+        const uint8_t* const pb = sp + sg.stream_off + start;
         const uint32_t off = 16u * threadIdx.x;
         const uint32_t nv = cnt > off ? min(16u, cnt - off) : 0u;
         uint32_t wd[4] = {0u, 0u, 0u, 0u};
-        if (nv == 16 && ((reinterpret_cast<uintptr_t>(p + off) & 15) == 0)) {
-            const uint4 v = *reinterpret_cast<const uint4*>(p + off);
+        if (nv == 16 && ((reinterpret_cast<uintptr_t>(pb + off) & 15) == 0)) {
+            const uint4 v = *reinterpret_cast<const uint4*>(pb + off);
             wd[0] = v.x;
             wd[1] = v.y;
             wd[2] = v.z;
             wd[3] = v.w;
         } else {
-            for (uint32_t i = 0; i < nv; ++i) wd[i >> 2] |= (uint32_t)p[off + i] << (8 * (i & 3));
+            for (uint32_t i = 0; i < nv; ++i) wd[i >> 2] |= (uint32_t)pb[off + i] << (8 * (i & 3));
         }
         uint32_t tsum = 0, nlit = 0;
 #pragma unroll
@@ -1529,7 +1615,41 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_INTERNAL);
             continue;
         }
-        if (Mode == kDecodeRecord) {
+        if (threadIdx.x == 0 && start + cnt == L && base + csum != B) raise_status(status, TLC_ERR_CORRUPT);
+        uint64_t pos = base + texcl;
+        bool bad = false;
+        if (Mode == kDecodeWrite || Mode == kDecodeAdd) {
+            if (nlit) {  // lanes whose bytes hold no nonzero code write nothing
+                float* const yy = y + sg.elem_off;
+                const float ms = msc * s;
+#pragma unroll
+                for (uint32_t i = 0; i < 16; ++i) {
+                    const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
+                    if (i < nv) {
+                        if (byte < 243u) {
+                            if (pos >= B) {
+                                bad = true;
+                            } else if (byte != kZero) {
+                                uint32_t rest = byte;
+#pragma unroll
+                                for (uint32_t d = 0; d < 5; ++d) {
+                                    const uint32_t digit = rest % 3u;
+                                    rest /= 3u;
+                                    const uint64_t e = 5u * pos + d;
+                                    if (digit != 1u && e < n) {
+                                        const float val = (float)((int)digit - 1) * ms;
+                                        yy[e] = Mode == kDecodeAdd ? yy[e] + val : val;
+                                    }
+                                }
+                            }
+                            pos += 1;
+                        } else {
+                            pos += byte - kRunBase;
+                        }
+                    }
+                }
+            }
+        } else if (Mode == kDecodeRecord) {
             // A lane's 16 bytes expand to at most 224 quartic bytes, so at
             // most one tile boundary (a multiple of 1024) falls inside them,
             // d quartic bytes after the lane's first; the lane's literal bytes
@@ -1538,7 +1658,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             const uint32_t d = (uint32_t)((kETileBytes - p0 % kETileBytes) % kETileBytes);
             const uint32_t lim = (uint32_t)min<uint64_t>(B - min(B, p0), 1u << 16);  // quartic bytes left in the tensor
             uint32_t rel = 0, bi = 16, bskip = 0;
-            bool lit_lo = false, lit_hi = false, bad = false;
+            bool lit_lo = false, lit_hi = false;
 #pragma unroll
             for (uint32_t i = 0; i < 16; ++i) {
                 const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
@@ -1559,36 +1679,40 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                 }
             }
             if (bi < 16 && d < lim) tstart[sg.etile0 + (p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
-            if (bad) {
-                raise_status(status, TLC_ERR_CORRUPT);
-            } else {
+            if (!bad) {
                 if (lit_lo) tlit[sg.etile0 + p0 / kETileBytes] = 1u;
                 if (lit_hi) tlit[sg.etile0 + (p0 + d) / kETileBytes] = 1u;
             }
-        } else if (nlit) {
-            float* const yy = y + sg.elem_off;
-            const float ms = msc * s;
-            uint64_t pos = base + texcl;
-            bool bad = false;
-#pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {
-                const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
-                if (i < nv) {
+        } else {
+            // quartic mode: the lane's quartic positions [pos, pos + tsum) of
+            // the tensor's slot, cut at B.  First all of them as byte 121,
+            // then the literal bytes over them (this lane's own stores, so
+            // they land in program order).
+            uint8_t* const qt = qbuf + (uint64_t)p * qstride + sg.stream_off;
+            const uint64_t q0 = min(pos, B), q1 = min(pos + tsum, B);
+            if (q1 > q0) fill_elements<1>(qt, q0, q1, kZero);
+            if (nlit || pos + tsum > B) {  // literals to place, or bytes past B to report
+                uint8_t* const fl = yfl + (uint64_t)p * yflag_bytes(N);
+                const uint64_t eo = sg.elem_off;
+                uint64_t lastY = ~0ull;
+                uint32_t w0 = wd[0], w1 = wd[1], w2 = wd[2], w3 = wd[3];
+#pragma unroll 1
+                for (uint32_t i = 0; i < nv; ++i) {
+                    const uint32_t byte = w0 & 255u;
+                    w0 = (w0 >> 8) | (w1 << 24);
+                    w1 = (w1 >> 8) | (w2 << 24);
+                    w2 = (w2 >> 8) | (w3 << 24);
+                    w3 >>= 8;
                     if (byte < 243u) {
                         if (pos >= B) {
                             bad = true;
                         } else if (byte != kZero) {
-                            uint32_t rest = byte;
-#pragma unroll
-                            for (uint32_t d = 0; d < 5; ++d) {
-                                const uint32_t digit = rest % 3u;
-                                rest /= 3u;
-                                const uint64_t e = 5u * pos + d;
-                                if (digit != 1u && e < n) {
-                                    const float val = (float)((int)digit - 1) * ms;
-                                    yy[e] = Mode == kDecodeAdd ? yy[e] + val : val;
-                                }
-                            }
+                            qt[pos] = (uint8_t)byte;
+                            // the y-blocks its five elements reach
+                            const uint64_t e0 = eo + 5 * pos, e1 = eo + min(5 * pos + 4, (uint64_t)n - 1);
+                            if (e0 / kYBlock != lastY) fl[e0 / kYBlock] = 1;
+                            if (e1 / kYBlock != e0 / kYBlock) fl[e1 / kYBlock] = 1;
+                            lastY = e1 / kYBlock;
                         }
                         pos += 1;
                     } else {
@@ -1596,9 +1720,130 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                     }
                 }
             }
-            if (bad) raise_status(status, TLC_ERR_CORRUPT);
         }
-        if (threadIdx.x == 0 && start + cnt == L && base + csum != B) raise_status(status, TLC_ERR_CORRUPT);
+        if (bad) raise_status(status, TLC_ERR_CORRUPT);
+    }
+}
+
+// Tensor holding group element e (e < the group's total).
+__device__ __forceinline__ uint32_t tensor_of(const GroupView& g, uint64_t e) {
+    if (!g.segs) return 0u;
+    const uint32_t info = g.ftile_info[e / kFTile];
+    const uint32_t g0 = info & ~kStraddle;
+    return (info & kStraddle) ? find_segment(g.segs, g0, min(g.count, g0 + kFTile + 1), e) : g0;
+}
+
+__device__ __forceinline__ YRec yrec_of(const GroupView& g, uint64_t b) {
+    if (g.yrec) return g.yrec[b];
+    YRec r;
+    r.qoff = 0;
+    r.u0 = (uint32_t)(b * kYBlock);
+    r.gi = 0;
+    return r;
+}
+
+__device__ __forceinline__ int field_code(uint32_t pat, uint32_t k) {  // sign-extended 2-bit field k
+    return (int)(pat << (30 - 2 * k)) >> 30;
+}
+
+// Codes of group elements e .. e+3 of a y-block that lies in one tensor:
+// tensor element u = r.u0 + (e - first element of the block), quartic bytes
+// u/5 and u/5 + 1 of the tensor's slot at q + r.qoff; 20 bits, element k in
+// bits 2k (the second byte is read only when an element < N needs it).
+__device__ __forceinline__ uint32_t codes4(const uint8_t* q, const YRec& r, uint32_t l, uint64_t e, uint64_t N,
+                                           const uint16_t* tab) {
+    const uint32_t u = r.u0 + 4 * l;
+    const uint64_t bq = r.qoff + u / 5;
+    const uint32_t d0 = u % 5;
+    const uint32_t x0 = q[bq];
+    const uint32_t x1 = d0 >= 2 && e + (5 - d0) < N ? q[bq + 1] : kZero;
+    const uint32_t p0 = tab ? tab[x0] : quartic_fields(x0), p1 = tab ? tab[x1] : quartic_fields(x1);
+    return ((p1 << 10) | p0) >> (2 * d0);
+}
+
+// The code of group element e in a y-block that spans tensors.
+__device__ __forceinline__ int code_at(const GroupView& g, const uint8_t* q, uint64_t e, uint32_t* gi) {
+    *gi = tensor_of(g, e);
+    const Seg sg = load_seg(g, *gi);
+    const uint64_t u = e - sg.elem_off;
+    return field_code(quartic_fields(q[sg.stream_off + u / 5]), (uint32_t)(u % 5));
+}
+
+// acc += q_p * (M_p*s) for payloads p = 0 .. payloads-1 in that order, only
+// where q_p != 0 (so an element no payload touches keeps its bits, -0.0
+// included).  One block per y-block, four elements per lane; a y-block where
+// no payload has a nonzero code is not touched.  Quartic bytes are split
+// into codes through a 243-entry table in LDS.
+__global__ __launch_bounds__(kThreads) void k_apply(GroupView g, uint64_t N, uint32_t payloads,
+                                                    const uint8_t* __restrict__ q, uint64_t qstride,
+                                                    const uint8_t* __restrict__ yfl,
+                                                    const float* __restrict__ scales, float s,
+                                                    float* __restrict__ acc) {
+    __shared__ uint16_t s_tab[243];
+    const uint64_t b = blockIdx.x;
+    const uint64_t fstride = yflag_bytes(N);
+    uint32_t any = 0;
+    for (uint32_t p = 0; p < payloads; ++p) any |= yfl[p * fstride + b];
+    if (!any) return;
+    if (threadIdx.x < 243) s_tab[threadIdx.x] = (uint16_t)quartic_fields(threadIdx.x);
+    const uint64_t e = (b * kThreads + threadIdx.x) * 4;
+    const bool full = e + 4 <= N;
+    f4 a = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (full) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(acc + e));
+    } else {
+        if (e < N) a.x = acc[e];
+        if (e + 1 < N) a.y = acc[e + 1];
+        if (e + 2 < N) a.z = acc[e + 2];
+    }
+    const YRec r = yrec_of(g, b);
+    __syncthreads();
+    const bool span = (r.gi & kStraddle) != 0;
+    constexpr uint32_t kGroupP = 8;  // payloads whose loads are in flight together
+    for (uint32_t p0 = 0; p0 < payloads; p0 += kGroupP) {
+        uint32_t cs[kGroupP];
+        float ms[kGroupP];
+#pragma unroll
+        for (uint32_t k = 0; k < kGroupP; ++k) {
+            cs[k] = 0;
+            ms[k] = 0.0f;
+            const uint32_t p = p0 + k;
+            if (p < payloads && yfl[p * fstride + b] && !span && e < N) {
+                ms[k] = scales[(uint64_t)p * g.count + r.gi] * s;
+                cs[k] = codes4(q + p * qstride, r, threadIdx.x, e, N, s_tab);
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kGroupP; ++k) {
+            const uint32_t p = p0 + k;
+            if (p >= payloads || !yfl[p * fstride + b]) continue;
+            float m[4] = {ms[k], ms[k], ms[k], ms[k]};
+            uint32_t c = cs[k];
+            if (span) {  // per element: its tensor's code and M*s
+                c = 0;
+#pragma unroll
+                for (uint32_t i = 0; i < 4; ++i) {
+                    if (e + i < N) {
+                        uint32_t gi;
+                        const int qq = code_at(g, q + p * qstride, e + i, &gi);
+                        c |= (uint32_t)(qq & 3) << (2 * i);
+                        m[i] = scales[(uint64_t)p * g.count + gi] * s;
+                    }
+                }
+            }
+            const int q0 = field_code(c, 0), q1 = field_code(c, 1), q2 = field_code(c, 2), q3 = field_code(c, 3);
+            if (q0) a.x = a.x + (float)q0 * m[0];
+            if (q1) a.y = a.y + (float)q1 * m[1];
+            if (q2) a.z = a.z + (float)q2 * m[2];
+            if (q3) a.w = a.w + (float)q3 * m[3];
+        }
+    }
+    if (full) {
+        __builtin_nontemporal_store(a, reinterpret_cast<f4*>(acc + e));
+    } else {
+        if (e < N) acc[e] = a.x;
+        if (e + 1 < N) acc[e + 1] = a.y;
+        if (e + 2 < N) acc[e + 2] = a.z;
     }
 }
 
@@ -1984,7 +2229,7 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
 // device.  Such kernels hand work to their blocks or waves round-robin, so a
 // grid larger than this leaves a second, partial round of blocks running
 // alone at the end.
-enum GridKind { kGridPack, kGridDecode, kGridDecodeAdd, kGridDecodeRecord, kGridKinds };
+enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridDecodeQuartic, kGridKinds };
 uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap) {
     static std::mutex mu;
     static std::vector<uint32_t> per_dev;  // kGridKinds entries per device, 0 = not queried
@@ -2016,7 +2261,7 @@ constexpr uint64_t chunks_host(uint64_t n) {
 
 // Sizes of everything a call needs, for one tensor or a group.
 struct Dims {
-    uint64_t count, total, ftiles, etiles, spans, chunks;
+    uint64_t count, total, ftiles, etiles, spans, chunks, stream_bytes;
 };
 
 struct Layout {
@@ -2053,7 +2298,9 @@ constexpr Layout ws_layout(const Dims& d) {
     return l;
 }
 
-constexpr Dims single_dims(uint64_t n) { return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n)}; }
+constexpr Dims single_dims(uint64_t n) {
+    return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n), align_up((n + 4) / 5, 16)};
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_s(float s) { return s >= 1.0f && s < 2.0f; }  // false for NaN
@@ -2073,7 +2320,7 @@ Plan single_plan(uint64_t n) {
 }
 
 struct TableLayout {
-    size_t segs, ftile_info, span_seg, etile_seg, total;
+    size_t segs, ftile_info, span_seg, etile_seg, yrec, total;
 };
 TableLayout table_layout(const Dims& d) {
     TableLayout t;
@@ -2081,12 +2328,14 @@ TableLayout table_layout(const Dims& d) {
     t.ftile_info = align_up(t.segs + d.count * sizeof(Seg), 16);
     t.span_seg = align_up(t.ftile_info + d.ftiles * sizeof(uint32_t), 16);
     t.etile_seg = align_up(t.span_seg + d.spans * sizeof(uint32_t), 16);
-    t.total = align_up(t.etile_seg + d.etiles * sizeof(uint32_t), 16);
+    t.yrec = align_up(t.etile_seg + d.etiles * sizeof(uint32_t), 16);
+    t.total = align_up(t.yrec + yblocks_of(d.total) * sizeof(YRec), 16);
     return t;
 }
 
 Dims dims_of(const tlc_group_info* info) {
-    return {info->count, info->total_elems, ftiles_of(info->total_elems), info->tiles, info->spans, info->chunks};
+    return {info->count, info->total_elems, ftiles_of(info->total_elems), info->tiles, info->spans, info->chunks,
+            info->stream_bytes};
 }
 
 int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
@@ -2101,6 +2350,7 @@ int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
     p->g.ftile_info = reinterpret_cast<const uint32_t*>(base + t.ftile_info);
     p->g.span_seg = reinterpret_cast<const uint32_t*>(base + t.span_seg);
     p->g.etile_seg = reinterpret_cast<const uint32_t*>(base + t.etile_seg);
+    p->g.yrec = reinterpret_cast<const YRec*>(base + t.yrec);
     p->g.count = (uint32_t)info->count;
     return TLC_OK;
 }
@@ -2173,6 +2423,97 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
     });
 }
 
+// Decoder state in a workspace: look-back flags and the chunk map for
+// `payloads` payloads, per-unit ticket counters and first chunks; for the
+// dense decompress the tile starts and literal flags; for accumulate-many
+// each payload's quartic bytes and y-block flags.
+struct DecState {
+    uint32_t* ctrl;
+    uint64_t* flags;
+    uint32_t* map;
+    uint32_t* first;
+    uint32_t* tickets;
+    uint64_t* tstart;
+    uint32_t* tlit;
+    uint8_t* qbuf;  // payload p's quartic bytes at qbuf + p * stream_bytes
+    uint8_t* yfl;   // payload p's y-block flags at yfl + p * yflag_bytes
+};
+
+// Decompress and the single-payload accumulate use the call's workspace:
+// the compressor's per-tile summaries and maxima are not needed there, so
+// their slots hold the tile starts and literal flags.
+DecState dec_state_single(const Layout& l, char* w) {
+    DecState d;
+    d.ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
+    d.flags = reinterpret_cast<uint64_t*>(w + l.dec_flags);
+    d.map = reinterpret_cast<uint32_t*>(w + l.dec_map);
+    d.first = reinterpret_cast<uint32_t*>(w + l.dec_first);
+    d.tickets = reinterpret_cast<uint32_t*>(w + l.chunk_tickets);
+    d.tstart = reinterpret_cast<uint64_t*>(w + l.etile_agg);
+    d.tlit = reinterpret_cast<uint32_t*>(w + l.etmax);
+    d.qbuf = nullptr;
+    d.yfl = nullptr;
+    return d;
+}
+
+// Workspace of an accumulate-many call on P payloads.
+struct ManyLayout {
+    size_t ctrl = 0, flags = 0, map = 0, first = 0, tickets = 0, qbuf = 0, yfl = 0, total = 0;
+};
+constexpr ManyLayout many_layout(const Dims& d, uint64_t P) {
+    ManyLayout l;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    l.ctrl = take(256);
+    l.flags = take(P * d.chunks * sizeof(uint64_t));
+    l.map = take(P * d.chunks * sizeof(uint32_t));
+    l.first = take(P * d.count * sizeof(uint32_t));
+    l.tickets = take(P * d.count * sizeof(uint32_t));
+    l.qbuf = take(P * d.stream_bytes);
+    l.yfl = take(P * yflag_bytes(d.total));
+    l.total = off;
+    return l;
+}
+
+// k_prep, then k_decode in `mode` over the chunks of `payloads` payloads.
+// n_fill: elements of y to zero first (sparse decompress); hint: where the
+// streams' density class goes.
+int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in, uint64_t in_stride,
+                  const uint64_t* in_lens, const float* scales, float s, float* y, uint64_t n_fill,
+                  const DecState& ds, int* status, uint32_t* hint, hipStream_t st) {
+    const GroupView g = p.g;
+    const uint64_t chunks = p.d.chunks * payloads, etiles = p.d.etiles;
+    const uint64_t nyfl = mode == kDecodeQuartic ? payloads * yflag_bytes(p.d.total) : 0;
+    uint64_t* const tstart = mode == kDecodeRecord ? ds.tstart : nullptr;
+    const uint64_t blocks = std::max(std::max((n_fill / 4 + kThreads - 1) / kThreads,
+                                              (std::max(chunks, tstart ? etiles : 0) + kThreads - 1) / kThreads),
+                                     (nyfl / 16 + kThreads - 1) / kThreads);
+    const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
+    int rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
+        k_prep<<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart, ds.tlit,
+                                               etiles, ds.yfl, nyfl, ds.map, ds.first, ds.tickets, ds.ctrl, status,
+                                               hint);
+    });
+    if (rc) return rc;
+    auto kern = mode == kDecodeWrite     ? k_decode<kDecodeWrite>
+                : mode == kDecodeAdd     ? k_decode<kDecodeAdd>
+                : mode == kDecodeRecord  ? k_decode<kDecodeRecord>
+                                         : k_decode<kDecodeQuartic>;
+    const GridKind gk = (GridKind)(kGridDecodeWrite + mode);
+    static const char* const names[] = {"tlc_decode", "tlc_decode_add", "tlc_decode_record", "tlc_decode_quartic"};
+    const uint32_t grid =
+        (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
+    return launch(names[mode], st, [&] {
+        kern<<<grid, kThreads, 0, st>>>(g, p.d.total, in, in_stride, p.d.stream_bytes, in_lens, scales, s, y, tstart,
+                                        ds.tlit, ds.qbuf, ds.yfl, ds.flags, ds.map, ds.first, ds.tickets, ds.ctrl,
+                                        status);
+    });
+}
+
 // Decompress takes one of two launch sequences, both giving the same y.
 // Sparse: k_prep zero-fills y, then k_decode writes the nonzero codes over
 // the fill.  Dense: k_decode records where each encode tile begins and
@@ -2180,96 +2521,61 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
 // hold a nonzero code (the fill is the fastest way to write y, and few lines
 // are written twice); the dense path once most tiles do (the scattered writes
 // then land on lines the fill has already written).  The host cannot see the
-// stream lengths without a synchronisation, so under TLC_DECODE_AUTO it
-// follows the density that the previous decompress on the same workspace
-// found: k_prep writes it to a slot of pinned host memory.
-std::atomic<int> g_decode_policy{TLC_DECODE_AUTO};
-constexpr uint32_t kHintSlots = 64;
-
-struct HintSlots {
-    bool tried = false;
-    uint32_t* host = nullptr;  // kHintSlots words of pinned host memory
-    uint32_t* dev = nullptr;   // the same words as the device addresses them
-};
-
-HintSlots hint_slots() {
-    static std::mutex mu;
-    static std::vector<HintSlots> per_dev;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return HintSlots{};
-    std::lock_guard<std::mutex> lk(mu);
-    if ((size_t)dev >= per_dev.size()) per_dev.resize(dev + 1);
-    HintSlots& h = per_dev[dev];
-    if (!h.tried) {
-        h.tried = true;
-        void* hp = nullptr;
-        void* dp = nullptr;
-        if (hipHostMalloc(&hp, kHintSlots * sizeof(uint32_t), hipHostMallocDefault) == hipSuccess) {
-            memset(hp, 0, kHintSlots * sizeof(uint32_t));
-            if (hipHostGetDevicePointer(&dp, hp, 0) == hipSuccess) {
-                h.host = static_cast<uint32_t*>(hp);
-                h.dev = static_cast<uint32_t*>(dp);
-            } else {
-                (void)hipHostFree(hp);
-            }
-        }
-        (void)hipGetLastError();  // a failed set-up leaves no error behind; AUTO then stays sparse
-    }
-    return h;
-}
-
+// stream lengths without a synchronisation, so it follows the caller's hint
+// word (host memory the device can write): the density class the previous
+// decompress given the same word left there.  No word: the sparse path.
 int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, const float* scales, float s,
-                   float* y, void* ws, size_t ws_bytes, int* status, hipStream_t st, int accumulate) {
+                   float* y, void* ws, size_t ws_bytes, int* status, uint32_t* hint, uint32_t* dev_hint,
+                   hipStream_t st, int accumulate) {
     if (!in || !in_lens || !scales || !y || !status) return TLC_ERR_INVALID_ARG;
     if (!aligned16(y) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
     Layout l;
     int rc = check_ws(p, ws, ws_bytes, &l);
     if (rc) return rc;
-    char* w = static_cast<char*>(ws);
-    uint32_t* ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
-    uint64_t* flags = reinterpret_cast<uint64_t*>(w + l.dec_flags);
-    uint32_t* dec_map = reinterpret_cast<uint32_t*>(w + l.dec_map);
-    uint32_t* dec_first = reinterpret_cast<uint32_t*>(w + l.dec_first);
-    uint32_t* chunk_tickets = reinterpret_cast<uint32_t*>(w + l.chunk_tickets);
-    bool dense = false;
-    uint32_t* hint = nullptr;
-    if (!accumulate) {
-        const int policy = g_decode_policy.load(std::memory_order_relaxed);
-        const HintSlots h = hint_slots();
-        const uint32_t slot = (uint32_t)((reinterpret_cast<uintptr_t>(ws) >> 8) % kHintSlots);
-        if (h.host) hint = h.dev + slot;
-        dense = policy == TLC_DECODE_DENSE ||
-                (policy == TLC_DECODE_AUTO && h.host && reinterpret_cast<volatile uint32_t*>(h.host)[slot] != 0u);
-    }
-    // dense decompress: the compressor's per-tile summaries and maxima are not
-    // needed here, so their slots hold the tile starts and literal flags
-    uint64_t* tstart = dense ? reinterpret_cast<uint64_t*>(w + l.etile_agg) : nullptr;
-    uint32_t* tlit = reinterpret_cast<uint32_t*>(w + l.etmax);
-    const GroupView g = p.g;
-    const uint64_t chunks = p.d.chunks, etiles = p.d.etiles;
-    const uint64_t n_fill = accumulate || dense ? 0 : p.d.total;
-    const uint64_t blocks =
-        std::max((n_fill / 4 + kThreads - 1) / kThreads, (std::max(chunks, etiles) + kThreads - 1) / kThreads);
-    const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
-    rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
-        k_prep<<<prep_grid, kThreads, 0, st>>>(g, y, n_fill, in_lens, flags, chunks, tstart, tlit, etiles, dec_map,
-                                               dec_first, chunk_tickets, ctrl, status, hint);
-    });
-    if (rc) return rc;
-    const int mode = accumulate ? kDecodeAdd : dense ? kDecodeRecord : kDecodeWrite;
-    auto kern = mode == kDecodeAdd ? k_decode<kDecodeAdd> : mode == kDecodeRecord ? k_decode<kDecodeRecord>
-                                                                                  : k_decode<kDecodeWrite>;
-    const GridKind gk = mode == kDecodeAdd ? kGridDecodeAdd : mode == kDecodeRecord ? kGridDecodeRecord : kGridDecode;
-    const uint32_t grid =
-        (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
-    rc = launch("tlc_decode", st, [&] {
-        kern<<<grid, kThreads, 0, st>>>(g, in, in_lens, scales, s, y, tstart, tlit, flags, dec_map, dec_first,
-                                        chunk_tickets, ctrl, status);
-    });
+    const DecState ds = dec_state_single(l, static_cast<char*>(ws));
+    if (accumulate) return launch_decode(p, 1, kDecodeAdd, in, 0, in_lens, scales, s, y, 0, ds, status, nullptr, st);
+    const bool dense = hint && reinterpret_cast<volatile uint32_t*>(hint)[0] != 0u;
+    rc = launch_decode(p, 1, dense ? kDecodeRecord : kDecodeWrite, in, 0, in_lens, scales, s, y,
+                       dense ? 0 : p.d.total, ds, status, dev_hint, st);
     if (rc || !dense) return rc;
+    const GroupView g = p.g;
+    const uint64_t etiles = p.d.etiles;
     return launch("tlc_expand", st, [&] {
         k_expand<<<xcd_grid((etiles + kWaves - 1) / kWaves), kThreads, 0, st>>>(g, (uint32_t)etiles, in, in_lens,
-                                                                                 scales, s, tstart, tlit, y, status);
+                                                                                 scales, s, ds.tstart, ds.tlit, y,
+                                                                                 status);
+    });
+}
+
+// Accumulate-many: the quartic bytes of every payload in one decoder launch,
+// then one pass over acc that applies them in payload order.
+int run_accumulate_many(const Plan& p, uint32_t payloads, const uint8_t* in, uint64_t in_stride,
+                        const uint64_t* in_lens, const float* scales, float s, float* acc, void* ws,
+                        size_t ws_bytes, int* status, hipStream_t st) {
+    if (!in || !in_lens || !scales || !acc || !status) return TLC_ERR_INVALID_ARG;
+    if (payloads == 0 || payloads > kMaxPayloads || !aligned16(acc) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
+    if (payloads > 1 && (in_stride < p.d.stream_bytes || (in_stride & 15))) return TLC_ERR_INVALID_ARG;
+    const ManyLayout ml = many_layout(p.d, payloads);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < ml.total) return TLC_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    DecState ds;
+    ds.ctrl = reinterpret_cast<uint32_t*>(w + ml.ctrl);
+    ds.flags = reinterpret_cast<uint64_t*>(w + ml.flags);
+    ds.map = reinterpret_cast<uint32_t*>(w + ml.map);
+    ds.first = reinterpret_cast<uint32_t*>(w + ml.first);
+    ds.tickets = reinterpret_cast<uint32_t*>(w + ml.tickets);
+    ds.tstart = nullptr;
+    ds.tlit = nullptr;
+    ds.qbuf = reinterpret_cast<uint8_t*>(w + ml.qbuf);
+    ds.yfl = reinterpret_cast<uint8_t*>(w + ml.yfl);
+    int rc = launch_decode(p, payloads, kDecodeQuartic, in, in_stride, in_lens, scales, s, nullptr, 0, ds, status,
+                           nullptr, st);
+    if (rc) return rc;
+    const GroupView g = p.g;
+    const uint64_t N = p.d.total;
+    return launch("tlc_apply", st, [&] {
+        k_apply<<<(uint32_t)yblocks_of(N), kThreads, 0, st>>>(g, N, payloads, ds.qbuf, p.d.stream_bytes, ds.yfl,
+                                                              scales, s, acc);
     });
 }
 
@@ -2415,25 +2721,41 @@ int tlc_server_compress(const float* acc, uint32_t workers, float* err, uint64_t
                         workspace_bytes, status, static_cast<hipStream_t>(stream));
 }
 
+// The device address of the caller's hint word (pinned host memory), or
+// nullptr; false if the word is not memory the device can reach.
+bool hint_word(uint32_t* host, uint32_t** dev) {
+    *dev = nullptr;
+    if (!host) return true;
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return false;
+    }
+    *dev = static_cast<uint32_t*>(d);
+    return true;
+}
+
 int tlc_decompress(const uint8_t* in, const uint64_t* in_len, const float* scale, uint64_t n, float s, float* y,
-                   void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream) {
+                   void* workspace, size_t workspace_bytes, int* status, uint32_t* path_hint, tlc_stream_t stream) {
     if (n == 0 || n > kMaxN) return TLC_ERR_INVALID_ARG;
-    return run_decompress(single_plan(n), in, in_len, scale, s, y, workspace, workspace_bytes, status,
-                          static_cast<hipStream_t>(stream), 0);
+    uint32_t* dev_hint;
+    if (!hint_word(path_hint, &dev_hint)) return TLC_ERR_INVALID_ARG;
+    return run_decompress(single_plan(n), in, in_len, scale, s, y, workspace, workspace_bytes, status, path_hint,
+                          dev_hint, static_cast<hipStream_t>(stream), 0);
 }
 
 int tlc_decompress_accumulate(const uint8_t* in, const uint64_t* in_len, const float* scale, uint64_t n, float s,
                               float* acc, void* workspace, size_t workspace_bytes, int* status,
                               tlc_stream_t stream) {
     if (n == 0 || n > kMaxN) return TLC_ERR_INVALID_ARG;
-    return run_decompress(single_plan(n), in, in_len, scale, s, acc, workspace, workspace_bytes, status,
-                          static_cast<hipStream_t>(stream), 1);
+    return run_decompress(single_plan(n), in, in_len, scale, s, acc, workspace, workspace_bytes, status, nullptr,
+                          nullptr, static_cast<hipStream_t>(stream), 1);
 }
 
 int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, void* table,
                    size_t table_capacity, uint64_t* stream_offset) {
     if (!sizes || !info || count == 0 || count > 0x7FFFFFFFull) return TLC_ERR_INVALID_ARG;
-    Dims d = {count, 0, 0, 0, 0, 0};
+    Dims d = {count, 0, 0, 0, 0, 0, 0};
     uint64_t stream = 0;
     for (uint64_t i = 0; i < count; ++i) {
         const uint64_t n = sizes[i];
@@ -2445,6 +2767,7 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
         stream = align_up(stream, 16) + tlc_compress_bound(n);
     }
     d.ftiles = ftiles_of(d.total);
+    d.stream_bytes = align_up(stream, 16);
     if (d.ftiles + d.count > 0xFFFFFFFFull || d.etiles > 0xFFFFFFFFull || d.chunks > 0xFFFFFFFFull)
         return TLC_ERR_INVALID_ARG;
     const TableLayout t = table_layout(d);
@@ -2462,6 +2785,8 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
     uint32_t* ftile_info = table ? reinterpret_cast<uint32_t*>(base + t.ftile_info) : nullptr;
     uint32_t* span_seg = table ? reinterpret_cast<uint32_t*>(base + t.span_seg) : nullptr;
     uint32_t* etile_seg = table ? reinterpret_cast<uint32_t*>(base + t.etile_seg) : nullptr;
+    char* const yrec = table ? base + t.yrec : nullptr;
+    uint64_t yb = 0;  // next y-block to describe
     if (table) {
         memset(base, 0, t.total);
         TableHeader h = {kMagic, count, d.ftiles, d.etiles, d.spans, d.chunks, d.total, info->stream_bytes};
@@ -2483,11 +2808,19 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
             memcpy(base + t.segs + i * sizeof(Seg), &sg, sizeof(Seg));
             for (uint64_t k = 0; k < spans_host(n); ++k) span_seg[span + k] = (uint32_t)i | (spans_host(n) > 1 ? kMulti : 0u);
             for (uint64_t k = 0; k < etiles_host(n); ++k) etile_seg[etile + k] = (uint32_t)i;
-            // flat tiles whose first element lies in this tensor
+            // flat tiles and y-blocks whose first element lies in this tensor
             const uint64_t end = eoff + n;
             for (; ft < d.ftiles && ft * kFTile < end; ++ft) {
                 const uint64_t last = std::min<uint64_t>(d.total, (ft + 1) * kFTile) - 1;
                 ftile_info[ft] = (uint32_t)i | (last >= end ? kStraddle : 0u);
+            }
+            for (; yb < yblocks_of(d.total) && yb * kYBlock < end; ++yb) {
+                const uint64_t last = std::min<uint64_t>(d.total, (yb + 1) * kYBlock) - 1;
+                YRec r;
+                r.qoff = soff;
+                r.u0 = (uint32_t)(yb * kYBlock - eoff);
+                r.gi = (uint32_t)i | (last >= end ? kStraddle : 0u);
+                memcpy(yrec + yb * sizeof(YRec), &r, sizeof(YRec));
             }
         }
         etile += etiles_host(n);
@@ -2543,11 +2876,13 @@ int tlc_server_compress_group(const tlc_group_info* info, const void* d_table, c
 
 int tlc_decompress_group(const tlc_group_info* info, const void* d_table, const uint8_t* in,
                          const uint64_t* in_lens, const float* scales, float s, float* y, void* workspace,
-                         size_t workspace_bytes, int* status, tlc_stream_t stream) {
+                         size_t workspace_bytes, int* status, uint32_t* path_hint, tlc_stream_t stream) {
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_decompress(p, in, in_lens, scales, s, y, workspace, workspace_bytes, status,
+    uint32_t* dev_hint;
+    if (!hint_word(path_hint, &dev_hint)) return TLC_ERR_INVALID_ARG;
+    return run_decompress(p, in, in_lens, scales, s, y, workspace, workspace_bytes, status, path_hint, dev_hint,
                           static_cast<hipStream_t>(stream), 0);
 }
 
@@ -2557,8 +2892,24 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_decompress(p, in, in_lens, scales, s, acc, workspace, workspace_bytes, status,
+    return run_decompress(p, in, in_lens, scales, s, acc, workspace, workspace_bytes, status, nullptr, nullptr,
                           static_cast<hipStream_t>(stream), 1);
+}
+
+uint64_t tlc_accumulate_many_workspace_size(const tlc_group_info* info, uint32_t payloads) {
+    if (!info || info->count == 0 || payloads == 0 || payloads > kMaxPayloads) return 0;
+    return many_layout(dims_of(info), payloads).total;
+}
+
+int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void* d_table, uint32_t payloads,
+                                         const uint8_t* in, uint64_t in_stride, const uint64_t* in_lens,
+                                         const float* scales, float s, float* acc, void* workspace,
+                                         size_t workspace_bytes, int* status, tlc_stream_t stream) {
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_accumulate_many(p, payloads, in, in_stride, in_lens, scales, s, acc, workspace, workspace_bytes,
+                               status, static_cast<hipStream_t>(stream));
 }
 
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream) {
@@ -2587,13 +2938,6 @@ int tlc_planes_scatter(const float* src, const uint64_t* src_off, float* dst, co
 int tlc_profile_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_on = enable != 0;
-    return TLC_OK;
-}
-
-int tlc_set_decode_policy(int policy) {
-    if (policy != TLC_DECODE_AUTO && policy != TLC_DECODE_SPARSE && policy != TLC_DECODE_DENSE)
-        return TLC_ERR_INVALID_ARG;
-    g_decode_policy.store(policy, std::memory_order_relaxed);
     return TLC_OK;
 }
 

@@ -66,22 +66,24 @@ _SIGS = {
     "tlc_decompress_fixed": (_I, [_P, _P, _U64, _F, _I, _P, _P, _P]),
     "tlc_compress_fixed_group": (_I, [ctypes.POINTER(GroupInfo), _P, _I, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "tlc_decompress_fixed_group": (_I, [ctypes.POINTER(GroupInfo), _P, _I, _P, _P, _P, _F, _P, _P, _P]),
-    "tlc_decompress": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P, _P]),
     "tlc_decompress_accumulate": (_I, [_P, _P, _P, _U64, _F, _P, _P, _SZ, _P, _P]),
     "tlc_group_plan": (_I, [_P, _U64, ctypes.POINTER(GroupInfo), _P, _SZ, _P]),
     "tlc_compress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "tlc_server_compress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U32, _P, _F, _P, _P, _P, _P, _SZ,
                                        _P, _P]),
-    "tlc_decompress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ, _P, _P]),
+    "tlc_decompress_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ, _P, _P, _P]),
     "tlc_decompress_accumulate_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _F, _P, _P, _SZ,
                                              _P, _P]),
+    "tlc_accumulate_many_workspace_size": (_U64, [ctypes.POINTER(GroupInfo), _U32]),
+    "tlc_decompress_accumulate_many_group": (_I, [ctypes.POINTER(GroupInfo), _P, _U32, _P, _U64, _P, _P, _F, _P,
+                                                  _P, _SZ, _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_copy_probe": (_I, [_P, _P, _U64, _P]),
     "tlc_profile_enable": (_I, [_I]),
     "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
     "tlc_profile_only": (_I, [ctypes.c_char_p]),
-    "tlc_set_decode_policy": (_I, [_I]),
 }
 
 
@@ -127,6 +129,23 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def path_hint() -> torch.Tensor:
+    """A decompress path hint word: one uint32 (held as int32) in pinned host
+    memory, starting at 0 (the sparse sequence).  Pass the same tensor to
+    every decompress of a stream of steps; the device keeps it up to date."""
+    return torch.zeros(1, dtype=torch.int32, pin_memory=True)
+
+
+def _hint_ptr(h: torch.Tensor | None):
+    if h is None:
+        return None
+    if h.is_cuda or not h.is_pinned():
+        raise ValueError("path_hint must be a pinned host tensor (tlc.path_hint())")
+    if h.dtype != torch.int32 or h.numel() < 1 or not h.is_contiguous():
+        raise ValueError("path_hint must hold one contiguous int32")
+    return ctypes.c_void_p(h.data_ptr())
 
 
 def _need(t: torch.Tensor | None, count: int, name: str):
@@ -305,10 +324,11 @@ def decompress_fixed(inp: torch.Tensor, scale: torch.Tensor, n: int, s: float, e
 
 
 def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: int, s: float, *, y=None,
-               workspace=None, status=None, stream=None):
+               workspace=None, status=None, path_hint=None, stream=None):
     """Returns (y, status).  inp holds at least ceil(n/5) bytes (the capacity
     tlc_compress writes into), so that no device length can send a read past
-    its end."""
+    its end.  path_hint: None (sparse sequence) or a tensor from
+    tlc.path_hint(), read on entry and rewritten by the device."""
     dev = inp.device
     y = y if y is not None else torch.empty(n, dtype=torch.float32, device=dev)
     status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
@@ -321,7 +341,7 @@ def decompress(inp: torch.Tensor, in_len: torch.Tensor, scale: torch.Tensor, n: 
     rc = lib().tlc_decompress(_ptr(inp, torch.uint8, "in"), _ptr(in_len, torch.int64, "in_len"),
                               _ptr(scale, torch.float32, "scale"), n, s, _ptr(y, torch.float32, "y"),
                               _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                              _ptr(status, torch.int32, "status"), _stream(stream))
+                              _ptr(status, torch.int32, "status"), _hint_ptr(path_hint), _stream(stream))
     _check(rc, "tlc_decompress")
     return y, status
 
@@ -497,8 +517,9 @@ class Group:
         _check(rc, "tlc_decompress_fixed_group")
         return y, status
 
-    def decompress(self, inp, in_lens, scales, s, *, y=None, workspace=None, status=None, stream=None):
-        """Returns (y, status)."""
+    def decompress(self, inp, in_lens, scales, s, *, y=None, workspace=None, status=None, path_hint=None,
+                   stream=None):
+        """Returns (y, status).  path_hint as for decompress()."""
         dev = self.device
         y = y if y is not None else torch.empty(self.total, dtype=torch.float32, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
@@ -508,7 +529,8 @@ class Group:
                                         _ptr(inp, torch.uint8, "in"), _ptr(in_lens, torch.int64, "in_lens"),
                                         _ptr(scales, torch.float32, "scales"), s, _ptr(y, torch.float32, "y"),
                                         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                        _ptr(status, torch.int32, "status"), _stream(stream))
+                                        _ptr(status, torch.int32, "status"), _hint_ptr(path_hint),
+                                        _stream(stream))
         _check(rc, "tlc_decompress_group")
         return y, status
 
@@ -524,6 +546,42 @@ class Group:
             _ptr(acc, torch.float32, "acc"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
             _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_decompress_accumulate_group")
+        return acc, status
+
+    def accumulate_many_workspace_size(self, payloads: int) -> int:
+        nb = int(lib().tlc_accumulate_many_workspace_size(ctypes.byref(self.info), int(payloads)))
+        if nb == 0:
+            raise ValueError(f"payloads must be 1..64, got {payloads}")
+        return nb
+
+    def decompress_accumulate_many(self, inp, in_lens, scales, s, acc, *, payloads=None, workspace=None,
+                                   status=None, stream=None):
+        """tlc_decompress_accumulate_many_group: payload p's streams in
+        inp[p] (a uint8 tensor of shape (payloads, stream_bytes) or a flat
+        one of payloads * stream_bytes), its lengths and scales in row p of
+        in_lens / scales (payloads x count); acc += every payload's values in
+        payload order.  Returns (acc, status)."""
+        dev = self.device
+        P = int(payloads if payloads is not None else (inp.shape[0] if inp.dim() == 2 else 1))
+        stride = int(inp.shape[1]) if inp.dim() == 2 else self.stream_bytes
+        if P < 1 or P > 64:
+            raise ValueError(f"payloads must be 1..64, got {P}")
+        if P > 1 and (stride < self.stream_bytes or stride % 16):
+            raise ValueError("each payload's stream buffer needs stream_bytes bytes at a 16-byte multiple stride")
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        _need(inp, (P - 1) * stride + self.stream_bytes, "in")
+        _need(in_lens, P * self.count, "in_lens")
+        _need(scales, P * self.count, "scales")
+        _need(acc, self.total, "acc")
+        _need(status, 1, "status")
+        wsb = self.accumulate_many_workspace_size(P)
+        workspace = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+        rc = lib().tlc_decompress_accumulate_many_group(
+            ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"), P, _ptr(inp, torch.uint8, "in"),
+            stride, _ptr(in_lens, torch.int64, "in_lens"), _ptr(scales, torch.float32, "scales"), s,
+            _ptr(acc, torch.float32, "acc"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_decompress_accumulate_many_group")
         return acc, status
 
 
@@ -559,15 +617,6 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
 
 def profile_enable(on: bool = True):
     _check(lib().tlc_profile_enable(1 if on else 0), "tlc_profile_enable")
-
-
-DECODE_AUTO, DECODE_SPARSE, DECODE_DENSE = 0, 1, 2
-
-
-def set_decode_policy(policy: int):
-    """Decompress launch sequence (tlc_set_decode_policy): DECODE_AUTO, or
-    DECODE_SPARSE / DECODE_DENSE to force one; the output is the same."""
-    _check(lib().tlc_set_decode_policy(int(policy)), "tlc_set_decode_policy")
 
 
 def profile_only(kernel_name: str | None):

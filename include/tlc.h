@@ -28,14 +28,12 @@
  *     stream) and the call returns without synchronising.  Results written to
  *     device memory (out_len, scale, status, ...) are valid once the stream
  *     reaches that point.
- *   - The library never allocates, frees or synchronises device memory; the
- *     caller owns every buffer.  (Its one allocation is 256 bytes of pinned
- *     host memory per device, made at the first decompress on that device
- *     and kept until the process ends: the decode-path hints of
- *     tlc_set_decode_policy.)  Scratch memory is the caller's `workspace`
- *     (device, 256-byte aligned, at least the size the *_workspace_size call
- *     returns; its contents need not survive between calls).  Calls that may
- *     run at the same time need separate workspaces and separate status
+ *   - The library never allocates, frees or synchronises memory; the caller
+ *     owns every buffer.  Scratch memory is the caller's `workspace` (device,
+ *     256-byte aligned, at least the size the *_workspace_size call returns;
+ *     its contents need not survive between calls), except for
+ *     tlc_compress_static, whose scratch is a fixed device array.  Calls that
+ *     may run at the same time need separate workspaces and separate status
  *     words.
  *   - fp32 buffers (x, err, y, acc) must be 16-byte aligned and must not
  *     alias each other or the byte streams.
@@ -79,11 +77,15 @@ const char* tlc_status_string(int code);
 /* Library version string.  Host only. */
 const char* tlc_version(void);
 
-/* Bytes a compressed stream of n values can take: ceil(n/5) (zero-run
- * encoding never expands the quartic bytes).  Host only; 0 for n == 0. */
+/* Bytes a compressed stream of n values can take: ceil(n/5), the quartic
+ * bytes of n values ("Proposed method", second item), since the zero-run
+ * encoding (third item) never makes them longer.  Host only; 0 for n == 0. */
 uint64_t tlc_compress_bound(uint64_t n);
 
-/* Workspace bytes for any single-tensor call on n values.  Host only. */
+/* Workspace bytes for any single-tensor call on n values (compress,
+ * decompress, accumulate): the per-tile state of the page's compress steps
+ * ("Proposed method", first to third items) and of their reverse.  Host
+ * only; 0 for n == 0 or n > 2^32-1. */
 size_t tlc_workspace_size(uint64_t n);
 
 /* Compress one tensor (all steps of the 3LC compress path).
@@ -165,18 +167,38 @@ int tlc_server_compress(const float* acc, uint32_t workers, float* err, uint64_t
                         uint8_t* out, uint64_t out_capacity, uint64_t* out_len, float* scale,
                         void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
 
-/* Decompress one tensor: y[i] = q_i * (M*s) for i < n, with q decoded from
- * the stream in[0 .. *in_len) (device length, so no host round trip is
- * needed after tlc_compress).  `in` must be readable for *in_len bytes.
- * scale: device fp32 M.  A stream that does not expand to exactly ceil(n/5)
- * bytes sets *status = TLC_ERR_CORRUPT (y is then partly written). */
+/* Decompress one tensor: the reverse of the page's encodings ("Proposed
+ * method", second and third items): the zero-run codes expanded back into
+ * quartic bytes, each quartic byte split into its five ternary codes, and
+ * y[i] = q_i * (M*s) for i < n.  The stream is in[0 .. *in_len) (device
+ * length, so no host round trip is needed after tlc_compress); `in` must be
+ * readable for min(*in_len, ceil(n/5)) bytes.  scale: device fp32 M.  A
+ * stream that does not expand to exactly ceil(n/5) bytes sets *status =
+ * TLC_ERR_CORRUPT (y is then partly written).
+ *   path_hint   optional (NULL allowed): a uint32 the caller owns in pinned
+ *               host memory (hipHostMalloc), which selects one of two launch
+ *               sequences that give the same y bit for bit.  On entry the host
+ *               reads it: 0 = sparse (zero fill of y, then the nonzero codes
+ *               written over it; fastest while few 5120-value tiles hold a
+ *               nonzero code), 1 = dense (every tile decoded and written once;
+ *               fastest for streams longer than about 0.104 bytes per quartic
+ *               byte, reached after some tens of steps of error feedback).  The
+ *               call's first kernel then overwrites it with the class of this
+ *               call's streams, so passing the same word every step makes each
+ *               decompress follow the previous one's density without a host
+ *               synchronisation.  NULL: the sparse sequence.  Memory the device
+ *               cannot reach returns TLC_ERR_INVALID_ARG.  A word shared by
+ *               calls in flight at once only changes which sequence runs. */
 int tlc_decompress(const uint8_t* in, const uint64_t* in_len, const float* scale,
                    uint64_t n, float s, float* y,
-                   void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+                   void* workspace, size_t workspace_bytes, int* status, uint32_t* path_hint,
+                   tlc_stream_t stream);
 
 /* As tlc_decompress, but acc[i] += q_i * (M*s) where q_i != 0; every other
- * element of acc keeps its bits.  Applying the payloads of several workers
- * one call after another gives their sum in call order. */
+ * element of acc keeps its bits.  This is the receiving side of the page's
+ * exchange of compressed state changes ("Proposed method", first and fourth
+ * items: the receivers apply the decoded changes).  Applying the payloads of
+ * several workers one call after another gives their sum in call order. */
 int tlc_decompress_accumulate(const uint8_t* in, const uint64_t* in_len, const float* scale,
                               uint64_t n, float s, float* acc,
                               void* workspace, size_t workspace_bytes, int* status,
@@ -239,11 +261,12 @@ int tlc_server_compress_group(const tlc_group_info* info, const void* d_table,
 
 /* Grouped decompress into flat y[info->total_elems].  in: the grouped stream
  * buffer laid out as by tlc_compress_group; in_lens: device uint64[count];
- * scales: device fp32[count]. */
+ * scales: device fp32[count]; path_hint as for tlc_decompress (the density
+ * class is that of the whole group's streams). */
 int tlc_decompress_group(const tlc_group_info* info, const void* d_table,
                          const uint8_t* in, const uint64_t* in_lens, const float* scales, float s,
                          float* y, void* workspace, size_t workspace_bytes, int* status,
-                         tlc_stream_t stream);
+                         uint32_t* path_hint, tlc_stream_t stream);
 
 /* Grouped decompress-and-accumulate into flat acc[info->total_elems]. */
 int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_table,
@@ -251,6 +274,35 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
                                     const float* scales, float s, float* acc,
                                     void* workspace, size_t workspace_bytes, int* status,
                                     tlc_stream_t stream);
+
+/* Decompress-and-accumulate several payloads of one group into acc in one
+ * launch sequence: for p = 0 .. payloads-1 in that order, acc[i] +=
+ * q_{p,i} * (M_{p,t}*s) where q_{p,i} != 0; the result is bit for bit that
+ * of `payloads` tlc_decompress_accumulate_group calls in order.  This is the
+ * receiving side of the page's exchange ("Proposed method", first and fourth
+ * items) for many senders: every payload's quartic bytes are decoded into
+ * the workspace in one launch, then acc is read and written once, skipping
+ * every 1024-value block where no payload has a nonzero code.
+ *   payloads       1 .. 64.
+ *   in             payload p's stream buffer (laid out as by
+ *                  tlc_compress_group) at in + p * in_stride; in_stride >=
+ *                  info->stream_bytes and a multiple of 16 (ignored for one
+ *                  payload).
+ *   in_lens        device uint64[payloads * count], payload p's lengths at
+ *                  in_lens + p * count.
+ *   scales         device fp32[payloads * count], likewise.
+ *   acc            flat fp32[info->total_elems], updated in place.
+ *   workspace      at least tlc_accumulate_many_workspace_size(info,
+ *                  payloads) bytes (about payloads * (stream_bytes +
+ *                  total_elems / 1024)).
+ * Errors as for tlc_decompress_accumulate_group; TLC_ERR_INVALID_ARG for
+ * payloads outside 1 .. 64 or a bad in_stride. */
+uint64_t tlc_accumulate_many_workspace_size(const tlc_group_info* info, uint32_t payloads);
+int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void* d_table, uint32_t payloads,
+                                         const uint8_t* in, uint64_t in_stride, const uint64_t* in_lens,
+                                         const float* scales, float s, float* acc,
+                                         void* workspace, size_t workspace_bytes, int* status,
+                                         tlc_stream_t stream);
 
 /* ---- five-plane byte layout (ablation) --------------------------------------
  * The 3LC page ("Proposed method", second item) packs five ternary values per
@@ -285,25 +337,6 @@ int tlc_planes_scatter(const float* src, const uint64_t* src_off, float* dst, co
 /* Streaming copy of `bytes` bytes (a multiple of 16, both pointers 16-byte
  * aligned): the achievable-HBM-bandwidth yardstick for the codec kernels. */
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream);
-
-/* Which of two launch sequences decompress (not accumulate) uses; both give
- * the same y, bit for bit, so this is a performance setting only.
- *   TLC_DECODE_SPARSE  zero fill of y, then the nonzero codes written over it:
- *                      fastest while few encode tiles hold a nonzero code.
- *   TLC_DECODE_DENSE   every encode tile decoded in LDS and written once:
- *                      fastest once most tiles do (streams longer than about
- *                      0.104 bytes per quartic byte, where runs of zeros
- *                      alone give 1/14 = 0.071; reached after some tens of
- *                      steps of error feedback).
- *   TLC_DECODE_AUTO    (default) the host cannot see the stream lengths
- *                      without a synchronisation, so it takes the path that
- *                      suits the streams of the previous decompress on the
- *                      same workspace (the device leaves that density in a
- *                      word of pinned host memory, one of 64 per device
- *                      chosen by the workspace address); sparse at first.
- * Process-wide, host only; returns TLC_ERR_INVALID_ARG for another value. */
-enum tlc_decode_policy { TLC_DECODE_AUTO = 0, TLC_DECODE_SPARSE = 1, TLC_DECODE_DENSE = 2 };
-int tlc_set_decode_policy(int policy);
 
 /* Kernel timing with HIP events.  While enabled, every kernel the library
  * launches is bracketed by two events recorded on the same stream.

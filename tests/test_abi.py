@@ -91,6 +91,21 @@ def test_group_plan_layout():
         first, last = t * 512, min(N, (t + 1) * 512) - 1
         want = int(seg_of[first]) | (0x80000000 if seg_of[last] != seg_of[first] else 0)
         assert int(info_arr[t]) == want, t
+    # per 1024-element block (after the span owners and the encode-tile owners): the stream slot of
+    # its first element's tensor, that element's index in it, the tensor, high bit if the block
+    # also holds a later tensor
+    up = lambda v: -(-v // 16) * 16
+    span_at = up(fi_at + 4 * ftiles)
+    et_at = up(span_at + 4 * spans)
+    y_at = up(et_at + 4 * etiles)
+    yb = -(-N // 1024)
+    assert info.table_bytes == up(y_at + 16 * yb)
+    yrec = np.frombuffer(table[y_at:y_at + 16 * yb], dtype=np.dtype([("qoff", "<u8"), ("u0", "<u4"), ("gi", "<u4")]))
+    for b in range(yb):
+        first, last = b * 1024, min(N, (b + 1) * 1024) - 1
+        t = int(seg_of[first])
+        assert int(yrec["qoff"][b]) == offs[t] and int(yrec["u0"][b]) == first - int(starts[t]), b
+        assert int(yrec["gi"][b]) == t | (0x80000000 if seg_of[last] != t else 0), b
 
 
 def test_group_plan_rejects_bad_sizes():
@@ -138,9 +153,9 @@ def test_argument_errors_return_before_any_launch():
     assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, V(0x20010), 4096, fake,
                           None) == tlc.ERR_WORKSPACE
     assert L.tlc_compress(fake, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, None, None) == tlc.ERR_INVALID_ARG
-    assert L.tlc_decompress(fake, fake, fake, 0, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
-    assert L.tlc_decompress(fake, fake, fake, 10, 1.5, odd, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
-    assert L.tlc_decompress(fake, None, fake, 10, 1.5, fake, ws, 4096, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, fake, fake, 0, 1.5, fake, ws, 4096, fake, None, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, fake, fake, 10, 1.5, odd, ws, 4096, fake, None, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress(fake, None, fake, 10, 1.5, fake, ws, 4096, fake, None, None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_accumulate(fake, fake, fake, 10, 1.99, fake, ws, 1, fake, None) == tlc.ERR_WORKSPACE
     assert L.tlc_copy_probe(fake, fake, 17, None) == tlc.ERR_INVALID_ARG
     # fixed-length encodings: lengths, unknown encodings, capacity
@@ -169,7 +184,7 @@ def test_argument_errors_return_before_any_launch():
                                 None) == tlc.ERR_INVALID_ARG
     assert L.tlc_compress_group(ctypes.byref(info), None, fake, fake, 1.5, fake, fake, fake, ws, 1 << 20, fake,
                                 None) == tlc.ERR_INVALID_ARG
-    assert L.tlc_decompress_group(ctypes.byref(info), fake, fake, fake, fake, 1.5, fake, ws, 16, fake,
+    assert L.tlc_decompress_group(ctypes.byref(info), fake, fake, fake, fake, 1.5, fake, ws, 16, fake, None,
                                   None) == tlc.ERR_WORKSPACE
     assert L.tlc_server_compress_group(ctypes.byref(info), fake, fake, 0, fake, 1.5, fake, fake, fake, ws,
                                        1 << 20, fake, None) == tlc.ERR_INVALID_ARG
@@ -186,12 +201,55 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         tlc.lib()
 
 
-def test_decode_policy_argument_check():
-    for p in (tlc.DECODE_SPARSE, tlc.DECODE_DENSE, tlc.DECODE_AUTO):
-        tlc.set_decode_policy(p)
-    for bad in (-1, 3, 99):
-        assert tlc.lib().tlc_set_decode_policy(bad) == tlc.ERR_INVALID_ARG
-    tlc.set_decode_policy(tlc.DECODE_AUTO)
+def test_accumulate_many_host_checks():
+    # workspace size and argument errors of the many-payload accumulate, all
+    # decided before any launch
+    L = tlc.lib()
+    V = ctypes.c_void_p
+    fake, ws = V(0x10000), V(0x20000)
+    sizes = [100, 200, 5121]
+    info, _, _ = tlc.group_plan(sizes)
+    N, C = int(info.total_elems), len(sizes)
+    one = L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 1)
+    eight = L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 8)
+    assert one > 0 and eight > 0 and one % 256 == 0 and eight % 256 == 0
+    # per payload: its quartic bytes in the stream layout and a flag byte per 1024 values, plus the
+    # decoder's state
+    yb = -(-N // 1024)
+    assert eight >= 8 * (int(info.stream_bytes) + yb)
+    assert eight - one == 7 * (eight - one) // 7
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 0) == 0
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 65) == 0
+    SB = int(info.stream_bytes)
+
+    def call(P, stride, ws_bytes, s=1.5, acc=fake):
+        return L.tlc_decompress_accumulate_many_group(ctypes.byref(info), fake, P, fake, stride, fake, fake, s,
+                                                      acc, ws, ws_bytes, fake, None)
+    assert call(0, SB, eight) == tlc.ERR_INVALID_ARG
+    assert call(65, SB, 1 << 40) == tlc.ERR_INVALID_ARG
+    assert call(8, SB - 16, eight) == tlc.ERR_INVALID_ARG    # payload buffers would overlap
+    assert call(8, SB + 8, eight) == tlc.ERR_INVALID_ARG     # stride not a multiple of 16
+    assert call(8, SB, eight - 256) == tlc.ERR_WORKSPACE
+    assert call(8, SB, eight, s=2.0) == tlc.ERR_INVALID_ARG
+    assert call(8, SB, eight, acc=V(0x10004)) == tlc.ERR_INVALID_ARG
+    # the binding's own checks
+    import torch
+    g = tlc.Group(sizes, device="cpu")
+    with pytest.raises(ValueError, match="stream buffer needs"):
+        g.decompress_accumulate_many(torch.zeros((8, SB - 16), dtype=torch.uint8), torch.zeros(8 * C, dtype=torch.int64),
+                                     torch.zeros(8 * C), 1.5, torch.zeros(N))
+    with pytest.raises(ValueError, match="in holds"):
+        g.decompress_accumulate_many(torch.zeros(8 * SB - 1, dtype=torch.uint8), torch.zeros(8 * C, dtype=torch.int64),
+                                     torch.zeros(8 * C), 1.5, torch.zeros(N), payloads=8)
+    with pytest.raises(ValueError, match="in_lens holds"):
+        g.decompress_accumulate_many(torch.zeros((8, SB), dtype=torch.uint8), torch.zeros(8 * C - 1, dtype=torch.int64),
+                                     torch.zeros(8 * C), 1.5, torch.zeros(N))
+    with pytest.raises(ValueError, match="acc holds"):
+        g.decompress_accumulate_many(torch.zeros((2, SB), dtype=torch.uint8), torch.zeros(2 * C, dtype=torch.int64),
+                                     torch.zeros(2 * C), 1.5, torch.zeros(N - 1))
+    with pytest.raises(ValueError, match="payloads"):
+        g.decompress_accumulate_many(torch.zeros((65, SB), dtype=torch.uint8), torch.zeros(65 * C, dtype=torch.int64),
+                                     torch.zeros(65 * C), 1.5, torch.zeros(N))
 
 
 def test_static_compress_rejects_n_above_its_maximum():

@@ -7,7 +7,8 @@ benchmark uses (grouped calls over the whole gradient set):
 * resnet50     161 tensors, s in {1.0, 1.5, 1.9}, error reset for each s
 * bert_large   391 tensors, workers 0..7 (seed 500+w) each compressed from a
                zero error buffer, then the 8 payloads decompress-accumulated in
-               order into one fp32 sum, and the server's compress of their mean
+               order into one fp32 sum (one call per payload, and all eight in
+               one many-payload call), and the server's compress of their mean
 
 Everything is compared bit for bit with the CPU oracle: every tensor's stream
 and length, M, the error buffer, the decompressed values and the sum.  The
@@ -93,6 +94,9 @@ def test_bert_large_eight_workers_accumulate():
     acc_h = np.zeros(N, np.float32)
     x = np.empty(N, np.float32)
     ws = g.workspace()
+    pay = torch.empty((8, g.stream_bytes), dtype=torch.uint8, device="cuda:0")  # the 8 workers' payloads
+    pay_lens = torch.empty((8, len(sizes)), dtype=torch.int64, device="cuda:0")
+    pay_scales = torch.empty((8, len(sizes)), dtype=torch.float32, device="cuda:0")
     hint = None  # worker 0: zeros; worker w > 0: worker w-1's M
     for wk in range(8):
         say(f"case bert_large worker {wk}: generate")
@@ -103,6 +107,9 @@ def test_bert_large_eight_workers_accumulate():
         out, lens, scales, (streams, Ms) = check_group(g, x, zero, s, label=f"bert_large worker {wk}", want=want,
                                                        hint=hint)
         hint = Ms
+        pay[wk].copy_(out)
+        pay_lens[wk].copy_(lens)
+        pay_scales[wk].copy_(scales)
         _, st = g.decompress_accumulate(out, lens, scales, s, acc_d, workspace=ws)
         off = 0
         for t, n in enumerate(sizes):
@@ -113,6 +120,14 @@ def test_bert_large_eight_workers_accumulate():
         del out, lens, scales
     say("case bert_large: 8-payload sum")
     assert np.array_equal(bits(acc_d.cpu().numpy()), bits(acc_h))
+    # the same eight payloads in one many-payload call from a zero sum
+    say("case bert_large: 8 payloads in one call")
+    acc_m = torch.zeros(N, dtype=torch.float32, device="cuda:0")
+    _, st = g.decompress_accumulate_many(pay, pay_lens.view(-1), pay_scales.view(-1), s, acc_m)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(bits(acc_m.cpu().numpy()), bits(acc_h))
+    del acc_m, pay
     # model-delta direction: the server compresses the workers' mean with its
     # own (zero) error buffer; every tensor's stream, M and error bit for bit
     say("case bert_large: server compress of the 8-worker mean")

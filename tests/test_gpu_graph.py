@@ -4,18 +4,29 @@ replays and the error buffer carried, must give the same stream bytes,
 lengths, M, error buffer and y as the same calls made eagerly on a second set
 of buffers, and the last replay must match the CPU oracle.  The library
 launches only kernels on the caller's stream (no memset nodes, no host
-synchronisation), so the captured step is the eager one."""
+synchronisation, no allocation), so the captured step is the eager one, and
+it can be captured before any eager call: the second test captures it as the
+first use of the library in a fresh process.  Both decompress launch
+sequences are captured (a path hint word holding 0, then 1, at capture; the
+eager calls get a word holding the same value each step)."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 
-import oracle
+if __name__ == "__main__":  # run as a script: the repository root on the path
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
-from gpu_util import bits, oracle_group_compress, say, to_dev
+import oracle  # noqa: E402
+
+from gpu_util import bits, oracle_group_compress, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager_and_oracle():
+def scenario(warm_up: bool, path: int):
     import torch
     from gradient_compression_distributed_lc_amd import tlc
     rng = np.random.default_rng(123)
@@ -33,12 +44,15 @@ def test_graph_replays_match_eager_and_oracle():
                     scales=torch.zeros(len(sizes), dtype=torch.float32, device=dev),
                     st_c=torch.empty(1, dtype=torch.int32, device=dev),
                     st_d=torch.empty(1, dtype=torch.int32, device=dev),
-                    ws=g.workspace())
+                    ws=g.workspace(),
+                    hint=tlc.path_hint())
 
     def step(g, b):  # on torch's current stream
+        b["hint"][0] = path  # read on entry (at capture, for the graph)
         g.compress(b["x"], b["err"], s, out=b["out"], out_lens=b["lens"], scales=b["scales"], workspace=b["ws"],
                    status=b["st_c"])
-        g.decompress(b["out"], b["lens"], b["scales"], s, y=b["y"], workspace=b["ws"], status=b["st_d"])
+        g.decompress(b["out"], b["lens"], b["scales"], s, y=b["y"], workspace=b["ws"], status=b["st_d"],
+                     path_hint=b["hint"])
 
     g = tlc.Group(sizes)
     gb, eb = buffers(g), buffers(g)
@@ -47,12 +61,12 @@ def test_graph_replays_match_eager_and_oracle():
         x = (rng.standard_normal(N) * 1e-3).astype(np.float32)
         x[rng.random(N) < 0.3] = 0
         inputs.append(x)
-    # warm-up outside capture (one-time set-up: occupancy queries, decode-path hint memory)
-    step(g, gb)
-    torch.cuda.synchronize()
-    gb["err"].zero_()
-    gb["scales"].zero_()
-    torch.cuda.synchronize()
+    if warm_up:  # an eager step before the capture (then undone)
+        step(g, gb)
+        torch.cuda.synchronize()
+        gb["err"].zero_()
+        gb["scales"].zero_()
+        torch.cuda.synchronize()
 
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -68,7 +82,7 @@ def test_graph_replays_match_eager_and_oracle():
 
     err_h = np.zeros(N, np.float32)
     for k, x in enumerate(inputs):
-        say(f"case graph replay {k}")
+        say(f"case graph replay {k}, decompress sequence {path}")
         xd = to_dev(x)
         gb["x"].copy_(xd)
         eb["x"].copy_(xd)
@@ -97,3 +111,24 @@ def test_graph_replays_match_eager_and_oracle():
             for t in range(len(sizes)):
                 o = g.offsets[t]
                 assert lens[t] == streams[t].size and np.array_equal(out_g[o:o + lens[t]], streams[t]), t
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_graph_replays_match_eager_and_oracle(path):
+    scenario(warm_up=True, path=path)
+
+
+@pytest.mark.timeout(300)
+def test_graph_captured_before_any_eager_call():
+    # a fresh process: the capture is the library's first use there
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "test_gpu_graph.py")], capture_output=True, text=True,
+                       timeout=240)
+    say(r.stdout[-2000:])
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "graph scenario ok" in r.stdout
+
+
+if __name__ == "__main__":
+    scenario(warm_up=False, path=1)
+    print("graph scenario ok", flush=True)

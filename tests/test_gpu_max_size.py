@@ -1,6 +1,8 @@
 """GPU parity at the largest tensor the library takes: n = 2^32 - 1 fp32
-values (16 GiB), one compress, a decompress on each of the two decode paths
-and an accumulate, through the C ABI.
+values (16 GiB): compress (with a zero hint and with the exact M), decompress
+on both launch sequences (sparse, and dense through a path hint word of 1),
+accumulate, and the many-payload accumulate of the stream twice, through the
+C ABI.
 
 The input is a zero tensor with seeded spikes (first and last element
 included), so the oracle's results are computed exactly without holding the
@@ -87,17 +89,17 @@ def test_max_size_tensor():
     want_y = oracle.decompress(small, M, val.size, s)
     assert np.array_equal(bits(y[ti].cpu().numpy()), bits(want_y))
     assert int(torch.count_nonzero(y).item()) == int(nz.sum())
-    # the dense path on the same stream (its tile records hold 32-bit byte
-    # offsets within the tensor, largest here): the same y
-    say("case max size: decompress ok, dense path")
+    # the dense sequence on the same stream (its tile records hold 32-bit
+    # byte offsets within the tensor, largest here): the same y; the device
+    # then writes the stream's class (sparse) into the hint word
+    say("case max size: decompress ok, dense sequence")
     y.fill_(1.0)
-    tlc.set_decode_policy(tlc.DECODE_DENSE)
-    try:
-        y, st = tlc.decompress(c.out, c.out_len, c.scale, n, s, y=y)
-        torch.cuda.synchronize()
-    finally:
-        tlc.set_decode_policy(tlc.DECODE_AUTO)
+    h = tlc.path_hint()
+    h[0] = 1
+    y, st = tlc.decompress(c.out, c.out_len, c.scale, n, s, y=y, workspace=ws, path_hint=h)
+    torch.cuda.synchronize()
     assert int(st.item()) == 0
+    assert int(h[0]) == 0
     assert np.array_equal(bits(y[ti].cpu().numpy()), bits(want_y))
     assert int(torch.count_nonzero(y).item()) == int(nz.sum())
     del y
@@ -110,5 +112,24 @@ def test_max_size_tensor():
     # the oracle's accumulate over the spikes alone: elements without a spike
     # hold 0 and get nothing added
     exp = oracle.decompress_accumulate(small, M, val.size, s, e_sp.copy())
+    assert np.array_equal(bits(acc[ti].cpu().numpy()), bits(exp))
+    assert int(torch.count_nonzero(acc).item()) == int(np.count_nonzero(exp))
+
+    # the many-payload accumulate at the same size: the stream twice, as two
+    # payloads (y-block words and code bytes at offsets past 2^30)
+    say("case max size: accumulate ok, two payloads in one call")
+    B = tlc.compress_bound(n)
+    stride = -(-B // 16) * 16
+    two = torch.empty(2 * stride, dtype=torch.uint8, device=dev)
+    two[:B].copy_(c.out[:B])
+    two[stride:stride + B].copy_(c.out[:B])
+    g = tlc.Group([n], device=dev)
+    lens2 = torch.cat([c.out_len, c.out_len])
+    scales2 = torch.cat([c.scale, c.scale])
+    _, st = g.decompress_accumulate_many(two.view(2, stride), lens2, scales2, s, acc)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for _ in range(2):
+        exp = oracle.decompress_accumulate(small, M, val.size, s, exp)
     assert np.array_equal(bits(acc[ti].cpu().numpy()), bits(exp))
     assert int(torch.count_nonzero(acc).item()) == int(np.count_nonzero(exp))

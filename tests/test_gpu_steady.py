@@ -17,7 +17,8 @@ every tensor's stream, length, M and new error, and the decompressed values,
 bit for bit with the oracle run from the copied state.  Step 150 is run twice
 from the same state: with the previous M as the hint (the candidate-list path)
 and with a zero hint (the path that reads the error buffer again); both must
-equal the oracle."""
+equal the oracle, and so must the decompress of its streams on both launch
+sequences (sparse, and dense through a path hint word of 1)."""
 import numpy as np
 import pytest
 
@@ -100,5 +101,13 @@ def test_bert_large_steady_state_step_matches_oracle():
         if not np.array_equal(ge, bits(want_e)):
             i = int(np.flatnonzero(ge != bits(want_e))[0])
             raise AssertionError(f"{label}: err differs first at {i}")
+        assert np.array_equal(bits(y.cpu().numpy()), bits(want_y)), label
+        # the dense decompress sequence on the same streams (a hint word of 1)
+        hw = tlc.path_hint()
+        hw[0] = 1
+        y.fill_(7.0)
+        _, st_d = g.decompress(out, lens, sc, s, y=y, workspace=ws, path_hint=hw)
+        torch.cuda.synchronize()
+        assert int(st_d.item()) == 0 and int(hw[0]) == 1, label
         assert np.array_equal(bits(y.cpu().numpy()), bits(want_y)), label
         del e_run, y
