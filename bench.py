@@ -3,32 +3,42 @@
 One step = one worker's grouped compress of a whole gradient set (error
 accumulation, per-tensor scale, ternary quantization, quartic packing,
 zero-run encoding) followed by the grouped decompress of that payload
-(zero-run decoding, quartic decoding, dequantization).  The error buffer is
-carried from step to step, as in training, and every step sees a different
-gradient set (the generated set rotated by k * 1,000,003 elements).  Inputs
-are generated once on the host (seeded, synthetic) and are resident in HBM
-before timing starts.
+(zero-run decoding, quartic decoding, dequantization).  Inputs are seeded
+and synthetic, generated on the host and resident in HBM before any timing.
 
-Default workload: the BERT-large gradient set (391 tensors, 335,141,888
-fp32 values, 30% exact zeros, the rest N(0, 1e-4)), s = 1.75.
+Headline line (BERT-large gradient set, 391 tensors, 335,141,888 fp32 values,
+30% exact zeros, the rest N(0, 1e-4), s = 1.75): K steps with the error
+buffer carried from step to step, as in training, each step on a different
+gradient set (the generated set rotated by k * 1,000,003 elements, 32 such
+sets used in turn).  Each step is bracketed by HIP events: the line gives the
+mean (value), median and min step time, the roofline of the dominant kernel
+(the 12-byte/element pass over x and err) timed with HIP events on its own
+stream inside the timed region, bits per value, and the CPU oracle timed on
+the host.  The decompress follows a path hint word carried from step to step.
 
-Printed: one JSON line with the whole-job throughput in GB/s of fp32 input
-(4 bytes x values / (compress + decompress time)), the roofline of the
-dominant kernel (the 12-byte/element pass over x and err) measured with HIP
-events inside the timed region, bits per value, and the CPU oracle timed on
-the host over the same workload (single-threaded, and as independent
-per-tensor calls over up to 16 host cores).  Also reported, outside the timed steps:
-compress and decompress timed apart, the 8-payload accumulate, the same
-step after --steady-steps steps of error feedback (the error buffer then
-keeps every encode tile active and the streams are about twice as dense),
-the model-delta direction's server step (the workers' sum, then the
-compress of their mean with the server's error buffer), and the ablations:
-the same codes as quartic bytes only and as 2-bit fields (no zero-run
-encoding), with the zero-run gain of the first step; and the same steps
-pipelined over two streams (the decompress of payload k-1 while batch k is
-compressed).
+Per-configuration records (``configs``), each with the median and min over at
+least 20 repetitions, GB/s of fp32 input, the fraction of the HBM roofline of
+the step's algorithmic bytes and of the measured copy rate, and bits/value:
+* single_1m: one compress+decompress from a zero error buffer (restored
+  outside the timed window before every repetition);
+* single_16m: 10 consecutive steps on fresh inputs (seed 200+t) with the
+  error carried, run 3 times, every step timed;
+* resnet110: one grouped step (329 tensors), also in us and tensors/s;
+* resnet50: one grouped step at each s in {1.0, 1.5, 1.9};
+* bert_large_first_step: worker w's set (seed 500+w, w = 0..7) compressed
+  from a zero error buffer and decompressed, 3 repetitions per worker; then
+  the 8 workers' payloads decompressed and accumulated into one fp32 sum,
+  in one many-payload call and as 8 calls in worker order (bit-identical);
+* bert_large_steady: the headline's steps continued until the error buffer
+  has filled (every encode tile active, streams about twice as dense), 20
+  steps timed; then each worker's own 150-step error-feedback run, and the
+  8 steady-state payloads accumulated as above.
 
-    python bench.py [--steps K] [--warmup W] [--workload bert_large] [--no-cpu]
+Also reported: compress and decompress timed apart, the same steps pipelined
+over two streams, the model-delta direction's server step, and the ablations
+(the codes as quartic bytes only or as 2-bit fields, the five-plane layout).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--only CONFIG]
 """
 from __future__ import annotations
 
@@ -48,6 +58,9 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 DOMINANT = "tlc_accum_max"      # reads x and err, writes err: 12 B per element
 DOMINANT_BYTES_PER_ELEM = 12
 METRIC = "3LC compress+decompress GB/s (fp32 in) and % of HBM roofline; bits/value"
+ROT = 1_000_003                 # rotation between the gradient sets of consecutive steps
+WORKERS = 8
+RECORDS = ("single_1m", "single_16m", "resnet110", "resnet50", "bert_large_first_step", "bert_large_steady")
 
 
 def kernel_source_hash(kernel: str = "k_accum_max") -> str:
@@ -173,19 +186,410 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# timing helpers
+
+
+def timed(torch, reps: int, body, before=None):
+    """Runs body(r, mark) for r < reps on torch's current stream, each
+    repetition bracketed by HIP events (mark() records one more in between);
+    before(r), if given, runs outside the brackets.  Returns, per repetition,
+    the list of segment times in ms (one synchronisation at the end)."""
+    marks = []
+    for r in range(reps):
+        if before is not None:
+            before(r)
+        m = []
+
+        def mark(m=m):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            m.append(e)
+
+        mark()
+        body(r, mark)
+        mark()
+        marks.append(m)
+    torch.cuda.synchronize()
+    return [[m[i].elapsed_time(m[i + 1]) for i in range(len(m) - 1)] for m in marks]
+
+
+def stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "mean": round(float(a.mean()), 4), "reps": int(a.size)}
+
+
+def frac(nbytes: float, ms: float, peak_gbps: float):
+    return round(nbytes / (ms * 1e-3) / 1e9 / peak_gbps, 4) if ms and peak_gbps else None
+
+
+def step_record(N: int, tensors: int, s: float, L: int, step_ms, comp_ms, dec_ms, copy_gbps, dom=None):
+    """The measurement table of one configuration: times over the
+    repetitions, and the roofline of the step's algorithmic bytes
+    (compress 12 B/value + stream + 4 B per M; decompress 4 B/value +
+    stream) at the median step time."""
+    st, sc, sd = stats(step_ms), stats(comp_ms), stats(dec_ms)
+    alg_c = 12.0 * N + L + 4 * tensors
+    alg_d = 4.0 * N + L
+    med = st["median"]
+    achieved = (alg_c + alg_d) / (med * 1e-3) / 1e9
+    rec = {
+        "values": N, "tensors": tensors, "s": s,
+        "ms_per_step": st,
+        "compress_ms": sc,
+        "decompress_ms": sd,
+        "GBps_fp32_in": round(4.0 * N / (med * 1e-3) / 1e9, 1),
+        "compress_GBps_fp32_in": round(4.0 * N / (sc["median"] * 1e-3) / 1e9, 1),
+        "decompress_GBps_fp32_in": round(4.0 * N / (sd["median"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "bytes_per_step": int(alg_c + alg_d),
+                     "what": "compress+decompress algorithmic bytes over the median step"},
+        "compress_roofline_frac": frac(alg_c, sc["median"], HBM_PEAK_GBPS),
+        "compress_roofline_frac_nominal_12p3B": frac(12.3 * N, sc["median"], HBM_PEAK_GBPS),
+        "decompress_roofline_frac": frac(alg_d, sd["median"], HBM_PEAK_GBPS),
+        "copy_ceiling_frac": round(achieved / copy_gbps, 4) if copy_gbps else None,
+        "bits_per_value": round(8.0 * L / N, 4),
+        "bits_per_value_with_scale": round(8.0 * (L + 4 * tensors) / N, 4),
+    }
+    if dom is not None:
+        launches, ms = dom
+        if launches:
+            avg = ms / launches
+            ach = DOMINANT_BYTES_PER_ELEM * N / (avg * 1e-3) / 1e9
+            rec["dominant_kernel"] = {"kernel": DOMINANT, "avg_ms": round(avg, 4), "achieved": round(ach, 1),
+                                      "frac": round(ach / HBM_PEAK_GBPS, 4), "launches": launches}
+    return rec
+
+
+class Bench:
+    """Device state shared by the records."""
+
+    def __init__(self, args):
+        import torch
+
+        from gradient_compression_distributed_lc_amd import tlc, workloads
+        self.torch, self.tlc, self.workloads, self.args = torch, tlc, workloads, args
+        self.dev = torch.device("cuda:0")
+        self.copy_gbps = None
+
+    # -- yardstick ------------------------------------------------------------
+    def copy_yardstick(self):
+        torch, tlc = self.torch, self.tlc
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
+        for _ in range(2):
+            tlc.copy_probe(src, dst, nbytes)
+        t = timed(torch, 10, lambda r, mark: tlc.copy_probe(src, dst, nbytes))
+        ms = stats([v[0] for v in t])["median"]
+        self.copy_gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+        del src, dst
+        torch.cuda.empty_cache()
+
+    def status_ok(self, *sts, what=""):
+        got = [int(v.item()) for v in sts]
+        if any(got):
+            raise SystemExit(f"device status not ok ({what}): {got}")
+
+    # -- one compress+decompress step from a zero error buffer ----------------
+    def one_step(self, name: str, x_host: np.ndarray, sizes, s: float, reps: int):
+        torch, tlc = self.torch, self.tlc
+        dev = self.dev
+        N = int(x_host.size)
+        single = len(sizes) == 1
+        x = torch.from_numpy(x_host).to(dev)
+        err = torch.zeros(N, dtype=torch.float32, device=dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        st_c = torch.empty(1, dtype=torch.int32, device=dev)
+        st_d = torch.empty(1, dtype=torch.int32, device=dev)
+        hint = tlc.path_hint()
+        if single:
+            out = torch.empty(tlc.compress_bound(N), dtype=torch.uint8, device=dev)
+            lens = torch.empty(1, dtype=torch.int64, device=dev)
+            scales = torch.zeros(1, dtype=torch.float32, device=dev)
+            ws = torch.empty(tlc.workspace_size(N), dtype=torch.uint8, device=dev)
+
+            def comp():
+                tlc.compress(x, err, s, out=out, out_len=lens, scale=scales, workspace=ws, status=st_c)
+
+            def dec():
+                tlc.decompress(out, lens, scales, N, s, y=y, workspace=ws, status=st_d, path_hint=hint)
+        else:
+            g = tlc.Group(sizes, device=dev)
+            out = torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev)
+            lens = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+            scales = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+            ws = g.workspace()
+
+            def comp():
+                g.compress(x, err, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st_c)
+
+            def dec():
+                g.decompress(out, lens, scales, s, y=y, workspace=ws, status=st_d, path_hint=hint)
+
+        def before(r):  # a first step: zero error buffer, no previous M
+            err.zero_()
+            scales.zero_()
+
+        def body(r, mark):
+            comp()
+            mark()
+            dec()
+
+        timed(torch, 3, body, before)
+        tlc.profile_read()
+        tlc.profile_only(DOMINANT)
+        tlc.profile_enable(True)
+        t = timed(torch, reps, body, before)
+        tlc.profile_enable(False)
+        dom = tlc.profile_read().get(DOMINANT, (0, 0.0))
+        self.status_ok(st_c, st_d, what=name)
+        L = int(lens.sum().item())
+        rec = step_record(N, len(sizes), s, L, [a + b for a, b in t], [a for a, _ in t], [b for _, b in t],
+                          self.copy_gbps, dom)
+        rec["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
+        return rec
+
+    def record_single_1m(self):
+        w = self.workloads.get("single_1m")
+        return self.one_step("single_1m", self.workloads.generate("single_1m"), w.sizes, w.s_values[0],
+                             self.args.reps)
+
+    def record_resnet110(self):
+        w = self.workloads.get("resnet110")
+        rec = self.one_step("resnet110", self.workloads.generate("resnet110"), w.sizes, w.s_values[0],
+                            max(self.args.reps, 30))
+        med = rec["ms_per_step"]["median"]
+        rec["us_per_step"] = {k: round(v * 1e3, 1) for k, v in rec["ms_per_step"].items() if k != "reps"}
+        rec["tensors_per_s"] = round(len(w.sizes) / (med * 1e-3), 0)
+        rec["note"] = "launch-bound: 1.73M values in 329 tensors; the step is the kernels' fixed latencies"
+        return rec
+
+    def record_resnet50(self):
+        w = self.workloads.get("resnet50")
+        x = self.workloads.generate("resnet50")
+        return {f"s={s}": self.one_step(f"resnet50 s={s}", x, w.sizes, s, self.args.reps) for s in w.s_values}
+
+    def record_single_16m(self):
+        """10 steps with fresh inputs (seed 200+t) and the error carried,
+        the whole sequence run 3 times from a zero error buffer."""
+        torch, tlc = self.torch, self.tlc
+        dev = self.dev
+        w = self.workloads.get("single_16m")
+        s, N = w.s_values[0], w.total
+        xs = [torch.from_numpy(self.workloads.generate("single_16m", step=t)).to(dev) for t in range(10)]
+        err = torch.zeros(N, dtype=torch.float32, device=dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        out = torch.empty(tlc.compress_bound(N), dtype=torch.uint8, device=dev)
+        lens = torch.empty(1, dtype=torch.int64, device=dev)
+        scales = torch.zeros(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(tlc.workspace_size(N), dtype=torch.uint8, device=dev)
+        st_c = torch.empty(1, dtype=torch.int32, device=dev)
+        st_d = torch.empty(1, dtype=torch.int32, device=dev)
+        hint = tlc.path_hint()
+
+        def step(t):
+            tlc.compress(xs[t], err, s, out=out, out_len=lens, scale=scales, workspace=ws, status=st_c)
+
+        def dec():
+            tlc.decompress(out, lens, scales, N, s, y=y, workspace=ws, status=st_d, path_hint=hint)
+
+        # an untimed run that reads each step's length
+        err.zero_()
+        scales.zero_()
+        step_L = []
+        for t in range(10):
+            step(t)
+            dec()
+            step_L.append(int(lens.item()))
+        runs = 3
+        per_step = [[] for _ in range(10)]
+        comp, decm, tot = [], [], []
+        for _ in range(runs):
+            torch.cuda.synchronize()
+            err.zero_()
+            scales.zero_()
+
+            def body(t, mark):
+                step(t)
+                mark()
+                dec()
+
+            t_ms = timed(torch, 10, body)
+            for t, (a, b) in enumerate(t_ms):
+                per_step[t].append(a + b)
+                comp.append(a)
+                decm.append(b)
+            tot.append(sum(a + b for a, b in t_ms))
+        self.status_ok(st_c, st_d, what="single_16m")
+        # bits over the 10 steps' streams
+        L_mean = int(round(np.mean(step_L)))
+        rec = step_record(N, 1, s, L_mean, [a for v in per_step for a in v], comp, decm, self.copy_gbps)
+        rec["per_step_ms_median"] = [round(float(np.median(v)), 4) for v in per_step]
+        rec["bits_per_value_per_step"] = [round(8.0 * v / N, 4) for v in step_L]
+        rec["ten_steps_ms"] = stats(tot)
+        rec["how"] = (f"{runs} runs of the 10 carried steps from a zero error buffer; ms_per_step pools "
+                      f"all {10 * runs} steps; bits_per_value is the mean over the 10 steps")
+        return rec
+
+    # -- BERT-large workers -----------------------------------------------------
+    def bert_workers(self, steady_steps: int, cpu: bool):
+        """Worker w's set (seed 500+w) for w < 8, resident on the device; each
+        worker's first payload (zero error buffer) and, if steady_steps, its
+        payload after steady_steps steps of its own error feedback (step k on
+        the set rotated by (k mod 32) * 1,000,003)."""
+        torch, tlc = self.torch, self.tlc
+        dev = self.dev
+        wl = self.workloads.get("bert_large")
+        sizes, N, s = wl.sizes, wl.total, wl.s_values[0]
+        g = tlc.Group(sizes, device=dev)
+        self.bert_group = g
+        SB = g.stream_bytes
+        pay = {k: (torch.empty((WORKERS, SB), dtype=torch.uint8, device=dev),
+                   torch.empty((WORKERS, len(sizes)), dtype=torch.int64, device=dev),
+                   torch.zeros((WORKERS, len(sizes)), dtype=torch.float32, device=dev))
+               for k in (("first", "steady") if steady_steps else ("first",))}
+        err = torch.zeros(N, dtype=torch.float32, device=dev)
+        stage = torch.empty(N, dtype=torch.float32, device=dev)
+        st_c = torch.empty(1, dtype=torch.int32, device=dev)
+        ws = g.workspace()
+        xs = []
+        oracle_first = []
+        for w in range(WORKERS):
+            t0 = time.perf_counter()
+            xh = self.workloads.generate("bert_large", worker=w)
+            xd = torch.from_numpy(xh).to(dev)
+            xs.append(xd)
+            if cpu:
+                import oracle
+                offs = self.workloads.offsets(sizes)
+                e = np.zeros(N, np.float32)
+                cur = []
+                for t, n in enumerate(sizes):
+                    o = np.empty(-(-n // 5), np.uint8)
+                    L, M = oracle.compress_inplace(xh[offs[t]:offs[t + 1]], e[offs[t]:offs[t + 1]], s, o)
+                    cur.append((o[:L].copy(), np.float32(M)))
+                oracle_first.append(cur)
+                del e
+            del xh
+            err.zero_()
+            o, ln, sc = pay["first"]
+            g.compress(xd, err, s, out=o[w], out_lens=ln[w], scales=sc[w], workspace=ws, status=st_c)
+            if steady_steps:
+                so, sl, ss = pay["steady"]
+                ss[w].copy_(sc[w])
+                for k in range(1, steady_steps):
+                    sh = (k % 32) * ROT % N
+                    stage[sh:].copy_(xd[:N - sh])
+                    stage[:sh].copy_(xd[N - sh:])
+                    g.compress(stage, err, s, out=so[w], out_lens=sl[w], scales=ss[w], workspace=ws, status=st_c)
+            torch.cuda.synchronize()
+            self.status_ok(st_c, what=f"bert_large worker {w}")
+            log(f"worker {w}: set, first payload{' and steady payload' if steady_steps else ''} "
+                f"in {time.perf_counter() - t0:.1f}s")
+        del stage, err
+        torch.cuda.empty_cache()
+        parity = None
+        if cpu:
+            o, ln, sc = (v.cpu().numpy() for v in pay["first"])
+            ok = True
+            for w in range(WORKERS):
+                for t, (stt, M) in enumerate(oracle_first[w]):
+                    off = g.offsets[t]
+                    ok &= int(ln[w, t]) == stt.size and np.array_equal(o[w, off:off + stt.size], stt)
+                    ok &= np.float32(sc[w, t]).view(np.uint32) == M.view(np.uint32)
+            parity = ok
+        return xs, pay, oracle_first, parity
+
+    def accumulate_record(self, payload, oracle_payloads=None):
+        """The 8 payloads decompressed and accumulated into one fp32 sum in
+        worker order: one many-payload call against 8 single-payload calls,
+        20 repetitions each, acc cleared outside the timed window."""
+        torch, tlc = self.torch, self.tlc
+        g = self.bert_group
+        N, count = g.total, g.count
+        s = self.workloads.get("bert_large").s_values[0]
+        o, ln, sc = payload
+        acc = torch.empty(N, dtype=torch.float32, device=self.dev)
+        st = torch.empty(1, dtype=torch.int32, device=self.dev)
+        ws_many = torch.empty(g.accumulate_many_workspace_size(WORKERS), dtype=torch.uint8, device=self.dev)
+        ws = g.workspace()
+        lflat, sflat = ln.reshape(-1), sc.reshape(-1)
+
+        def many(r, mark):
+            g.decompress_accumulate_many(o, lflat, sflat, s, acc, workspace=ws_many, status=st)
+
+        def seq(r, mark):
+            for w in range(WORKERS):
+                g.decompress_accumulate(o[w], ln[w], sc[w], s, acc, workspace=ws, status=st)
+
+        def clear(r):
+            acc.zero_()
+
+        reps = self.args.reps
+        timed(torch, 2, many, clear)
+        tlc.profile_read()
+        tlc.profile_only(None)
+        tlc.profile_enable(True)
+        t_many = [v[0] for v in timed(torch, reps, many, clear)]
+        tlc.profile_enable(False)
+        k_many = tlc.profile_read()
+        self.status_ok(st, what="accumulate many")
+        acc_many = acc.clone()
+        timed(torch, 2, seq, clear)
+        t_seq = [v[0] for v in timed(torch, reps, seq, clear)]
+        self.status_ok(st, what="accumulate sequential")
+        same = bool(torch.equal(acc.view(torch.int32), acc_many.view(torch.int32)))
+        L = int(ln.sum().item())
+        alg = 8.0 * N + L  # one pass over acc (read and write) plus every stream
+        sm = stats(t_many)
+        rec = {"payloads": WORKERS, "stream_bytes_total": L,
+               "bits_per_value_mean": round(8.0 * L / WORKERS / N, 4),
+               "many_call_ms": sm, "sequential_calls_ms": stats(t_seq),
+               "many_call_roofline": {"bound": "hbm", "achieved": round(alg / (sm["median"] * 1e-3) / 1e9, 1),
+                                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                      "frac": frac(alg, sm["median"], HBM_PEAK_GBPS),
+                                      "bytes": int(alg),
+                                      "what": "one read and write of all of acc (8 B/value) plus the 8 streams; "
+                                              "blocks of 1024 values no payload touches are skipped, so sparse "
+                                              "payloads can exceed 1"},
+               "many_call_kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in k_many.items() if v[0]},
+               "many_equals_sequential": same}
+        if oracle_payloads is not None:
+            import oracle
+            want = np.zeros(N, np.float32)
+            offs = self.workloads.offsets(g.sizes)
+            for w in range(WORKERS):
+                for t, (stt, M) in enumerate(oracle_payloads[w]):
+                    oracle.decompress_accumulate(stt, M, g.sizes[t], s, want[offs[t]:offs[t + 1]])
+            rec["parity"] = ("bit-exact vs the oracle's accumulate of its own 8 payloads in worker order"
+                             if np.array_equal(acc_many.cpu().numpy().view(np.uint32), want.view(np.uint32))
+                             else "MISMATCH")
+        del acc, acc_many, ws_many
+        return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20, help="repetitions per configuration record (>= 20)")
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--s", type=float, default=None)
     ap.add_argument("--cpu-passes", type=int, default=8, help="oracle passes over the workload (about 10-15 s)")
     ap.add_argument("--pool", type=int, default=32, help="distinct gradient sets cycled through (HBM: 4 B/value each)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--no-copy", action="store_true", help="skip the copy-bandwidth yardstick")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle legs (profiling runs)")
+    ap.add_argument("--no-records", action="store_true", help="headline only")
+    ap.add_argument("--only", choices=RECORDS, default=None,
+                    help="run one configuration record and print it (profiling runs)")
     ap.add_argument("--steady-steps", type=int, default=150,
-                    help="error-feedback steps before the steady-state figure (0: skip it)")
+                    help="error-feedback steps before the steady-state figures (0: skip them)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,6 +606,28 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    bench = Bench(args)
+    bench.copy_yardstick()
+    copy_gbps = bench.copy_gbps
+
+    if args.only:
+        log(f"record {args.only}")
+        if args.only.startswith("bert_large"):
+            steady = args.only == "bert_large_steady"
+            xs, pay, _, _ = bench.bert_workers(args.steady_steps if steady else 0, False)
+            rec = bench.accumulate_record(pay["steady" if steady else "first"])
+        else:
+            rec = getattr(bench, f"record_{args.only}")()
+        print(json.dumps({"record": args.only, **rec}), flush=True)
+        return
+
+    records = {}
+    if not args.no_records:
+        for name in ("single_1m", "single_16m", "resnet110", "resnet50"):
+            log(f"record {name}")
+            records[name] = getattr(bench, f"record_{name}")()
+            torch.cuda.empty_cache()
+
     wl = workloads.get(args.workload)
     s = args.s if args.s is not None else wl.s_values[0]
     sizes = wl.sizes
@@ -209,8 +635,7 @@ def main():
 
     t_gen = time.perf_counter()
     x_host = workloads.generate(args.workload)
-    print(f"[bench] generated {args.workload}: {len(sizes)} tensors, {N} values in "
-          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    log(f"generated {args.workload}: {len(sizes)} tensors, {N} values in {time.perf_counter() - t_gen:.1f}s")
 
     group = tlc.Group(sizes, device=dev)
     x0 = torch.from_numpy(x_host).to(dev)
@@ -218,24 +643,31 @@ def main():
     # rotated by k * 1,000,003 elements (same distribution, different values),
     # so the error buffer evolves as it does in training.  Repeating one
     # gradient instead makes the buffer pile up and is not the workload.
-    pool = max(1, min(args.steps + args.warmup, args.pool))
-    xs = [x0] + [torch.roll(x0, shifts=k * 1_000_003) for k in range(1, pool)]
+    pool = max(1, min(max(args.steps + args.warmup, args.steady_steps), args.pool))
+    xs = [x0] + [torch.roll(x0, shifts=k * ROT) for k in range(1, pool)]
     ed = torch.zeros(N, dtype=torch.float32, device=dev)
     yd = torch.empty(N, dtype=torch.float32, device=dev)
     out = torch.empty(group.stream_bytes, dtype=torch.uint8, device=dev)
     lens = torch.empty(len(sizes), dtype=torch.int64, device=dev)
-    scales = torch.empty(len(sizes), dtype=torch.float32, device=dev)
+    scales = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
     st_c = torch.empty(1, dtype=torch.int32, device=dev)
     st_d = torch.empty(1, dtype=torch.int32, device=dev)
     ws = group.workspace()
+    hint = tlc.path_hint()
 
     counter = [0]
 
-    def step():
+    def compress_next():
         xd = xs[counter[0] % pool]
         counter[0] += 1
         group.compress(xd, ed, s, out=out, out_lens=lens, scales=scales, workspace=ws, status=st_c)
-        group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d)
+
+    def decompress():
+        group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d, path_hint=hint)
+
+    def step():
+        compress_next()
+        decompress()
 
     # first step from a zero error buffer on the unrotated set: kept for the parity check
     step()
@@ -248,39 +680,35 @@ def main():
     # the state the timed steps start from, for the pipelined measurement below
     e_warm, c_warm, sc_warm = ed.clone(), counter[0], scales.clone()
 
-    # timed region: K steps; HIP events bracket the dominant kernel on its stream
+    # timed region: K steps, an event between consecutive steps; the library
+    # brackets the dominant kernel with HIP events on its own stream
     tlc.profile_read()
     tlc.profile_only(DOMINANT)
     tlc.profile_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for k in range(args.steps):
         step()
-    ev1.record()
+        evs[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     tlc.profile_enable(False)
     kt = tlc.profile_read()
+    step_ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]
+    ms_total = evs[0].elapsed_time(evs[-1])
+    ms_per_step = ms_total / args.steps
     last_bits = 8.0 * float(lens.sum().item()) / N
+    hint_after = "dense" if int(hint[0]) else "sparse"
 
     # phase times: compress calls alone, then decompress calls alone, each
-    # bracketed as a whole (the error buffer keeps evolving; inputs rotate)
-    kp = min(args.steps, 10)
-    p0, p1, p2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    p0.record()
-    for _ in range(kp):
-        group.compress(xs[counter[0] % pool], ed, s, out=out, out_lens=lens, scales=scales, workspace=ws,
-                       status=st_c)
-        counter[0] += 1
-    p1.record()
-    for _ in range(kp):
-        group.decompress(out, lens, scales, s, y=yd, workspace=ws, status=st_d)
-    p2.record()
-    torch.cuda.synchronize()
-    comp_ms = p0.elapsed_time(p1) / kp
-    dec_ms = p1.elapsed_time(p2) / kp
+    # call bracketed (the error buffer keeps evolving; inputs rotate)
+    kp = max(args.steps, 20)
+    tc = timed(torch, kp, lambda r, mark: compress_next())
+    td = timed(torch, kp, lambda r, mark: decompress())
+    comp_st, dec_st = stats([v[0] for v in tc]), stats([v[0] for v in td])
+    comp_ms, dec_ms = comp_st["mean"], dec_st["mean"]
 
     # Pipelined: a worker's receive side does not wait for its own compress,
     # so the decompress of payload k-1 runs on a second stream while batch k
@@ -291,6 +719,8 @@ def main():
     ed.copy_(e_warm)
     sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
     ws_d = group.workspace()
+    hint_d = tlc.path_hint()
+    hint_d[0] = int(hint[0])
     pay = [(torch.empty_like(out), torch.empty_like(lens), sc_warm.clone()) for _ in range(2)]
     st_pc, st_pd = torch.zeros_like(st_c), torch.zeros_like(st_d)
     ev_c = [torch.cuda.Event() for _ in range(2)]
@@ -308,7 +738,8 @@ def main():
     def pdec(k):
         b = k % 2
         sB.wait_event(ev_c[b])
-        group.decompress(pay[b][0], pay[b][1], pay[b][2], s, y=yd, workspace=ws_d, status=st_pd, stream=sB)
+        group.decompress(pay[b][0], pay[b][1], pay[b][2], s, y=yd, workspace=ws_d, status=st_pd,
+                         path_hint=hint_d, stream=sB)
         ev_d[b].record(sB)
 
     def pipeline(K, base):
@@ -346,8 +777,6 @@ def main():
     torch.cuda.synchronize()
     tlc.profile_enable(False)
     kt_all = tlc.profile_read()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
     if (int(st_c.item()), int(st_d.item())) != (0, 0) or first["status"] != (0, 0):
         raise SystemExit(f"device status not ok: {first['status']} / {(int(st_c.item()), int(st_d.item()))}")
 
@@ -358,26 +787,15 @@ def main():
     dom_ms = per_launch(DOMINANT, kt)
     achieved = DOMINANT_BYTES_PER_ELEM * N / (dom_ms * 1e-3) / 1e9 if dom_ms else 0.0
 
-    # accumulate of the same payload, 8 times (the 8-worker receive side)
+    # model-delta direction, server side: the workers' sum (the payload decoded
+    # into acc, then accumulated 7 more times), then the server's compress of
+    # the 8-worker mean with its own error buffer (carried)
     acc = torch.zeros(N, dtype=torch.float32, device=dev)
     st_a = torch.empty(1, dtype=torch.int32, device=dev)
-    group.decompress_accumulate(out, lens, scales, s, acc, workspace=ws, status=st_a)
-    torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record()
-    for _ in range(8):
-        group.decompress_accumulate(out, lens, scales, s, acc, workspace=ws, status=st_a)
-    a1.record()
-    torch.cuda.synchronize()
-    acc_ms = a0.elapsed_time(a1) / 8
-
-    # model-delta direction, server side: the workers' sum (the payload decoded
-    # densely into acc, then accumulated 7 more times), then the server's
-    # compress of the 8-worker mean with its own error buffer (carried)
     err_srv = torch.zeros(N, dtype=torch.float32, device=dev)
     out_srv = torch.empty(group.stream_bytes, dtype=torch.uint8, device=dev)
     lens_srv = torch.empty(len(sizes), dtype=torch.int64, device=dev)
-    scales_srv = torch.empty(len(sizes), dtype=torch.float32, device=dev)
+    scales_srv = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
     st_s = torch.empty(1, dtype=torch.int32, device=dev)
 
     def server_step():
@@ -405,6 +823,7 @@ def main():
     srv_step_ms = s0.elapsed_time(s1) / ks
     srv_comp_ms = s1.elapsed_time(s2) / ks
     L_srv = int(lens_srv.sum().item())
+    del acc, err_srv, out_srv
 
     # ablations (3LC page, method items two and three): the same quantization
     # with the codes written as quartic bytes only, or as 2-bit fields; each
@@ -440,10 +859,8 @@ def main():
         d_ms = f1.elapsed_time(f2) / 5
         ablations[name] = {"bits_per_value": round(8.0 * nbytes / N, 4), "compress_ms": round(c_ms, 4),
                            "decompress_ms": round(d_ms, 4),
-                           "compress_roofline_frac": round((12.0 * N + nbytes) / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                                           4),
-                           "decompress_roofline_frac": round((4.0 * N + nbytes) / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                                             4)}
+                           "compress_roofline_frac": frac(12.0 * N + nbytes, c_ms, HBM_PEAK_GBPS),
+                           "decompress_roofline_frac": frac(4.0 * N + nbytes, d_ms, HBM_PEAK_GBPS)}
         del out_fx, y_fx
     del err_fx
     B_total = sum(-(-n // 5) for n in sizes)
@@ -507,47 +924,49 @@ def main():
         "how": "gather into the five-plane order, the grouped codec on the padded plan, scatter back "
                "(times include the gather and scatter)"}
 
-    # steady state of error feedback: the same step continued until the error
-    # buffer has filled (every encode tile active, denser streams), then timed
+    # steady state of error feedback: the same steps continued until the error
+    # buffer has filled (every encode tile active, denser streams), then 20
+    # steps timed one by one
     steady = None
     if args.steady_steps > 0:
         while counter[0] < args.steady_steps:
             step()
         torch.cuda.synchronize()
-        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        q0.record()
-        for _ in range(10):
-            step()
-        q1.record()
-        torch.cuda.synchronize()
-        st_ms = q0.elapsed_time(q1) / 10
+        after = counter[0]
+        tlc.profile_read()
+        tlc.profile_only(DOMINANT)
+        tlc.profile_enable(True)
+        t = timed(torch, max(args.reps, 20), lambda r, mark: (compress_next(), mark(), decompress()))
+        tlc.profile_enable(False)
+        dom_steady = tlc.profile_read().get(DOMINANT, (0, 0.0))
         if (int(st_c.item()), int(st_d.item())) != (0, 0):
             raise SystemExit("device status not ok in the steady-state steps")
-        steady = {"after_steps": counter[0] - 10, "ms_per_step": round(st_ms, 4),
-                  "GBps_fp32_in": round(4.0 * N / (st_ms * 1e-3) / 1e9, 1),
-                  "bits_per_value": round(8.0 * float(lens.sum().item()) / N, 4)}
+        L_steady = int(lens.sum().item())
+        steady = step_record(N, len(sizes), s, L_steady, [a + b for a, b in t], [a for a, _ in t],
+                             [b for _, b in t], copy_gbps, dom_steady)
+        steady["after_steps"] = after
+        steady["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
+        # the per-kernel breakdown at this state (every kernel bracketed)
+        tlc.profile_only(None)
+        tlc.profile_enable(True)
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        tlc.profile_enable(False)
+        steady["kernels_ms_per_launch_events"] = {k: round(v[1] / v[0], 4) for k, v in tlc.profile_read().items()
+                                                  if v[0]}
         # the same state pipelined over the two streams (10 more steps)
         for b in range(2):
             pay[b][2].copy_(scales)
+        hint_d[0] = int(hint[0])
         torch.cuda.synchronize()
         pa.record(sA)
         pipeline(10, counter[0])
         pb.record(sB)
         torch.cuda.synchronize()
-        out_pl_last = pay[(10 - 1) % 2]
         if (int(st_pc.item()), int(st_pd.item())) != (0, 0):
             raise SystemExit("device status not ok in the pipelined steady-state steps")
         steady["pipelined_ms_per_step"] = round(pa.elapsed_time(pb) / 10, 4)
-        # the receive side at this density: the last payload accumulated 8 times
-        a0.record()
-        for _ in range(8):
-            group.decompress_accumulate(out_pl_last[0], out_pl_last[1], out_pl_last[2], s, acc, workspace=ws,
-                                        status=st_a)
-        a1.record()
-        torch.cuda.synchronize()
-        if int(st_a.item()) != 0:
-            raise SystemExit("device status not ok in the steady-state accumulate")
-        steady["accumulate_ms_per_payload"] = round(a0.elapsed_time(a1) / 8, 4)
         # the two byte layouts on the same codes: quantization does not depend
         # on the layout, so one more step's input and this error state, taken
         # by each layout on copies of the error buffer
@@ -562,32 +981,15 @@ def main():
         ablations["five_plane"]["bits_per_value_steady"] = round(8.0 * int(lens_pl.sum().item()) / N, 4)
         ablations["five_plane"]["consecutive_bits_per_value_steady"] = round(8.0 * int(lens.sum().item()) / N, 4)
         del e_a
-    del pay, ws_d, gp, xp, ep, err_pl, out_pl, ws_pl
-
-
-    # copy yardstick: what a plain streaming copy reaches on this GPU
-    copy_gbps = None
-    if not args.no_copy:
-        nbytes = 1 << 30
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            tlc.copy_probe(src, dst, nbytes)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(10):
-            tlc.copy_probe(src, dst, nbytes)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-        del src, dst
+    del pay, ws_d, gp, xp, ep, err_pl, out_pl, ws_pl, xs, x0
+    torch.cuda.empty_cache()
 
     L_total = int(first["lens"].sum())
     bits = 8.0 * L_total / N
     bits_hdr = 8.0 * (L_total + 4 * len(sizes)) / N
     alg_bytes_comp = 12.0 * N + L_total + 4 * len(sizes)
     alg_bytes_dec = 4.0 * N + L_total
-    # server step: dense decode of the first payload (4 B/value + stream), 7
+    # server step: the first payload decoded into acc (4 B/value + stream), 7
     # sparse accumulates (stream + 8 B per nonzero code), the mean's compress
     nnz_bytes = 0.0  # the nonzero codes are a few thousand here: below rounding
     alg_bytes_srv = (4.0 * N + L_total) + 7 * (L_total + nnz_bytes) + (12.0 * N + L_srv + 4 * len(sizes))
@@ -596,7 +998,7 @@ def main():
     cpu = cpu_all = None
     parity = "not checked (--no-cpu)"
     if not args.no_cpu:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        log("timing the CPU oracle")
         cpu, streams, Ms, err0 = cpu_baseline(x_host, sizes, s, args.cpu_passes)
         ok = np.array_equal(first["scales"].view(np.uint32), np.asarray(Ms, np.float32).view(np.uint32))
         ok &= np.array_equal(first["err"].view(np.uint32), err0.view(np.uint32))
@@ -606,12 +1008,67 @@ def main():
             ok &= L == streams[t].size and np.array_equal(first["out"][o:o + L], streams[t])
         parity = "bit-exact vs oracle (streams, M, error buffer; first step)" if ok else "MISMATCH"
         if not ok:
-            print("[bench] PARITY MISMATCH", file=sys.stderr, flush=True)
+            log("PARITY MISMATCH")
         cpu["host_cpu"] = host_cpu_model()
-        print("[bench] timing the CPU oracle on all cores", file=sys.stderr, flush=True)
+        log("timing the CPU oracle on all cores")
         cpu_all = cpu_baseline_all_cores(x_host, sizes, s, args.cpu_passes)
+    del x_host
+
+    # the 8 workers of the BERT-large configuration: each worker's first step
+    # from a zero error buffer (timed), and the receive side's accumulate of
+    # the 8 seed-distinct payloads, first-step and steady-state
+    if not args.no_records and args.workload == "bert_large":
+        log("bert_large workers")
+        wxs, wpay, oracle_first, wparity = bench.bert_workers(args.steady_steps, not args.no_cpu)
+        # first step per worker: 3 repetitions each, error buffer and M cleared outside the window
+        err_w = torch.zeros(N, dtype=torch.float32, device=dev)
+        sc_w = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+        hint_w = tlc.path_hint()
+
+        def w_before(r):
+            err_w.zero_()
+            sc_w.zero_()
+
+        def w_body(r, mark):
+            group.compress(wxs[r % WORKERS], err_w, s, out=out, out_lens=lens, scales=sc_w, workspace=ws,
+                           status=st_c)
+            mark()
+            group.decompress(out, lens, sc_w, s, y=yd, workspace=ws, status=st_d, path_hint=hint_w)
+
+        timed(torch, 3, w_body, w_before)
+        tlc.profile_read()
+        tlc.profile_only(DOMINANT)
+        tlc.profile_enable(True)
+        tw = timed(torch, 3 * WORKERS, w_body, w_before)
+        tlc.profile_enable(False)
+        dom_w = tlc.profile_read().get(DOMINANT, (0, 0.0))
+        if (int(st_c.item()), int(st_d.item())) != (0, 0):
+            raise SystemExit("device status not ok in the workers' first steps")
+        L_first = int(wpay["first"][1].sum().item()) // WORKERS
+        rec = step_record(N, len(sizes), s, L_first, [a + b for a, b in tw], [a for a, _ in tw],
+                          [b for _, b in tw], copy_gbps, dom_w)
+        rec["how"] = ("worker w's set (seed 500+w), compress from a zero error buffer and no previous M, "
+                      "then decompress; 3 repetitions per worker, w = 0..7")
+        rec["decompress_sequence"] = "dense" if int(hint_w[0]) else "sparse"
+        if wparity is not None:
+            rec["parity"] = ("bit-exact vs oracle (8 workers' streams and M)" if wparity else "MISMATCH")
+        del err_w, sc_w, wxs
+        torch.cuda.empty_cache()
+        log("accumulate of the 8 first-step payloads")
+        rec["accumulate_8"] = bench.accumulate_record(wpay["first"], oracle_first if not args.no_cpu else None)
+        records["bert_large_first_step"] = rec
+        if steady is not None:
+            log("accumulate of the 8 steady-state payloads")
+            steady["accumulate_8"] = bench.accumulate_record(wpay["steady"])
+            steady["accumulate_8"]["how"] = (f"worker w's payload after {args.steady_steps} steps of its own "
+                                             f"error feedback (step k on its set rotated by "
+                                             f"(k mod 32) * {ROT})")
+        del wpay
+    if steady is not None:
+        records["bert_large_steady"] = steady
 
     traffic = stored_traffic(args.workload)
+    sm = stats(step_ms)
     result = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -620,13 +1077,17 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": sm["median"],
+        "ms_per_step_min": sm["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "tensors": len(sizes), "values": N, "s": s,
-                   "values_dist": wl.description, "parallelism": "single GPU"},
+                   "values_dist": wl.description, "parallelism": "single GPU",
+                   "steps_timed": f"steps {c_warm + 1}..{c_warm + args.steps} of a carried error buffer, "
+                                  f"inputs cycled through {pool} rotated copies of the set"},
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_elem": DOMINANT_BYTES_PER_ELEM,
@@ -639,36 +1100,31 @@ def main():
         "compression_ratio_vs_fp32": round(32.0 / bits_hdr, 1),
         "compress_ms": round(comp_ms, 4),
         "decompress_ms": round(dec_ms, 4),
+        "compress_ms_median": comp_st["median"],
+        "decompress_ms_median": dec_st["median"],
+        "decompress_sequence_after_timed_steps": hint_after,
         "compress_GBps_fp32_in": round(4.0 * N / (comp_ms * 1e-3) / 1e9, 1) if comp_ms else None,
         "decompress_GBps_fp32_in": round(4.0 * N / (dec_ms * 1e-3) / 1e9, 1) if dec_ms else None,
-        "path_roofline_frac": round((alg_bytes_comp + alg_bytes_dec) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                    4),
-        "compress_roofline_frac": round(alg_bytes_comp / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
-        if comp_ms else None,
-        "compress_roofline_frac_nominal_12p3B": round(12.3 * N / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
-        if comp_ms else None,
-        "decompress_roofline_frac": round(alg_bytes_dec / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
-        if dec_ms else None,
-        "accumulate_ms_per_payload": round(acc_ms, 4),
+        "path_roofline_frac": frac(alg_bytes_comp + alg_bytes_dec, ms_per_step, HBM_PEAK_GBPS),
+        "compress_roofline_frac": frac(alg_bytes_comp, comp_ms, HBM_PEAK_GBPS),
+        "compress_roofline_frac_nominal_12p3B": frac(12.3 * N, comp_ms, HBM_PEAK_GBPS),
+        "decompress_roofline_frac": frac(alg_bytes_dec, dec_ms, HBM_PEAK_GBPS),
         "server_step_ms": round(srv_step_ms, 4),
-        "server_step_roofline_frac": round(alg_bytes_srv / (srv_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "server_step_roofline_frac": frac(alg_bytes_srv, srv_step_ms, HBM_PEAK_GBPS),
         "server_compress_ms": round(srv_comp_ms, 4),
-        "server_compress_roofline_frac": round((12.0 * N + L_srv + 4 * len(sizes)) / (srv_comp_ms * 1e-3) / 1e9
-                                               / HBM_PEAK_GBPS, 4),
+        "server_compress_roofline_frac": frac(12.0 * N + L_srv + 4 * len(sizes), srv_comp_ms, HBM_PEAK_GBPS),
         "server_bits_per_value": round(8.0 * L_srv / N, 4),
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         # the same algorithmic bytes against the measured copy rate instead of the nominal peak
-        "path_copy_ceiling_frac": round((alg_bytes_comp + alg_bytes_dec) / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4)
-        if copy_gbps else None,
+        "path_copy_ceiling_frac": frac(alg_bytes_comp + alg_bytes_dec, ms_per_step, copy_gbps),
         "dominant_copy_ceiling_frac": round(achieved / copy_gbps, 4) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
-        "steady_state": steady,
         "pipelined": {"ms_per_step": round(pipe_ms, 4), "GBps_fp32_in": round(4.0 * N / (pipe_ms * 1e-3) / 1e9, 1),
-                      "path_roofline_frac": round((alg_bytes_comp + alg_bytes_dec) / (pipe_ms * 1e-3) / 1e9
-                                                  / HBM_PEAK_GBPS, 4),
+                      "path_roofline_frac": frac(alg_bytes_comp + alg_bytes_dec, pipe_ms, HBM_PEAK_GBPS),
                       "how": "compress of batch k on one stream, decompress of payload k-1 on another "
                              "(receive side overlapped with the send side), same inputs and error state "
                              "as the timed steps"},
+        "configs": records,
         "ablations": ablations,
         "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "wall_s_timed": round(wall, 3),

@@ -119,25 +119,15 @@ struct TableHeader {
     uint64_t magic, count, ftiles, etiles, spans, chunks, total_elems, stream_bytes;
 };
 static_assert(sizeof(TableHeader) == 64, "table layout");
-constexpr uint64_t kMagic = 0x33434c5433ull;  // "3TLC3"
+constexpr uint64_t kMagic = 0x34434c5433ull;  // "3TLC4"
 constexpr uint32_t kStraddle = 0x80000000u;   // ftile_info flag: the flat tile spans tensors
 constexpr uint32_t kMulti = 0x80000000u;      // span_seg / dec_map flag: the tensor has several spans / chunks
-
-// Per 1024-element block of the group (a "y-block", the unit of the
-// decompress-side streams): where its first element's quartic byte lives.
-struct YRec {
-    uint64_t qoff;  // stream slot offset of the tensor of its first element
-    uint32_t u0;    // that element's index in its tensor
-    uint32_t gi;    // that tensor | kStraddle when the block spans tensors
-};
-static_assert(sizeof(YRec) == 16, "table layout");
 
 struct GroupView {
     const Seg* segs;            // device table, or nullptr for one tensor
     const uint32_t* ftile_info; // per flat tile: tensor of its first element | kStraddle
     const uint32_t* span_seg;   // per k_emit span: tensor
     const uint32_t* etile_seg;  // per encode tile: tensor
-    const YRec* yrec;           // per y-block
     uint32_t count;
     Seg one;
 };
@@ -1350,10 +1340,9 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 // k_decode records where every encode tile begins and k_expand decodes each
 // tile in LDS and writes it once.  The accumulate of one payload adds its
 // nonzero codes to acc straight from the stream.  The accumulate of many
-// payloads decodes each payload's quartic bytes into the workspace (laid out
-// like the streams, with one flag byte per 1024-element "y-block" that holds
-// a nonzero code) in one k_decode launch, then k_apply reads and writes acc
-// once, y-block by y-block, applying the payloads in order.
+// payloads records the tile starts of every payload in one k_decode launch,
+// then k_apply reads and writes each tile of acc once, decoding every
+// payload's bytes for the tile in LDS and adding them in payload order.
 
 // Where k_decode found encode tile j of a tensor to begin (decompress only):
 // the stream byte, counted from the tensor's first, whose expansion holds
@@ -1369,12 +1358,7 @@ __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { r
 // 0.109).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
 constexpr uint64_t kDenseNum = 104, kDenseDen = 1000;
 
-constexpr uint32_t kYBlock = 1024;            // elements per y-block (256 lanes x 4)
-constexpr uint32_t kMaxPayloads = 64;         // payloads of one accumulate-many call
-
-__host__ __device__ constexpr uint64_t yblocks_of(uint64_t total) { return (total + kYBlock - 1) / kYBlock; }
-// y-block flags of one payload, padded to whole 16-byte rows
-__host__ __device__ constexpr uint64_t yflag_bytes(uint64_t total) { return (yblocks_of(total) + 15) / 16 * 16; }
+constexpr uint32_t kMaxPayloads = 64;  // payloads of one accumulate-many call (one wavefront lane each)
 
 // Decoder state reset and set-up, for `payloads` payloads of the group (unit
 // u = p * count + t is tensor t of payload p; in_lens and scales are indexed
@@ -1384,8 +1368,8 @@ __host__ __device__ constexpr uint64_t yflag_bytes(uint64_t total) { return (ybl
 // stores per lane, slows it by 10-40%), with a nontemporal hint: y is not
 // read again here, and the kernels that follow (the caller's next compress)
 // run faster when the caches do not hold y's dirty lines.  Dense decompress
-// (tstart set): the tile starts and literal flags are reset.  Accumulate-many
-// (nyfl > 0): the y-block flags are reset.
+// and accumulate-many (tstart set): the tile starts and literal flags of
+// every payload are reset.
 // Always: the look-back flags, and the list of stream chunks: unit u has
 // max(1, ceil(min(L_u, B_t) / kChunk)) chunks, numbered dec_first[u] ...;
 // chunk r belongs to unit dec_map[r]; ctrl[3] = number of chunks.  Block 0
@@ -1394,8 +1378,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
                                                    uint64_t n_fill, const uint64_t* __restrict__ in_lens,
                                                    uint64_t* __restrict__ flags, uint64_t nflags,
                                                    uint64_t* __restrict__ tstart, uint32_t* __restrict__ tlit,
-                                                   uint64_t ntiles, uint8_t* __restrict__ yfl, uint64_t nyfl,
-                                                   uint32_t* __restrict__ dec_map, uint32_t* __restrict__ dec_first,
+                                                   uint64_t ntiles, uint32_t* __restrict__ dec_map,
+                                                   uint32_t* __restrict__ dec_first,
                                                    uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
                                                    int* __restrict__ status, uint32_t* hint) {
     __shared__ uint32_t s_u[kWaves];
@@ -1413,7 +1397,6 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
             tstart[i] = kNoStart;
             tlit[i] = 0;
         }
-    for (uint64_t i = tid; i < nyfl / 16; i += stride) reinterpret_cast<uint4*>(yfl)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (blockIdx.x == 0) {
         uint32_t carry = 0;
         uint64_t sum_l = 0, sum_b = 0;
@@ -1468,70 +1451,21 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
 enum DecodeMode {
     kDecodeWrite = 0,    // sparse decompress: nonzero codes written over k_prep's zero fill
     kDecodeAdd = 1,      // accumulate one payload: nonzero codes added to acc in place
-    kDecodeRecord = 2,   // dense decompress: tile starts and literal flags for k_expand
-    kDecodeQuartic = 3,  // accumulate-many: the payload's quartic bytes and y-block flags for k_apply
+    kDecodeRecord = 2,   // dense decompress and accumulate-many: tile starts and literal flags
 };
-
-// The five codes of a quartic byte as 2-bit fields (q & 3), first element
-// lowest.
-__host__ __device__ constexpr uint32_t quartic_fields(uint32_t byte) {
-    uint32_t pat = 0;
-    for (uint32_t d = 0; d < 5; ++d) {
-        const uint32_t digit = byte % 3u;
-        byte /= 3u;
-        pat |= (digit == 1u ? 0u : digit == 2u ? 1u : 3u) << (2 * d);
-    }
-    return pat;
-}
-
-// Elements [a, b) of an array of E-byte elements at `base` set to the
-// pattern v (E = 1: a byte; E = 2: a 16-bit field): aligned 16-byte stores
-// where whole 16-byte pieces lie inside, the largest aligned power-of-two
-// stores at the two ends (pieces shared with another lane are written only
-// where they are this range's).
-template <int E>
-__device__ __forceinline__ void fill_elements(uint8_t* base, uint64_t a, uint64_t b, uint32_t v) {
-    const uint64_t pat = E == 1 ? 0x0101010101010101ull * v : 0x0001000100010001ull * v;
-    uint64_t A = a * E;
-    const uint64_t Z = b * E;
-    auto piece = [&](uint64_t end) {  // [A, end), end - A < 16 or A unaligned
-        while (A < end) {
-            const uint64_t room = end - A;
-            if ((A & 7) == 0 && room >= 8) {
-                *reinterpret_cast<uint64_t*>(base + A) = pat;
-                A += 8;
-            } else if ((A & 3) == 0 && room >= 4) {
-                *reinterpret_cast<uint32_t*>(base + A) = (uint32_t)pat;
-                A += 4;
-            } else if ((A & 1) == 0 && room >= 2) {
-                *reinterpret_cast<uint16_t*>(base + A) = (uint16_t)pat;
-                A += 2;
-            } else {
-                base[A] = (uint8_t)pat;
-                A += 1;
-            }
-        }
-    };
-    piece(min(Z, (A + 15) & ~15ull));
-    const uint4 p4 = make_uint4((uint32_t)pat, (uint32_t)(pat >> 32), (uint32_t)pat, (uint32_t)(pat >> 32));
-    for (; A + 16 <= Z; A += 16) *reinterpret_cast<uint4*>(base + A) = p4;
-    piece(Z);
-}
 
 // One block per stream chunk (kChunk bytes, 16 per lane): expansion lengths,
 // block scan, look-back across the unit's chunks for the quartic byte index
 // of the chunk, then the work of Mode (one instantiation each, so that each
-// keeps only its own registers).  In quartic mode every lane writes the
-// quartic bytes its stream bytes expand to (runs as byte 121) and sets the
-// flag of each y-block that one of its literal bytes reaches.
+// keeps only its own registers).  Record mode writes payload p's tile
+// records at p * rstride.
 template <int Mode>
-__global__ __launch_bounds__(kThreads) void k_decode(GroupView g, uint64_t N, const uint8_t* __restrict__ in,
-                                                     uint64_t in_stride, uint64_t qstride,
+__global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t* __restrict__ in,
+                                                     uint64_t in_stride, uint64_t rstride,
                                                      const uint64_t* __restrict__ in_lens,
                                                      const float* __restrict__ scales, float s,
                                                      float* __restrict__ y, uint64_t* __restrict__ tstart,
-                                                     uint32_t* __restrict__ tlit, uint8_t* __restrict__ qbuf,
-                                                     uint8_t* __restrict__ yfl, uint64_t* __restrict__ flags,
+                                                     uint32_t* __restrict__ tlit, uint64_t* __restrict__ flags,
                                                      const uint32_t* __restrict__ dec_map,
                                                      const uint32_t* __restrict__ dec_first,
                                                      uint32_t* __restrict__ tickets, const uint32_t* __restrict__ ctrl,
@@ -1649,7 +1583,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, uint64_t N, co
                     }
                 }
             }
-        } else if (Mode == kDecodeRecord) {
+        } else {
             // A lane's 16 bytes expand to at most 224 quartic bytes, so at
             // most one tile boundary (a multiple of 1024) falls inside them,
             // d quartic bytes after the lane's first; the lane's literal bytes
@@ -1678,172 +1612,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, uint64_t N, co
                     rel += len;
                 }
             }
-            if (bi < 16 && d < lim) tstart[sg.etile0 + (p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
+            uint64_t* const ts = tstart + (uint64_t)p * rstride + sg.etile0;
+            uint32_t* const tl = tlit + (uint64_t)p * rstride + sg.etile0;
+            if (bi < 16 && d < lim) ts[(p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
             if (!bad) {
-                if (lit_lo) tlit[sg.etile0 + p0 / kETileBytes] = 1u;
-                if (lit_hi) tlit[sg.etile0 + (p0 + d) / kETileBytes] = 1u;
-            }
-        } else {
-            // quartic mode: the lane's quartic positions [pos, pos + tsum) of
-            // the tensor's slot, cut at B.  First all of them as byte 121,
-            // then the literal bytes over them (this lane's own stores, so
-            // they land in program order).
-            uint8_t* const qt = qbuf + (uint64_t)p * qstride + sg.stream_off;
-            const uint64_t q0 = min(pos, B), q1 = min(pos + tsum, B);
-            if (q1 > q0) fill_elements<1>(qt, q0, q1, kZero);
-            if (nlit || pos + tsum > B) {  // literals to place, or bytes past B to report
-                uint8_t* const fl = yfl + (uint64_t)p * yflag_bytes(N);
-                const uint64_t eo = sg.elem_off;
-                uint64_t lastY = ~0ull;
-                uint32_t w0 = wd[0], w1 = wd[1], w2 = wd[2], w3 = wd[3];
-#pragma unroll 1
-                for (uint32_t i = 0; i < nv; ++i) {
-                    const uint32_t byte = w0 & 255u;
-                    w0 = (w0 >> 8) | (w1 << 24);
-                    w1 = (w1 >> 8) | (w2 << 24);
-                    w2 = (w2 >> 8) | (w3 << 24);
-                    w3 >>= 8;
-                    if (byte < 243u) {
-                        if (pos >= B) {
-                            bad = true;
-                        } else if (byte != kZero) {
-                            qt[pos] = (uint8_t)byte;
-                            // the y-blocks its five elements reach
-                            const uint64_t e0 = eo + 5 * pos, e1 = eo + min(5 * pos + 4, (uint64_t)n - 1);
-                            if (e0 / kYBlock != lastY) fl[e0 / kYBlock] = 1;
-                            if (e1 / kYBlock != e0 / kYBlock) fl[e1 / kYBlock] = 1;
-                            lastY = e1 / kYBlock;
-                        }
-                        pos += 1;
-                    } else {
-                        pos += byte - kRunBase;
-                    }
-                }
+                if (lit_lo) tl[p0 / kETileBytes] = 1u;
+                if (lit_hi) tl[(p0 + d) / kETileBytes] = 1u;
             }
         }
         if (bad) raise_status(status, TLC_ERR_CORRUPT);
-    }
-}
-
-// Tensor holding group element e (e < the group's total).
-__device__ __forceinline__ uint32_t tensor_of(const GroupView& g, uint64_t e) {
-    if (!g.segs) return 0u;
-    const uint32_t info = g.ftile_info[e / kFTile];
-    const uint32_t g0 = info & ~kStraddle;
-    return (info & kStraddle) ? find_segment(g.segs, g0, min(g.count, g0 + kFTile + 1), e) : g0;
-}
-
-__device__ __forceinline__ YRec yrec_of(const GroupView& g, uint64_t b) {
-    if (g.yrec) return g.yrec[b];
-    YRec r;
-    r.qoff = 0;
-    r.u0 = (uint32_t)(b * kYBlock);
-    r.gi = 0;
-    return r;
-}
-
-__device__ __forceinline__ int field_code(uint32_t pat, uint32_t k) {  // sign-extended 2-bit field k
-    return (int)(pat << (30 - 2 * k)) >> 30;
-}
-
-// Codes of group elements e .. e+3 of a y-block that lies in one tensor:
-// tensor element u = r.u0 + (e - first element of the block), quartic bytes
-// u/5 and u/5 + 1 of the tensor's slot at q + r.qoff; 20 bits, element k in
-// bits 2k (the second byte is read only when an element < N needs it).
-__device__ __forceinline__ uint32_t codes4(const uint8_t* q, const YRec& r, uint32_t l, uint64_t e, uint64_t N,
-                                           const uint16_t* tab) {
-    const uint32_t u = r.u0 + 4 * l;
-    const uint64_t bq = r.qoff + u / 5;
-    const uint32_t d0 = u % 5;
-    const uint32_t x0 = q[bq];
-    const uint32_t x1 = d0 >= 2 && e + (5 - d0) < N ? q[bq + 1] : kZero;
-    const uint32_t p0 = tab ? tab[x0] : quartic_fields(x0), p1 = tab ? tab[x1] : quartic_fields(x1);
-    return ((p1 << 10) | p0) >> (2 * d0);
-}
-
-// The code of group element e in a y-block that spans tensors.
-__device__ __forceinline__ int code_at(const GroupView& g, const uint8_t* q, uint64_t e, uint32_t* gi) {
-    *gi = tensor_of(g, e);
-    const Seg sg = load_seg(g, *gi);
-    const uint64_t u = e - sg.elem_off;
-    return field_code(quartic_fields(q[sg.stream_off + u / 5]), (uint32_t)(u % 5));
-}
-
-// acc += q_p * (M_p*s) for payloads p = 0 .. payloads-1 in that order, only
-// where q_p != 0 (so an element no payload touches keeps its bits, -0.0
-// included).  One block per y-block, four elements per lane; a y-block where
-// no payload has a nonzero code is not touched.  Quartic bytes are split
-// into codes through a 243-entry table in LDS.
-__global__ __launch_bounds__(kThreads) void k_apply(GroupView g, uint64_t N, uint32_t payloads,
-                                                    const uint8_t* __restrict__ q, uint64_t qstride,
-                                                    const uint8_t* __restrict__ yfl,
-                                                    const float* __restrict__ scales, float s,
-                                                    float* __restrict__ acc) {
-    __shared__ uint16_t s_tab[243];
-    const uint64_t b = blockIdx.x;
-    const uint64_t fstride = yflag_bytes(N);
-    uint32_t any = 0;
-    for (uint32_t p = 0; p < payloads; ++p) any |= yfl[p * fstride + b];
-    if (!any) return;
-    if (threadIdx.x < 243) s_tab[threadIdx.x] = (uint16_t)quartic_fields(threadIdx.x);
-    const uint64_t e = (b * kThreads + threadIdx.x) * 4;
-    const bool full = e + 4 <= N;
-    f4 a = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (full) {
-        a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(acc + e));
-    } else {
-        if (e < N) a.x = acc[e];
-        if (e + 1 < N) a.y = acc[e + 1];
-        if (e + 2 < N) a.z = acc[e + 2];
-    }
-    const YRec r = yrec_of(g, b);
-    __syncthreads();
-    const bool span = (r.gi & kStraddle) != 0;
-    constexpr uint32_t kGroupP = 8;  // payloads whose loads are in flight together
-    for (uint32_t p0 = 0; p0 < payloads; p0 += kGroupP) {
-        uint32_t cs[kGroupP];
-        float ms[kGroupP];
-#pragma unroll
-        for (uint32_t k = 0; k < kGroupP; ++k) {
-            cs[k] = 0;
-            ms[k] = 0.0f;
-            const uint32_t p = p0 + k;
-            if (p < payloads && yfl[p * fstride + b] && !span && e < N) {
-                ms[k] = scales[(uint64_t)p * g.count + r.gi] * s;
-                cs[k] = codes4(q + p * qstride, r, threadIdx.x, e, N, s_tab);
-            }
-        }
-#pragma unroll
-        for (uint32_t k = 0; k < kGroupP; ++k) {
-            const uint32_t p = p0 + k;
-            if (p >= payloads || !yfl[p * fstride + b]) continue;
-            float m[4] = {ms[k], ms[k], ms[k], ms[k]};
-            uint32_t c = cs[k];
-            if (span) {  // per element: its tensor's code and M*s
-                c = 0;
-#pragma unroll
-                for (uint32_t i = 0; i < 4; ++i) {
-                    if (e + i < N) {
-                        uint32_t gi;
-                        const int qq = code_at(g, q + p * qstride, e + i, &gi);
-                        c |= (uint32_t)(qq & 3) << (2 * i);
-                        m[i] = scales[(uint64_t)p * g.count + gi] * s;
-                    }
-                }
-            }
-            const int q0 = field_code(c, 0), q1 = field_code(c, 1), q2 = field_code(c, 2), q3 = field_code(c, 3);
-            if (q0) a.x = a.x + (float)q0 * m[0];
-            if (q1) a.y = a.y + (float)q1 * m[1];
-            if (q2) a.z = a.z + (float)q2 * m[2];
-            if (q3) a.w = a.w + (float)q3 * m[3];
-        }
-    }
-    if (full) {
-        __builtin_nontemporal_store(a, reinterpret_cast<f4*>(acc + e));
-    } else {
-        if (e < N) acc[e] = a.x;
-        if (e + 1 < N) acc[e + 1] = a.y;
-        if (e + 2 < N) acc[e + 2] = a.z;
     }
 }
 
@@ -1983,6 +1760,343 @@ __global__ __launch_bounds__(kThreads) void k_expand(GroupView g, uint32_t etile
             if (u0 + 2 >= 0 && u0 + 2 < (int32_t)nel) yt[u0 + 2] = v.z;
             if (u0 + 3 < (int32_t)nel) yt[u0 + 3] = v.w;
         }
+    }
+}
+
+// Payload l's 64-bit value held by lane l, in scalar registers (l uniform).
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, (int)l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)l);
+    return (uint64_t)hi << 32 | lo;
+}
+
+// Inclusive prefix sum over the wavefront with DPP moves: shifts of 1, 2, 4
+// and 8 lanes within each row of 16, then the last lane of row 0 added to
+// row 1 and that of row 2 to row 3 (row_bcast:15), then the last lane of
+// row 1 added to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_sum_dpp(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+    return x;
+}
+
+// The five codes of a quartic byte as 2-bit fields, first element lowest:
+// bit 2d is set when code d is nonzero, bit 2d+1 when the value it adds is
+// negative: q = -1 adds -M*s, and q = 0 adds -0.0, which leaves every
+// finite value's bits unchanged (x + -0.0 = x, -0.0 included).
+__device__ __forceinline__ uint32_t quartic_fields(uint32_t byte) {
+    uint32_t pat = 0;
+    for (uint32_t d = 0; d < 5; ++d) {
+        const uint32_t digit = byte % 3u;
+        byte /= 3u;
+        pat |= (digit == 1u ? 2u : digit == 2u ? 1u : 3u) << (2 * d);
+    }
+    return pat;
+}
+
+// Where an encode tile's bytes lie in a payload's stream, from the tile's
+// start record: from byte sb (whose expansion holds `skip` quartic bytes of
+// the tile before) to the byte where the tensor's next tile begins (a run
+// can straddle), at most 1024 bytes (each covers at least one quartic
+// byte), cut at the stream's end.
+struct TileBytes {
+    uint64_t sb, have;
+    uint32_t skip;
+};
+__device__ __forceinline__ TileBytes tile_bytes(uint64_t ts, uint64_t tn, uint64_t L, uint64_t B, bool last_tile) {
+    TileBytes t;
+    t.sb = ts & 0xFFFFFFFFull;
+    uint64_t eb = min(min(L, B), t.sb + kETileBytes);
+    if (!last_tile && tn != kNoStart) eb = min(eb, (tn & 0xFFFFFFFFull) + 1);
+    t.have = eb > t.sb ? eb - t.sb : 0;
+    t.skip = (uint32_t)(ts >> 32);
+    return t;
+}
+
+// Dword w of the 4-byte-aligned window holding a tile's bytes (lane l of
+// block b loads dword 64 b + l), or 0 past the bytes; a dword loaded holds
+// a byte of the tile, so it lies in a readable page.
+__device__ __forceinline__ uint32_t tile_dword(const uint8_t* tensor_stream, const TileBytes& t, uint32_t w) {
+    const uint8_t* const a4 = tensor_stream + (t.sb & ~3ull);
+    const uint64_t o4 = t.sb & 3u;
+    return 4ull * w < o4 + t.have ? reinterpret_cast<const uint32_t*>(a4)[w] : 0u;
+}
+
+// Where encode tile e lies (wave-uniform).
+struct ApplyTile {
+    uint64_t a0;    // group element of its first value
+    uint64_t soff;  // stream slot of its tensor
+    uint64_t B;     // quartic bytes of its tensor
+    uint32_t gi, nel, need;
+    int32_t mis;    // a0 mod 4
+    uint32_t last;  // 1 for the tensor's last tile
+};
+__device__ __forceinline__ ApplyTile apply_tile(const Seg& sg, uint32_t gi, uint32_t e) {
+    ApplyTile t;
+    t.gi = gi;
+    const uint32_t j = e - sg.etile0;
+    t.nel = min(kETile, sg.n - j * kETile);
+    t.B = quartic_len(sg.n);
+    t.need = (uint32_t)min((uint64_t)kETileBytes, t.B - (uint64_t)j * kETileBytes);
+    t.last = (uint64_t)(j + 1) * kETileBytes >= t.B ? 1u : 0u;
+    t.a0 = sg.elem_off + (uint64_t)j * kETile;
+    t.mis = (int32_t)(t.a0 & 3);
+    t.soff = sg.stream_off;
+    return t;
+}
+
+// Payload `lane`'s record of tile e (lanes past the payloads hold none).
+struct ApplyRec {
+    uint64_t ts, tn, L;
+    uint32_t lit;
+    float ms;
+};
+__device__ __forceinline__ ApplyRec apply_rec(const GroupView& g, uint32_t etiles, uint32_t payloads, uint32_t e,
+                                              uint32_t gi, const uint64_t* tstart, const uint32_t* tlit,
+                                              const uint64_t* in_lens, const float* scales, float s) {
+    ApplyRec r;
+    r.ts = kNoStart;
+    r.tn = kNoStart;
+    r.L = 0;
+    r.lit = 0;
+    r.ms = 0.0f;
+    const uint32_t lane = (uint32_t)lane_id();
+    if (lane < payloads) {
+        const uint64_t i = (uint64_t)lane * etiles + e;
+        const uint64_t u = (uint64_t)lane * g.count + gi;
+        r.ts = tstart[i];
+        if (e + 1 < etiles) r.tn = tstart[i + 1];
+        r.lit = tlit[i];
+        r.L = in_lens[u];
+        r.ms = scales[u] * s;
+    }
+    return r;
+}
+
+// acc += q_p * (M_p*s) for payloads p = 0 .. payloads-1 in that order, only
+// where q_p != 0 (an element no payload touches keeps its bits, -0.0
+// included).  Persistent wavefronts (one per block), each over a contiguous
+// range of encode tiles (up to 5120 elements of one tensor), the ranges
+// contiguous per XCD.  For each tile, lane p reads payload p's record:
+// where the tile begins in its stream, and whether the bytes there hold a
+// nonzero code; a tile where no payload has one is not touched.  Otherwise
+// the tile of acc is copied into LDS (tile element u at word u + mis, so
+// that float4 group h is LDS words 4h .. 4h+3).  Then, one payload after the
+// other, its bytes for the tile are walked 256 at a time: lane l takes bytes
+// l, l+64, l+128 and l+192 (ds_bpermute from the lanes that loaded them as
+// dwords), four wave scans of their expansion lengths give each byte's
+// quartic position, and every element of every literal byte is read from
+// LDS, has its code's value added (+-M*s, or -0.0 for a zero code, which
+// leaves the bits unchanged) and is written back; bytes that are not
+// literals use a dummy word of their lane.  Within one payload no two
+// literals share an element, and the payloads follow each other in order.
+// Neighbouring lanes hold neighbouring bytes, so their elements fall in
+// different LDS banks.  The tile is written back once.  While one tile is
+// decoded, the next tile's acc and its payloads' first 256 bytes (8
+// payloads' worth) are in flight, and the records of the one after.
+constexpr uint32_t kApplyFetch = 8;                           // payloads whose first bytes are fetched ahead
+constexpr uint32_t kApplyVec = ((kETile + 6) / 4 + 63) / 64;  // float4 groups per lane: 21
+constexpr uint32_t kApplyWords = (kETile + 3 + 3) / 4 * 4;    // LDS words of a tile: 5124
+
+__device__ __forceinline__ void apply_fetch(const ApplyTile& t, const ApplyRec& r, uint64_t lits, const float* acc,
+                                            const uint8_t* in, uint64_t in_stride, f4 (&v)[kApplyVec],
+                                            uint32_t (&dw)[kApplyFetch]) {
+    const int lane = lane_id();
+    const float* const at = acc + t.a0;
+    const int32_t ng = (t.mis + (int32_t)t.nel + 3) / 4;
+#pragma unroll
+    for (uint32_t k = 0; k < kApplyVec; ++k) {
+        const int32_t h = lane + 64 * (int32_t)k;
+        const int32_t u0 = 4 * h - t.mis;
+        v[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (lits && h < ng) {
+            if (u0 >= 0 && u0 + 4 <= (int32_t)t.nel) {
+                v[k] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(at + u0));
+            } else {
+#pragma unroll
+                for (int32_t i = 0; i < 4; ++i)
+                    if (u0 + i >= 0 && u0 + i < (int32_t)t.nel) v[k][i] = at[u0 + i];
+            }
+        }
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kApplyFetch; ++k) {
+        dw[k] = 0u;
+        if (lits & (1ull << k)) {
+            const TileBytes tb =
+                tile_bytes(readlane64(r.ts, k), readlane64(r.tn, k), readlane64(r.L, k), t.B, t.last != 0u);
+            dw[k] = tile_dword(in + (uint64_t)k * in_stride + t.soff, tb, (uint32_t)lane);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64, 2) void k_apply(GroupView g, uint32_t etiles, uint32_t nwaves, uint32_t payloads,
+                                                 const uint8_t* __restrict__ in, uint64_t in_stride,
+                                                 const uint64_t* __restrict__ in_lens,
+                                                 const float* __restrict__ scales, float s,
+                                                 const uint64_t* __restrict__ tstart,
+                                                 const uint32_t* __restrict__ tlit, float* __restrict__ acc,
+                                                 int* __restrict__ status) {
+    __shared__ __align__(16) float s_acc[kApplyWords + 64];  // the tile, then a dummy word per lane
+    __shared__ uint16_t s_tab[256];
+    const int lane = lane_id();
+    const uint32_t w = xcd_unit(blockIdx.x, nwaves);
+    if (w >= nwaves) return;
+    const uint32_t per = (etiles + nwaves - 1) / nwaves;
+    const uint32_t e_end = min(etiles, (w + 1) * per);
+    uint32_t e = w * per;
+    if (e >= e_end) return;
+    for (uint32_t t = (uint32_t)lane; t < 243u; t += 64u) s_tab[t] = (uint16_t)quartic_fields(t);
+
+    // the tensor of the furthest tile looked up so far; tiles are in tensor
+    // order, so the next one is the same tensor or the one after
+    uint32_t gi_f = etile_owner(g, e);
+    Seg sg_f = load_seg(g, gi_f);
+    auto tile_at = [&](uint32_t te) {
+        while (gi_f + 1 < g.count && te - sg_f.etile0 >= etiles_of(sg_f.n)) sg_f = load_seg(g, ++gi_f);
+        return apply_tile(sg_f, gi_f, te);
+    };
+    ApplyTile t0 = tile_at(e);
+    ApplyRec r0 = apply_rec(g, etiles, payloads, e, t0.gi, tstart, tlit, in_lens, scales, s);
+    uint64_t lits0 = __ballot(r0.lit != 0u && r0.ts != kNoStart);
+    f4 v[kApplyVec];  // the acc of the tile about to be decoded, on its way to LDS
+    uint32_t d0[kApplyFetch];
+    apply_fetch(t0, r0, lits0, acc, in, in_stride, v, d0);
+    bool has1 = e + 1 < e_end;
+    ApplyTile t1 = t0;
+    ApplyRec r1 = r0;
+    if (has1) {
+        t1 = tile_at(e + 1);
+        r1 = apply_rec(g, etiles, payloads, e + 1, t1.gi, tstart, tlit, in_lens, scales, s);
+    }
+    // ds_bpermute byte addresses: byte 64 q + l of a 256-byte window is byte
+    // l & 3 of the dword of lane 16 q + l / 4
+    const uint32_t src_lane = (uint32_t)lane >> 2, src_shift = 8u * ((uint32_t)lane & 3u);
+    for (;;) {
+        if (__ballot((uint32_t)lane < payloads && r0.ts == kNoStart) && lane == 0)
+            raise_status(status, TLC_ERR_CORRUPT);  // a stream that never reached this tile
+        const int32_t ng = (t0.mis + (int32_t)t0.nel + 3) / 4;
+        if (lits0) {
+#pragma unroll
+            for (uint32_t k = 0; k < kApplyVec; ++k) {
+                const int32_t h = lane + 64 * (int32_t)k;
+                if (h < ng) reinterpret_cast<f4*>(s_acc)[h] = v[k];
+            }
+        }
+        wave_sync();
+        // the next tile's data and the records of the one after, in flight
+        // while this tile is decoded
+        uint64_t lits1 = 0;
+        uint32_t d1[kApplyFetch];
+        if (has1) {
+            lits1 = __ballot(r1.lit != 0u && r1.ts != kNoStart);
+            apply_fetch(t1, r1, lits1, acc, in, in_stride, v, d1);
+        }
+        const bool has2 = e + 2 < e_end;
+        ApplyTile t2 = t1;
+        ApplyRec r2 = r1;
+        if (has2) {
+            t2 = tile_at(e + 2);
+            r2 = apply_rec(g, etiles, payloads, e + 2, t2.gi, tstart, tlit, in_lens, scales, s);
+        }
+        if (lits0) {
+            for (uint32_t p = 0; p < payloads; ++p) {
+                if (!((lits0 >> p) & 1u)) continue;
+                const uint32_t mb = (uint32_t)__builtin_amdgcn_readlane(__builtin_bit_cast(int, r0.ms), (int)p);
+                const uint8_t* const ps = in + (uint64_t)p * in_stride + t0.soff;
+                const TileBytes tb = tile_bytes(readlane64(r0.ts, p), readlane64(r0.tn, p), readlane64(r0.L, p), t0.B,
+                                                t0.last != 0u);
+                const uint32_t o4 = (uint32_t)(tb.sb & 3u);
+                const uint32_t span = o4 + (uint32_t)tb.have;  // window bytes to walk
+                uint32_t carry = 0;                             // quartic bytes of the tile so far
+                uint32_t cur = 0;
+#pragma unroll
+                for (uint32_t k = 0; k < kApplyFetch; ++k)
+                    if (p == k) cur = d0[k];
+                for (uint32_t b = 0; 256u * b < span; ++b) {
+                    if (b > 0 || p >= kApplyFetch) cur = tile_dword(ps, tb, 64u * b + (uint32_t)lane);
+                    uint32_t len[4], pat[4], byte[4], excl[4], tot[4];
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        const uint32_t wpos = 256u * b + 64u * q + (uint32_t)lane;  // window byte of this lane
+                        const uint32_t word =
+                            (uint32_t)__builtin_amdgcn_ds_bpermute((int)((16u * q + src_lane) * 4u), (int)cur);
+                        byte[q] = (word >> src_shift) & 255u;
+                        pat[q] = s_tab[min(byte[q], 242u)];
+                        const bool valid = wpos >= o4 && wpos < span;
+                        len[q] = valid ? (byte[q] < 243u ? 1u : byte[q] - kRunBase) : 0u;
+                        if (wpos == o4) len[q] = len[q] > tb.skip ? len[q] - tb.skip : 0u;
+                    }
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        const uint32_t incl = wave_incl_sum_dpp(len[q]);
+                        excl[q] = incl - len[q];
+                        tot[q] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                    }
+                    // every element of every literal byte, read before any is written
+                    uint32_t at_[4];
+                    uint32_t base = carry;
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        const uint32_t pos = base + excl[q];  // tile quartic byte of this lane's byte
+                        const bool lit = len[q] != 0u && byte[q] < 243u && byte[q] != kZero && pos < t0.need;
+                        at_[q] = lit ? 5u * pos + (uint32_t)t0.mis : kApplyWords + (uint32_t)lane;
+                        pat[q] = lit ? pat[q] : 0x2AAu;  // five zero codes
+                        base += tot[q];
+                    }
+                    carry = base;
+                    float x[4][5];
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+#pragma unroll
+                        for (uint32_t d = 0; d < 5; ++d) x[q][d] = s_acc[at_[q] + (pat[q] == 0x2AAu ? 0u : d)];
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+#pragma unroll
+                        for (uint32_t d = 0; d < 5; ++d) {
+                            const uint32_t mask = (uint32_t)__builtin_amdgcn_sbfe((int)pat[q], 2 * d, 1);
+                            const uint32_t neg = __builtin_amdgcn_ubfe(pat[q], 2 * d + 1, 1);
+                            x[q][d] = x[q][d] + __builtin_bit_cast(float, (neg << 31) | (mb & mask));
+                        }
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+#pragma unroll
+                        for (uint32_t d = 0; d < 5; ++d) s_acc[at_[q] + (pat[q] == 0x2AAu ? 0u : d)] = x[q][d];
+                }
+                if (carry < t0.need && lane == 0) raise_status(status, TLC_ERR_CORRUPT);
+            }
+            wave_sync();  // every element's sum is in LDS
+            float* const at = acc + t0.a0;
+#pragma unroll
+            for (uint32_t k = 0; k < kApplyVec; ++k) {
+                const int32_t h = lane + 64 * (int32_t)k;
+                const int32_t u0 = 4 * h - t0.mis;
+                if (h < ng) {
+                    const f4 v = reinterpret_cast<const f4*>(s_acc)[h];
+                    if (u0 >= 0 && u0 + 4 <= (int32_t)t0.nel) {
+                        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(at + u0));
+                    } else {
+#pragma unroll
+                        for (int32_t i = 0; i < 4; ++i)
+                            if (u0 + i >= 0 && u0 + i < (int32_t)t0.nel) at[u0 + i] = v[i];
+                    }
+                }
+            }
+        }
+        if (!has1) break;
+        ++e;
+        t0 = t1;
+        r0 = r1;
+        lits0 = lits1;
+#pragma unroll
+        for (uint32_t k = 0; k < kApplyFetch; ++k) d0[k] = d1[k];
+        t1 = t2;
+        r1 = r2;
+        has1 = has2;
     }
 }
 
@@ -2229,8 +2343,8 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
 // device.  Such kernels hand work to their blocks or waves round-robin, so a
 // grid larger than this leaves a second, partial round of blocks running
 // alone at the end.
-enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridDecodeQuartic, kGridKinds };
-uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap) {
+enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridApply, kGridKinds };
+uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap, int threads = kThreads) {
     static std::mutex mu;
     static std::vector<uint32_t> per_dev;  // kGridKinds entries per device, 0 = not queried
     int dev = 0;
@@ -2241,7 +2355,7 @@ uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap) {
     if (!per_dev[at]) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) == hipSuccess && cus > 0 &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) == hipSuccess && cus > 0 &&
             per_cu > 0)
             per_dev[at] = (uint32_t)std::min<int64_t>((int64_t)cus * per_cu, cap);
         else
@@ -2261,7 +2375,7 @@ constexpr uint64_t chunks_host(uint64_t n) {
 
 // Sizes of everything a call needs, for one tensor or a group.
 struct Dims {
-    uint64_t count, total, ftiles, etiles, spans, chunks, stream_bytes;
+    uint64_t count, total, ftiles, etiles, spans, chunks;
 };
 
 struct Layout {
@@ -2298,9 +2412,7 @@ constexpr Layout ws_layout(const Dims& d) {
     return l;
 }
 
-constexpr Dims single_dims(uint64_t n) {
-    return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n), align_up((n + 4) / 5, 16)};
-}
+constexpr Dims single_dims(uint64_t n) { return {1, n, ftiles_of(n), etiles_host(n), spans_host(n), chunks_host(n)}; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_s(float s) { return s >= 1.0f && s < 2.0f; }  // false for NaN
@@ -2320,7 +2432,7 @@ Plan single_plan(uint64_t n) {
 }
 
 struct TableLayout {
-    size_t segs, ftile_info, span_seg, etile_seg, yrec, total;
+    size_t segs, ftile_info, span_seg, etile_seg, total;
 };
 TableLayout table_layout(const Dims& d) {
     TableLayout t;
@@ -2328,14 +2440,12 @@ TableLayout table_layout(const Dims& d) {
     t.ftile_info = align_up(t.segs + d.count * sizeof(Seg), 16);
     t.span_seg = align_up(t.ftile_info + d.ftiles * sizeof(uint32_t), 16);
     t.etile_seg = align_up(t.span_seg + d.spans * sizeof(uint32_t), 16);
-    t.yrec = align_up(t.etile_seg + d.etiles * sizeof(uint32_t), 16);
-    t.total = align_up(t.yrec + yblocks_of(d.total) * sizeof(YRec), 16);
+    t.total = align_up(t.etile_seg + d.etiles * sizeof(uint32_t), 16);
     return t;
 }
 
 Dims dims_of(const tlc_group_info* info) {
-    return {info->count, info->total_elems, ftiles_of(info->total_elems), info->tiles, info->spans, info->chunks,
-            info->stream_bytes};
+    return {info->count, info->total_elems, ftiles_of(info->total_elems), info->tiles, info->spans, info->chunks};
 }
 
 int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
@@ -2350,7 +2460,6 @@ int group_plan_of(const tlc_group_info* info, const void* d_table, Plan* p) {
     p->g.ftile_info = reinterpret_cast<const uint32_t*>(base + t.ftile_info);
     p->g.span_seg = reinterpret_cast<const uint32_t*>(base + t.span_seg);
     p->g.etile_seg = reinterpret_cast<const uint32_t*>(base + t.etile_seg);
-    p->g.yrec = reinterpret_cast<const YRec*>(base + t.yrec);
     p->g.count = (uint32_t)info->count;
     return TLC_OK;
 }
@@ -2433,10 +2542,8 @@ struct DecState {
     uint32_t* map;
     uint32_t* first;
     uint32_t* tickets;
-    uint64_t* tstart;
-    uint32_t* tlit;
-    uint8_t* qbuf;  // payload p's quartic bytes at qbuf + p * stream_bytes
-    uint8_t* yfl;   // payload p's y-block flags at yfl + p * yflag_bytes
+    uint64_t* tstart;  // payload p's tile starts at tstart + p * etiles
+    uint32_t* tlit;    // payload p's literal flags at tlit + p * etiles
 };
 
 // Decompress and the single-payload accumulate use the call's workspace:
@@ -2451,14 +2558,12 @@ DecState dec_state_single(const Layout& l, char* w) {
     d.tickets = reinterpret_cast<uint32_t*>(w + l.chunk_tickets);
     d.tstart = reinterpret_cast<uint64_t*>(w + l.etile_agg);
     d.tlit = reinterpret_cast<uint32_t*>(w + l.etmax);
-    d.qbuf = nullptr;
-    d.yfl = nullptr;
     return d;
 }
 
 // Workspace of an accumulate-many call on P payloads.
 struct ManyLayout {
-    size_t ctrl = 0, flags = 0, map = 0, first = 0, tickets = 0, qbuf = 0, yfl = 0, total = 0;
+    size_t ctrl = 0, flags = 0, map = 0, first = 0, tickets = 0, tstart = 0, tlit = 0, total = 0;
 };
 constexpr ManyLayout many_layout(const Dims& d, uint64_t P) {
     ManyLayout l;
@@ -2473,8 +2578,8 @@ constexpr ManyLayout many_layout(const Dims& d, uint64_t P) {
     l.map = take(P * d.chunks * sizeof(uint32_t));
     l.first = take(P * d.count * sizeof(uint32_t));
     l.tickets = take(P * d.count * sizeof(uint32_t));
-    l.qbuf = take(P * d.stream_bytes);
-    l.yfl = take(P * yflag_bytes(d.total));
+    l.tstart = take(P * d.etiles * sizeof(uint64_t));
+    l.tlit = take(P * d.etiles * sizeof(uint32_t));
     l.total = off;
     return l;
 }
@@ -2487,30 +2592,26 @@ int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in,
                   const DecState& ds, int* status, uint32_t* hint, hipStream_t st) {
     const GroupView g = p.g;
     const uint64_t chunks = p.d.chunks * payloads, etiles = p.d.etiles;
-    const uint64_t nyfl = mode == kDecodeQuartic ? payloads * yflag_bytes(p.d.total) : 0;
     uint64_t* const tstart = mode == kDecodeRecord ? ds.tstart : nullptr;
-    const uint64_t blocks = std::max(std::max((n_fill / 4 + kThreads - 1) / kThreads,
-                                              (std::max(chunks, tstart ? etiles : 0) + kThreads - 1) / kThreads),
-                                     (nyfl / 16 + kThreads - 1) / kThreads);
+    const uint64_t ntiles = tstart ? payloads * etiles : 0;
+    const uint64_t blocks = std::max((n_fill / 4 + kThreads - 1) / kThreads,
+                                     (std::max(chunks, ntiles) + kThreads - 1) / kThreads);
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
     int rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
         k_prep<<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart, ds.tlit,
-                                               etiles, ds.yfl, nyfl, ds.map, ds.first, ds.tickets, ds.ctrl, status,
-                                               hint);
+                                               ntiles, ds.map, ds.first, ds.tickets, ds.ctrl, status, hint);
     });
     if (rc) return rc;
-    auto kern = mode == kDecodeWrite     ? k_decode<kDecodeWrite>
-                : mode == kDecodeAdd     ? k_decode<kDecodeAdd>
-                : mode == kDecodeRecord  ? k_decode<kDecodeRecord>
-                                         : k_decode<kDecodeQuartic>;
+    auto kern = mode == kDecodeWrite ? k_decode<kDecodeWrite>
+                : mode == kDecodeAdd ? k_decode<kDecodeAdd>
+                                     : k_decode<kDecodeRecord>;
     const GridKind gk = (GridKind)(kGridDecodeWrite + mode);
-    static const char* const names[] = {"tlc_decode", "tlc_decode_add", "tlc_decode_record", "tlc_decode_quartic"};
+    static const char* const names[] = {"tlc_decode", "tlc_decode_add", "tlc_decode_record"};
     const uint32_t grid =
         (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
     return launch(names[mode], st, [&] {
-        kern<<<grid, kThreads, 0, st>>>(g, p.d.total, in, in_stride, p.d.stream_bytes, in_lens, scales, s, y, tstart,
-                                        ds.tlit, ds.qbuf, ds.yfl, ds.flags, ds.map, ds.first, ds.tickets, ds.ctrl,
-                                        status);
+        kern<<<grid, kThreads, 0, st>>>(g, in, in_stride, etiles, in_lens, scales, s, y, tstart, ds.tlit, ds.flags,
+                                        ds.map, ds.first, ds.tickets, ds.ctrl, status);
     });
 }
 
@@ -2547,14 +2648,15 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     });
 }
 
-// Accumulate-many: the quartic bytes of every payload in one decoder launch,
-// then one pass over acc that applies them in payload order.
-int run_accumulate_many(const Plan& p, uint32_t payloads, const uint8_t* in, uint64_t in_stride,
-                        const uint64_t* in_lens, const float* scales, float s, float* acc, void* ws,
-                        size_t ws_bytes, int* status, hipStream_t st) {
+// Accumulate-many: the tile starts of every payload in one decoder launch,
+// then one pass over acc that decodes and applies them tile by tile.
+// stream_bytes: the group's stream buffer size (a payload's slots).
+int run_accumulate_many(const Plan& p, uint64_t stream_bytes, uint32_t payloads, const uint8_t* in,
+                        uint64_t in_stride, const uint64_t* in_lens, const float* scales, float s, float* acc,
+                        void* ws, size_t ws_bytes, int* status, hipStream_t st) {
     if (!in || !in_lens || !scales || !acc || !status) return TLC_ERR_INVALID_ARG;
     if (payloads == 0 || payloads > kMaxPayloads || !aligned16(acc) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
-    if (payloads > 1 && (in_stride < p.d.stream_bytes || (in_stride & 15))) return TLC_ERR_INVALID_ARG;
+    if (payloads > 1 && (in_stride < stream_bytes || (in_stride & 15))) return TLC_ERR_INVALID_ARG;
     const ManyLayout ml = many_layout(p.d, payloads);
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < ml.total) return TLC_ERR_WORKSPACE;
     char* w = static_cast<char*>(ws);
@@ -2564,18 +2666,18 @@ int run_accumulate_many(const Plan& p, uint32_t payloads, const uint8_t* in, uin
     ds.map = reinterpret_cast<uint32_t*>(w + ml.map);
     ds.first = reinterpret_cast<uint32_t*>(w + ml.first);
     ds.tickets = reinterpret_cast<uint32_t*>(w + ml.tickets);
-    ds.tstart = nullptr;
-    ds.tlit = nullptr;
-    ds.qbuf = reinterpret_cast<uint8_t*>(w + ml.qbuf);
-    ds.yfl = reinterpret_cast<uint8_t*>(w + ml.yfl);
-    int rc = launch_decode(p, payloads, kDecodeQuartic, in, in_stride, in_lens, scales, s, nullptr, 0, ds, status,
+    ds.tstart = reinterpret_cast<uint64_t*>(w + ml.tstart);
+    ds.tlit = reinterpret_cast<uint32_t*>(w + ml.tlit);
+    int rc = launch_decode(p, payloads, kDecodeRecord, in, in_stride, in_lens, scales, s, nullptr, 0, ds, status,
                            nullptr, st);
     if (rc) return rc;
     const GroupView g = p.g;
-    const uint64_t N = p.d.total;
+    const uint64_t etiles = p.d.etiles;
+    const uint32_t nwaves = (uint32_t)std::min<uint64_t>(
+        etiles, resident_grid(kGridApply, reinterpret_cast<const void*>(k_apply), 1u << 16, 64));
     return launch("tlc_apply", st, [&] {
-        k_apply<<<(uint32_t)yblocks_of(N), kThreads, 0, st>>>(g, N, payloads, ds.qbuf, p.d.stream_bytes, ds.yfl,
-                                                              scales, s, acc);
+        k_apply<<<xcd_grid(nwaves), 64, 0, st>>>(g, (uint32_t)etiles, nwaves, payloads, in, in_stride, in_lens,
+                                                scales, s, ds.tstart, ds.tlit, acc, status);
     });
 }
 
@@ -2755,7 +2857,7 @@ int tlc_decompress_accumulate(const uint8_t* in, const uint64_t* in_len, const f
 int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, void* table,
                    size_t table_capacity, uint64_t* stream_offset) {
     if (!sizes || !info || count == 0 || count > 0x7FFFFFFFull) return TLC_ERR_INVALID_ARG;
-    Dims d = {count, 0, 0, 0, 0, 0, 0};
+    Dims d = {count, 0, 0, 0, 0, 0};
     uint64_t stream = 0;
     for (uint64_t i = 0; i < count; ++i) {
         const uint64_t n = sizes[i];
@@ -2767,7 +2869,6 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
         stream = align_up(stream, 16) + tlc_compress_bound(n);
     }
     d.ftiles = ftiles_of(d.total);
-    d.stream_bytes = align_up(stream, 16);
     if (d.ftiles + d.count > 0xFFFFFFFFull || d.etiles > 0xFFFFFFFFull || d.chunks > 0xFFFFFFFFull)
         return TLC_ERR_INVALID_ARG;
     const TableLayout t = table_layout(d);
@@ -2785,8 +2886,6 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
     uint32_t* ftile_info = table ? reinterpret_cast<uint32_t*>(base + t.ftile_info) : nullptr;
     uint32_t* span_seg = table ? reinterpret_cast<uint32_t*>(base + t.span_seg) : nullptr;
     uint32_t* etile_seg = table ? reinterpret_cast<uint32_t*>(base + t.etile_seg) : nullptr;
-    char* const yrec = table ? base + t.yrec : nullptr;
-    uint64_t yb = 0;  // next y-block to describe
     if (table) {
         memset(base, 0, t.total);
         TableHeader h = {kMagic, count, d.ftiles, d.etiles, d.spans, d.chunks, d.total, info->stream_bytes};
@@ -2808,19 +2907,11 @@ int tlc_group_plan(const uint64_t* sizes, uint64_t count, tlc_group_info* info, 
             memcpy(base + t.segs + i * sizeof(Seg), &sg, sizeof(Seg));
             for (uint64_t k = 0; k < spans_host(n); ++k) span_seg[span + k] = (uint32_t)i | (spans_host(n) > 1 ? kMulti : 0u);
             for (uint64_t k = 0; k < etiles_host(n); ++k) etile_seg[etile + k] = (uint32_t)i;
-            // flat tiles and y-blocks whose first element lies in this tensor
+            // flat tiles whose first element lies in this tensor
             const uint64_t end = eoff + n;
             for (; ft < d.ftiles && ft * kFTile < end; ++ft) {
                 const uint64_t last = std::min<uint64_t>(d.total, (ft + 1) * kFTile) - 1;
                 ftile_info[ft] = (uint32_t)i | (last >= end ? kStraddle : 0u);
-            }
-            for (; yb < yblocks_of(d.total) && yb * kYBlock < end; ++yb) {
-                const uint64_t last = std::min<uint64_t>(d.total, (yb + 1) * kYBlock) - 1;
-                YRec r;
-                r.qoff = soff;
-                r.u0 = (uint32_t)(yb * kYBlock - eoff);
-                r.gi = (uint32_t)i | (last >= end ? kStraddle : 0u);
-                memcpy(yrec + yb * sizeof(YRec), &r, sizeof(YRec));
             }
         }
         etile += etiles_host(n);
@@ -2908,8 +2999,8 @@ int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void*
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_accumulate_many(p, payloads, in, in_stride, in_lens, scales, s, acc, workspace, workspace_bytes,
-                               status, static_cast<hipStream_t>(stream));
+    return run_accumulate_many(p, info->stream_bytes, payloads, in, in_stride, in_lens, scales, s, acc, workspace,
+                               workspace_bytes, status, static_cast<hipStream_t>(stream));
 }
 
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream) {

@@ -91,21 +91,13 @@ def test_group_plan_layout():
         first, last = t * 512, min(N, (t + 1) * 512) - 1
         want = int(seg_of[first]) | (0x80000000 if seg_of[last] != seg_of[first] else 0)
         assert int(info_arr[t]) == want, t
-    # per 1024-element block (after the span owners and the encode-tile owners): the stream slot of
-    # its first element's tensor, that element's index in it, the tensor, high bit if the block
-    # also holds a later tensor
+    # then the span owners and the encode-tile owners, and nothing after them
     up = lambda v: -(-v // 16) * 16
     span_at = up(fi_at + 4 * ftiles)
     et_at = up(span_at + 4 * spans)
-    y_at = up(et_at + 4 * etiles)
-    yb = -(-N // 1024)
-    assert info.table_bytes == up(y_at + 16 * yb)
-    yrec = np.frombuffer(table[y_at:y_at + 16 * yb], dtype=np.dtype([("qoff", "<u8"), ("u0", "<u4"), ("gi", "<u4")]))
-    for b in range(yb):
-        first, last = b * 1024, min(N, (b + 1) * 1024) - 1
-        t = int(seg_of[first])
-        assert int(yrec["qoff"][b]) == offs[t] and int(yrec["u0"][b]) == first - int(starts[t]), b
-        assert int(yrec["gi"][b]) == t | (0x80000000 if seg_of[last] != t else 0), b
+    assert info.table_bytes == up(et_at + 4 * etiles)
+    et = np.frombuffer(table[et_at:et_at + 4 * etiles], dtype=np.uint32)
+    assert et.tolist() == [t for t, n in enumerate(sizes) for _ in range(-(-n // 5120))]
 
 
 def test_group_plan_rejects_bad_sizes():
@@ -213,11 +205,14 @@ def test_accumulate_many_host_checks():
     one = L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 1)
     eight = L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 8)
     assert one > 0 and eight > 0 and one % 256 == 0 and eight % 256 == 0
-    # per payload: its quartic bytes in the stream layout and a flag byte per 1024 values, plus the
-    # decoder's state
-    yb = -(-N // 1024)
-    assert eight >= 8 * (int(info.stream_bytes) + yb)
-    assert eight - one == 7 * (eight - one) // 7
+    # per payload: a start record (8 bytes) and a literal flag (4 bytes) per encode tile, plus the
+    # decoder's state; nothing the size of the streams (checked on a larger group)
+    big, _, _ = tlc.group_plan(sizes + [3_000_000])
+    T, K = int(big.tiles), int(big.chunks)
+    b1 = L.tlc_accumulate_many_workspace_size(ctypes.byref(big), 1)
+    b8 = L.tlc_accumulate_many_workspace_size(ctypes.byref(big), 8)
+    assert b8 >= 8 * 12 * T and b8 - b1 >= 7 * 12 * T
+    assert b8 < 8 * (12 * T + 16 * K + 8 * len(sizes) + 8) + 8 * 256 and b8 < int(big.stream_bytes)
     assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 0) == 0
     assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 65) == 0
     SB = int(info.stream_bytes)
