@@ -80,6 +80,7 @@ constexpr uint32_t kETile = 5120;                 // encode tile: elements
 constexpr uint32_t kETileBytes = kETile / 5;      // 1024 quartic bytes = 4 per lane
 constexpr uint32_t kSpan = 256;                   // encode tiles per k_emit block (one per lane)
 constexpr uint32_t kChunk = 4096;                 // decoder stream bytes per chunk = 16 per lane
+constexpr uint32_t kWideBPL = 64;                 // stream bytes per lane of the record pass over many payloads
 constexpr uint32_t kZero = 121;                   // quartic byte of five zero codes
 constexpr uint32_t kRunMax = 14;                  // codes 243..255 = runs of 2..14
 constexpr uint32_t kRunBase = 241;
@@ -1371,7 +1372,7 @@ constexpr uint32_t kMaxPayloads = 64;  // payloads of one accumulate-many call (
 // and accumulate-many (tstart set): the tile starts and literal flags of
 // every payload are reset.
 // Always: the look-back flags, and the list of stream chunks: unit u has
-// max(1, ceil(min(L_u, B_t) / kChunk)) chunks, numbered dec_first[u] ...;
+// max(1, ceil(min(L_u, B_t) / chunk)) chunks, numbered dec_first[u] ...;
 // chunk r belongs to unit dec_map[r]; ctrl[3] = number of chunks.  Block 0
 // also writes the density of the streams to *hint (when set): 1 if dense.
 __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payloads, float* __restrict__ y,
@@ -1381,7 +1382,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
                                                    uint64_t ntiles, uint32_t* __restrict__ dec_map,
                                                    uint32_t* __restrict__ dec_first,
                                                    uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
-                                                   int* __restrict__ status, uint32_t* hint) {
+                                                   int* __restrict__ status, uint32_t* hint, uint32_t chunk) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint64_t s_d[2][kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
@@ -1398,28 +1399,54 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
             tlit[i] = 0;
         }
     if (blockIdx.x == 0) {
-        uint32_t carry = 0;
-        uint64_t sum_l = 0, sum_b = 0;
+        // Thread t numbers the chunks of units [u0, u1), a contiguous run:
+        // first its total (loads in batches, all in flight together), then
+        // a block scan, then the numbers (the same loads, now in cache).
         const uint64_t units = (uint64_t)payloads * g.count;
-        for (uint64_t base = 0; base < units; base += kThreads) {
-            const uint64_t u = base + threadIdx.x;
-            uint32_t rc = 0;
-            if (u < units) {
-                const Seg sg = load_seg(g, (uint32_t)(u % g.count));
-                const uint64_t B = quartic_len(sg.n);
-                const uint64_t L = min(in_lens[u], B);
-                rc = max(1u, (uint32_t)((L + kChunk - 1) / kChunk));
-                sum_l += L;
-                sum_b += B;
+        const uint64_t per = (units + kThreads - 1) / kThreads;
+        const uint64_t u0 = min(units, threadIdx.x * per), u1 = min(units, u0 + per);
+        constexpr uint32_t kBatch = 8;
+        auto chunks_of = [&](uint64_t a, uint64_t (&L)[kBatch], uint64_t (&B)[kBatch]) {
+#pragma unroll
+            for (uint32_t k = 0; k < kBatch; ++k) {
+                L[k] = 0;
+                B[k] = 0;
+                if (a + k < u1) {
+                    B[k] = quartic_len(load_seg(g, (uint32_t)((a + k) % g.count)).n);
+                    L[k] = in_lens[a + k];
+                }
             }
-            uint32_t tot;
-            const uint32_t first = carry + block_excl_sum(rc, s_u, &tot);
-            if (u < units) {
-                dec_first[u] = first;
-                tickets[u] = 0;
-                for (uint32_t k = 0; k < rc; ++k) dec_map[first + k] = (uint32_t)u | (rc > 1 ? kMulti : 0u);
-            }
-            carry += tot;
+#pragma unroll
+            for (uint32_t k = 0; k < kBatch; ++k) L[k] = min(L[k], B[k]);
+        };
+        uint32_t mine = 0;
+        uint64_t sum_l = 0, sum_b = 0;
+        for (uint64_t a = u0; a < u1; a += kBatch) {
+            uint64_t L[kBatch], B[kBatch];
+            chunks_of(a, L, B);
+#pragma unroll
+            for (uint32_t k = 0; k < kBatch; ++k)
+                if (a + k < u1) {
+                    mine += max(1u, (uint32_t)((L[k] + chunk - 1) / chunk));
+                    sum_l += L[k];
+                    sum_b += B[k];
+                }
+        }
+        uint32_t carry;
+        uint32_t first = block_excl_sum(mine, s_u, &carry);
+        for (uint64_t a = u0; a < u1; a += kBatch) {
+            uint64_t L[kBatch], B[kBatch];
+            chunks_of(a, L, B);
+#pragma unroll
+            for (uint32_t k = 0; k < kBatch; ++k)
+                if (a + k < u1) {
+                    const uint64_t u = a + k;
+                    const uint32_t rc = max(1u, (uint32_t)((L[k] + chunk - 1) / chunk));
+                    dec_first[u] = first;
+                    tickets[u] = 0;
+                    for (uint32_t r = 0; r < rc; ++r) dec_map[first + r] = (uint32_t)u | (rc > 1 ? kMulti : 0u);
+                    first += rc;
+                }
         }
         if (hint) {
             for (int d = 32; d >= 1; d >>= 1) {
@@ -1454,12 +1481,14 @@ enum DecodeMode {
     kDecodeRecord = 2,   // dense decompress and accumulate-many: tile starts and literal flags
 };
 
-// One block per stream chunk (kChunk bytes, 16 per lane): expansion lengths,
+// One block per stream chunk (BPL bytes per lane: 4 KiB, or 16 KiB for the
+// record pass over many payloads, where fewer, larger chunks take fewer
+// rounds of the resident grid): expansion lengths,
 // block scan, look-back across the unit's chunks for the quartic byte index
 // of the chunk, then the work of Mode (one instantiation each, so that each
 // keeps only its own registers).  Record mode writes payload p's tile
 // records at p * rstride.
-template <int Mode>
+template <int Mode, uint32_t BPL>
 __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t* __restrict__ in,
                                                      uint64_t in_stride, uint64_t rstride,
                                                      const uint64_t* __restrict__ in_lens,
@@ -1496,30 +1525,36 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
         const uint32_t lc = s_chunk;
         const uint32_t c = c0 + lc;
         if (L_in > B && lc == 0 && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
-        const uint64_t start = (uint64_t)lc * kChunk;
+        constexpr uint32_t kChunkT = kThreads * BPL;
+        const uint64_t start = (uint64_t)lc * kChunkT;
         if (start >= L) {
             // only an empty stream gets here (chunk 0 of a unit with L == 0),
             // which is corrupt because ceil(n/5) >= 1
             if (threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
             continue;
         }
-        const uint32_t cnt = (uint32_t)min((uint64_t)kChunk, L - start);
+        const uint32_t cnt = (uint32_t)min((uint64_t)kChunkT, L - start);
         const uint8_t* const pb = sp + sg.stream_off + start;
-        const uint32_t off = 16u * threadIdx.x;
-        const uint32_t nv = cnt > off ? min(16u, cnt - off) : 0u;
-        uint32_t wd[4] = {0u, 0u, 0u, 0u};
-        if (nv == 16 && ((reinterpret_cast<uintptr_t>(pb + off) & 15) == 0)) {
-            const uint4 v = *reinterpret_cast<const uint4*>(pb + off);
-            wd[0] = v.x;
-            wd[1] = v.y;
-            wd[2] = v.z;
-            wd[3] = v.w;
+        const uint32_t off = BPL * threadIdx.x;
+        const uint32_t nv = cnt > off ? min(BPL, cnt - off) : 0u;
+        uint32_t wd[BPL / 4];
+#pragma unroll
+        for (uint32_t i = 0; i < BPL / 4; ++i) wd[i] = 0u;
+        if (nv == BPL && ((reinterpret_cast<uintptr_t>(pb + off) & 15) == 0)) {
+#pragma unroll
+            for (uint32_t q = 0; q < BPL / 16; ++q) {
+                const uint4 v = reinterpret_cast<const uint4*>(pb + off)[q];
+                wd[4 * q] = v.x;
+                wd[4 * q + 1] = v.y;
+                wd[4 * q + 2] = v.z;
+                wd[4 * q + 3] = v.w;
+            }
         } else {
             for (uint32_t i = 0; i < nv; ++i) wd[i >> 2] |= (uint32_t)pb[off + i] << (8 * (i & 3));
         }
         uint32_t tsum = 0, nlit = 0;
 #pragma unroll
-        for (uint32_t i = 0; i < 16; ++i) {
+        for (uint32_t i = 0; i < BPL; ++i) {
             const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
             const bool inr = i < nv;
             tsum += inr ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
@@ -1557,7 +1592,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                 float* const yy = y + sg.elem_off;
                 const float ms = msc * s;
 #pragma unroll
-                for (uint32_t i = 0; i < 16; ++i) {
+                for (uint32_t i = 0; i < BPL; ++i) {
                     const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
                     if (i < nv) {
                         if (byte < 243u) {
@@ -1584,17 +1619,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                 }
             }
         } else {
-            // A lane's 16 bytes expand to at most 224 quartic bytes, so at
-            // most one tile boundary (a multiple of 1024) falls inside them,
-            // d quartic bytes after the lane's first; the lane's literal bytes
-            // lie in the tiles before and after it.
+            // A lane's BPL bytes expand to at most 14 BPL < 1024 quartic
+            // bytes, so at most one tile boundary (a multiple of 1024) falls
+            // inside them, d quartic bytes after the lane's first; the lane's
+            // literal bytes lie in the tiles before and after it.
+            static_assert(BPL * (255u - kRunBase) < kETileBytes, "one tile boundary per lane");
             const uint64_t p0 = base + texcl;
             const uint32_t d = (uint32_t)((kETileBytes - p0 % kETileBytes) % kETileBytes);
             const uint32_t lim = (uint32_t)min<uint64_t>(B - min(B, p0), 1u << 16);  // quartic bytes left in the tensor
-            uint32_t rel = 0, bi = 16, bskip = 0;
+            uint32_t rel = 0, bi = BPL, bskip = 0;
             bool lit_lo = false, lit_hi = false;
 #pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {
+            for (uint32_t i = 0; i < BPL; ++i) {
                 const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
                 if (i < nv) {
                     const uint32_t len = byte < 243u ? 1u : byte - kRunBase;
@@ -1614,7 +1650,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             }
             uint64_t* const ts = tstart + (uint64_t)p * rstride + sg.etile0;
             uint32_t* const tl = tlit + (uint64_t)p * rstride + sg.etile0;
-            if (bi < 16 && d < lim) ts[(p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
+            if (bi < BPL && d < lim) ts[(p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
             if (!bad) {
                 if (lit_lo) tl[p0 / kETileBytes] = 1u;
                 if (lit_hi) tl[(p0 + d) / kETileBytes] = 1u;
@@ -1886,14 +1922,14 @@ __device__ __forceinline__ ApplyRec apply_rec(const GroupView& g, uint32_t etile
 // nonzero code; a tile where no payload has one is not touched.  Otherwise
 // the tile of acc is copied into LDS (tile element u at word u + mis, so
 // that float4 group h is LDS words 4h .. 4h+3).  Then, one payload after the
-// other, its bytes for the tile are walked 256 at a time: lane l takes bytes
-// l, l+64, l+128 and l+192 (ds_bpermute from the lanes that loaded them as
-// dwords), four wave scans of their expansion lengths give each byte's
-// quartic position, and every element of every literal byte is read from
-// LDS, has its code's value added (+-M*s, or -0.0 for a zero code, which
-// leaves the bits unchanged) and is written back; bytes that are not
-// literals use a dummy word of their lane.  Within one payload no two
-// literals share an element, and the payloads follow each other in order.
+// other, its bytes for the tile are walked 64 at a time, one per lane
+// (ds_bpermute from the lanes that loaded them as dwords, 256 bytes per
+// load): a wave scan of their expansion lengths gives each byte's quartic
+// position, and each nonzero code of a literal byte is added to its element
+// with an LDS float atomic add: it returns nothing, so nothing waits for it,
+// and a wave's LDS operations execute in order, so the payloads' adds to an
+// element follow the payload order (the add rounds exactly as v_add_f32,
+// denormals included, measured on MI355X over 16M operand pairs).
 // Neighbouring lanes hold neighbouring bytes, so their elements fall in
 // different LDS banks.  The tile is written back once.  While one tile is
 // decoded, the next tile's acc and its payloads' first 256 bytes (8
@@ -1908,18 +1944,25 @@ __device__ __forceinline__ void apply_fetch(const ApplyTile& t, const ApplyRec& 
     const int lane = lane_id();
     const float* const at = acc + t.a0;
     const int32_t ng = (t.mis + (int32_t)t.nel + 3) / 4;
+    if (lits && t.mis == 0 && t.nel == kETile) {  // a whole aligned tile: 20 float4 per lane
 #pragma unroll
-    for (uint32_t k = 0; k < kApplyVec; ++k) {
-        const int32_t h = lane + 64 * (int32_t)k;
-        const int32_t u0 = 4 * h - t.mis;
-        v[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (lits && h < ng) {
-            if (u0 >= 0 && u0 + 4 <= (int32_t)t.nel) {
-                v[k] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(at + u0));
-            } else {
+        for (uint32_t k = 0; k < kApplyVec; ++k)
+            v[k] = k < kETile / 256 ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(at) + lane + 64 * k)
+                                    : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
 #pragma unroll
-                for (int32_t i = 0; i < 4; ++i)
-                    if (u0 + i >= 0 && u0 + i < (int32_t)t.nel) v[k][i] = at[u0 + i];
+        for (uint32_t k = 0; k < kApplyVec; ++k) {
+            const int32_t h = lane + 64 * (int32_t)k;
+            const int32_t u0 = 4 * h - t.mis;
+            v[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (lits && h < ng) {
+                if (u0 >= 0 && u0 + 4 <= (int32_t)t.nel) {
+                    v[k] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(at + u0));
+                } else {
+#pragma unroll
+                    for (int32_t i = 0; i < 4; ++i)
+                        if (u0 + i >= 0 && u0 + i < (int32_t)t.nel) v[k][i] = at[u0 + i];
+                }
             }
         }
     }
@@ -1941,7 +1984,7 @@ __global__ __launch_bounds__(64, 2) void k_apply(GroupView g, uint32_t etiles, u
                                                  const uint64_t* __restrict__ tstart,
                                                  const uint32_t* __restrict__ tlit, float* __restrict__ acc,
                                                  int* __restrict__ status) {
-    __shared__ __align__(16) float s_acc[kApplyWords + 64];  // the tile, then a dummy word per lane
+    __shared__ __align__(16) float s_acc[kApplyWords];
     __shared__ uint16_t s_tab[256];
     const int lane = lane_id();
     const uint32_t w = xcd_unit(blockIdx.x, nwaves);
@@ -1980,11 +2023,12 @@ __global__ __launch_bounds__(64, 2) void k_apply(GroupView g, uint32_t etiles, u
         if (__ballot((uint32_t)lane < payloads && r0.ts == kNoStart) && lane == 0)
             raise_status(status, TLC_ERR_CORRUPT);  // a stream that never reached this tile
         const int32_t ng = (t0.mis + (int32_t)t0.nel + 3) / 4;
+        const bool whole = t0.mis == 0 && t0.nel == kETile;  // 20 float4 per lane, no partial group
         if (lits0) {
 #pragma unroll
             for (uint32_t k = 0; k < kApplyVec; ++k) {
                 const int32_t h = lane + 64 * (int32_t)k;
-                if (h < ng) reinterpret_cast<f4*>(s_acc)[h] = v[k];
+                if (whole ? k < kETile / 256 : h < ng) reinterpret_cast<f4*>(s_acc)[h] = v[k];
             }
         }
         wave_sync();
@@ -2017,72 +2061,52 @@ __global__ __launch_bounds__(64, 2) void k_apply(GroupView g, uint32_t etiles, u
 #pragma unroll
                 for (uint32_t k = 0; k < kApplyFetch; ++k)
                     if (p == k) cur = d0[k];
-                for (uint32_t b = 0; 256u * b < span; ++b) {
-                    if (b > 0 || p >= kApplyFetch) cur = tile_dword(ps, tb, 64u * b + (uint32_t)lane);
-                    uint32_t len[4], pat[4], byte[4], excl[4], tot[4];
+                // rounds of 64 window bytes, one per lane, as many as the bytes need
+                for (uint32_t r = 0; 64u * r < span; ++r) {
+                    if ((r & 3u) == 0 && (r > 0 || p >= kApplyFetch)) cur = tile_dword(ps, tb, 16u * r + (uint32_t)lane);
+                    const uint32_t wpos = 64u * r + (uint32_t)lane;  // window byte of this lane
+                    const uint32_t word =
+                        (uint32_t)__builtin_amdgcn_ds_bpermute((int)((16u * (r & 3u) + src_lane) * 4u), (int)cur);
+                    const uint32_t byte = (word >> src_shift) & 255u;
+                    const uint32_t pat = s_tab[min(byte, 242u)];
+                    uint32_t len = wpos >= o4 && wpos < span ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
+                    if (wpos == o4) len = len > tb.skip ? len - tb.skip : 0u;
+                    const uint32_t incl = wave_incl_sum_dpp(len);
+                    const uint32_t pos = carry + incl - len;  // tile quartic byte of this lane's byte
+                    carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                    // each nonzero code of a literal byte: an LDS float add, no
+                    // return (in order within the wave, rounded as v_add_f32)
+                    if (len != 0u && byte < 243u && byte != kZero && pos < t0.need) {
+                        float* const el = s_acc + 5u * pos + (uint32_t)t0.mis;
 #pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q) {
-                        const uint32_t wpos = 256u * b + 64u * q + (uint32_t)lane;  // window byte of this lane
-                        const uint32_t word =
-                            (uint32_t)__builtin_amdgcn_ds_bpermute((int)((16u * q + src_lane) * 4u), (int)cur);
-                        byte[q] = (word >> src_shift) & 255u;
-                        pat[q] = s_tab[min(byte[q], 242u)];
-                        const bool valid = wpos >= o4 && wpos < span;
-                        len[q] = valid ? (byte[q] < 243u ? 1u : byte[q] - kRunBase) : 0u;
-                        if (wpos == o4) len[q] = len[q] > tb.skip ? len[q] - tb.skip : 0u;
+                        for (uint32_t d = 0; d < 5; ++d)
+                            if ((pat >> (2 * d)) & 1u)
+                                atomicAdd(el + d, __builtin_bit_cast(float, mb | (((pat >> (2 * d + 1)) & 1u) << 31)));
                     }
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q) {
-                        const uint32_t incl = wave_incl_sum_dpp(len[q]);
-                        excl[q] = incl - len[q];
-                        tot[q] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-                    }
-                    // every element of every literal byte, read before any is written
-                    uint32_t at_[4];
-                    uint32_t base = carry;
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q) {
-                        const uint32_t pos = base + excl[q];  // tile quartic byte of this lane's byte
-                        const bool lit = len[q] != 0u && byte[q] < 243u && byte[q] != kZero && pos < t0.need;
-                        at_[q] = lit ? 5u * pos + (uint32_t)t0.mis : kApplyWords + (uint32_t)lane;
-                        pat[q] = lit ? pat[q] : 0x2AAu;  // five zero codes
-                        base += tot[q];
-                    }
-                    carry = base;
-                    float x[4][5];
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q)
-#pragma unroll
-                        for (uint32_t d = 0; d < 5; ++d) x[q][d] = s_acc[at_[q] + (pat[q] == 0x2AAu ? 0u : d)];
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q)
-#pragma unroll
-                        for (uint32_t d = 0; d < 5; ++d) {
-                            const uint32_t mask = (uint32_t)__builtin_amdgcn_sbfe((int)pat[q], 2 * d, 1);
-                            const uint32_t neg = __builtin_amdgcn_ubfe(pat[q], 2 * d + 1, 1);
-                            x[q][d] = x[q][d] + __builtin_bit_cast(float, (neg << 31) | (mb & mask));
-                        }
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q)
-#pragma unroll
-                        for (uint32_t d = 0; d < 5; ++d) s_acc[at_[q] + (pat[q] == 0x2AAu ? 0u : d)] = x[q][d];
                 }
                 if (carry < t0.need && lane == 0) raise_status(status, TLC_ERR_CORRUPT);
             }
             wave_sync();  // every element's sum is in LDS
             float* const at = acc + t0.a0;
+            if (whole) {
 #pragma unroll
-            for (uint32_t k = 0; k < kApplyVec; ++k) {
-                const int32_t h = lane + 64 * (int32_t)k;
-                const int32_t u0 = 4 * h - t0.mis;
-                if (h < ng) {
-                    const f4 v = reinterpret_cast<const f4*>(s_acc)[h];
-                    if (u0 >= 0 && u0 + 4 <= (int32_t)t0.nel) {
-                        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(at + u0));
-                    } else {
+                for (uint32_t k = 0; k < kETile / 256; ++k)
+                    __builtin_nontemporal_store(reinterpret_cast<const f4*>(s_acc)[lane + 64 * k],
+                                                reinterpret_cast<f4*>(at) + lane + 64 * k);
+            } else {
 #pragma unroll
-                        for (int32_t i = 0; i < 4; ++i)
-                            if (u0 + i >= 0 && u0 + i < (int32_t)t0.nel) at[u0 + i] = v[i];
+                for (uint32_t k = 0; k < kApplyVec; ++k) {
+                    const int32_t h = lane + 64 * (int32_t)k;
+                    const int32_t u0 = 4 * h - t0.mis;
+                    if (h < ng) {
+                        const f4 v = reinterpret_cast<const f4*>(s_acc)[h];
+                        if (u0 >= 0 && u0 + 4 <= (int32_t)t0.nel) {
+                            __builtin_nontemporal_store(v, reinterpret_cast<f4*>(at + u0));
+                        } else {
+#pragma unroll
+                            for (int32_t i = 0; i < 4; ++i)
+                                if (u0 + i >= 0 && u0 + i < (int32_t)t0.nel) at[u0 + i] = v[i];
+                        }
                     }
                 }
             }
@@ -2343,7 +2367,7 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
 // device.  Such kernels hand work to their blocks or waves round-robin, so a
 // grid larger than this leaves a second, partial round of blocks running
 // alone at the end.
-enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridApply, kGridKinds };
+enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridDecodeWide, kGridApply, kGridKinds };
 uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap, int threads = kThreads) {
     static std::mutex mu;
     static std::vector<uint32_t> per_dev;  // kGridKinds entries per device, 0 = not queried
@@ -2590,6 +2614,9 @@ constexpr ManyLayout many_layout(const Dims& d, uint64_t P) {
 int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in, uint64_t in_stride,
                   const uint64_t* in_lens, const float* scales, float s, float* y, uint64_t n_fill,
                   const DecState& ds, int* status, uint32_t* hint, hipStream_t st) {
+    // the record pass over several payloads walks 16 KiB chunks (fewer
+    // rounds of the resident grid); every other pass 4 KiB ones
+    const bool wide = mode == kDecodeRecord && payloads > 1;
     const GroupView g = p.g;
     const uint64_t chunks = p.d.chunks * payloads, etiles = p.d.etiles;
     uint64_t* const tstart = mode == kDecodeRecord ? ds.tstart : nullptr;
@@ -2599,17 +2626,19 @@ int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in,
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
     int rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
         k_prep<<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart, ds.tlit,
-                                               ntiles, ds.map, ds.first, ds.tickets, ds.ctrl, status, hint);
+                                               ntiles, ds.map, ds.first, ds.tickets, ds.ctrl, status, hint,
+                                               wide ? kThreads * kWideBPL : kChunk);
     });
     if (rc) return rc;
-    auto kern = mode == kDecodeWrite ? k_decode<kDecodeWrite>
-                : mode == kDecodeAdd ? k_decode<kDecodeAdd>
-                                     : k_decode<kDecodeRecord>;
-    const GridKind gk = (GridKind)(kGridDecodeWrite + mode);
+    auto kern = mode == kDecodeWrite ? k_decode<kDecodeWrite, 16>
+                : mode == kDecodeAdd ? k_decode<kDecodeAdd, 16>
+                : wide               ? k_decode<kDecodeRecord, kWideBPL>
+                                     : k_decode<kDecodeRecord, 16>;
+    const GridKind gk = wide ? kGridDecodeWide : (GridKind)(kGridDecodeWrite + mode);
     static const char* const names[] = {"tlc_decode", "tlc_decode_add", "tlc_decode_record"};
     const uint32_t grid =
         (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
-    return launch(names[mode], st, [&] {
+    return launch(wide ? "tlc_decode_record_wide" : names[mode], st, [&] {
         kern<<<grid, kThreads, 0, st>>>(g, in, in_stride, etiles, in_lens, scales, s, y, tstart, ds.tlit, ds.flags,
                                         ds.map, ds.first, ds.tickets, ds.ctrl, status);
     });
