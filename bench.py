@@ -574,6 +574,133 @@ class Bench:
         return rec
 
 
+PROFILE_PHASES = ("early", "steady", "receive", "resnet110", "calibrate")
+
+
+def profile_phase(args):
+    """One phase of the workload alone, for a profiler run (rocprofv3 sees
+    every kernel of the process): `early` the headline's warm-up and timed
+    steps; `steady` 150 steps, then the timed steps; `receive` the 8
+    BERT-large workers' payloads (150 steps each), then the many-payload and
+    the single-payload accumulates of the steady-state and of the first-step
+    payloads; `resnet110` one-step repetitions of the ResNet-110 group;
+    `calibrate` the copy and gather yardsticks of the traffic counters.  A
+    64 KiB tlc_copy_probe marks the start of every part that a summary
+    reads (parts in the order listed in the printed line)."""
+    import torch
+
+    from gradient_compression_distributed_lc_amd import tlc, workloads
+    dev = torch.device("cuda:0")
+    mark_a = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    mark_b = torch.empty_like(mark_a)
+
+    def marker():
+        tlc.copy_probe(mark_a, mark_b, 1 << 16)
+
+    out = {"profile": args.profile, "steps": args.steps}
+    if args.profile in ("early", "steady"):
+        wl = workloads.get("bert_large")
+        sizes, N, s = wl.sizes, wl.total, wl.s_values[0]
+        g = tlc.Group(sizes, device=dev)
+        x0 = torch.from_numpy(workloads.generate("bert_large")).to(dev)
+        xs = [x0] + [torch.roll(x0, shifts=k * ROT) for k in range(1, 32)]
+        err = torch.zeros(N, dtype=torch.float32, device=dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        o = torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev)
+        ln = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+        sc = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+        ws = g.workspace()
+        st = torch.empty(2, dtype=torch.int32, device=dev)
+        hint = tlc.path_hint()
+        k = 0
+        before = args.warmup if args.profile == "early" else args.steady_steps
+        out["parts"] = ["timed steps"]
+        for phase in ("before", "timed"):
+            if phase == "timed":
+                torch.cuda.synchronize()
+                marker()
+            for _ in range(before if phase == "before" else args.steps):
+                g.compress(xs[k % 32], err, s, out=o, out_lens=ln, scales=sc, workspace=ws, status=st[:1])
+                g.decompress(o, ln, sc, s, y=y, workspace=ws, status=st[1:], path_hint=hint)
+                k += 1
+        torch.cuda.synchronize()
+        out["status"] = st.cpu().tolist()
+        out["bits_per_value"] = round(8.0 * int(ln.sum().item()) / N, 4)
+        out["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
+    elif args.profile == "receive":
+        bench = Bench(args)
+        xs, pay, _, _ = bench.bert_workers(args.steady_steps, False)
+        del xs
+        torch.cuda.empty_cache()
+        g = bench.bert_group
+        s = workloads.get("bert_large").s_values[0]
+        acc = torch.zeros(g.total, dtype=torch.float32, device=dev)
+        wsm = torch.empty(g.accumulate_many_workspace_size(WORKERS), dtype=torch.uint8, device=dev)
+        ws = g.workspace()
+        st = torch.empty(1, dtype=torch.int32, device=dev)
+        out["parts"] = []
+        for kind in ("steady", "first"):
+            o, ln, sc = pay[kind]
+            out["parts"] += [f"{kind}: one call for 8 payloads", f"{kind}: 8 single-payload calls"]
+            torch.cuda.synchronize()
+            marker()
+            for _ in range(args.steps):
+                g.decompress_accumulate_many(o, ln.reshape(-1), sc.reshape(-1), s, acc, workspace=wsm, status=st)
+            torch.cuda.synchronize()
+            marker()
+            for _ in range(args.steps):
+                for w in range(WORKERS):
+                    g.decompress_accumulate(o[w], ln[w], sc[w], s, acc, workspace=ws, status=st)
+        torch.cuda.synchronize()
+        out["status"] = int(st.item())
+    elif args.profile == "resnet110":
+        wl = workloads.get("resnet110")
+        sizes, N, s = wl.sizes, wl.total, wl.s_values[0]
+        g = tlc.Group(sizes, device=dev)
+        x = torch.from_numpy(workloads.generate("resnet110")).to(dev)
+        err = torch.zeros(N, dtype=torch.float32, device=dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        o = torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev)
+        ln = torch.empty(len(sizes), dtype=torch.int64, device=dev)
+        sc = torch.zeros(len(sizes), dtype=torch.float32, device=dev)
+        ws = g.workspace()
+        st = torch.empty(2, dtype=torch.int32, device=dev)
+        hint = tlc.path_hint()
+        out["parts"] = ["timed steps"]
+        for phase in ("before", "timed"):
+            if phase == "timed":
+                torch.cuda.synchronize()
+                marker()
+            for _ in range(args.warmup if phase == "before" else args.steps):
+                err.zero_()
+                sc.zero_()
+                g.compress(x, err, s, out=o, out_lens=ln, scales=sc, workspace=ws, status=st[:1])
+                g.decompress(o, ln, sc, s, y=y, workspace=ws, status=st[1:], path_hint=hint)
+        torch.cuda.synchronize()
+        out["status"] = st.cpu().tolist()
+    else:  # calibrate: 1 GiB streaming copy; 4M one-value reads from distinct 128-byte lines
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        n = 1 << 22
+        lines = torch.randperm(nbytes // 128, device=dev)[:n].to(torch.int64)
+        idx = (lines * 32 + torch.randint(0, 32, (n,), device=dev)).to(torch.int32)
+        gdst = torch.empty(n, dtype=torch.float32, device=dev)
+        out["parts"] = [f"copy of {nbytes} bytes", f"gather of {n} values from distinct 128-byte lines"]
+        torch.cuda.synchronize()
+        marker()
+        for _ in range(args.steps):
+            tlc.copy_probe(src, dst, nbytes)
+        torch.cuda.synchronize()
+        marker()
+        for _ in range(args.steps):
+            tlc.gather_probe(src.view(torch.float32), idx, gdst)
+        torch.cuda.synchronize()
+        out["copy_bytes"] = 2 * nbytes
+        out["gather_values"] = n
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -590,6 +717,8 @@ def main():
                     help="run one configuration record and print it (profiling runs)")
     ap.add_argument("--steady-steps", type=int, default=150,
                     help="error-feedback steps before the steady-state figures (0: skip them)")
+    ap.add_argument("--profile", choices=PROFILE_PHASES, default=None,
+                    help="run one phase alone for a profiler and print a short line (not the benchmark line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -606,6 +735,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile:
+        profile_phase(args)
+        return
     bench = Bench(args)
     bench.copy_yardstick()
     copy_gbps = bench.copy_gbps

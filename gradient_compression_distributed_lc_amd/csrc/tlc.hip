@@ -1375,6 +1375,7 @@ constexpr uint32_t kMaxPayloads = 64;  // payloads of one accumulate-many call (
 // max(1, ceil(min(L_u, B_t) / chunk)) chunks, numbered dec_first[u] ...;
 // chunk r belongs to unit dec_map[r]; ctrl[3] = number of chunks.  Block 0
 // also writes the density of the streams to *hint (when set): 1 if dense.
+template <bool kFill>
 __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payloads, float* __restrict__ y,
                                                    uint64_t n_fill, const uint64_t* __restrict__ in_lens,
                                                    uint64_t* __restrict__ flags, uint64_t nflags,
@@ -1387,11 +1388,13 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
     __shared__ uint64_t s_d[2][kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    const uint64_t n4 = n_fill >> 2;
-    float4* const y4 = reinterpret_cast<float4*>(y);
-    for (uint64_t i = tid; i < n4; i += stride)
-        __builtin_nontemporal_store(f4{0.0f, 0.0f, 0.0f, 0.0f}, reinterpret_cast<f4*>(y4 + i));
-    if (tid < (n_fill & 3)) y[(n4 << 2) + tid] = 0.0f;
+    if (kFill) {  // a distinct kernel, so that profiles tell the two apart
+        const uint64_t n4 = n_fill >> 2;
+        float4* const y4 = reinterpret_cast<float4*>(y);
+        for (uint64_t i = tid; i < n4; i += stride)
+            __builtin_nontemporal_store(f4{0.0f, 0.0f, 0.0f, 0.0f}, reinterpret_cast<f4*>(y4 + i));
+        if (tid < (n_fill & 3)) y[(n4 << 2) + tid] = 0.0f;
+    }
     for (uint64_t i = tid; i < nflags; i += stride) flags[i] = 0;
     if (tstart)
         for (uint64_t i = tid; i < ntiles; i += stride) {
@@ -2320,6 +2323,14 @@ __global__ __launch_bounds__(kThreads) void k_planes(const float* __restrict__ s
     }
 }
 
+// dst[i] = src[idx[i]]: one 4-byte read at each index (the scattered-read
+// yardstick of the traffic counters).
+__global__ __launch_bounds__(kThreads) void k_gather(const float* __restrict__ src, const uint32_t* __restrict__ idx,
+                                                     float* __restrict__ dst, uint64_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) dst[i] = src[idx[i]];
+}
+
 __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ src, float4* __restrict__ dst,
                                                    uint64_t n4) {
     const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -2624,10 +2635,16 @@ int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in,
     const uint64_t blocks = std::max((n_fill / 4 + kThreads - 1) / kThreads,
                                      (std::max(chunks, ntiles) + kThreads - 1) / kThreads);
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
+    const uint32_t chunk = wide ? kThreads * kWideBPL : kChunk;
     int rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
-        k_prep<<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart, ds.tlit,
-                                               ntiles, ds.map, ds.first, ds.tickets, ds.ctrl, status, hint,
-                                               wide ? kThreads * kWideBPL : kChunk);
+        if (n_fill)
+            k_prep<true><<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart,
+                                                         ds.tlit, ntiles, ds.map, ds.first, ds.tickets, ds.ctrl,
+                                                         status, hint, chunk);
+        else
+            k_prep<false><<<prep_grid, kThreads, 0, st>>>(g, payloads, y, 0, in_lens, ds.flags, chunks, tstart,
+                                                          ds.tlit, ntiles, ds.map, ds.first, ds.tickets, ds.ctrl,
+                                                          status, hint, chunk);
     });
     if (rc) return rc;
     auto kern = mode == kDecodeWrite ? k_decode<kDecodeWrite, 16>
@@ -3042,6 +3059,14 @@ int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stre
     return launch("tlc_copy_probe", st, [&] {
         k_copy<<<(uint32_t)blocks, kThreads, 0, st>>>(static_cast<const float4*>(src), static_cast<float4*>(dst),
                                                        n4);
+    });
+}
+
+int tlc_gather_probe(const float* src, const uint32_t* idx, uint64_t n, float* dst, tlc_stream_t stream) {
+    if (!src || !idx || !dst || n == 0 || n > (1ull << 32)) return TLC_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch("tlc_gather_probe", st, [&] {
+        k_gather<<<(uint32_t)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(src, idx, dst, n);
     });
 }
 

@@ -80,6 +80,7 @@ _SIGS = {
                                                   _P, _SZ, _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
+    "tlc_gather_probe": (_I, [_P, _P, _U64, _P, _P]),
     "tlc_copy_probe": (_I, [_P, _P, _U64, _P]),
     "tlc_profile_enable": (_I, [_I]),
     "tlc_profile_read": (_I, [ctypes.POINTER(KernelTime), _I, ctypes.POINTER(_I)]),
@@ -606,6 +607,17 @@ def planes_scatter(src: torch.Tensor, src_off: torch.Tensor, dst: torch.Tensor, 
                                     _ptr(dst, torch.float32, "dst"), _ptr(dst_off, torch.int64, "dst_off"),
                                     _ptr(n, torch.int64, "n"), n.numel(), int(max_n), _stream(stream)),
            "tlc_planes_scatter")
+
+
+def gather_probe(src: torch.Tensor, idx: torch.Tensor, dst: torch.Tensor, stream=None):
+    """dst[i] = src[idx[i]] (tlc_gather_probe).  idx: int32 indices into src,
+    checked here."""
+    n = idx.numel()
+    _need(dst, n, "dst")
+    if n == 0 or int(idx.min().item()) < 0 or int(idx.max().item()) >= src.numel():
+        raise ValueError("idx must hold indices into src")
+    _check(lib().tlc_gather_probe(_ptr(src, torch.float32, "src"), _ptr(idx, torch.int32, "idx"), n,
+                                  _ptr(dst, torch.float32, "dst"), _stream(stream)), "tlc_gather_probe")
 
 
 def copy_probe(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):

@@ -338,6 +338,11 @@ int tlc_planes_scatter(const float* src, const uint64_t* src_off, float* dst, co
  * aligned): the achievable-HBM-bandwidth yardstick for the codec kernels. */
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream);
 
+/* dst[i] = src[idx[i]] for i < n (n <= 2^32): one 4-byte read per index, the
+ * scattered-read yardstick of the HBM traffic counters.  All pointers are
+ * device pointers; idx entries must lie inside src (not checked). */
+int tlc_gather_probe(const float* src, const uint32_t* idx, uint64_t n, float* dst, tlc_stream_t stream);
+
 /* Kernel timing with HIP events.  While enabled, every kernel the library
  * launches is bracketed by two events recorded on the same stream.
  * tlc_profile_read synchronises those events and returns, per kernel name,
