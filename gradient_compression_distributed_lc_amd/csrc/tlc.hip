@@ -1484,6 +1484,26 @@ enum DecodeMode {
     kDecodeRecord = 2,   // dense decompress and accumulate-many: tile starts and literal flags
 };
 
+// Sum of the expansion lengths of the four bytes of w (1 for a literal, b -
+// 241 for a run code b >= 243): with S = sum of the bytes and D = sum of
+// |b - 242| (two v_sad_u8), S + D - 4*242 = 2 * sum of (b - 242) over the
+// run codes.
+__device__ __forceinline__ uint32_t runs_len4(uint32_t w) {
+    const uint32_t sum = __builtin_amdgcn_sad_u8(w, 0u, 0u), dev = __builtin_amdgcn_sad_u8(w, 0xF2F2F2F2u, 0u);
+    return 4u + ((sum + dev - 4u * 242u) >> 1);
+}
+
+// Bit 8i+7 set when byte i of w is a literal holding a nonzero code (not a
+// run code >= 243, not 121): a byte is >= 243 when its top bit is set and
+// its low seven bits plus 13 carry into bit 7; it is 121 when it xor 0x79 is
+// zero (bit 7 of ~(((t & 0x7F) + 0x7F) | t | 0x7F)).  No carry crosses a byte.
+__device__ __forceinline__ uint32_t literal_bits(uint32_t w) {
+    const uint32_t run = ((w & 0x7F7F7F7Fu) + 0x0D0D0D0Du) & w & 0x80808080u;
+    const uint32_t t = w ^ 0x79797979u;
+    const uint32_t zero = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t | 0x7F7F7F7Fu);
+    return ~(run | zero) & 0x80808080u;
+}
+
 // One block per stream chunk (BPL bytes per lane: 4 KiB, or 16 KiB for the
 // record pass over many payloads, where fewer, larger chunks take fewer
 // rounds of the resident grid): expansion lengths,
@@ -1556,12 +1576,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             for (uint32_t i = 0; i < nv; ++i) wd[i >> 2] |= (uint32_t)pb[off + i] << (8 * (i & 3));
         }
         uint32_t tsum = 0, nlit = 0;
+        if (nv == BPL) {  // whole words: four bytes at a time
 #pragma unroll
-        for (uint32_t i = 0; i < BPL; ++i) {
-            const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
-            const bool inr = i < nv;
-            tsum += inr ? (byte < 243u ? 1u : byte - kRunBase) : 0u;
-            nlit += (inr && byte < 243u && byte != kZero) ? 1u : 0u;
+            for (uint32_t k = 0; k < BPL / 4; ++k) {
+                tsum += runs_len4(wd[k]);
+                if (Mode != kDecodeRecord) nlit += __popc(literal_bits(wd[k]));
+            }
+        } else {
+            for (uint32_t i = 0; i < nv; ++i) {
+                const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
+                tsum += byte < 243u ? 1u : byte - kRunBase;
+                nlit += (byte < 243u && byte != kZero) ? 1u : 0u;
+            }
         }
         uint32_t csum;
         const uint32_t texcl = block_excl_sum(tsum, s_u, &csum);
@@ -1630,23 +1656,61 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             const uint64_t p0 = base + texcl;
             const uint32_t d = (uint32_t)((kETileBytes - p0 % kETileBytes) % kETileBytes);
             const uint32_t lim = (uint32_t)min<uint64_t>(B - min(B, p0), 1u << 16);  // quartic bytes left in the tensor
-            uint32_t rel = 0, bi = BPL, bskip = 0;
+            uint32_t bi = BPL, bskip = 0;  // the byte whose expansion holds the boundary
             bool lit_lo = false, lit_hi = false;
+            if (nv == BPL) {
+                // the word holding the boundary, from the words' length sums;
+                // literals per word; then the byte within that word.  A
+                // literal past the tensor's end makes the stream longer than
+                // its quartic length, which the chunk that ends it reports.
+                uint32_t rel = 0, relc = 0, wc = 0, kc = BPL / 4;
+                uint32_t before = 0, after = 0;  // literal bits of the words before and after word kc
 #pragma unroll
-            for (uint32_t i = 0; i < BPL; ++i) {
-                const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
-                if (i < nv) {
+                for (uint32_t k = 0; k < BPL / 4; ++k) {
+                    const uint32_t len = runs_len4(wd[k]);
+                    const uint32_t lb = literal_bits(wd[k]);
+                    const bool here = kc == BPL / 4 && d < rel + len;
+                    if (here) {
+                        kc = k;
+                        relc = rel;
+                        wc = wd[k];
+                    }
+                    if (kc == BPL / 4) before |= lb;
+                    else if (!here) after |= lb;
+                    rel += len;
+                }
+                if (kc < BPL / 4) {
+                    uint32_t r = relc, j = 4;
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        const uint32_t byte = (wc >> (8 * q)) & 255u;
+                        const uint32_t len = byte < 243u ? 1u : byte - kRunBase;
+                        if (j == 4 && d < r + len) {
+                            j = q;
+                            bskip = d - r;
+                        }
+                        r += len;
+                    }
+                    bi = 4 * kc + j;
+                    const uint32_t lc = literal_bits(wc);
+                    const uint32_t lo_mask = j == 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * j));
+                    lit_lo = (before | (lc & lo_mask)) != 0u;
+                    lit_hi = (after | (lc & ~lo_mask)) != 0u;
+                } else {
+                    lit_lo = before != 0u;
+                }
+            } else {
+                uint32_t rel = 0;
+                for (uint32_t i = 0; i < nv; ++i) {
+                    const uint32_t byte = (wd[i >> 2] >> (8 * (i & 3))) & 255u;
                     const uint32_t len = byte < 243u ? 1u : byte - kRunBase;
                     if (d >= rel && d < rel + len) {
                         bi = i;
                         bskip = d - rel;
                     }
-                    if (byte < 243u) {
-                        bad |= rel >= lim;
-                        if (byte != kZero) {
-                            lit_lo |= rel < d;
-                            lit_hi |= rel >= d;
-                        }
+                    if (byte < 243u && byte != kZero) {
+                        lit_lo |= rel < d;
+                        lit_hi |= rel >= d;
                     }
                     rel += len;
                 }
@@ -1654,10 +1718,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
             uint64_t* const ts = tstart + (uint64_t)p * rstride + sg.etile0;
             uint32_t* const tl = tlit + (uint64_t)p * rstride + sg.etile0;
             if (bi < BPL && d < lim) ts[(p0 + d) / kETileBytes] = tile_start(start + off + bi, bskip);
-            if (!bad) {
-                if (lit_lo) tl[p0 / kETileBytes] = 1u;
-                if (lit_hi) tl[(p0 + d) / kETileBytes] = 1u;
-            }
+            // flags only for tiles of this tensor
+            if (lit_lo && lim > 0) tl[p0 / kETileBytes] = 1u;
+            if (lit_hi && d < lim) tl[(p0 + d) / kETileBytes] = 1u;
         }
         if (bad) raise_status(status, TLC_ERR_CORRUPT);
     }
