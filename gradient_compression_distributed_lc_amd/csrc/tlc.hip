@@ -2632,8 +2632,8 @@ int run_compress(const Plan& p, const float* x, float x_div, float* err, float s
 
 // Decoder state in a workspace: look-back flags and the chunk map for
 // `payloads` payloads, per-unit ticket counters and first chunks; for the
-// dense decompress the tile starts and literal flags; for accumulate-many
-// each payload's quartic bytes and y-block flags.
+// dense decompress and accumulate-many, each payload's tile starts and
+// literal flags (one record of each per encode tile).
 struct DecState {
     uint32_t* ctrl;
     uint64_t* flags;

@@ -116,7 +116,8 @@ def test_max_size_tensor():
     assert int(torch.count_nonzero(acc).item()) == int(np.count_nonzero(exp))
 
     # the many-payload accumulate at the same size: the stream twice, as two
-    # payloads (y-block words and code bytes at offsets past 2^30)
+    # payloads (the second one's bytes start ~859 MB into the buffer, and its
+    # tile records follow the first one's 838,861)
     say("case max size: accumulate ok, two payloads in one call")
     B = tlc.compress_bound(n)
     stride = -(-B // 16) * 16
