@@ -509,7 +509,10 @@ class Bench:
     def accumulate_record(self, payload, oracle_payloads=None):
         """The 8 payloads decompressed and accumulated into one fp32 sum in
         worker order: one many-payload call against 8 single-payload calls,
-        20 repetitions each, acc cleared outside the timed window."""
+        20 repetitions each, acc cleared outside the timed window.  The many
+        call runs with one path hint word carried from call to call (as a
+        caller would pass it; the first call takes the sparse sequence), and
+        with each launch sequence forced (a fresh word per call)."""
         torch, tlc = self.torch, self.tlc
         g = self.bert_group
         N, count = g.total, g.count
@@ -521,8 +524,23 @@ class Bench:
         ws = g.workspace()
         lflat, sflat = ln.reshape(-1), sc.reshape(-1)
 
+        carried = tlc.path_hint()
+        carried[0] = 0
+
         def many(r, mark):
-            g.decompress_accumulate_many(o, lflat, sflat, s, acc, workspace=ws_many, status=st)
+            g.decompress_accumulate_many(o, lflat, sflat, s, acc, workspace=ws_many, status=st, path_hint=carried)
+
+        def forced(route):
+            words = []
+            for _ in range(self.args.reps + 2):
+                w = tlc.path_hint()
+                w[0] = route
+                words.append(w)
+
+            def body(r, mark):
+                g.decompress_accumulate_many(o, lflat, sflat, s, acc, workspace=ws_many, status=st,
+                                             path_hint=words.pop())
+            return body
 
         def seq(r, mark):
             for w in range(WORKERS):
@@ -533,14 +551,26 @@ class Bench:
 
         reps = self.args.reps
         timed(torch, 2, many, clear)
+        t_many = [v[0] for v in timed(torch, reps, many, clear)]
+        self.status_ok(st, what="accumulate many")
+        # the kernels' share, in repetitions of their own (events around every
+        # launch slow the call down)
         tlc.profile_read()
         tlc.profile_only(None)
         tlc.profile_enable(True)
-        t_many = [v[0] for v in timed(torch, reps, many, clear)]
+        timed(torch, 5, many, clear)
         tlc.profile_enable(False)
         k_many = tlc.profile_read()
-        self.status_ok(st, what="accumulate many")
+        self.status_ok(st, what="accumulate many, profiled")
         acc_many = acc.clone()
+        route_ms = {}
+        for route, name in ((0, "sparse"), (1, "dense")):
+            body = forced(route)
+            timed(torch, 2, body, clear)
+            route_ms[name] = stats([v[0] for v in timed(torch, reps, body, clear)])
+            self.status_ok(st, what=f"accumulate many, {name} sequence")
+            if not torch.equal(acc.view(torch.int32), acc_many.view(torch.int32)):
+                raise SystemExit(f"accumulate many: the {name} sequence's sum differs")
         timed(torch, 2, seq, clear)
         t_seq = [v[0] for v in timed(torch, reps, seq, clear)]
         self.status_ok(st, what="accumulate sequential")
@@ -550,13 +580,16 @@ class Bench:
         sm = stats(t_many)
         rec = {"payloads": WORKERS, "stream_bytes_total": L,
                "bits_per_value_mean": round(8.0 * L / WORKERS / N, 4),
-               "many_call_ms": sm, "sequential_calls_ms": stats(t_seq),
+               "many_call_ms": sm, "many_call_sequence": "dense" if int(carried[0]) else "sparse",
+               "many_call_ms_sparse_sequence": route_ms["sparse"], "many_call_ms_dense_sequence": route_ms["dense"],
+               "sequential_calls_ms": stats(t_seq),
                "many_call_roofline": {"bound": "hbm", "achieved": round(alg / (sm["median"] * 1e-3) / 1e9, 1),
                                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                       "frac": frac(alg, sm["median"], HBM_PEAK_GBPS),
                                       "bytes": int(alg),
                                       "what": "one read and write of all of acc (8 B/value) plus the 8 streams; "
-                                              "blocks of 1024 values no payload touches are skipped, so sparse "
+                                              "tiles no payload touches are skipped, and the sparse sequence "
+                                              "touches only the elements with a nonzero code, so sparse "
                                               "payloads can exceed 1"},
                "many_call_kernels_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in k_many.items() if v[0]},
                "many_equals_sequential": same}
@@ -581,9 +614,9 @@ def profile_phase(args):
     """One phase of the workload alone, for a profiler run (rocprofv3 sees
     every kernel of the process): `early` the headline's warm-up and timed
     steps; `steady` 150 steps, then the timed steps; `receive` the 8
-    BERT-large workers' payloads (150 steps each), then the many-payload and
-    the single-payload accumulates of the steady-state and of the first-step
-    payloads; `resnet110` one-step repetitions of the ResNet-110 group;
+    BERT-large workers' payloads (150 steps each), then the many-payload call
+    on each launch sequence and the single-payload accumulates, for the
+    steady-state and for the first-step payloads; `resnet110` one-step repetitions of the ResNet-110 group;
     `calibrate` the copy and gather yardsticks of the traffic counters.  A
     64 KiB tlc_copy_probe marks the start of every part that a summary
     reads (parts in the order listed in the printed line)."""
@@ -641,11 +674,17 @@ def profile_phase(args):
         out["parts"] = []
         for kind in ("steady", "first"):
             o, ln, sc = pay[kind]
-            out["parts"] += [f"{kind}: one call for 8 payloads", f"{kind}: 8 single-payload calls"]
-            torch.cuda.synchronize()
-            marker()
-            for _ in range(args.steps):
-                g.decompress_accumulate_many(o, ln.reshape(-1), sc.reshape(-1), s, acc, workspace=wsm, status=st)
+            out["parts"] += [f"{kind}: one call for 8 payloads, dense sequence",
+                             f"{kind}: one call for 8 payloads, sparse sequence", f"{kind}: 8 single-payload calls"]
+            for route in (1, 0):
+                words = [tlc.path_hint() for _ in range(args.steps)]
+                for w in words:
+                    w[0] = route
+                torch.cuda.synchronize()
+                marker()
+                for k in range(args.steps):
+                    g.decompress_accumulate_many(o, ln.reshape(-1), sc.reshape(-1), s, acc, workspace=wsm, status=st,
+                                                 path_hint=words[k])
             torch.cuda.synchronize()
             marker()
             for _ in range(args.steps):

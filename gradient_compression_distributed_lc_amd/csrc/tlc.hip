@@ -1350,6 +1350,9 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
 // quartic byte 1024 j, and how many quartic bytes of that expansion come
 // before it (a run byte can straddle two tiles).
 constexpr uint64_t kNoStart = ~0ull;
+
+// k_decode's unit range bound meaning "through the last unit".
+constexpr uint32_t kToEnd = ~0u;
 __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { return byte | skip << 32; }
 
 // Stream density (bytes per quartic byte) above which the dense decompress
@@ -1358,6 +1361,12 @@ __device__ __forceinline__ uint64_t tile_start(uint64_t byte, uint64_t skip) { r
 // each path forced (sparse ahead by 24 us at 0.094, dense ahead by 13 us at
 // 0.109).  An all-zero stream holds 1/14 = 0.071 (runs of 14).
 constexpr uint64_t kDenseNum = 104, kDenseDen = 1000;
+// The same for the accumulate of many payloads (one pass over acc for all of
+// them against one add pass per payload): 82/1000, measured on MI355X with 8
+// BERT-large workers' payloads from 40 to 100 steps of error feedback (the
+// add passes ahead by 116 us at 0.080, even at 0.082, behind by 73 us at
+// 0.086).
+constexpr uint64_t kManyDenseNum = 82;
 
 constexpr uint32_t kMaxPayloads = 64;  // payloads of one accumulate-many call (one wavefront lane each)
 
@@ -1383,7 +1392,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
                                                    uint64_t ntiles, uint32_t* __restrict__ dec_map,
                                                    uint32_t* __restrict__ dec_first,
                                                    uint32_t* __restrict__ tickets, uint32_t* __restrict__ ctrl,
-                                                   int* __restrict__ status, uint32_t* hint, uint32_t chunk) {
+                                                   int* __restrict__ status, uint32_t* hint, uint32_t chunk,
+                                                   uint32_t dense_num) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint64_t s_d[2][kWaves];
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
@@ -1467,7 +1477,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
                     tl += s_d[0][w];
                     tb += s_d[1][w];
                 }
-                *hint = kDenseDen * tl > kDenseNum * tb ? 1u : 0u;
+                *hint = kDenseDen * tl > dense_num * tb ? 1u : 0u;
             }
         }
         if (threadIdx.x == 0) {
@@ -1510,7 +1520,9 @@ __device__ __forceinline__ uint32_t literal_bits(uint32_t w) {
 // block scan, look-back across the unit's chunks for the quartic byte index
 // of the chunk, then the work of Mode (one instantiation each, so that each
 // keeps only its own registers).  Record mode writes payload p's tile
-// records at p * rstride.
+// records at p * rstride.  Only the chunks of units [u_lo, u_hi) are taken
+// (u_hi == kToEnd: through the last unit), so that the payloads of one set-up
+// can be decoded one launch after the other.
 template <int Mode, uint32_t BPL>
 __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t* __restrict__ in,
                                                      uint64_t in_stride, uint64_t rstride,
@@ -1521,14 +1533,17 @@ __global__ __launch_bounds__(kThreads) void k_decode(GroupView g, const uint8_t*
                                                      const uint32_t* __restrict__ dec_map,
                                                      const uint32_t* __restrict__ dec_first,
                                                      uint32_t* __restrict__ tickets, const uint32_t* __restrict__ ctrl,
-                                                     int* __restrict__ status) {
+                                                     int* __restrict__ status, uint32_t u_lo, uint32_t u_hi) {
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_chunk, s_ok;
     __shared__ uint64_t s_base;
     // The real chunk count is only known on the device: the grid is capped
     // near what the GPU holds at once and blocks loop over the chunks.
-    for (uint32_t slot = blockIdx.x; slot < ctrl[3]; slot += gridDim.x) {
-        if (slot != blockIdx.x) __syncthreads();  // s_chunk / s_base of the previous chunk are read
+    // Chunks are numbered in unit order, so a unit range is a chunk range.
+    const uint32_t lo = u_lo ? dec_first[u_lo] : 0u;
+    const uint32_t hi = u_hi == kToEnd ? ctrl[3] : dec_first[u_hi];
+    for (uint32_t slot = lo + blockIdx.x; slot < hi; slot += gridDim.x) {
+        if (slot != lo + blockIdx.x) __syncthreads();  // s_chunk / s_base of the previous chunk are read
         // A unit with several chunks hands them out in ticket order from its
         // own counter, so that the look-back only ever waits for blocks that
         // already hold a smaller ticket (and are working on that chunk).
@@ -2659,6 +2674,12 @@ DecState dec_state_single(const Layout& l, char* w) {
     return d;
 }
 
+// Whether P payloads of a group can be numbered: every (payload, tensor)
+// unit id below the decoder's flag bit, every chunk number in 32 bits.
+constexpr bool many_fits(const Dims& d, uint64_t P) {
+    return P * d.count <= 0x7FFFFFFFull && P * d.chunks <= 0xFFFFFFFFull;
+}
+
 // Workspace of an accumulate-many call on P payloads.
 struct ManyLayout {
     size_t ctrl = 0, flags = 0, map = 0, first = 0, tickets = 0, tstart = 0, tlit = 0, total = 0;
@@ -2682,46 +2703,69 @@ constexpr ManyLayout many_layout(const Dims& d, uint64_t P) {
     return l;
 }
 
-// k_prep, then k_decode in `mode` over the chunks of `payloads` payloads.
-// n_fill: elements of y to zero first (sparse decompress); hint: where the
-// streams' density class goes.
-int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in, uint64_t in_stride,
-                  const uint64_t* in_lens, const float* scales, float s, float* y, uint64_t n_fill,
-                  const DecState& ds, int* status, uint32_t* hint, hipStream_t st) {
-    // the record pass over several payloads walks 16 KiB chunks (fewer
-    // rounds of the resident grid); every other pass 4 KiB ones
-    const bool wide = mode == kDecodeRecord && payloads > 1;
+// k_prep for `payloads` payloads: n_fill: elements of y to zero first
+// (sparse decompress); records: reset the tile records (record mode); hint:
+// where the streams' density class goes (dense above dense_num / 1000
+// stream bytes per quartic byte).
+int launch_prep(const Plan& p, uint32_t payloads, bool records, uint32_t chunk, const uint64_t* in_lens, float* y,
+                uint64_t n_fill, const DecState& ds, int* status, uint32_t* hint, uint32_t dense_num,
+                hipStream_t st) {
     const GroupView g = p.g;
     const uint64_t chunks = p.d.chunks * payloads, etiles = p.d.etiles;
-    uint64_t* const tstart = mode == kDecodeRecord ? ds.tstart : nullptr;
+    uint64_t* const tstart = records ? ds.tstart : nullptr;
     const uint64_t ntiles = tstart ? payloads * etiles : 0;
     const uint64_t blocks = std::max((n_fill / 4 + kThreads - 1) / kThreads,
                                      (std::max(chunks, ntiles) + kThreads - 1) / kThreads);
     const uint32_t prep_grid = (uint32_t)std::min<uint64_t>(std::max<uint64_t>(blocks, 1), 1u << 20);
-    const uint32_t chunk = wide ? kThreads * kWideBPL : kChunk;
-    int rc = launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
+    return launch(n_fill ? "tlc_prep_fill" : "tlc_prep", st, [&] {
         if (n_fill)
             k_prep<true><<<prep_grid, kThreads, 0, st>>>(g, payloads, y, n_fill, in_lens, ds.flags, chunks, tstart,
                                                          ds.tlit, ntiles, ds.map, ds.first, ds.tickets, ds.ctrl,
-                                                         status, hint, chunk);
+                                                         status, hint, chunk, dense_num);
         else
             k_prep<false><<<prep_grid, kThreads, 0, st>>>(g, payloads, y, 0, in_lens, ds.flags, chunks, tstart,
                                                           ds.tlit, ntiles, ds.map, ds.first, ds.tickets, ds.ctrl,
-                                                          status, hint, chunk);
+                                                          status, hint, chunk, dense_num);
     });
-    if (rc) return rc;
+}
+
+// k_decode in `mode` over the chunks of units [u_lo, u_hi) of the last
+// k_prep's set-up; `max_chunks` bounds their number (grid size).
+int launch_dec(const Plan& p, int mode, bool wide, const uint8_t* in, uint64_t in_stride, const uint64_t* in_lens,
+               const float* scales, float s, float* y, const DecState& ds, int* status, uint32_t u_lo, uint32_t u_hi,
+               uint64_t max_chunks, hipStream_t st) {
+    const GroupView g = p.g;
+    const uint64_t etiles = p.d.etiles;
+    uint64_t* const tstart = mode == kDecodeRecord ? ds.tstart : nullptr;
     auto kern = mode == kDecodeWrite ? k_decode<kDecodeWrite, 16>
                 : mode == kDecodeAdd ? k_decode<kDecodeAdd, 16>
                 : wide               ? k_decode<kDecodeRecord, kWideBPL>
                                      : k_decode<kDecodeRecord, 16>;
     const GridKind gk = wide ? kGridDecodeWide : (GridKind)(kGridDecodeWrite + mode);
     static const char* const names[] = {"tlc_decode", "tlc_decode_add", "tlc_decode_record"};
-    const uint32_t grid =
-        (uint32_t)std::min<uint64_t>(chunks, resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(
+        std::max<uint64_t>(max_chunks, 1), resident_grid(gk, reinterpret_cast<const void*>(kern), kDecodeGrid));
     return launch(wide ? "tlc_decode_record_wide" : names[mode], st, [&] {
         kern<<<grid, kThreads, 0, st>>>(g, in, in_stride, etiles, in_lens, scales, s, y, tstart, ds.tlit, ds.flags,
-                                        ds.map, ds.first, ds.tickets, ds.ctrl, status);
+                                        ds.map, ds.first, ds.tickets, ds.ctrl, status, u_lo, u_hi);
     });
+}
+
+// k_prep, then k_decode in `mode` over the chunks of all `payloads` payloads.
+// n_fill: elements of y to zero first (sparse decompress); hint: where the
+// streams' density class goes, with the crossover dense_num / 1000.
+int launch_decode(const Plan& p, uint32_t payloads, int mode, const uint8_t* in, uint64_t in_stride,
+                  const uint64_t* in_lens, const float* scales, float s, float* y, uint64_t n_fill,
+                  const DecState& ds, int* status, uint32_t* hint, uint32_t dense_num, hipStream_t st) {
+    // the record pass over several payloads walks 16 KiB chunks (fewer
+    // rounds of the resident grid); every other pass 4 KiB ones
+    const bool wide = mode == kDecodeRecord && payloads > 1;
+    const uint32_t chunk = wide ? kThreads * kWideBPL : kChunk;
+    int rc = launch_prep(p, payloads, mode == kDecodeRecord, chunk, in_lens, y, n_fill, ds, status, hint, dense_num,
+                         st);
+    if (rc) return rc;
+    return launch_dec(p, mode, wide, in, in_stride, in_lens, scales, s, y, ds, status, 0u, kToEnd,
+                      p.d.chunks * payloads, st);
 }
 
 // Decompress takes one of two launch sequences, both giving the same y.
@@ -2743,10 +2787,12 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     int rc = check_ws(p, ws, ws_bytes, &l);
     if (rc) return rc;
     const DecState ds = dec_state_single(l, static_cast<char*>(ws));
-    if (accumulate) return launch_decode(p, 1, kDecodeAdd, in, 0, in_lens, scales, s, y, 0, ds, status, nullptr, st);
+    if (accumulate)
+        return launch_decode(p, 1, kDecodeAdd, in, 0, in_lens, scales, s, y, 0, ds, status, nullptr,
+                             (uint32_t)kDenseNum, st);
     const bool dense = hint && reinterpret_cast<volatile uint32_t*>(hint)[0] != 0u;
     rc = launch_decode(p, 1, dense ? kDecodeRecord : kDecodeWrite, in, 0, in_lens, scales, s, y,
-                       dense ? 0 : p.d.total, ds, status, dev_hint, st);
+                       dense ? 0 : p.d.total, ds, status, dev_hint, (uint32_t)kDenseNum, st);
     if (rc || !dense) return rc;
     const GroupView g = p.g;
     const uint64_t etiles = p.d.etiles;
@@ -2757,14 +2803,23 @@ int run_decompress(const Plan& p, const uint8_t* in, const uint64_t* in_lens, co
     });
 }
 
-// Accumulate-many: the tile starts of every payload in one decoder launch,
-// then one pass over acc that decodes and applies them tile by tile.
-// stream_bytes: the group's stream buffer size (a payload's slots).
+// Accumulate-many takes one of two launch sequences, both giving the same
+// acc.  Dense (no hint word, or a word holding 1): the tile starts of every
+// payload in one decoder launch, then one pass over acc that decodes and
+// applies them tile by tile.  Sparse (a word holding 0): one set-up for all
+// payloads, then one add-mode decoder launch per payload in payload order,
+// each touching only the elements its literal codes land on; while few tiles
+// hold a nonzero code this moves far fewer bytes than a pass over every tile
+// that any payload touches.  k_prep writes the density class of all the
+// payloads' streams into the word.  stream_bytes: the group's stream buffer
+// size (a payload's slots).
 int run_accumulate_many(const Plan& p, uint64_t stream_bytes, uint32_t payloads, const uint8_t* in,
                         uint64_t in_stride, const uint64_t* in_lens, const float* scales, float s, float* acc,
-                        void* ws, size_t ws_bytes, int* status, hipStream_t st) {
+                        void* ws, size_t ws_bytes, int* status, uint32_t* hint, uint32_t* dev_hint,
+                        hipStream_t st) {
     if (!in || !in_lens || !scales || !acc || !status) return TLC_ERR_INVALID_ARG;
     if (payloads == 0 || payloads > kMaxPayloads || !aligned16(acc) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
+    if (!many_fits(p.d, payloads)) return TLC_ERR_TOO_LARGE;
     if (payloads > 1 && (in_stride < stream_bytes || (in_stride & 15))) return TLC_ERR_INVALID_ARG;
     const ManyLayout ml = many_layout(p.d, payloads);
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < ml.total) return TLC_ERR_WORKSPACE;
@@ -2777,8 +2832,18 @@ int run_accumulate_many(const Plan& p, uint64_t stream_bytes, uint32_t payloads,
     ds.tickets = reinterpret_cast<uint32_t*>(w + ml.tickets);
     ds.tstart = reinterpret_cast<uint64_t*>(w + ml.tstart);
     ds.tlit = reinterpret_cast<uint32_t*>(w + ml.tlit);
+    const bool sparse = hint && reinterpret_cast<volatile uint32_t*>(hint)[0] == 0u;
+    if (sparse) {
+        int rc = launch_prep(p, payloads, false, kChunk, in_lens, nullptr, 0, ds, status, dev_hint,
+                             (uint32_t)kManyDenseNum, st);
+        for (uint32_t q = 0; q < payloads && !rc; ++q)
+            rc = launch_dec(p, kDecodeAdd, false, in, in_stride, in_lens, scales, s, acc, ds, status,
+                            q * (uint32_t)p.d.count, q + 1 < payloads ? (q + 1) * (uint32_t)p.d.count : kToEnd,
+                            p.d.chunks, st);
+        return rc;
+    }
     int rc = launch_decode(p, payloads, kDecodeRecord, in, in_stride, in_lens, scales, s, nullptr, 0, ds, status,
-                           nullptr, st);
+                           dev_hint, (uint32_t)kManyDenseNum, st);
     if (rc) return rc;
     const GroupView g = p.g;
     const uint64_t etiles = p.d.etiles;
@@ -3098,18 +3163,22 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
 
 uint64_t tlc_accumulate_many_workspace_size(const tlc_group_info* info, uint32_t payloads) {
     if (!info || info->count == 0 || payloads == 0 || payloads > kMaxPayloads) return 0;
-    return many_layout(dims_of(info), payloads).total;
+    const Dims d = dims_of(info);
+    return many_fits(d, payloads) ? many_layout(d, payloads).total : 0;
 }
 
 int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void* d_table, uint32_t payloads,
                                          const uint8_t* in, uint64_t in_stride, const uint64_t* in_lens,
                                          const float* scales, float s, float* acc, void* workspace,
-                                         size_t workspace_bytes, int* status, tlc_stream_t stream) {
+                                         size_t workspace_bytes, int* status, uint32_t* path_hint,
+                                         tlc_stream_t stream) {
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
+    uint32_t* dev_hint;
+    if (!hint_word(path_hint, &dev_hint)) return TLC_ERR_INVALID_ARG;
     return run_accumulate_many(p, info->stream_bytes, payloads, in, in_stride, in_lens, scales, s, acc, workspace,
-                               workspace_bytes, status, static_cast<hipStream_t>(stream));
+                               workspace_bytes, status, path_hint, dev_hint, static_cast<hipStream_t>(stream));
 }
 
 int tlc_copy_probe(const void* src, void* dst, uint64_t bytes, tlc_stream_t stream) {

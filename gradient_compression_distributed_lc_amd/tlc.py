@@ -77,7 +77,7 @@ _SIGS = {
                                              _P, _P]),
     "tlc_accumulate_many_workspace_size": (_U64, [ctypes.POINTER(GroupInfo), _U32]),
     "tlc_decompress_accumulate_many_group": (_I, [ctypes.POINTER(GroupInfo), _P, _U32, _P, _U64, _P, _P, _F, _P,
-                                                  _P, _SZ, _P, _P]),
+                                                  _P, _SZ, _P, _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_gather_probe": (_I, [_P, _P, _U64, _P, _P]),
@@ -552,16 +552,18 @@ class Group:
     def accumulate_many_workspace_size(self, payloads: int) -> int:
         nb = int(lib().tlc_accumulate_many_workspace_size(ctypes.byref(self.info), int(payloads)))
         if nb == 0:
-            raise ValueError(f"payloads must be 1..64, got {payloads}")
+            raise ValueError(f"payloads must be 1..64 (and payloads x tensors below 2^31), got {payloads}")
         return nb
 
     def decompress_accumulate_many(self, inp, in_lens, scales, s, acc, *, payloads=None, workspace=None,
-                                   status=None, stream=None):
+                                   status=None, path_hint=None, stream=None):
         """tlc_decompress_accumulate_many_group: payload p's streams in
         inp[p] (a uint8 tensor of shape (payloads, stream_bytes) or a flat
         one of payloads * stream_bytes), its lengths and scales in row p of
         in_lens / scales (payloads x count); acc += every payload's values in
-        payload order.  Returns (acc, status)."""
+        payload order.  path_hint: None (the dense sequence) or a word from
+        path_hint() holding 0 (sparse) or 1 (dense), rewritten by the device
+        with the payloads' density class.  Returns (acc, status)."""
         dev = self.device
         P = int(payloads if payloads is not None else (inp.shape[0] if inp.dim() == 2 else 1))
         stride = int(inp.shape[1]) if inp.dim() == 2 else self.stream_bytes
@@ -581,7 +583,7 @@ class Group:
             ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"), P, _ptr(inp, torch.uint8, "in"),
             stride, _ptr(in_lens, torch.int64, "in_lens"), _ptr(scales, torch.float32, "scales"), s,
             _ptr(acc, torch.float32, "acc"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-            _ptr(status, torch.int32, "status"), _stream(stream))
+            _ptr(status, torch.int32, "status"), _hint_ptr(path_hint), _stream(stream))
         _check(rc, "tlc_decompress_accumulate_many_group")
         return acc, status
 

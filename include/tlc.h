@@ -276,13 +276,18 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
                                     tlc_stream_t stream);
 
 /* Decompress-and-accumulate several payloads of one group into acc in one
- * launch sequence: for p = 0 .. payloads-1 in that order, acc[i] +=
- * q_{p,i} * (M_{p,t}*s) where q_{p,i} != 0; the result is bit for bit that
- * of `payloads` tlc_decompress_accumulate_group calls in order.  This is the
+ * call: for p = 0 .. payloads-1 in that order, acc[i] += q_{p,i} *
+ * (M_{p,t}*s) where q_{p,i} != 0; the result is bit for bit that of
+ * `payloads` tlc_decompress_accumulate_group calls in order.  This is the
  * receiving side of the page's exchange ("Proposed method", first and fourth
- * items) for many senders: every payload's quartic bytes are decoded into
- * the workspace in one launch, then acc is read and written once, skipping
- * every 1024-value block where no payload has a nonzero code.
+ * items) for many senders.  Two launch sequences give the same acc:
+ *   dense:  one decoder pass records where every 5120-value tile of every
+ *           payload begins, then one pass reads and writes each tile of acc
+ *           once (tiles no payload has a nonzero code in are skipped),
+ *           adding every payload's codes for it in payload order;
+ *   sparse: one decoder set-up, then one pass per payload in order, each
+ *           adding only that payload's nonzero codes (fastest while the
+ *           streams are near all-zero, e.g. early in error feedback).
  *   payloads       1 .. 64.
  *   in             payload p's stream buffer (laid out as by
  *                  tlc_compress_group) at in + p * in_stride; in_stride >=
@@ -293,16 +298,22 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
  *   scales         device fp32[payloads * count], likewise.
  *   acc            flat fp32[info->total_elems], updated in place.
  *   workspace      at least tlc_accumulate_many_workspace_size(info,
- *                  payloads) bytes (about payloads * (stream_bytes +
- *                  total_elems / 1024)).
+ *                  payloads) bytes (per payload: the decoder's chunk map and
+ *                  flags, and 12 bytes per 5120-value tile).
+ *   path_hint      optional (NULL allowed), as for tlc_decompress: 0 = the
+ *                  sparse sequence, 1 = the dense one; the call's first kernel
+ *                  overwrites it with the density class of all the payloads'
+ *                  streams together.  NULL: the dense sequence.
  * Errors as for tlc_decompress_accumulate_group; TLC_ERR_INVALID_ARG for
- * payloads outside 1 .. 64 or a bad in_stride. */
+ * payloads outside 1 .. 64, a bad in_stride or a hint word the device cannot
+ * reach; TLC_ERR_TOO_LARGE when payloads * count exceeds 2^31 - 1 or the
+ * payloads' decoder chunks 2^32 - 1 (the workspace size is then 0). */
 uint64_t tlc_accumulate_many_workspace_size(const tlc_group_info* info, uint32_t payloads);
 int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void* d_table, uint32_t payloads,
                                          const uint8_t* in, uint64_t in_stride, const uint64_t* in_lens,
                                          const float* scales, float s, float* acc,
                                          void* workspace, size_t workspace_bytes, int* status,
-                                         tlc_stream_t stream);
+                                         uint32_t* path_hint, tlc_stream_t stream);
 
 /* ---- five-plane byte layout (ablation) --------------------------------------
  * The 3LC page ("Proposed method", second item) packs five ternary values per

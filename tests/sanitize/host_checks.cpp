@@ -146,11 +146,18 @@ int main() {
           TLC_ERR_INVALID_ARG);
     CHECK(tlc_decompress_group(&g, fake, fb, fl, ff, 1.5f, ff, ws, 16, fs, nullptr, nullptr) == TLC_ERR_WORKSPACE);
     CHECK(tlc_decompress_accumulate_many_group(&g, fake, 0, fb, g.stream_bytes, fl, ff, 1.5f, ff, ws, 1 << 20, fs,
-                                               nullptr) == TLC_ERR_INVALID_ARG);
+                                               nullptr, nullptr) == TLC_ERR_INVALID_ARG);
     CHECK(tlc_decompress_accumulate_many_group(&g, fake, 2, fb, g.stream_bytes - 16, fl, ff, 1.5f, ff, ws, 1 << 20,
-                                               fs, nullptr) == TLC_ERR_INVALID_ARG);
+                                               fs, nullptr, nullptr) == TLC_ERR_INVALID_ARG);
     CHECK(tlc_decompress_accumulate_many_group(&g, fake, 2, fb, g.stream_bytes, fl, ff, 1.5f, ff, ws, 16, fs,
-                                               nullptr) == TLC_ERR_WORKSPACE);
+                                               nullptr, nullptr) == TLC_ERR_WORKSPACE);
+    {
+        tlc_group_info huge = g;  // unit ids of payloads x tensors must stay below 2^31
+        huge.count = 1ull << 26;
+        huge.chunks = 1ull << 26;
+        CHECK(tlc_accumulate_many_workspace_size(&huge, 31) > 0);
+        CHECK(tlc_accumulate_many_workspace_size(&huge, 32) == 0);
+    }
     CHECK(tlc_planes_gather(ff, fl, ff, fl, nullptr, 3, 100, nullptr) == TLC_ERR_INVALID_ARG);
     CHECK(tlc_planes_scatter(ff, fl, ff, fl, fl, 65536, 100, nullptr) == TLC_ERR_INVALID_ARG);
 

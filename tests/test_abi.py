@@ -215,11 +215,19 @@ def test_accumulate_many_host_checks():
     assert b8 < 8 * (12 * T + 16 * K + 8 * len(sizes) + 8) + 8 * 256 and b8 < int(big.stream_bytes)
     assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 0) == 0
     assert L.tlc_accumulate_many_workspace_size(ctypes.byref(info), 65) == 0
+    # payloads x tensors must stay below 2^31 (the decoder's unit ids), and the payloads' chunks below 2^32
+    huge = tlc.GroupInfo.from_buffer_copy(info)
+    huge.count, huge.chunks = 1 << 26, 1 << 26
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(huge), 31) > 0
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(huge), 32) == 0
+    huge.count, huge.chunks = 3, (1 << 27) + 1
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(huge), 31) > 0
+    assert L.tlc_accumulate_many_workspace_size(ctypes.byref(huge), 32) == 0
     SB = int(info.stream_bytes)
 
     def call(P, stride, ws_bytes, s=1.5, acc=fake):
         return L.tlc_decompress_accumulate_many_group(ctypes.byref(info), fake, P, fake, stride, fake, fake, s,
-                                                      acc, ws, ws_bytes, fake, None)
+                                                      acc, ws, ws_bytes, fake, None, None)
     assert call(0, SB, eight) == tlc.ERR_INVALID_ARG
     assert call(65, SB, 1 << 40) == tlc.ERR_INVALID_ARG
     assert call(8, SB - 16, eight) == tlc.ERR_INVALID_ARG    # payload buffers would overlap

@@ -120,13 +120,19 @@ def test_bert_large_eight_workers_accumulate():
         del out, lens, scales
     say("case bert_large: 8-payload sum")
     assert np.array_equal(bits(acc_d.cpu().numpy()), bits(acc_h))
-    # the same eight payloads in one many-payload call from a zero sum
-    say("case bert_large: 8 payloads in one call")
+    # the same eight payloads in one many-payload call from a zero sum, on
+    # both launch sequences (one pass over the sum; one add pass per payload)
     acc_m = torch.zeros(N, dtype=torch.float32, device="cuda:0")
-    _, st = g.decompress_accumulate_many(pay, pay_lens.view(-1), pay_scales.view(-1), s, acc_m)
-    torch.cuda.synchronize()
-    assert int(st.item()) == 0
-    assert np.array_equal(bits(acc_m.cpu().numpy()), bits(acc_h))
+    for route in (1, 0):
+        say(f"case bert_large: 8 payloads in one call, sequence {route}")
+        acc_m.zero_()
+        h = tlc.path_hint()
+        h[0] = route
+        _, st = g.decompress_accumulate_many(pay, pay_lens.view(-1), pay_scales.view(-1), s, acc_m, path_hint=h)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert np.array_equal(bits(acc_m.cpu().numpy()), bits(acc_h)), route
+        assert int(h[0]) == 0  # first-step payloads are sparse
     del acc_m, pay
     # model-delta direction: the server compresses the workers' mean with its
     # own (zero) error buffer; every tensor's stream, M and error bit for bit

@@ -118,7 +118,7 @@ def test_max_size_tensor():
     # the many-payload accumulate at the same size: the stream twice, as two
     # payloads (the second one's bytes start ~859 MB into the buffer, and its
     # tile records follow the first one's 838,861)
-    say("case max size: accumulate ok, two payloads in one call")
+    say("case max size: accumulate ok")
     B = tlc.compress_bound(n)
     stride = -(-B // 16) * 16
     two = torch.empty(2 * stride, dtype=torch.uint8, device=dev)
@@ -127,10 +127,16 @@ def test_max_size_tensor():
     g = tlc.Group([n], device=dev)
     lens2 = torch.cat([c.out_len, c.out_len])
     scales2 = torch.cat([c.scale, c.scale])
-    _, st = g.decompress_accumulate_many(two.view(2, stride), lens2, scales2, s, acc)
-    torch.cuda.synchronize()
-    assert int(st.item()) == 0
-    for _ in range(2):
-        exp = oracle.decompress_accumulate(small, M, val.size, s, exp)
-    assert np.array_equal(bits(acc[ti].cpu().numpy()), bits(exp))
-    assert int(torch.count_nonzero(acc).item()) == int(np.count_nonzero(exp))
+    for route in (None, 0):  # one pass over acc; one add pass per payload
+        say(f"case max size: two payloads in one call, sequence {route}")
+        h = None
+        if route is not None:
+            h = tlc.path_hint()
+            h[0] = route
+        _, st = g.decompress_accumulate_many(two.view(2, stride), lens2, scales2, s, acc, path_hint=h)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        for _ in range(2):
+            exp = oracle.decompress_accumulate(small, M, val.size, s, exp)
+        assert np.array_equal(bits(acc[ti].cpu().numpy()), bits(exp))
+        assert int(torch.count_nonzero(acc).item()) == int(np.count_nonzero(exp))
