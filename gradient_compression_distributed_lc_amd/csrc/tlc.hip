@@ -81,6 +81,8 @@ constexpr uint32_t kETileBytes = kETile / 5;      // 1024 quartic bytes = 4 per 
 constexpr uint32_t kSpan = 256;                   // encode tiles per k_emit block (one per lane)
 constexpr uint32_t kChunk = 4096;                 // decoder stream bytes per chunk = 16 per lane
 constexpr uint32_t kWideBPL = 64;                 // stream bytes per lane of the record pass over many payloads
+static_assert((kChunk & (kChunk - 1)) == 0 && ((kThreads * kWideBPL) & (kThreads * kWideBPL - 1)) == 0,
+              "decoder chunks are powers of two (k_prep numbers them with shifts)");
 constexpr uint32_t kZero = 121;                   // quartic byte of five zero codes
 constexpr uint32_t kRunMax = 14;                  // codes 243..255 = runs of 2..14
 constexpr uint32_t kRunBase = 241;
@@ -1370,6 +1372,15 @@ constexpr uint64_t kManyDenseNum = 82;
 
 constexpr uint32_t kMaxPayloads = 64;  // payloads of one accumulate-many call (one wavefront lane each)
 
+// p[0 .. n) = v by one thread: 16-byte stores between a 4-byte head and tail.
+__device__ __forceinline__ void fill_words(uint32_t* p, uint32_t n, uint32_t v) {
+    uint32_t i = 0;
+    for (; i < n && (reinterpret_cast<uintptr_t>(p + i) & 15); ++i) p[i] = v;
+    const uint4 v4 = make_uint4(v, v, v, v);
+    for (; i + 4 <= n; i += 4) *reinterpret_cast<uint4*>(p + i) = v4;
+    for (; i < n; ++i) p[i] = v;
+}
+
 // Decoder state reset and set-up, for `payloads` payloads of the group (unit
 // u = p * count + t is tensor t of payload p; in_lens and scales are indexed
 // by unit).
@@ -1415,17 +1426,19 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
         // Thread t numbers the chunks of units [u0, u1), a contiguous run:
         // first its total (loads in batches, all in flight together), then
         // a block scan, then the numbers (the same loads, now in cache).
-        const uint64_t units = (uint64_t)payloads * g.count;
-        const uint64_t per = (units + kThreads - 1) / kThreads;
-        const uint64_t u0 = min(units, threadIdx.x * per), u1 = min(units, u0 + per);
+        // Unit ids are below 2^31 and chunk is a power of two.
+        const uint32_t units = payloads * g.count;
+        const uint32_t per = (units + kThreads - 1) / kThreads;
+        const uint32_t u0 = min(units, threadIdx.x * per), u1 = min(units, u0 + per);
+        const uint32_t lg = 31u - (uint32_t)__clz(chunk);
         constexpr uint32_t kBatch = 8;
-        auto chunks_of = [&](uint64_t a, uint64_t (&L)[kBatch], uint64_t (&B)[kBatch]) {
+        auto chunks_of = [&](uint32_t a, uint64_t (&L)[kBatch], uint64_t (&B)[kBatch]) {
 #pragma unroll
             for (uint32_t k = 0; k < kBatch; ++k) {
                 L[k] = 0;
                 B[k] = 0;
                 if (a + k < u1) {
-                    B[k] = quartic_len(load_seg(g, (uint32_t)((a + k) % g.count)).n);
+                    B[k] = quartic_len(load_seg(g, (a + k) % g.count).n);
                     L[k] = in_lens[a + k];
                 }
             }
@@ -1434,30 +1447,30 @@ __global__ __launch_bounds__(kThreads) void k_prep(GroupView g, uint32_t payload
         };
         uint32_t mine = 0;
         uint64_t sum_l = 0, sum_b = 0;
-        for (uint64_t a = u0; a < u1; a += kBatch) {
+        for (uint32_t a = u0; a < u1; a += kBatch) {
             uint64_t L[kBatch], B[kBatch];
             chunks_of(a, L, B);
 #pragma unroll
             for (uint32_t k = 0; k < kBatch; ++k)
                 if (a + k < u1) {
-                    mine += max(1u, (uint32_t)((L[k] + chunk - 1) / chunk));
+                    mine += max(1u, (uint32_t)((L[k] + chunk - 1) >> lg));
                     sum_l += L[k];
                     sum_b += B[k];
                 }
         }
         uint32_t carry;
         uint32_t first = block_excl_sum(mine, s_u, &carry);
-        for (uint64_t a = u0; a < u1; a += kBatch) {
+        for (uint32_t a = u0; a < u1; a += kBatch) {
             uint64_t L[kBatch], B[kBatch];
             chunks_of(a, L, B);
 #pragma unroll
             for (uint32_t k = 0; k < kBatch; ++k)
                 if (a + k < u1) {
-                    const uint64_t u = a + k;
-                    const uint32_t rc = max(1u, (uint32_t)((L[k] + chunk - 1) / chunk));
+                    const uint32_t u = a + k;
+                    const uint32_t rc = max(1u, (uint32_t)((L[k] + chunk - 1) >> lg));
                     dec_first[u] = first;
                     tickets[u] = 0;
-                    for (uint32_t r = 0; r < rc; ++r) dec_map[first + r] = (uint32_t)u | (rc > 1 ? kMulti : 0u);
+                    fill_words(dec_map + first, rc, u | (rc > 1 ? kMulti : 0u));
                     first += rc;
                 }
         }
