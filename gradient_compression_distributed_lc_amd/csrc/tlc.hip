@@ -1060,6 +1060,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(GroupView g, float* __r
 // once.
 constexpr uint32_t kEmitLds = 40960;
 
+// Staged chunks of a span up to which k_emit keeps a table of each chunk's
+// tile in LDS (one byte each) instead of searching the tiles' chunk prefix
+// for every chunk: a span of the BERT-large set holds ~1,200-2,600.
+constexpr uint32_t kOwnCap = 4096;
+
 __device__ __forceinline__ uint8_t byte_of(const uint4& v, uint32_t i) {  // byte i (0..15) of v
     const uint32_t w = i < 4 ? v.x : i < 8 ? v.y : i < 12 ? v.z : v.w;
     return (uint8_t)(w >> (8 * (i & 3)));
@@ -1083,6 +1088,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     __shared__ uint8_t s_fin[kThreads];       // closing remainder code of the tensor's last tile, or 0
     __shared__ uint32_t s_cpre[kThreads + 1];  // prefix of staged 16-byte chunks over the span's tiles
     __shared__ __align__(16) uint32_t s_out[(kEmitLds + 16) / 4];  // the span's bytes, inverted and shifted by the store misalignment
+    __shared__ uint8_t s_own[kOwnCap];           // tile of each staged chunk (spans of at most kOwnCap chunks)
     __shared__ uint32_t s_span, s_E, s_r, s_ok, s_clo, s_chi;
 
     // Block b belongs to the tensor of span b.  A tensor with several spans
@@ -1112,10 +1118,16 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     // bytes 16c .. 16c + 15), and the first 256 chunks are loaded before it.
     const uint8_t* const stg = staging + (uint64_t)(sg.etile0 + lsp * kSpan) * kETileBytes;
     uint32_t tot_chunks;
-    s_cpre[threadIdx.x] = block_excl_sum((kint + 15) / 16, s_u, &tot_chunks);
+    const uint32_t my_chunks = (kint + 15) / 16;
+    const uint32_t my_first = block_excl_sum(my_chunks, s_u, &tot_chunks);
+    s_cpre[threadIdx.x] = my_first;
     if (threadIdx.x == 0) s_cpre[kThreads] = tot_chunks;
+    const bool own = tot_chunks <= kOwnCap;  // block-uniform
+    if (own)
+        for (uint32_t i = 0; i < my_chunks; ++i) s_own[my_first + i] = (uint8_t)threadIdx.x;
     __syncthreads();
-    auto chunk_owner = [&](uint32_t cv) {  // tile holding staged chunk cv of the span
+    auto chunk_owner = [&](uint32_t cv) -> uint32_t {  // tile holding staged chunk cv of the span
+        if (own) return s_own[cv];
         uint32_t k = 0, hi2 = kThreads;
         while (hi2 - k > 1) {
             const uint32_t mid = (k + hi2) >> 1;
@@ -1261,6 +1273,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
     // byte is written once and no barrier waits on HBM.
     constexpr uint32_t kWin = kEmitLds / 16;  // store chunks per window
     const uint32_t so = s_off[threadIdx.x] + lead + (rem ? 1u : 0u);  // span byte of this tile's first staged byte
+    const bool one_window = nchunks <= kWin;  // block-uniform: the whole span in one window
     for (uint32_t w0 = 0; w0 < nchunks; w0 += kWin) {
         const uint32_t wn = min(kWin, nchunks - w0);
         const int32_t lo = (int32_t)(16 * w0) - (int32_t)mis;
@@ -1273,12 +1286,24 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
             reinterpret_cast<uint4*>(s_out)[c] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
         // the staged chunks that meet the window are consecutive: their range
-        // is the min and max over the tiles
-        if (kint) {
-            const int32_t a = max(lo - (int32_t)so, 0), b = min(hi - (int32_t)so, (int32_t)kint);
-            if (a < b) {
-                atomicMin(&s_clo, s_cpre[threadIdx.x] + (uint32_t)a / 16);
-                atomicMax(&s_chi, s_cpre[threadIdx.x] + ((uint32_t)b + 15) / 16);
+        // is the min and max over the tiles (all of them when one window
+        // holds the span), reduced per wavefront before the LDS atomics
+        if (!one_window) {
+            uint32_t clo = ~0u, chi = 0u;
+            if (kint) {
+                const int32_t a = max(lo - (int32_t)so, 0), b = min(hi - (int32_t)so, (int32_t)kint);
+                if (a < b) {
+                    clo = my_first + (uint32_t)a / 16;
+                    chi = my_first + ((uint32_t)b + 15) / 16;
+                }
+            }
+            for (int d = 32; d >= 1; d >>= 1) {
+                clo = min(clo, (uint32_t)__shfl_xor((int)clo, d, 64));
+                chi = max(chi, (uint32_t)__shfl_xor((int)chi, d, 64));
+            }
+            if (lane_id() == 0) {
+                atomicMin(&s_clo, clo);
+                atomicMax(&s_chi, chi);
             }
         }
         auto or_byte = [&](int32_t p, uint32_t b) {  // span byte p in [lo, hi)
@@ -1290,8 +1315,8 @@ __global__ __launch_bounds__(kThreads) void k_emit(GroupView g, const uint64_t* 
             if (rem && pr < (int32_t)end && pr >= lo && pr < hi) or_byte(pr, rem);
             if (fin && pf < (int32_t)end && pf >= lo && pf < hi) or_byte(pf, fin);
         }
-        __syncthreads();
-        copy_staged(s_clo, s_chi, [&](uint32_t p, uint32_t nb, uint4 v) {
+        if (!one_window) __syncthreads();  // s_clo, s_chi
+        copy_staged(one_window ? 0u : s_clo, one_window ? tot_chunks : s_chi, [&](uint32_t p, uint32_t nb, uint4 v) {
             // bytes j of the chunk with j < nb and lo <= p + j < hi, inverted
             // (the others zeroed), shifted to the byte offset of p - lo in its
             // word, into the five words of s_out they meet
