@@ -342,17 +342,41 @@ class Bench:
             dec()
 
         timed(torch, 3, body, before)
+        t = timed(torch, reps, body, before)
+        self.status_ok(st_c, st_d, what=name)
+        # the dominant kernel's duration, in repetitions of their own (the
+        # events around it cost a small step several microseconds)
         tlc.profile_read()
         tlc.profile_only(DOMINANT)
         tlc.profile_enable(True)
-        t = timed(torch, reps, body, before)
+        timed(torch, reps, body, before)
         tlc.profile_enable(False)
         dom = tlc.profile_read().get(DOMINANT, (0, 0.0))
-        self.status_ok(st_c, st_d, what=name)
         L = int(lens.sum().item())
         rec = step_record(N, len(sizes), s, L, [a + b for a, b in t], [a for a, _ in t], [b for _, b in t],
                           self.copy_gbps, dom)
         rec["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
+        # the same step captured once in a HIP graph and replayed (the library
+        # launches only kernels on the caller's stream, so a training loop can
+        # capture its codec calls); the first-step reset stays outside
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        before(0)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                comp()
+                dec()
+        torch.cuda.synchronize()
+
+        def replay(r, mark):
+            graph.replay()
+
+        timed(torch, 3, replay, before)
+        tg = timed(torch, reps, replay, before)
+        self.status_ok(st_c, st_d, what=f"{name}, graph replays")
+        rec["graph_ms_per_step"] = stats([v[0] for v in tg])
+        del graph
         return rec
 
     def record_single_1m(self):
@@ -367,6 +391,9 @@ class Bench:
         med = rec["ms_per_step"]["median"]
         rec["us_per_step"] = {k: round(v * 1e3, 1) for k, v in rec["ms_per_step"].items() if k != "reps"}
         rec["tensors_per_s"] = round(len(w.sizes) / (med * 1e-3), 0)
+        gmed = rec["graph_ms_per_step"]["median"]
+        rec["graph_us_per_step"] = {k: round(v * 1e3, 1) for k, v in rec["graph_ms_per_step"].items() if k != "reps"}
+        rec["graph_tensors_per_s"] = round(len(w.sizes) / (gmed * 1e-3), 0)
         rec["note"] = "launch-bound: 1.73M values in 329 tensors; the step is the kernels' fixed latencies"
         return rec
 

@@ -415,16 +415,6 @@ __device__ __forceinline__ int ternary(float v, float thr) {
     return fabsf(v) >= thr ? (v > 0.0f ? 1 : -1) : 0;
 }
 
-// tensor holding element e: largest k in [lo, hi) with segs[k].elem_off <= e
-__device__ uint32_t find_segment(const Seg* segs, uint32_t lo, uint32_t hi, uint64_t e) {
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (segs[mid].elem_off <= e) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
 // ---------------------------------------------------------------------------
 // compress kernels
 
@@ -439,8 +429,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
                                                         uint32_t* __restrict__ ctrl, int* __restrict__ status) {
     __shared__ float sm[kAccThreads / 64];
     __shared__ uint32_t s_cc[kAccThreads / 64];
-    __shared__ uint32_t s_part[kFTile];  // per-tensor maxima of a tile that spans tensors
-    __shared__ uint32_t s_last;
+    __shared__ uint32_t s_part[kFTile + 1];   // per-tensor maxima of a tile that spans tensors
+    __shared__ uint32_t s_start[kFTile + 1];  // their first elements, relative to the tile
     const uint32_t t = blockIdx.x;
     const uint32_t info = g.segs ? g.ftile_info[t] : 0u;  // issued before the stream loads
     const uint64_t i4 = (uint64_t)t * (kFTile / 4) + threadIdx.x;
@@ -513,23 +503,38 @@ __global__ __launch_bounds__(kAccThreads) void k_accum_max(GroupView g, uint64_t
         }
         if (threadIdx.x == 0) cand_cnt[t] = (cb != INFINITY && total <= kCand) ? (uint16_t)total : kCandNone;
     } else {
-        // the tile spans tensors g0..g1: one partial max per tensor, in slot t + g
+        // the tile spans tensors g0..g1: one partial max per tensor, in slot
+        // t + g.  The first elements of the tensors that can meet it (g0 up
+        // to the tensor of the next tile's first element: at most kFTile + 1,
+        // as no tensor is empty) go to LDS, where each element finds its
+        // tensor without a search through the table.
         const uint32_t g0 = info & ~kStraddle;
-        const uint32_t hi = min(g.count, g0 + kFTile + 1);
-        for (uint32_t k = threadIdx.x; k < kFTile; k += kAccThreads) s_part[k] = 0;
-        if (threadIdx.x == 0) {
-            const uint64_t last = min(N, (uint64_t)(t + 1) * kFTile) - 1;
-            s_last = find_segment(g.segs, g0, hi, last);
+        const uint64_t tile0 = (uint64_t)t * kFTile;
+        const uint64_t last = min(N, tile0 + kFTile) - 1;
+        const uint32_t gn = tile0 + kFTile < N ? (g.ftile_info[t + 1] & ~kStraddle) : g.count - 1;
+        const uint32_t nk = gn - g0 + 1;
+        for (uint32_t k = threadIdx.x; k < nk; k += kAccThreads) {
+            const uint64_t eo = g.segs[g0 + k].elem_off;
+            s_start[k] = eo <= tile0 ? 0u : (uint32_t)min<uint64_t>(eo - tile0, kFTile);
+            s_part[k] = 0;
         }
         __syncthreads();
-        for (int j = 0; j < 4; ++j) {
-            if (el + j < N) {
-                const uint32_t k = find_segment(g.segs, g0, hi, el + j) - g0;
-                atomicMax(&s_part[k], __float_as_uint(fabsf(v[j])));  // order of non-negative floats
+        auto tensor_of = [&](uint32_t i) {  // the last k with s_start[k] <= i (s_start[0] == 0)
+            uint32_t lo = 0, hi = nk;
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (s_start[mid] <= i) lo = mid;
+                else hi = mid;
             }
+            return lo;
+        };
+        for (int j = 0; j < 4; ++j) {
+            if (el + j < N)  // order of non-negative floats
+                atomicMax(&s_part[tensor_of((uint32_t)(el + j - tile0))], __float_as_uint(fabsf(v[j])));
         }
+        const uint32_t klast = tensor_of((uint32_t)(last - tile0));
         __syncthreads();
-        for (uint32_t k = threadIdx.x; k <= s_last - g0; k += kAccThreads) pmax[t + g0 + k] = __uint_as_float(s_part[k]);
+        for (uint32_t k = threadIdx.x; k <= klast; k += kAccThreads) pmax[t + g0 + k] = __uint_as_float(s_part[k]);
         if (threadIdx.x == 0) cand_cnt[t] = kCandNone;  // a tile shared by tensors is read again in full
     }
     // look-back state of k_emit starts empty on every call
