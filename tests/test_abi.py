@@ -340,3 +340,26 @@ def test_binding_rejects_undersized_group_buffers():
         g.decompress_fixed(_t(total_q, u8), _t(C - 1, i64), _t(C, f32), 1.5, tlc.ENC_QUARTIC, y=_t(N, f32))
     with pytest.raises(ValueError, match="y holds"):
         g.decompress_fixed(_t(total_q, u8), _t(C, i64), _t(C, f32), 1.5, tlc.ENC_QUARTIC, y=_t(N - 1, f32))
+
+
+def test_path_hint_word_is_checked_on_the_host():
+    """The decompress and many-payload accumulate take the caller's hint word
+    only as one pinned int32 on the host; anything else is refused before the
+    library is called (no device is needed to check this)."""
+    import torch
+    assert tlc._hint_ptr(None) is None
+    with pytest.raises(ValueError, match="pinned host tensor"):
+        tlc._hint_ptr(torch.zeros(1, dtype=torch.int32))  # pageable host memory
+    # the C ABI refuses a word the device cannot reach (here: no device at all,
+    # or an address that is not pinned memory) with TLC_ERR_INVALID_ARG
+    L = tlc.lib()
+    info, _, _ = tlc.group_plan([1000, 2000])
+    V = ctypes.c_void_p
+    word = ctypes.c_uint32(0)
+    rc = L.tlc_decompress_group(ctypes.byref(info), V(0x10000), V(0x10000), V(0x10000), V(0x10000), 1.5,
+                                V(0x10000), V(0x20000), 1 << 30, V(0x10000), ctypes.byref(word), None)
+    assert rc == tlc.ERR_INVALID_ARG
+    rc = L.tlc_decompress_accumulate_many_group(ctypes.byref(info), V(0x10000), 2, V(0x10000),
+                                                int(info.stream_bytes), V(0x10000), V(0x10000), 1.5, V(0x10000),
+                                                V(0x20000), 1 << 30, V(0x10000), ctypes.byref(word), None)
+    assert rc == tlc.ERR_INVALID_ARG
