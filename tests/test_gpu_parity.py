@@ -283,6 +283,19 @@ def test_group_of_tiny_tensors():
         check_group(g, x, e, s, label=f"tiny s={s}")
 
 
+def test_flat_tiles_of_one_element_tensors():
+    # 512 one-element tensors fill a 512-element flat tile of the first pass,
+    # the most tensors a tile can meet; each element is its own tensor's
+    # maximum, so every code is nonzero
+    from gradient_compression_distributed_lc_amd import tlc
+    sizes = [1] * 1100 + [4097, 1, 2] + [1] * 600 + [511, 1, 512]
+    g = tlc.Group(sizes)
+    x, e = rand(sum(sizes), 33)
+    for s in (1.0, 1.5):
+        say(f"case one-element tensors s={s}")
+        check_group(g, x, e, s, label=f"ones s={s}")
+
+
 def test_hint_paths_give_identical_results():
     # The M buffer is read on entry as a hint for the second pass's candidate
     # lists.  Exact, too-large (lists rejected), too-small (lists overflow),
