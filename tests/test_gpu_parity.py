@@ -296,6 +296,26 @@ def test_flat_tiles_of_one_element_tensors():
         check_group(g, x, e, s, label=f"ones s={s}")
 
 
+def test_emit_span_at_the_chunk_table_limit():
+    # one tensor of 256 encode tiles (one k_emit span) whose tiles each open
+    # with 256 literal quartic bytes and end in zeros: 16 staged 16-byte
+    # chunks per tile, 4096 in the span, the most for which k_emit keeps a
+    # table of each chunk's tile in LDS; then one literal more in the first
+    # tile (4097 chunks: the span searches the tiles' chunk prefix instead).
+    # The span's output (~80 KB) also takes several LDS windows.
+    from gpu_util import check_single
+    T = 256
+    n = T * 5120
+    for extra in (0, 1):
+        x = np.zeros(n, np.float32)
+        for t in range(T):
+            nb = 256 + (extra if t == 0 else 0)
+            x[t * 5120:t * 5120 + 5 * nb:5] = 1.0  # digit 0 of each of the tile's first nb quartic bytes
+        e = np.zeros(n, np.float32)
+        say(f"case emit span of {4096 + extra} staged chunks")
+        check_single(x, e, 1.5, label=f"emit chunks {4096 + extra}")
+
+
 def test_hint_paths_give_identical_results():
     # The M buffer is read on entry as a hint for the second pass's candidate
     # lists.  Exact, too-large (lists rejected), too-small (lists overflow),
