@@ -5,8 +5,9 @@
 // for Distributed Machine Learning", section "Proposed method"): error
 // accumulation and 3-value quantization with a sparsity multiplier, quartic
 // encoding (five ternary values per byte), zero-run encoding of the all-zero
-// byte, and the reverse path.  The page's implementation is vectorised CPU
-// code; here every step runs in the kernels below, laid out for CDNA4.
+// byte, and the reverse path.  The page keeps the codec cheap with vectorised,
+// byte-level operations; here every step runs in the kernels below, laid out
+// for CDNA4.
 //
 // compress (five launches):
 //   k_accum_max   the one full HBM pass: v = x + err written back to err, and
@@ -48,6 +49,12 @@
 //             recorded)
 //             -> k_expand (dense streams: one wavefront per encode tile
 //             decodes it in LDS and writes it once).
+// accumulate of many payloads: k_prep for all of them -> dense streams:
+//             k_decode records where every payload's encode tiles begin
+//             (16 KiB chunks) -> k_apply (persistent wavefronts: each tile of
+//             acc through LDS once, every payload's nonzero codes added in
+//             payload order); sparse streams: one add-mode k_decode launch
+//             per payload, in payload order.
 // fixed-length encodings (ablations: quartic bytes alone, 2-bit fields): the
 //             compress kernels up to k_quant_pack, which writes each tile's
 //             bytes at a fixed place over k_fixed_fill's zero-code bytes;
