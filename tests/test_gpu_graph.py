@@ -129,6 +129,59 @@ def test_graph_captured_before_any_eager_call():
     assert "graph scenario ok" in r.stdout
 
 
+@pytest.mark.parametrize("path", [0, 1])
+def test_graph_of_many_payload_accumulate(path):
+    """tlc_decompress_accumulate_many_group captured in a HIP graph on each
+    launch sequence (a hint word of 0: one set-up and one add pass per
+    payload; 1: the record pass and one pass over acc) and replayed: every
+    replay, from acc reset eagerly in between, equals the eager call."""
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(7 + path)
+    sizes = [int(v) for v in rng.integers(1, 40_000, 30)] + [5120, 3, 100_001]
+    g = tlc.Group(sizes)
+    P, s = 6, 1.5
+    N = g.total
+    dev = torch.device("cuda:0")
+    streams = torch.zeros((P, g.stream_bytes), dtype=torch.uint8, device=dev)
+    lens = torch.empty((P, len(sizes)), dtype=torch.int64, device=dev)
+    scales = torch.zeros((P, len(sizes)), dtype=torch.float32, device=dev)
+    for p in range(P):  # payloads from the library's own compress (their parity is tested elsewhere)
+        x = (rng.standard_normal(N) * 1e-3).astype(np.float32)
+        e = (rng.uniform(-1, 1, N) * (3e-3 if p % 2 else 1e-4)).astype(np.float32)
+        g.compress(to_dev(x), to_dev(e), s, out=streams[p], out_lens=lens[p], scales=scales[p])
+    acc0 = to_dev((rng.standard_normal(N) * 1e-3).astype(np.float32))
+    ws = torch.empty(g.accumulate_many_workspace_size(P), dtype=torch.uint8, device=dev)
+    acc_g, acc_e = torch.empty_like(acc0), torch.empty_like(acc0)
+    st_g = torch.empty(1, dtype=torch.int32, device=dev)
+    st_e = torch.empty(1, dtype=torch.int32, device=dev)
+    hint = tlc.path_hint()
+    hint[0] = path
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            g.decompress_accumulate_many(streams, lens.view(-1), scales.view(-1), s, acc_g, workspace=ws,
+                                         status=st_g, path_hint=hint)
+    torch.cuda.synchronize()
+    ws_e = torch.empty_like(ws)
+    for k in range(3):
+        say(f"case graph of many-payload accumulate, sequence {path}, replay {k}")
+        acc_g.copy_(acc0)
+        acc_e.copy_(acc0)
+        torch.cuda.synchronize()
+        graph.replay()
+        word = tlc.path_hint()
+        word[0] = path
+        g.decompress_accumulate_many(streams, lens.view(-1), scales.view(-1), s, acc_e, workspace=ws_e, status=st_e,
+                                     path_hint=word)
+        torch.cuda.synchronize()
+        assert int(st_g.item()) == 0 and int(st_e.item()) == 0, k
+        assert torch.equal(acc_g.view(torch.int32), acc_e.view(torch.int32)), k
+
+
 if __name__ == "__main__":
     scenario(warm_up=False, path=1)
     print("graph scenario ok", flush=True)
