@@ -356,6 +356,7 @@ class Bench:
         rec = step_record(N, len(sizes), s, L, [a + b for a, b in t], [a for a, _ in t], [b for _, b in t],
                           self.copy_gbps, dom)
         rec["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
+        rec["nonzero_code_fraction"] = round(float(torch.count_nonzero(y).item()) / N, 6)
         # the same step captured once in a HIP graph and replayed (the library
         # launches only kernels on the caller's stream, so a training loop can
         # capture its codec calls); the first-step reset stays outside
@@ -898,6 +899,7 @@ def main():
     ms_total = evs[0].elapsed_time(evs[-1])
     ms_per_step = ms_total / args.steps
     last_bits = 8.0 * float(lens.sum().item()) / N
+    nonzero_last = float(torch.count_nonzero(yd).item()) / N  # the last step's decoded values: q != 0
     hint_after = "dense" if int(hint[0]) else "sparse"
 
     # phase times: compress calls alone, then decompress calls alone, each
@@ -1317,6 +1319,7 @@ def main():
         "path_copy_ceiling_frac": frac(alg_bytes_comp + alg_bytes_dec, ms_per_step, copy_gbps),
         "dominant_copy_ceiling_frac": round(achieved / copy_gbps, 4) if copy_gbps else None,
         "bits_per_value_last_step": round(last_bits, 4),
+        "nonzero_code_fraction_last_step": round(nonzero_last, 6),
         "pipelined": {"ms_per_step": round(pipe_ms, 4), "GBps_fp32_in": round(4.0 * N / (pipe_ms * 1e-3) / 1e9, 1),
                       "path_roofline_frac": frac(alg_bytes_comp + alg_bytes_dec, pipe_ms, HBM_PEAK_GBPS),
                       "how": "compress of batch k on one stream, decompress of payload k-1 on another "
