@@ -60,6 +60,12 @@ DOMINANT_BYTES_PER_ELEM = 12
 METRIC = "3LC compress+decompress GB/s (fp32 in) and % of HBM roofline; bits/value"
 ROT = 1_000_003                 # rotation between the gradient sets of consecutive steps
 WORKERS = 8
+# Per-kernel times from a pass where the library brackets every launch with two
+# events: the host then submits more slowly than short kernels run, so the GPU
+# waits between them and those waits land inside the brackets.
+EVENTS_NOTE = ("each launch bracketed by two HIP events in a pass of its own; kernels shorter than a few tens "
+               "of microseconds read long there (host submission gaps fall inside the brackets), so kernel "
+               "durations of the short kernels come from the rocprofv3 kernel traces")
 RECORDS = ("single_1m", "single_16m", "resnet110", "resnet50", "bert_large_first_step", "bert_large_steady")
 
 
@@ -1155,6 +1161,7 @@ def main():
         tlc.profile_enable(False)
         steady["kernels_ms_per_launch_events"] = {k: round(v[1] / v[0], 4) for k, v in tlc.profile_read().items()
                                                   if v[0]}
+        steady["kernels_events_note"] = EVENTS_NOTE
         # the same state pipelined over the two streams (10 more steps)
         for b in range(2):
             pay[b][2].copy_(scales)
@@ -1328,6 +1335,7 @@ def main():
         "configs": records,
         "ablations": ablations,
         "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
+        "kernels_events_note": EVENTS_NOTE,
         "wall_s_timed": round(wall, 3),
         "kernel_source": kernel_source_hash(),
     }
