@@ -234,11 +234,17 @@ def frac(nbytes: float, ms: float, peak_gbps: float):
     return round(nbytes / (ms * 1e-3) / 1e9 / peak_gbps, 4) if ms and peak_gbps else None
 
 
-def step_record(N: int, tensors: int, s: float, L: int, step_ms, comp_ms, dec_ms, copy_gbps, dom=None):
+def quartic_bytes(sizes) -> int:
+    """Bytes of the tensors' quartic encoding: five codes per byte."""
+    return sum(-(-int(n) // 5) for n in sizes)
+
+
+def step_record(N: int, tensors: int, s: float, L: int, step_ms, comp_ms, dec_ms, copy_gbps, dom=None, B=None):
     """The measurement table of one configuration: times over the
     repetitions, and the roofline of the step's algorithmic bytes
     (compress 12 B/value + stream + 4 B per M; decompress 4 B/value +
-    stream) at the median step time."""
+    stream) at the median step time.  B is the tensors' quartic byte count
+    (the sum of ceil(n/5)), for the zero-run encoding's ratio B/L."""
     st, sc, sd = stats(step_ms), stats(comp_ms), stats(dec_ms)
     alg_c = 12.0 * N + L + 4 * tensors
     alg_d = 4.0 * N + L
@@ -261,7 +267,10 @@ def step_record(N: int, tensors: int, s: float, L: int, step_ms, comp_ms, dec_ms
         "copy_ceiling_frac": round(achieved / copy_gbps, 4) if copy_gbps else None,
         "bits_per_value": round(8.0 * L / N, 4),
         "bits_per_value_with_scale": round(8.0 * (L + 4 * tensors) / N, 4),
+        "compression_ratio_vs_fp32": round(4.0 * N / L, 1),
     }
+    if B is not None:
+        rec["zero_run_ratio"] = round(B / L, 2)
     if dom is not None:
         launches, ms = dom
         if launches:
@@ -360,7 +369,7 @@ class Bench:
         dom = tlc.profile_read().get(DOMINANT, (0, 0.0))
         L = int(lens.sum().item())
         rec = step_record(N, len(sizes), s, L, [a + b for a, b in t], [a for a, _ in t], [b for _, b in t],
-                          self.copy_gbps, dom)
+                          self.copy_gbps, dom, B=quartic_bytes(sizes))
         rec["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
         rec["nonzero_code_fraction"] = round(float(torch.count_nonzero(y).item()) / N, 6)
         # the same step captured once in a HIP graph and replayed (the library
@@ -463,7 +472,8 @@ class Bench:
         self.status_ok(st_c, st_d, what="single_16m")
         # bits over the 10 steps' streams
         L_mean = int(round(np.mean(step_L)))
-        rec = step_record(N, 1, s, L_mean, [a for v in per_step for a in v], comp, decm, self.copy_gbps)
+        rec = step_record(N, 1, s, L_mean, [a for v in per_step for a in v], comp, decm, self.copy_gbps,
+                          B=quartic_bytes([N]))
         rec["per_step_ms_median"] = [round(float(np.median(v)), 4) for v in per_step]
         rec["bits_per_value_per_step"] = [round(8.0 * v / N, 4) for v in step_L]
         rec["ten_steps_ms"] = stats(tot)
@@ -1149,7 +1159,7 @@ def main():
             raise SystemExit("device status not ok in the steady-state steps")
         L_steady = int(lens.sum().item())
         steady = step_record(N, len(sizes), s, L_steady, [a + b for a, b in t], [a for a, _ in t],
-                             [b for _, b in t], copy_gbps, dom_steady)
+                             [b for _, b in t], copy_gbps, dom_steady, B=quartic_bytes(sizes))
         steady["after_steps"] = after
         steady["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
         # the per-kernel breakdown at this state (every kernel bracketed)
@@ -1253,7 +1263,7 @@ def main():
             raise SystemExit("device status not ok in the workers' first steps")
         L_first = int(wpay["first"][1].sum().item()) // WORKERS
         rec = step_record(N, len(sizes), s, L_first, [a + b for a, b in tw], [a for a, _ in tw],
-                          [b for _, b in tw], copy_gbps, dom_w)
+                          [b for _, b in tw], copy_gbps, dom_w, B=quartic_bytes(sizes))
         rec["how"] = ("worker w's set (seed 500+w), compress from a zero error buffer and no previous M, "
                       "then decompress; 3 repetitions per worker, w = 0..7")
         rec["decompress_sequence"] = "dense" if int(hint_w[0]) else "sparse"
