@@ -1818,7 +1818,7 @@ uint32_t xcd_grid(uint64_t units) { return (uint32_t)((units + 7) / 8 * 8); }
 
 // One wavefront per encode tile (5120 elements, 1024 quartic bytes), four per
 // block, with no block barrier: every element of the tile is written once,
-// y = q * (M*s), with nontemporal 16-byte stores (as the zero fill), so
+// y = q * (M*s), with streaming 16-byte stores (as the zero fill), so
 // decompress writes each line of y once (a zero fill with the nonzero values
 // scattered over it afterwards wrote every line that holds a nonzero code
 // twice).  A tile k_decode found no nonzero code in is written without
