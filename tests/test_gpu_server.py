@@ -57,7 +57,7 @@ def test_server_compress_single(n):
 def test_server_compress_special_values():
     # quotients that are subnormal, -0.0 sums, ties of the mean against M*s/2
     acc = np.array([3e-38, -1e-39, -0.0, 0.0, 6.0, -3.0, 1.5, 2.9999998, 3.0000002] * 5, np.float32)
-    for workers in (1, 2, 3, 6, 8):
+    for workers in (1, 2, 3, 6, 8, 16, 1024):
         for s in (1.0, 1.5, 1.99):
             say(f"case server special workers={workers} s={s}")
             check_server_single(acc, workers, np.zeros_like(acc), s, f"special w={workers} s={s}")
