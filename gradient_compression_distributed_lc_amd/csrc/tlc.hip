@@ -2922,7 +2922,7 @@ int run_accumulate_many(const Plan& p, uint64_t stream_bytes, uint32_t payloads,
 int run_decompress_fixed(const Plan& p, int enc, const uint8_t* in, const uint64_t* offs, const float* scales,
                          float s, float* y, int* status, hipStream_t st) {
     if (!in || !scales || !y || !status) return TLC_ERR_INVALID_ARG;
-    if (!valid_s(s)) return TLC_ERR_INVALID_ARG;
+    if (!aligned16(y) || !valid_s(s)) return TLC_ERR_INVALID_ARG;
     int rc = launch("tlc_status_ok", st, [&] { k_status_ok<<<1, 1, 0, st>>>(status); });
     if (rc) return rc;
     return launch("tlc_fixed_decode", st, [&] {

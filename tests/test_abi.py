@@ -159,6 +159,7 @@ def test_argument_errors_return_before_any_launch():
                                 None) == tlc.ERR_CAPACITY
     assert L.tlc_decompress_fixed(fake, fake, 10, 1.5, 0, fake, fake, None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_fixed(fake, fake, 10, 2.5, tlc.ENC_QUARTIC, fake, fake, None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_fixed(fake, fake, 10, 1.5, tlc.ENC_QUARTIC, odd, fake, None) == tlc.ERR_INVALID_ARG
     # server compress: no workers, no elements, capacity, s out of range
     assert L.tlc_server_compress(fake, 0, fake, 10, 1.5, fake, 10, fake, fake, ws, 4096, fake,
                                  None) == tlc.ERR_INVALID_ARG
@@ -183,6 +184,8 @@ def test_argument_errors_return_before_any_launch():
     assert L.tlc_compress_fixed_group(ctypes.byref(info), fake, tlc.ENC_QUARTIC, fake, fake, 1.5, fake, None,
                                       fake, ws, 1 << 20, fake, None) == tlc.ERR_INVALID_ARG
     assert L.tlc_decompress_fixed_group(ctypes.byref(info), fake, 7, fake, fake, fake, 1.5, fake, fake,
+                                        None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_decompress_fixed_group(ctypes.byref(info), fake, tlc.ENC_TWOBIT, fake, fake, fake, 1.5, odd, fake,
                                         None) == tlc.ERR_INVALID_ARG
 
 
