@@ -1438,9 +1438,9 @@ __device__ __forceinline__ void fill_words(uint32_t* p, uint32_t n, uint32_t v) 
 // by unit).
 // Sparse decompress (n_fill > 0): zero fill of y, one 16-byte store per lane
 // (the fastest fill measured on MI355X; any load before the store, or more
-// stores per lane, slows it by 10-40%), with a nontemporal hint: y is not
-// read again here, and the kernels that follow (the caller's next compress)
-// run faster when the caches do not hold y's dirty lines.  Dense decompress
+// stores per lane, slows it by 10-40%), with store_stream: y is not read
+// again here, and the kernels that follow (the caller's next compress) run
+// faster when the caches do not hold y's dirty lines.  Dense decompress
 // and accumulate-many (tstart set): the tile starts and literal flags of
 // every payload are reset.
 // Always: the look-back flags, and the list of stream chunks: unit u has
