@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "tlco_quartic_unpack_planes": (ctypes.c_int, [P, U64, P]),
             "tlco_compress_planes": (ctypes.c_int, [P, P, U64, F, P, U64, P, P]),
             "tlco_decompress_planes": (ctypes.c_int, [P, U64, F, U64, F, P]),
+            "tlco_wire_pack": (ctypes.c_int, [P, P, P, P, ctypes.c_uint32, P, U64, P]),
+            "tlco_wire_unpack": (ctypes.c_int, [P, U64, ctypes.c_uint32, P, P, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -292,3 +294,43 @@ def decompress_planes(stream, M, n: int, s: float) -> np.ndarray:
     y = np.empty(n, dtype=np.float32)
     _check(lib().tlco_decompress_planes(_ptr(stream), stream.size, float(M), n, s, _ptr(y)), "decompress_planes")
     return y
+
+
+# Wire message of a group (what one worker would send): count headers of
+# 8 bytes (L_t as little-endian uint32, M_t as little-endian fp32), then the
+# streams back to back.  A layout of this library, not of the pages.
+
+def wire_pack(streams, Ms) -> np.ndarray:
+    """The wire message of tensors whose streams and scales are given."""
+    count = len(streams)
+    lens = np.array([np.asarray(st).size for st in streams], dtype=np.uint64)
+    offs = np.zeros(count, dtype=np.uint64)
+    if count > 1:
+        offs[1:] = np.cumsum(lens)[:-1]
+    flat = np.concatenate([np.asarray(st, dtype=np.uint8) for st in streams] + [np.zeros(1, np.uint8)])
+    M = np.ascontiguousarray(Ms, dtype=np.float32)
+    cap = 8 * count + int(lens.sum())
+    wire = np.zeros(max(cap, 1), dtype=np.uint8)
+    wl = ctypes.c_uint64(0)
+    _check(lib().tlco_wire_pack(_ptr(flat), _ptr(offs), _ptr(lens), _ptr(M), count, _ptr(wire), cap,
+                                ctypes.byref(wl)), "wire_pack")
+    return wire[:wl.value]
+
+
+def wire_unpack(wire, sizes):
+    """(streams, Ms) of a wire message for tensors of the given sizes; raises
+    OracleError(ERR_CORRUPT) on a malformed message."""
+    count = len(sizes)
+    caps = np.array([quartic_len(int(n)) for n in sizes], dtype=np.uint64)
+    offs = np.zeros(count, dtype=np.uint64)
+    if count > 1:
+        offs[1:] = np.cumsum(caps)[:-1]
+    out = np.zeros(int(caps.sum()) + 1, dtype=np.uint8)
+    lens = np.zeros(count, dtype=np.uint64)
+    M = np.zeros(count, dtype=np.float32)
+    w = np.ascontiguousarray(wire, dtype=np.uint8)
+    w1 = w if w.size else np.zeros(1, np.uint8)
+    _check(lib().tlco_wire_unpack(_ptr(w1), w.size, count, _ptr(caps), _ptr(out), _ptr(offs), _ptr(lens), _ptr(M)),
+           "wire_unpack")
+    streams = [out[int(o):int(o) + int(l)].copy() for o, l in zip(offs, lens)]
+    return streams, M

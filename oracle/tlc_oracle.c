@@ -359,3 +359,59 @@ int tlco_decompress_planes(const uint8_t* in, uint64_t L, float M, uint64_t n, f
     free(bytes);
     return rc;
 }
+
+/* Wire message: count 8-byte headers (L_t, M_t; little-endian), then the
+ * streams in tensor order.  Bytes are written one at a time, so the layout
+ * does not depend on the host's byte order. */
+static void put_u32le(uint8_t* p, uint32_t v)
+{
+    for (unsigned k = 0; k < 4; ++k) p[k] = (uint8_t)(v >> (8u * k));
+}
+
+static uint32_t get_u32le(const uint8_t* p)
+{
+    uint32_t v = 0;
+    for (unsigned k = 0; k < 4; ++k) v |= (uint32_t)p[k] << (8u * k);
+    return v;
+}
+
+int tlco_wire_pack(const uint8_t* in, const uint64_t* offs, const uint64_t* lens, const float* M, uint32_t count,
+                   uint8_t* wire, uint64_t cap, uint64_t* wire_len)
+{
+    if (!in || !offs || !lens || !M || !wire || !wire_len || count == 0) return TLCO_ERR_INVALID_ARG;
+    uint64_t total = 8u * (uint64_t)count;
+    for (uint32_t t = 0; t < count; ++t) {
+        if (lens[t] > 0xFFFFFFFFu) return TLCO_ERR_INVALID_ARG;
+        total += lens[t];
+    }
+    if (total > cap) return TLCO_ERR_CAPACITY;
+    uint64_t pos = 8u * (uint64_t)count;
+    for (uint32_t t = 0; t < count; ++t) {
+        uint32_t mbits;
+        memcpy(&mbits, &M[t], 4);
+        put_u32le(wire + 8u * (uint64_t)t, (uint32_t)lens[t]);
+        put_u32le(wire + 8u * (uint64_t)t + 4u, mbits);
+        for (uint64_t i = 0; i < lens[t]; ++i) wire[pos + i] = in[offs[t] + i];
+        pos += lens[t];
+    }
+    *wire_len = total;
+    return TLCO_OK;
+}
+
+int tlco_wire_unpack(const uint8_t* wire, uint64_t wire_bytes, uint32_t count, const uint64_t* caps,
+                     uint8_t* out, const uint64_t* offs, uint64_t* lens, float* M)
+{
+    if (!wire || !caps || !out || !offs || !lens || !M || count == 0) return TLCO_ERR_INVALID_ARG;
+    uint64_t pos = 8u * (uint64_t)count;
+    if (pos > wire_bytes) return TLCO_ERR_CORRUPT;
+    for (uint32_t t = 0; t < count; ++t) {
+        uint64_t L = get_u32le(wire + 8u * (uint64_t)t);
+        uint32_t mbits = get_u32le(wire + 8u * (uint64_t)t + 4u);
+        if (L > caps[t] || L > wire_bytes - pos) return TLCO_ERR_CORRUPT;
+        memcpy(&M[t], &mbits, 4);
+        lens[t] = L;
+        for (uint64_t i = 0; i < L; ++i) out[offs[t] + i] = wire[pos + i];
+        pos += L;
+    }
+    return TLCO_OK;
+}

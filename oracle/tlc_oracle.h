@@ -124,6 +124,27 @@ int tlco_compress_planes(const float* x, float* err, uint64_t n, float s,
                          uint8_t* out, uint64_t cap, uint64_t* L, float* M);
 int tlco_decompress_planes(const uint8_t* in, uint64_t L, float M, uint64_t n, float s, float* y);
 
+/* Wire message of a group of `count` tensors, what one worker would send in
+ * the exchange (the 3LC page, "Proposed method": a compressed state change is
+ * its scale M and its byte stream; how a group's are laid out for the wire is
+ * not on the page, so this layout is a reading of this library, parity
+ * unpinned by the page and pinned by the worked example in tests/golden):
+ *   count headers of 8 bytes: header t = L_t as a little-endian uint32
+ *   (stream bytes of tensor t), then the bits of M_t as a little-endian fp32;
+ *   then the streams of tensors 0 .. count-1 back to back, no padding.
+ * Total length 8 * count + sum_t L_t.
+ * tlco_wire_pack: tensor t's stream is in[offs[t] .. offs[t] + lens[t]);
+ *   lens[t] must be below 2^32; TLCO_ERR_CAPACITY if cap is too small.
+ * tlco_wire_unpack: reads wire[0 .. wire_bytes) and writes tensor t's stream
+ *   to out[offs[t] ..], lens[t] and M[t]; a length above caps[t] (the most
+ *   bytes a stream of that tensor can hold) or a message shorter than its
+ *   headers and streams is TLCO_ERR_CORRUPT.  Bytes after the streams are
+ *   ignored. */
+int tlco_wire_pack(const uint8_t* in, const uint64_t* offs, const uint64_t* lens, const float* M, uint32_t count,
+                   uint8_t* wire, uint64_t cap, uint64_t* wire_len);
+int tlco_wire_unpack(const uint8_t* wire, uint64_t wire_bytes, uint32_t count, const uint64_t* caps,
+                     uint8_t* out, const uint64_t* offs, uint64_t* lens, float* M);
+
 #ifdef __cplusplus
 }
 #endif
