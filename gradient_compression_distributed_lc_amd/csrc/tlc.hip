@@ -2482,6 +2482,211 @@ __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ sr
 }
 
 // ---------------------------------------------------------------------------
+// wire message of a group: what one worker sends in the exchange
+//
+// count headers of 8 bytes (header t: L_t as a little-endian uint32, then the
+// bits of M_t), then the streams of tensors 0 .. count-1 back to back.  The
+// 3LC page ("Proposed method") says what a compressed state change consists
+// of, its scale and its byte stream; how a group's travel is this library's
+// layout.  A grouped stream keeps each tensor's bytes at the start of a slot
+// of ceil(n/5) bytes, so sending the message moves sum L_t + 8 count bytes
+// instead of the slots' capacity.
+
+constexpr uint32_t kWireChunk = 4096;  // stream bytes one block copies at a time (16 per lane)
+constexpr uint32_t kWirePer = 16;      // tensors per thread and round of k_wire_scan
+
+// One block over all tensors, kThreads * kWirePer per round: each stream's
+// length (pack: from in_lens; unpack: from its header), checked against its
+// slot (a longer one is TLC_ERR_CORRUPT and counts as empty); the headers
+// (pack) or out_lens and scales (unpack); the exclusive prefix of the lengths
+// (woff[t]: where stream t starts in the message body; woff[count]: their
+// sum) and of their 4 KiB chunks (cfirst[t]); ctrl[0] = chunks; the message
+// length (pack).  Unpack: a message shorter than its headers and streams is
+// TLC_ERR_CORRUPT, and then no chunk is copied.
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, const uint64_t* __restrict__ lens_in,
+                                                        const float* __restrict__ m_in, uint8_t* __restrict__ hdr_out,
+                                                        const uint8_t* __restrict__ hdr_in, uint64_t wire_bytes,
+                                                        uint64_t* __restrict__ lens_out, float* __restrict__ m_out,
+                                                        uint64_t* __restrict__ woff, uint32_t* __restrict__ cfirst,
+                                                        uint32_t* __restrict__ ctrl, uint64_t* __restrict__ wire_len,
+                                                        int* __restrict__ status) {
+    __shared__ uint64_t s_sm[kWaves];
+    __shared__ uint32_t s_u[kWaves];
+    const uint32_t count = g.count;
+    uint64_t carry_b = 0;  // bytes of the rounds before
+    uint32_t carry_c = 0;  // chunks of the rounds before
+    bool bad = false;
+    for (uint32_t r0 = 0; r0 < count; r0 += kThreads * kWirePer) {
+        const uint32_t t0 = r0 + threadIdx.x * kWirePer;
+        uint32_t L[kWirePer];
+        uint64_t my_b = 0;
+        uint32_t my_c = 0;
+#pragma unroll
+        for (int k = 0; k < (int)kWirePer; ++k) {
+            const uint32_t t = t0 + (uint32_t)k;
+            L[k] = 0;
+            if (t < count) {
+                const uint64_t cap = quartic_len(load_seg(g, t).n);
+                uint64_t l;
+                uint32_t mb;
+                if (kPack) {
+                    l = lens_in[t];
+                    mb = __float_as_uint(m_in[t]);
+                } else {
+                    const uint32_t* const h = reinterpret_cast<const uint32_t*>(hdr_in) + 2ull * t;
+                    l = h[0];
+                    mb = h[1];
+                }
+                if (l > cap) {
+                    bad = true;
+                    l = 0;
+                }
+                if (kPack) {
+                    uint32_t* const h = reinterpret_cast<uint32_t*>(hdr_out) + 2ull * t;
+                    h[0] = (uint32_t)l;
+                    h[1] = mb;
+                } else {
+                    lens_out[t] = l;
+                    m_out[t] = __uint_as_float(mb);
+                }
+                L[k] = (uint32_t)l;
+                my_b += l;
+                my_c += (uint32_t)((l + kWireChunk - 1) / kWireChunk);
+            }
+        }
+        uint64_t tot_b;
+        uint32_t tot_c;
+        uint64_t b = carry_b + block_excl_scan(my_b, 0ull, SumCompose(), s_sm, &tot_b);
+        uint32_t c = carry_c + block_excl_sum(my_c, s_u, &tot_c);
+#pragma unroll
+        for (int k = 0; k < (int)kWirePer; ++k) {
+            const uint32_t t = t0 + (uint32_t)k;
+            if (t < count) {
+                woff[t] = b;
+                cfirst[t] = c;
+                b += L[k];
+                c += (uint32_t)((L[k] + kWireChunk - 1) / kWireChunk);
+            }
+        }
+        carry_b += tot_b;
+        carry_c += tot_c;
+    }
+    if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
+    if (threadIdx.x == 0) {
+        woff[count] = carry_b;
+        const uint64_t total = 8ull * count + carry_b;
+        const bool fits = kPack || total <= wire_bytes;
+        if (!fits) raise_status(status, TLC_ERR_CORRUPT);
+        ctrl[0] = fits ? carry_c : 0u;
+        if (kPack) *wire_len = total;
+    }
+}
+
+// 16 bytes of the LDS buffer from byte `off` (0 <= off, off + 16 <= its size)
+__device__ __forceinline__ uint4 lds_bytes16(const uint32_t* buf, uint32_t off) {
+    const uint32_t w = off >> 2, sh = 8u * (off & 3u);
+    uint32_t d[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) d[k] = buf[w + k];
+    auto cut = [&](uint32_t lo, uint32_t hi) { return sh ? (lo >> sh) | (hi << (32u - sh)) : lo; };
+    return make_uint4(cut(d[0], d[1]), cut(d[1], d[2]), cut(d[2], d[3]), cut(d[3], d[4]));
+}
+
+// Copies every stream's bytes between its slot and the message body, one
+// 4 KiB chunk of one stream per block and round (the chunk's tensor by a
+// binary search over cfirst).  The chunk goes through LDS so that the side
+// the chunk is not 16-byte aligned on is read or written in whole aligned
+// words: pack reads its slot (aligned) and writes the body, where a word that
+// the chunk shares with a neighbour is written byte by byte; unpack reads the
+// body with whole words only inside [0, wire_bytes), byte by byte past that,
+// and writes its slot (aligned; the bytes after the stream in its last word
+// are written as 0, still inside the slot).
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void k_wire_copy(GroupView g, const uint8_t* __restrict__ src,
+                                                        uint8_t* __restrict__ dst, uint64_t body, uint64_t wire_bytes,
+                                                        const uint64_t* __restrict__ woff,
+                                                        const uint32_t* __restrict__ cfirst,
+                                                        const uint32_t* __restrict__ ctrl) {
+    __shared__ __align__(16) uint32_t s_buf[(kWireChunk + 32) / 4 + 8];
+    __shared__ uint32_t s_t;
+    const uint32_t nchunks = ctrl[0];
+    const uint32_t count = g.count;
+    const uint32_t i = threadIdx.x;
+    for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (i == 0) {  // the last tensor whose first chunk is <= c
+            uint32_t lo = 0, hi = count;
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (cfirst[mid] <= c) lo = mid;
+                else hi = mid;
+            }
+            s_t = lo;
+        }
+        __syncthreads();
+        const uint32_t t = s_t;
+        const Seg sg = load_seg(g, t);
+        const uint64_t k0 = (uint64_t)(c - cfirst[t]) * kWireChunk;  // first byte of the chunk in stream t
+        const uint64_t L = woff[t + 1] - woff[t];
+        const uint32_t len = (uint32_t)min<uint64_t>(kWireChunk, L - k0);
+        const uint64_t slot = sg.stream_off + k0;   // aligned
+        const uint64_t msg = body + woff[t] + k0;   // any alignment
+        if (kPack) {
+            // slot words straight into LDS: data byte m at buffer byte m
+            if (16u * i < len) reinterpret_cast<uint4*>(s_buf)[i] = reinterpret_cast<const uint4*>(src + slot)[i];
+            __syncthreads();
+            const uint32_t mis = (uint32_t)(msg & 15u);
+            const uint64_t a0 = msg - mis;  // aligned word j covers data bytes 16 j - mis .. + 15
+            const uint32_t nw = (mis + len + 15) / 16;  // up to 257
+            for (uint32_t wi = i; wi < nw; wi += kThreads) {
+                const int32_t m0 = 16 * (int32_t)wi - (int32_t)mis;
+                if (m0 >= 0 && m0 + 16 <= (int32_t)len) {
+                    *reinterpret_cast<uint4*>(dst + a0 + 16ull * wi) = lds_bytes16(s_buf, (uint32_t)m0);
+                } else {
+                    const uint8_t* const b8 = reinterpret_cast<const uint8_t*>(s_buf);
+                    for (int32_t j = 0; j < 16; ++j) {
+                        const int32_t m = m0 + j;
+                        if (m >= 0 && m < (int32_t)len) dst[a0 + 16ull * wi + (uint32_t)j] = b8[m];
+                    }
+                }
+            }
+        } else {
+            // body words into LDS: data byte m at buffer byte smis + m
+            const uint32_t smis = (uint32_t)(msg & 15u);
+            const uint64_t a0 = msg - smis;
+            const uint32_t nw = (smis + len + 15) / 16;  // up to 257
+            for (uint32_t wi = i; wi < nw; wi += kThreads) {
+                const uint64_t w = a0 + 16ull * wi;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (w + 16 <= wire_bytes) {
+                    v = *reinterpret_cast<const uint4*>(src + w);
+                } else {
+                    uint32_t d[4] = {0u, 0u, 0u, 0u};
+                    for (uint32_t j = 0; j < 16; ++j)
+                        if (w + j < wire_bytes) d[j >> 2] |= (uint32_t)src[w + j] << (8u * (j & 3u));
+                    v = make_uint4(d[0], d[1], d[2], d[3]);
+                }
+                reinterpret_cast<uint4*>(s_buf)[wi] = v;
+            }
+            __syncthreads();
+            if (16u * i < len) {
+                uint4 v = lds_bytes16(s_buf, smis + 16u * i);
+                const uint32_t keep = min(16u, len - 16u * i);  // data bytes of this word
+                if (keep < 16u) {
+                    uint32_t* const d = reinterpret_cast<uint32_t*>(&v);
+                    for (uint32_t j = 0; j < 4; ++j) {
+                        const uint32_t b = keep > 4 * j ? min(4u, keep - 4 * j) : 0u;
+                        d[j] &= b >= 4 ? ~0u : ((1u << (8 * b)) - 1u);
+                    }
+                }
+                *reinterpret_cast<uint4*>(dst + slot + 16ull * i) = v;
+            }
+        }
+        __syncthreads();  // s_buf and s_t are rewritten by the next chunk
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 struct ProfRec {
@@ -2520,7 +2725,9 @@ int launch(const char* name, hipStream_t st, Launch&& fn) {
 // device.  Such kernels hand work to their blocks or waves round-robin, so a
 // grid larger than this leaves a second, partial round of blocks running
 // alone at the end.
-enum GridKind { kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridDecodeWide, kGridApply, kGridKinds };
+enum GridKind {
+    kGridPack, kGridDecodeWrite, kGridDecodeAdd, kGridDecodeRecord, kGridDecodeWide, kGridApply, kGridWirePack, kGridWireUnpack, kGridKinds
+};
 uint32_t resident_grid(GridKind kind, const void* kern, uint32_t cap, int threads = kThreads) {
     static std::mutex mu;
     static std::vector<uint32_t> per_dev;  // kGridKinds entries per device, 0 = not queried
@@ -2984,6 +3191,69 @@ int run_planes(bool gather, const float* src, const uint64_t* src_off, float* ds
 // ---------------------------------------------------------------------------
 // C ABI
 
+// Workspace of the wire pack and unpack: each stream's place in the body
+// (count + 1), its first chunk, the chunk count.
+struct WireLayout {
+    size_t woff, cfirst, ctrl, total;
+};
+WireLayout wire_layout(uint64_t count) {
+    WireLayout l;
+    l.woff = 0;
+    l.cfirst = align_up(8 * (count + 1), 256);
+    l.ctrl = l.cfirst + align_up(4 * count, 256);
+    l.total = l.ctrl + 256;
+    return l;
+}
+
+int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint8_t* slots_in, const uint64_t* lens_in, const float* m_in,
+             uint8_t* wire, uint64_t wire_bytes, uint64_t* wire_len, const uint8_t* wire_in, uint8_t* slots_out,
+             uint64_t* lens_out, float* m_out, void* ws, size_t ws_bytes, int* status, hipStream_t st) {
+    const uint64_t count = p.d.count;
+    if (!status) return TLC_ERR_INVALID_ARG;
+    if (pack) {
+        if (!slots_in || !lens_in || !m_in || !wire || !wire_len || !aligned16(slots_in) || !aligned16(wire))
+            return TLC_ERR_INVALID_ARG;
+        if (wire_bytes < 8 * count + stream_bytes) return TLC_ERR_CAPACITY;
+    } else {
+        if (!wire_in || !slots_out || !lens_out || !m_out || !aligned16(wire_in) || !aligned16(slots_out))
+            return TLC_ERR_INVALID_ARG;
+        if (wire_bytes < 8 * count) return TLC_ERR_CAPACITY;
+    }
+    const WireLayout l = wire_layout(count);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < l.total) return TLC_ERR_WORKSPACE;
+    char* const w = static_cast<char*>(ws);
+    uint64_t* const woff = reinterpret_cast<uint64_t*>(w + l.woff);
+    uint32_t* const cfirst = reinterpret_cast<uint32_t*>(w + l.cfirst);
+    uint32_t* const ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
+    const GroupView g = p.g;
+    int rc = launch("tlc_status_ok", st, [&] { k_status_ok<<<1, 1, 0, st>>>(status); });
+    if (rc) return rc;
+    const uint64_t chunk_bound = stream_bytes / kWireChunk + count;
+    if (pack) {
+        rc = launch("tlc_wire_scan", st, [&] {
+            k_wire_scan<true><<<1, kThreads, 0, st>>>(g, lens_in, m_in, wire, nullptr, 0, nullptr, nullptr, woff,
+                                                      cfirst, ctrl, wire_len, status);
+        });
+        if (rc) return rc;
+        const uint32_t grid = (uint32_t)std::min<uint64_t>(
+            chunk_bound, resident_grid(kGridWirePack, reinterpret_cast<const void*>(k_wire_copy<true>), 1u << 16));
+        return launch("tlc_wire_pack", st, [&] {
+            k_wire_copy<true><<<grid, kThreads, 0, st>>>(g, slots_in, wire, 8 * count, wire_bytes, woff, cfirst, ctrl);
+        });
+    }
+    rc = launch("tlc_wire_scan", st, [&] {
+        k_wire_scan<false><<<1, kThreads, 0, st>>>(g, nullptr, nullptr, nullptr, wire_in, wire_bytes, lens_out, m_out,
+                                                   woff, cfirst, ctrl, nullptr, status);
+    });
+    if (rc) return rc;
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(
+        chunk_bound, resident_grid(kGridWireUnpack, reinterpret_cast<const void*>(k_wire_copy<false>), 1u << 16));
+    return launch("tlc_wire_unpack", st, [&] {
+        k_wire_copy<false><<<grid, kThreads, 0, st>>>(g, wire_in, slots_out, 8 * count, wire_bytes, woff, cfirst,
+                                                      ctrl);
+    });
+}
+
 extern "C" {
 
 const char* tlc_status_string(int code) {
@@ -3223,6 +3493,36 @@ int tlc_decompress_accumulate_group(const tlc_group_info* info, const void* d_ta
     if (rc) return rc;
     return run_decompress(p, in, in_lens, scales, s, acc, workspace, workspace_bytes, status, nullptr, nullptr,
                           static_cast<hipStream_t>(stream), 1);
+}
+
+uint64_t tlc_wire_bound(const tlc_group_info* info) {
+    if (!info || info->count == 0) return 0;
+    return 8 * info->count + info->stream_bytes;
+}
+
+uint64_t tlc_wire_workspace_size(const tlc_group_info* info) {
+    if (!info || info->count == 0) return 0;
+    return wire_layout(info->count).total;
+}
+
+int tlc_wire_pack_group(const tlc_group_info* info, const void* d_table, const uint8_t* in, const uint64_t* in_lens,
+                        const float* scales, uint8_t* wire, uint64_t wire_capacity, uint64_t* wire_len,
+                        void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream) {
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_wire(true, p, info->stream_bytes, in, in_lens, scales, wire, wire_capacity, wire_len, nullptr, nullptr, nullptr, nullptr,
+                    workspace, workspace_bytes, status, static_cast<hipStream_t>(stream));
+}
+
+int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const uint8_t* wire, uint64_t wire_bytes,
+                          uint8_t* out, uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
+                          int* status, tlc_stream_t stream) {
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    return run_wire(false, p, info->stream_bytes, nullptr, nullptr, nullptr, nullptr, wire_bytes, nullptr, wire, out, out_lens, scales,
+                    workspace, workspace_bytes, status, static_cast<hipStream_t>(stream));
 }
 
 uint64_t tlc_accumulate_many_workspace_size(const tlc_group_info* info, uint32_t payloads) {

@@ -78,6 +78,10 @@ _SIGS = {
     "tlc_accumulate_many_workspace_size": (_U64, [ctypes.POINTER(GroupInfo), _U32]),
     "tlc_decompress_accumulate_many_group": (_I, [ctypes.POINTER(GroupInfo), _P, _U32, _P, _U64, _P, _P, _F, _P,
                                                   _P, _SZ, _P, _P, _P]),
+    "tlc_wire_bound": (_U64, [ctypes.POINTER(GroupInfo)]),
+    "tlc_wire_workspace_size": (_U64, [ctypes.POINTER(GroupInfo)]),
+    "tlc_wire_pack_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
+    "tlc_wire_unpack_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_gather_probe": (_I, [_P, _P, _U64, _P, _P]),
@@ -548,6 +552,63 @@ class Group:
             _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_decompress_accumulate_group")
         return acc, status
+
+    def wire_bound(self) -> int:
+        """Most bytes a wire message of this group can need."""
+        return int(lib().tlc_wire_bound(ctypes.byref(self.info)))
+
+    def wire_workspace(self) -> torch.Tensor:
+        nb = int(lib().tlc_wire_workspace_size(ctypes.byref(self.info)))
+        return torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+
+    def wire_pack(self, inp, in_lens, scales, *, wire=None, wire_len=None, workspace=None, status=None,
+                  stream=None):
+        """tlc_wire_pack_group: the payload (inp, in_lens, scales) as one
+        contiguous message.  Returns (wire, wire_len, status); the message is
+        wire[:wire_len]."""
+        dev = self.device
+        wire = wire if wire is not None else torch.empty(self.wire_bound(), dtype=torch.uint8, device=dev)
+        wire_len = wire_len if wire_len is not None else torch.empty(1, dtype=torch.int64, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        _need(inp, self.stream_bytes, "in")
+        _need(in_lens, self.count, "in_lens")
+        _need(scales, self.count, "scales")
+        _need(wire, self.wire_bound(), "wire")
+        _need(wire_len, 1, "wire_len")
+        _need(status, 1, "status")
+        workspace = workspace if workspace is not None else self.wire_workspace()
+        rc = lib().tlc_wire_pack_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                       _ptr(inp, torch.uint8, "in"), _ptr(in_lens, torch.int64, "in_lens"),
+                                       _ptr(scales, torch.float32, "scales"), _ptr(wire, torch.uint8, "wire"),
+                                       wire.numel(), _ptr(wire_len, torch.int64, "wire_len"),
+                                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                       _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_wire_pack_group")
+        return wire, wire_len, status
+
+    def wire_unpack(self, wire, *, wire_bytes=None, out=None, out_lens=None, scales=None, workspace=None,
+                    status=None, stream=None):
+        """tlc_wire_unpack_group: a message back into a payload.  wire_bytes:
+        how many bytes of `wire` may be read (default all of it).  Returns
+        (out, out_lens, scales, status)."""
+        dev = self.device
+        out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
+        out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
+        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        nb = wire.numel() if wire_bytes is None else int(wire_bytes)
+        if nb > wire.numel():
+            raise ValueError("wire_bytes exceeds the wire tensor")
+        self._need_out(out, out_lens, scales, status)
+        workspace = workspace if workspace is not None else self.wire_workspace()
+        rc = lib().tlc_wire_unpack_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                         _ptr(wire, torch.uint8, "wire"), nb, _ptr(out, torch.uint8, "out"),
+                                         _ptr(out_lens, torch.int64, "out_lens"),
+                                         _ptr(scales, torch.float32, "scales"),
+                                         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                         _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_wire_unpack_group")
+        return out, out_lens, scales, status
 
     def accumulate_many_workspace_size(self, payloads: int) -> int:
         nb = int(lib().tlc_accumulate_many_workspace_size(ctypes.byref(self.info), int(payloads)))

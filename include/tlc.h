@@ -315,6 +315,49 @@ int tlc_decompress_accumulate_many_group(const tlc_group_info* info, const void*
                                          void* workspace, size_t workspace_bytes, int* status,
                                          uint32_t* path_hint, tlc_stream_t stream);
 
+/* ---- wire message of a group (the exchange between workers) -----------------
+ * The 3LC page ("Proposed method", first three items) has each worker send
+ * its compressed state changes: per tensor, the scale M and the zero-run
+ * encoded byte stream.  A grouped stream keeps tensor t's L_t bytes at the
+ * start of a slot of ceil(n_t/5) bytes, so the slots hold mostly unused
+ * capacity; these calls turn a group's payload into one contiguous message of
+ * the bytes alone, and back, on the device (no host synchronisation: the
+ * lengths stay in device memory).  The layout is this library's, the page
+ * gives none:
+ *   count headers of 8 bytes, header t = L_t as a little-endian uint32, then
+ *   the bits of M_t as a little-endian fp32; then the streams of tensors
+ *   0 .. count-1 back to back, no padding.  Length 8*count + sum_t L_t.
+ * tlc_wire_bound: the most bytes a message of the group can need,
+ *   8*count + info->stream_bytes (0 for a null or empty info).
+ * tlc_wire_workspace_size: workspace bytes either call needs (256-byte aligned
+ *   device memory; contents need not survive between calls).
+ * tlc_wire_pack_group: in, in_lens, scales as tlc_compress_group wrote them
+ *   (in 16-byte aligned, info->stream_bytes long); writes the message to wire
+ *   (16-byte aligned, wire_capacity >= tlc_wire_bound bytes) and its length
+ *   to *wire_len (device uint64).  A length above its tensor's ceil(n/5) sets
+ *   TLC_ERR_CORRUPT in *status and that stream is sent empty.
+ * tlc_wire_unpack_group: reads wire[0 .. wire_bytes) (16-byte aligned; the
+ *   message may be followed by other bytes) and writes each stream to its
+ *   slot in out (16-byte aligned, info->stream_bytes long; the bytes after a
+ *   stream in its last 16-byte word are written as 0), its length to
+ *   out_lens and its M to scales, so that out/out_lens/scales decompress as
+ *   the sender's payload did.  A header length above its tensor's ceil(n/5)
+ *   (that stream is taken as empty), or a message longer than wire_bytes (no
+ *   stream is copied) sets TLC_ERR_CORRUPT in *status.
+ * Asynchronous on `stream`; no allocation.  Synchronous returns:
+ * TLC_ERR_INVALID_ARG for a null or misaligned pointer or an inconsistent
+ * info/table pair, TLC_ERR_CAPACITY for wire_capacity below the bound (pack)
+ * or wire_bytes below 8*count (unpack), TLC_ERR_WORKSPACE for a missing,
+ * misaligned or small workspace, TLC_ERR_HIP for a failed launch. */
+uint64_t tlc_wire_bound(const tlc_group_info* info);
+uint64_t tlc_wire_workspace_size(const tlc_group_info* info);
+int tlc_wire_pack_group(const tlc_group_info* info, const void* d_table, const uint8_t* in, const uint64_t* in_lens,
+                        const float* scales, uint8_t* wire, uint64_t wire_capacity, uint64_t* wire_len,
+                        void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const uint8_t* wire, uint64_t wire_bytes,
+                          uint8_t* out, uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
+                          int* status, tlc_stream_t stream);
+
 /* ---- five-plane byte layout (ablation) --------------------------------------
  * The 3LC page ("Proposed method", second item) packs five ternary values per
  * byte without saying which five.  The codec above takes five consecutive

@@ -345,6 +345,40 @@ def test_binding_rejects_undersized_group_buffers():
         g.decompress_fixed(_t(total_q, u8), _t(C, i64), _t(C, f32), 1.5, tlc.ENC_QUARTIC, y=_t(N - 1, f32))
 
 
+def test_wire_host_checks():
+    # bound, workspace size and argument errors of the wire pack and unpack,
+    # all decided before any launch
+    L = tlc.lib()
+    V = ctypes.c_void_p
+    fake = V(0x10000)
+    odd = V(0x10008)
+    ws = V(0x20000)
+    info, _, offsets = tlc.group_plan([100, 7, 5121])
+    bound = 8 * 3 + info.stream_bytes
+    assert L.tlc_wire_bound(ctypes.byref(info)) == bound
+    assert L.tlc_wire_bound(None) == 0
+    wsz = L.tlc_wire_workspace_size(ctypes.byref(info))
+    assert wsz > 0 and wsz % 256 == 0 and L.tlc_wire_workspace_size(None) == 0
+    bi = ctypes.byref(info)
+    ok_pack = lambda *a: L.tlc_wire_pack_group(bi, fake, *a)
+    assert ok_pack(fake, fake, fake, fake, bound - 1, fake, ws, wsz, fake, None) == tlc.ERR_CAPACITY
+    assert ok_pack(None, fake, fake, fake, bound, fake, ws, wsz, fake, None) == tlc.ERR_INVALID_ARG
+    assert ok_pack(fake, fake, fake, odd, bound, fake, ws, wsz, fake, None) == tlc.ERR_INVALID_ARG
+    assert ok_pack(fake, fake, fake, fake, bound, None, ws, wsz, fake, None) == tlc.ERR_INVALID_ARG
+    assert ok_pack(fake, fake, fake, fake, bound, fake, ws, wsz, None, None) == tlc.ERR_INVALID_ARG
+    assert ok_pack(fake, fake, fake, fake, bound, fake, ws, wsz - 1, fake, None) == tlc.ERR_WORKSPACE
+    assert ok_pack(fake, fake, fake, fake, bound, fake, V(0x20010), wsz, fake, None) == tlc.ERR_WORKSPACE
+    ok_unpack = lambda *a: L.tlc_wire_unpack_group(bi, fake, *a)
+    assert ok_unpack(fake, 23, fake, fake, fake, ws, wsz, fake, None) == tlc.ERR_CAPACITY  # below 8 * count
+    assert ok_unpack(odd, 24, fake, fake, fake, ws, wsz, fake, None) == tlc.ERR_INVALID_ARG
+    assert ok_unpack(fake, 24, None, fake, fake, ws, wsz, fake, None) == tlc.ERR_INVALID_ARG
+    assert ok_unpack(fake, 24, fake, fake, fake, None, wsz, fake, None) == tlc.ERR_WORKSPACE
+    bad = tlc.GroupInfo.from_buffer_copy(info)
+    bad.table_bytes += 16
+    assert L.tlc_wire_pack_group(ctypes.byref(bad), fake, fake, fake, fake, fake, bound, fake, ws, wsz, fake,
+                                 None) == tlc.ERR_INVALID_ARG
+
+
 def test_path_hint_word_is_checked_on_the_host():
     """The decompress and many-payload accumulate take the caller's hint word
     only as one pinned int32 on the host; anything else is refused before the

@@ -1,0 +1,157 @@
+"""GPU parity of the wire message (tlc_wire_pack_group / tlc_wire_unpack_group):
+the message packed from a group's payload must equal, byte for byte, the
+oracle's wire message of the oracle's streams and scales; unpacking it into
+fresh buffers must give back every stream, length and M, so that it
+decompresses to the oracle's values; malformed lengths and short messages
+set TLC_ERR_CORRUPT without reading or writing outside the buffers."""
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import bits, oracle_group_compress, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def group_payload(sizes, seed, s=1.5, dense_every=3):
+    """A group compressed on the GPU with the oracle's results beside it."""
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(seed)
+    g = tlc.Group(sizes)
+    x = (rng.standard_normal(g.total) * 1e-3).astype(np.float32)
+    err = np.zeros(g.total, np.float32)
+    off = 0
+    for t, n in enumerate(sizes):  # some tensors with many nonzero codes, long streams
+        if t % dense_every == 0:
+            err[off:off + n] = (rng.uniform(-1, 1, n) * 3e-3).astype(np.float32)
+        off += n
+    streams, Ms, _ = oracle_group_compress(x, err, sizes, s)
+    out, lens, scales, st = g.compress(to_dev(x), to_dev(err), s)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return g, out, lens, scales, streams, Ms, s
+
+
+def check_round_trip(g, out, lens, scales, streams, Ms, s, label, trailing=0):
+    import torch
+    sizes = g.sizes
+    want = oracle.wire_pack(streams, Ms)
+    wire, wire_len, st = g.wire_pack(out, lens, scales)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, label
+    wl = int(wire_len.item())
+    assert wl == want.size == 8 * len(sizes) + sum(x.size for x in streams), (label, wl, want.size)
+    got = wire[:wl].cpu().numpy()
+    if not np.array_equal(got, want):
+        i = int(np.flatnonzero(got != want)[0])
+        raise AssertionError(f"{label}: message differs first at byte {i} of {wl}")
+    # unpack from a buffer holding the message and `trailing` other bytes
+    buf = torch.full((wl + trailing,), 0xA5, dtype=torch.uint8, device=wire.device)
+    buf[:wl] = wire[:wl]
+    o2, l2, s2, st2 = g.wire_unpack(buf, out=torch.full_like(out, 0x5A))
+    torch.cuda.synchronize()
+    assert int(st2.item()) == 0, label
+    assert np.array_equal(l2.cpu().numpy(), np.array([x.size for x in streams])), label
+    assert np.array_equal(bits(s2.cpu().numpy()), bits(Ms)), label
+    ob = o2.cpu().numpy()
+    for t, x in enumerate(streams):
+        o = g.offsets[t]
+        assert np.array_equal(ob[o:o + x.size], x), (label, t)
+        tail = (-(o + x.size)) % 16  # the rest of the stream's last 16-byte word is written as 0
+        assert not ob[o + x.size:o + x.size + tail].any(), (label, t)
+    y, st_d = g.decompress(o2, l2, s2, s)
+    torch.cuda.synchronize()
+    assert int(st_d.item()) == 0, label
+    want_y = np.concatenate([oracle.decompress(x, Ms[t], n, s) for t, (x, n) in enumerate(zip(streams, sizes))])
+    assert np.array_equal(bits(y.cpu().numpy()), bits(want_y)), label
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_groups_round_trip(seed):
+    rng = np.random.default_rng(seed)
+    sizes = [int(v) for v in rng.integers(1, 60_000, 50)] + [1, 2, 5, 6, 5120, 20_481, 100_003]
+    say(f"case wire ragged seed={seed}")
+    check_round_trip(*group_payload(sizes, seed), label=f"ragged {seed}", trailing=int(rng.integers(0, 40)))
+
+
+def test_thousands_of_tiny_tensors():
+    rng = np.random.default_rng(7)
+    sizes = [int(v) for v in rng.integers(1, 8, 3000)] + [4097, 3]
+    say("case wire tiny tensors")
+    check_round_trip(*group_payload(sizes, 7, s=1.2, dense_every=2), label="tiny")
+
+
+def test_long_streams_over_many_chunks():
+    # streams of several MB: every chunk boundary at every alignment
+    sizes = [16_777_216 + 3, 5_000_001, 17]
+    say("case wire long streams")
+    check_round_trip(*group_payload(sizes, 11, dense_every=1), label="long")
+
+
+def test_malformed_lengths_and_short_messages():
+    import torch
+    sizes = [10_000, 3, 25_000]
+    g, out, lens, scales, streams, Ms, s = group_payload(sizes, 3, dense_every=1)
+    caps = [-(-n // 5) for n in sizes]
+    # pack: a length above its tensor's capacity is corrupt and sent empty
+    bad = lens.clone()
+    bad[1] = caps[1] + 1
+    say("case wire pack with a length above its capacity")
+    wire, wl, st = g.wire_pack(out, bad, scales)
+    torch.cuda.synchronize()
+    assert int(st.item()) == oracle.ERR_CORRUPT
+    hdr = wire[:24].cpu().numpy().view("<u4")
+    assert hdr[2] == 0 and int(wl.item()) == 24 + streams[0].size + streams[2].size
+    # unpack: the good message, then cut short, then with a length above its capacity
+    wire, wl, st = g.wire_pack(out, lens, scales)
+    torch.cuda.synchronize()
+    n = int(wl.item())
+    for cut in (n - 1, 24 + streams[0].size, 24):
+        say(f"case wire unpack of {cut} of {n} bytes")
+        _, _, _, st2 = g.wire_unpack(wire, wire_bytes=cut)
+        torch.cuda.synchronize()
+        assert int(st2.item()) == oracle.ERR_CORRUPT, cut
+    w2 = wire.clone()
+    w2[8:12] = torch.tensor(list(int(caps[1] + 1).to_bytes(4, "little")), dtype=torch.uint8)
+    say("case wire unpack of a header length above its capacity")
+    _, l3, _, st3 = g.wire_unpack(w2, wire_bytes=n)
+    torch.cuda.synchronize()
+    assert int(st3.item()) == oracle.ERR_CORRUPT
+    assert int(l3[1].item()) == 0
+
+
+def test_workers_messages_into_one_sum():
+    """Eight workers' payloads packed, each message unpacked on the receiving
+    side, and all eight applied with the many-payload accumulate: the sum of
+    the oracle's decoded payloads in worker order."""
+    import torch
+    sizes = [30_000, 7, 5120, 12_345]
+    P = 8
+    msgs, want_payloads = [], []
+    for w in range(P):
+        g, out, lens, scales, streams, Ms, s = group_payload(sizes, 100 + w, dense_every=1 + w % 3)
+        wire, wl, st = g.wire_pack(out, lens, scales)
+        msgs.append((wire, int(wl.item())))
+        want_payloads.append((streams, Ms))
+    inp = torch.empty((P, g.stream_bytes), dtype=torch.uint8, device="cuda:0")
+    in_lens = torch.empty((P, len(sizes)), dtype=torch.int64, device="cuda:0")
+    in_sc = torch.empty((P, len(sizes)), dtype=torch.float32, device="cuda:0")
+    for w, (wire, wl) in enumerate(msgs):
+        _, _, _, st = g.wire_unpack(wire, wire_bytes=wl, out=inp[w], out_lens=in_lens[w], scales=in_sc[w])
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, w
+    acc0 = (np.random.default_rng(5).standard_normal(g.total) * 1e-3).astype(np.float32)
+    want = acc0.copy()
+    for streams, Ms in want_payloads:
+        off = 0
+        for t, n in enumerate(sizes):
+            oracle.decompress_accumulate(streams[t], Ms[t], n, s, want[off:off + n])
+            off += n
+    acc = to_dev(acc0)
+    say("case wire: 8 messages into one sum")
+    _, st = g.decompress_accumulate_many(inp, in_lens.view(-1), in_sc.view(-1), s, acc)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(bits(acc.cpu().numpy()), bits(want))
