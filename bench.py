@@ -281,6 +281,45 @@ def step_record(N: int, tensors: int, s: float, L: int, step_ms, comp_ms, dec_ms
     return rec
 
 
+def wire_record(torch, group, out, lens, scales, N: int, reps: int = 20):
+    """The payload as one wire message (tlc_wire_pack_group) and back
+    (tlc_wire_unpack_group): message bytes against the slots' capacity, and
+    the two calls' times.  Each moves the message once in and once out (the
+    headers included), so its roofline bytes are twice the message length."""
+    wire = torch.empty(group.wire_bound(), dtype=torch.uint8, device=out.device)
+    wire_len = torch.empty(1, dtype=torch.int64, device=out.device)
+    st_w = torch.empty(1, dtype=torch.int32, device=out.device)
+    st_u = torch.empty(1, dtype=torch.int32, device=out.device)
+    wws = group.wire_workspace()
+    out2, lens2 = torch.empty_like(out), torch.empty_like(lens)
+    sc2 = torch.empty_like(scales)
+
+    def pack():
+        group.wire_pack(out, lens, scales, wire=wire, wire_len=wire_len, workspace=wws, status=st_w)
+
+    def unpack():
+        group.wire_unpack(wire, out=out2, out_lens=lens2, scales=sc2, workspace=wws, status=st_u)
+
+    pack()
+    unpack()
+    torch.cuda.synchronize()
+    if int(st_w.item()) != 0 or int(st_u.item()) != 0:
+        raise SystemExit("device status not ok in the wire pack or unpack")
+    if not torch.equal(lens2, lens) or not torch.equal(sc2.view(torch.int32), scales.view(torch.int32)):
+        raise SystemExit("wire unpack did not give back the payload's lengths and scales")
+    wl = int(wire_len.item())
+    tp = timed(torch, reps, lambda r, mark: pack())
+    tu = timed(torch, reps, lambda r, mark: unpack())
+    sp, su = stats([v[0] for v in tp]), stats([v[0] for v in tu])
+    return {"message_bytes": wl, "slot_capacity_bytes": int(group.stream_bytes),
+            "how": "each call alone between two events, so the host's submission of its two launches is "
+                   "included; the kernel traces give the kernels' own time",
+            "bits_per_value_on_the_wire": round(8.0 * wl / N, 4),
+            "pack_ms": sp, "unpack_ms": su,
+            "pack_roofline_frac": frac(2.0 * wl, sp["median"], HBM_PEAK_GBPS),
+            "unpack_roofline_frac": frac(2.0 * wl, su["median"], HBM_PEAK_GBPS)}
+
+
 class Bench:
     """Device state shared by the records."""
 
@@ -657,7 +696,8 @@ PROFILE_PHASES = ("early", "steady", "receive", "resnet110", "calibrate")
 def profile_phase(args):
     """One phase of the workload alone, for a profiler run (rocprofv3 sees
     every kernel of the process): `early` the headline's warm-up and timed
-    steps; `steady` 150 steps, then the timed steps; `receive` the 8
+    steps, then the last payload packed into one wire message and unpacked,
+    as often; `steady` 150 steps, then the timed steps and the wire message; `receive` the 8
     BERT-large workers' payloads (150 steps each), then the many-payload call
     on each launch sequence and the single-payload accumulates, for the
     steady-state and for the first-step payloads; `resnet110` one-step repetitions of the ResNet-110 group;
@@ -691,7 +731,7 @@ def profile_phase(args):
         hint = tlc.path_hint()
         k = 0
         before = args.warmup if args.profile == "early" else args.steady_steps
-        out["parts"] = ["timed steps"]
+        out["parts"] = ["timed steps", "the last payload as one wire message and back"]
         for phase in ("before", "timed"):
             if phase == "timed":
                 torch.cuda.synchronize()
@@ -700,8 +740,20 @@ def profile_phase(args):
                 g.compress(xs[k % 32], err, s, out=o, out_lens=ln, scales=sc, workspace=ws, status=st[:1])
                 g.decompress(o, ln, sc, s, y=y, workspace=ws, status=st[1:], path_hint=hint)
                 k += 1
+        wire = torch.empty(g.wire_bound(), dtype=torch.uint8, device=dev)
+        wlen = torch.empty(1, dtype=torch.int64, device=dev)
+        wws = g.wire_workspace()
+        o2, ln2, sc2 = torch.empty_like(o), torch.empty_like(ln), torch.empty_like(sc)
+        st_w = torch.empty(2, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        marker()
+        for _ in range(args.steps):
+            g.wire_pack(o, ln, sc, wire=wire, wire_len=wlen, workspace=wws, status=st_w[:1])
+            g.wire_unpack(wire, out=o2, out_lens=ln2, scales=sc2, workspace=wws, status=st_w[1:])
         torch.cuda.synchronize()
         out["status"] = st.cpu().tolist()
+        out["wire_status"] = st_w.cpu().tolist()
+        out["wire_bytes"] = int(wlen.item())
         out["bits_per_value"] = round(8.0 * int(ln.sum().item()) / N, 4)
         out["decompress_sequence"] = "dense" if int(hint[0]) else "sparse"
     elif args.profile == "receive":
@@ -917,6 +969,8 @@ def main():
     last_bits = 8.0 * float(lens.sum().item()) / N
     nonzero_last = float(torch.count_nonzero(yd).item()) / N  # the last step's decoded values: q != 0
     hint_after = "dense" if int(hint[0]) else "sparse"
+    # the last timed step's payload as one wire message (outside the timed region)
+    wire_rec = wire_record(torch, group, out, lens, scales, N)
 
     # phase times: compress calls alone, then decompress calls alone, each
     # call bracketed (the error buffer keeps evolving; inputs rotate)
@@ -1190,6 +1244,7 @@ def main():
         if (int(st_pc.item()), int(st_pd.item())) != (0, 0):
             raise SystemExit("device status not ok in the pipelined steady-state steps")
         steady["pipelined_ms_per_step"] = round(pa.elapsed_time(pb) / 10, 4)
+        steady["wire"] = wire_record(torch, group, out, lens, scales, N)
         # the two byte layouts on the same codes: quantization does not depend
         # on the layout, so one more step's input and this error state, taken
         # by each layout on copies of the error buffer
@@ -1351,6 +1406,7 @@ def main():
                              "as the timed steps"},
         "configs": records,
         "ablations": ablations,
+        "wire": wire_rec,
         "kernels_ms_per_launch_events": {k: round(v[1] / v[0], 4) for k, v in kt_all.items() if v[0]},
         "kernels_events_note": EVENTS_NOTE,
         "wall_s_timed": round(wall, 3),

@@ -2495,7 +2495,8 @@ __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ sr
 constexpr uint32_t kWireChunk = 4096;  // stream bytes one block copies at a time (16 per lane)
 constexpr uint32_t kWirePer = 16;      // tensors per thread and round of k_wire_scan
 
-// One block over all tensors, kThreads * kWirePer per round: each stream's
+// One block over all tensors, kThreads * kWirePer per round (it also resets
+// *status, which only it raises): each stream's
 // length (pack: from in_lens; unpack: from its header), checked against its
 // slot (a longer one is TLC_ERR_CORRUPT and counts as empty); the headers
 // (pack) or out_lens and scales (unpack); the exclusive prefix of the lengths
@@ -2514,6 +2515,8 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, const uint6
     __shared__ uint64_t s_sm[kWaves];
     __shared__ uint32_t s_u[kWaves];
     const uint32_t count = g.count;
+    if (threadIdx.x == 0) *status = TLC_OK;  // the call's only kernel that reports
+    __syncthreads();
     uint64_t carry_b = 0;  // bytes of the rounds before
     uint32_t carry_c = 0;  // chunks of the rounds before
     bool bad = false;
@@ -2595,7 +2598,8 @@ __device__ __forceinline__ uint4 lds_bytes16(const uint32_t* buf, uint32_t off) 
 
 // Copies every stream's bytes between its slot and the message body, one
 // 4 KiB chunk of one stream per block and round (the chunk's tensor by a
-// binary search over cfirst).  The chunk goes through LDS so that the side
+// binary search over cfirst, held in LDS when the group has at most 4096
+// tensors).  The chunk goes through LDS so that the side
 // the chunk is not 16-byte aligned on is read or written in whole aligned
 // words: pack reads its slot (aligned) and writes the body, where a word that
 // the chunk shares with a neighbour is written byte by byte; unpack reads the
@@ -2608,17 +2612,25 @@ __global__ __launch_bounds__(kThreads) void k_wire_copy(GroupView g, const uint8
                                                         const uint64_t* __restrict__ woff,
                                                         const uint32_t* __restrict__ cfirst,
                                                         const uint32_t* __restrict__ ctrl) {
+    constexpr uint32_t kWireLdsTensors = 4096;  // groups up to this many tensors search their chunks in LDS
     __shared__ __align__(16) uint32_t s_buf[(kWireChunk + 32) / 4 + 8];
+    __shared__ uint32_t s_cf[kWireLdsTensors];
     __shared__ uint32_t s_t;
     const uint32_t nchunks = ctrl[0];
     const uint32_t count = g.count;
     const uint32_t i = threadIdx.x;
+    const bool in_lds = count <= kWireLdsTensors;
+    if (blockIdx.x >= nchunks) return;
+    if (in_lds) {
+        for (uint32_t k = i; k < count; k += kThreads) s_cf[k] = cfirst[k];
+        __syncthreads();
+    }
     for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         if (i == 0) {  // the last tensor whose first chunk is <= c
             uint32_t lo = 0, hi = count;
             while (hi - lo > 1) {
                 const uint32_t mid = (lo + hi) >> 1;
-                if (cfirst[mid] <= c) lo = mid;
+                if ((in_lds ? s_cf[mid] : cfirst[mid]) <= c) lo = mid;
                 else hi = mid;
             }
             s_t = lo;
@@ -3226,8 +3238,7 @@ int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint8_t* slo
     uint32_t* const cfirst = reinterpret_cast<uint32_t*>(w + l.cfirst);
     uint32_t* const ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
     const GroupView g = p.g;
-    int rc = launch("tlc_status_ok", st, [&] { k_status_ok<<<1, 1, 0, st>>>(status); });
-    if (rc) return rc;
+    int rc;
     const uint64_t chunk_bound = stream_bytes / kWireChunk + count;
     if (pack) {
         rc = launch("tlc_wire_scan", st, [&] {
