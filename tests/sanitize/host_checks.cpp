@@ -76,6 +76,11 @@ static void check_plan(const std::vector<uint64_t>& sizes) {
     CHECK(tlc_accumulate_many_workspace_size(&info, 0) == 0);
     CHECK(tlc_accumulate_many_workspace_size(&info, 65) == 0);
     CHECK(tlc_accumulate_many_workspace_size(nullptr, 1) == 0);
+    // the wire message: 8 header bytes per tensor plus every slot, and a
+    // workspace of the stream offsets, chunk numbers and one control block
+    CHECK(tlc_wire_bound(&info) == 8 * info.count + info.stream_bytes);
+    const uint64_t ww = tlc_wire_workspace_size(&info);
+    CHECK(ww % 256 == 0 && ww >= 8 * (info.count + 1) + 4 * info.count + 256);
 }
 
 int main() {
@@ -157,6 +162,21 @@ int main() {
         huge.chunks = 1ull << 26;
         CHECK(tlc_accumulate_many_workspace_size(&huge, 31) > 0);
         CHECK(tlc_accumulate_many_workspace_size(&huge, 32) == 0);
+    }
+    {
+        const uint64_t bound = tlc_wire_bound(&g), ww = tlc_wire_workspace_size(&g);
+        CHECK(tlc_wire_pack_group(&g, fake, fb, fl, ff, fb, bound - 1, fl, ws, ww, fs, nullptr) == TLC_ERR_CAPACITY);
+        CHECK(tlc_wire_pack_group(&g, fake, fb, fl, ff, fb, bound, fl, ws, ww - 1, fs, nullptr) == TLC_ERR_WORKSPACE);
+        CHECK(tlc_wire_pack_group(&g, fake, nullptr, fl, ff, fb, bound, fl, ws, ww, fs, nullptr) ==
+              TLC_ERR_INVALID_ARG);
+        CHECK(tlc_wire_pack_group(&bad, fake, fb, fl, ff, fb, bound, fl, ws, ww, fs, nullptr) == TLC_ERR_INVALID_ARG);
+        CHECK(tlc_wire_unpack_group(&g, fake, fb, 8 * g.count - 1, fb, fl, ff, ws, ww, fs, nullptr) ==
+              TLC_ERR_CAPACITY);
+        CHECK(tlc_wire_unpack_group(&g, fake, fb, 8 * g.count, fb, fl, ff, nullptr, ww, fs, nullptr) ==
+              TLC_ERR_WORKSPACE);
+        CHECK(tlc_wire_unpack_group(&g, fake, fb, 8 * g.count, fb, fl, nullptr, ws, ww, fs, nullptr) ==
+              TLC_ERR_INVALID_ARG);
+        CHECK(tlc_wire_bound(nullptr) == 0 && tlc_wire_workspace_size(nullptr) == 0);
     }
     CHECK(tlc_planes_gather(ff, fl, ff, fl, nullptr, 3, 100, nullptr) == TLC_ERR_INVALID_ARG);
     CHECK(tlc_planes_scatter(ff, fl, ff, fl, fl, 65536, 100, nullptr) == TLC_ERR_INVALID_ARG);
