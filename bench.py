@@ -857,8 +857,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the codec runs on one device and this build has no "
-              "multi-GPU exchange; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the codec runs on one device and the library has no "
+              "transport between GPUs; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -2,7 +2,7 @@
 argument checks of every entry point) under AddressSanitizer and
 UndefinedBehaviorSanitizer: tlc.hip is compiled with both on its host
 code, linked with tests/sanitize/host_checks.cpp, and run on the CPU.  The
-driver plans ragged groups (1 to 3000 tensors, sizes from 1 to 2^32-1 and
+C++ program plans ragged groups (1 to 3000 tensors, sizes from 1 to 2^32-1 and
 around tile, chunk and span boundaries) into exactly sized buffers, checks
 the plans against the documented layout, and calls every entry point with
 arguments that must be refused before any launch.  No GPU is used."""
