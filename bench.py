@@ -589,6 +589,142 @@ class Bench:
             parity = ok
         return xs, pay, oracle_first, parity
 
+    def exchange_record(self, payload, reps: int = 10):
+        """One GPU's share of the sharded exchange at the BERT-large shape,
+        8 workers that are also the 8 owners of contiguous tensor ranges
+        (balanced by values), without the transport: GPU 0 packs its payload
+        into one wire message per owner (send); as owner of range 0 it
+        unpacks the 8 workers' messages for that range, adds them in worker
+        order with one many-payload call, compresses the mean with its own
+        error buffer and packs the result (owner); it unpacks the 8 owners'
+        messages and decodes each range of the model delta (receive).  The
+        messages GPU 0 receives are packed beforehand from the workers'
+        payloads and the owners' results."""
+        torch, tlc = self.torch, self.tlc
+        g = self.bert_group
+        sizes, N = g.sizes, g.total
+        s = self.workloads.get("bert_large").s_values[0]
+        o, ln, sc = payload
+        dev = self.dev
+        cuts, acc_n, k = [0], 0, 1
+        for t, n in enumerate(sizes):
+            acc_n += n
+            if k < WORKERS and acc_n >= k * N / WORKERS and t + 1 < len(sizes):
+                cuts.append(t + 1)
+                k += 1
+        cuts.append(len(sizes))
+        shards = [(lo, hi, tlc.Group(sizes[lo:hi], device=dev)) for lo, hi in zip(cuts[:-1], cuts[1:])]
+
+        def view(w, lo, hi, sub):  # worker w's payload restricted to tensors lo..hi-1
+            so = g.offsets[lo]
+            return o[w][so:so + sub.stream_bytes], ln[w][lo:hi], sc[w][lo:hi]
+
+        # messages to owner 0 from every worker, and every owner's result message
+        lo0, hi0, sub0 = shards[0]
+        ws0 = sub0.wire_workspace()
+        to_owner0 = []
+        for w in range(WORKERS):
+            wire, wl, _ = sub0.wire_pack(*view(w, lo0, hi0, sub0), workspace=ws0)
+            to_owner0.append((wire, wl))
+        owner_msgs = []
+        for lo, hi, sub in shards:
+            inp = torch.empty((WORKERS, sub.stream_bytes), dtype=torch.uint8, device=dev)
+            il = torch.empty((WORKERS, hi - lo), dtype=torch.int64, device=dev)
+            isc = torch.empty((WORKERS, hi - lo), dtype=torch.float32, device=dev)
+            for w in range(WORKERS):
+                a, b, c = view(w, lo, hi, sub)
+                inp[w].copy_(a)
+                il[w].copy_(b)
+                isc[w].copy_(c)
+            acc = torch.zeros(sub.total, dtype=torch.float32, device=dev)
+            sub.decompress_accumulate_many(inp, il.view(-1), isc.view(-1), s, acc)
+            e_srv = torch.zeros(sub.total, dtype=torch.float32, device=dev)
+            out_o, lens_o, sc_o, _ = sub.server_compress(acc, WORKERS, e_srv, s)
+            wire, wl, _ = sub.wire_pack(out_o, lens_o, sc_o)
+            owner_msgs.append((wire, int(wl.item())))
+            del inp, il, isc, acc, e_srv
+        torch.cuda.synchronize()
+        # GPU 0's buffers
+        send = [(sub.wire_bound(), sub) for _, _, sub in shards]
+        send_bufs = [torch.empty(b, dtype=torch.uint8, device=dev) for b, _ in send]
+        send_lens = torch.empty(WORKERS, dtype=torch.int64, device=dev)
+        wsw = [sub.wire_workspace() for _, _, sub in shards]
+        st = torch.zeros(8, dtype=torch.int32, device=dev)
+        inp0 = torch.empty((WORKERS, sub0.stream_bytes), dtype=torch.uint8, device=dev)
+        il0 = torch.empty((WORKERS, hi0 - lo0), dtype=torch.int64, device=dev)
+        isc0 = torch.empty((WORKERS, hi0 - lo0), dtype=torch.float32, device=dev)
+        acc0 = torch.empty(sub0.total, dtype=torch.float32, device=dev)
+        e0 = torch.zeros(sub0.total, dtype=torch.float32, device=dev)
+        wsm = torch.empty(sub0.accumulate_many_workspace_size(WORKERS), dtype=torch.uint8, device=dev)
+        wsc = sub0.workspace()
+        out0 = torch.empty(sub0.stream_bytes, dtype=torch.uint8, device=dev)
+        lens0 = torch.empty(hi0 - lo0, dtype=torch.int64, device=dev)
+        sc0 = torch.zeros(hi0 - lo0, dtype=torch.float32, device=dev)
+        wire0 = torch.empty(sub0.wire_bound(), dtype=torch.uint8, device=dev)
+        wl0 = torch.empty(1, dtype=torch.int64, device=dev)
+        hint_m = tlc.path_hint()
+        rx = [(torch.empty(sub.stream_bytes, dtype=torch.uint8, device=dev),
+               torch.empty(hi - lo, dtype=torch.int64, device=dev),
+               torch.empty(hi - lo, dtype=torch.float32, device=dev),
+               torch.empty(sub.total, dtype=torch.float32, device=dev), sub.workspace(), tlc.path_hint())
+              for lo, hi, sub in shards]
+
+        def do_send():
+            for k, (lo, hi, sub) in enumerate(shards):
+                sub.wire_pack(*view(0, lo, hi, sub), wire=send_bufs[k], wire_len=send_lens[k:k + 1],
+                              workspace=wsw[k], status=st[0:1])
+
+        def do_owner():
+            for w in range(WORKERS):
+                wire, wl = to_owner0[w]
+                sub0.wire_unpack(wire, out=inp0[w], out_lens=il0[w], scales=isc0[w], workspace=ws0, status=st[1:2])
+            sub0.decompress_accumulate_many(inp0, il0.view(-1), isc0.view(-1), s, acc0, workspace=wsm,
+                                            status=st[2:3], path_hint=hint_m)
+            sub0.server_compress(acc0, WORKERS, e0, s, out=out0, out_lens=lens0, scales=sc0, workspace=wsc,
+                                 status=st[3:4])
+            sub0.wire_pack(out0, lens0, sc0, wire=wire0, wire_len=wl0, workspace=ws0, status=st[4:5])
+
+        def do_recv():
+            for k, (lo, hi, sub) in enumerate(shards):
+                wire, wl = owner_msgs[k]
+                ob, lb, sb, yb, wsb, hb = rx[k]
+                sub.wire_unpack(wire, wire_bytes=wl, out=ob, out_lens=lb, scales=sb, workspace=wsw[k],
+                                status=st[5:6])
+                sub.decompress(ob, lb, sb, s, y=yb, workspace=wsb, status=st[6:7], path_hint=hb)
+
+        def before(r):
+            acc0.zero_()
+            e0.zero_()
+
+        def body(r, mark):
+            do_send()
+            mark()
+            do_owner()
+            mark()
+            do_recv()
+
+        timed(torch, 2, body, before)
+        t = timed(torch, reps, body, before)
+        if int(st.abs().sum().item()) != 0:
+            raise SystemExit(f"device status not ok in the exchange: {st.tolist()}")
+        sent = int(send_lens.sum().item())
+        recv_owner = sum(int(wl.item()) for _, wl in to_owner0)
+        recv_delta = sum(wl for _, wl in owner_msgs)
+        return {
+            "workers_and_owners": WORKERS,
+            "owner0_tensors": hi0 - lo0, "owner0_values": sub0.total,
+            "send_ms": stats([v[0] for v in t]), "owner_ms": stats([v[1] for v in t]),
+            "receive_ms": stats([v[2] for v in t]), "total_ms": stats([sum(v) for v in t]),
+            "bytes_sent_by_gpu0": sent, "bytes_received_as_owner": recv_owner,
+            "bytes_received_model_delta": recv_delta,
+            "dense_fp32_bytes_per_gpu": 4 * N,
+            "how": ("GPU 0's work in an exchange of first-step payloads without the transport: send = 8 wire "
+                    "messages of its payload; owner = unpack the 8 workers' messages for its range, one "
+                    "many-payload sum, the compress of the mean with its error buffer, one message; receive = "
+                    "unpack the 8 owners' messages and decode every range of the model delta.  Its own "
+                    "compress of the gradient set is the first-step record's compress_ms."),
+        }
+
     def accumulate_record(self, payload, oracle_payloads=None):
         """The 8 payloads decompressed and accumulated into one fp32 sum in
         worker order: one many-payload call against 8 single-payload calls,
@@ -1335,6 +1471,8 @@ def main():
         torch.cuda.empty_cache()
         log("accumulate of the 8 first-step payloads")
         rec["accumulate_8"] = bench.accumulate_record(wpay["first"], oracle_first if not args.no_cpu else None)
+        log("exchange of the 8 first-step payloads, one GPU's share")
+        rec["exchange_8"] = bench.exchange_record(wpay["first"])
         records["bert_large_first_step"] = rec
         if steady is not None:
             log("accumulate of the 8 steady-state payloads")
