@@ -597,7 +597,8 @@ class Bench:
         unpacks the 8 workers' messages for that range, adds them in worker
         order with one many-payload call, compresses the mean with its own
         error buffer and packs the result (owner); it unpacks the 8 owners'
-        messages and decodes each range of the model delta (receive).  The
+        messages into one payload of the whole group and decodes the model
+        delta with one grouped decompress (receive).  The
         messages GPU 0 receives are packed beforehand from the workers'
         payloads and the owners' results."""
         torch, tlc = self.torch, self.tlc
@@ -663,11 +664,15 @@ class Bench:
         wire0 = torch.empty(sub0.wire_bound(), dtype=torch.uint8, device=dev)
         wl0 = torch.empty(1, dtype=torch.int64, device=dev)
         hint_m = tlc.path_hint()
-        rx = [(torch.empty(sub.stream_bytes, dtype=torch.uint8, device=dev),
-               torch.empty(hi - lo, dtype=torch.int64, device=dev),
-               torch.empty(hi - lo, dtype=torch.float32, device=dev),
-               torch.empty(sub.total, dtype=torch.float32, device=dev), sub.workspace(), tlc.path_hint())
-              for lo, hi, sub in shards]
+        # the owners' messages land in one payload of the whole group (an
+        # owner's slots are the group's shifted by a multiple of 16), decoded
+        # by one grouped decompress
+        rx_out = torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev)
+        rx_lens = torch.empty(g.count, dtype=torch.int64, device=dev)
+        rx_sc = torch.empty(g.count, dtype=torch.float32, device=dev)
+        rx_y = torch.empty(N, dtype=torch.float32, device=dev)
+        rx_ws = g.workspace()
+        rx_hint = tlc.path_hint()
 
         def do_send():
             for k, (lo, hi, sub) in enumerate(shards):
@@ -687,10 +692,10 @@ class Bench:
         def do_recv():
             for k, (lo, hi, sub) in enumerate(shards):
                 wire, wl = owner_msgs[k]
-                ob, lb, sb, yb, wsb, hb = rx[k]
-                sub.wire_unpack(wire, wire_bytes=wl, out=ob, out_lens=lb, scales=sb, workspace=wsw[k],
-                                status=st[5:6])
-                sub.decompress(ob, lb, sb, s, y=yb, workspace=wsb, status=st[6:7], path_hint=hb)
+                so = g.offsets[lo]
+                sub.wire_unpack(wire, wire_bytes=wl, out=rx_out[so:so + sub.stream_bytes], out_lens=rx_lens[lo:hi],
+                                scales=rx_sc[lo:hi], workspace=wsw[k], status=st[5:6])
+            g.decompress(rx_out, rx_lens, rx_sc, s, y=rx_y, workspace=rx_ws, status=st[6:7], path_hint=rx_hint)
 
         def before(r):
             acc0.zero_()
@@ -721,8 +726,9 @@ class Bench:
             "how": ("GPU 0's work in an exchange of first-step payloads without the transport: send = 8 wire "
                     "messages of its payload; owner = unpack the 8 workers' messages for its range, one "
                     "many-payload sum, the compress of the mean with its error buffer, one message; receive = "
-                    "unpack the 8 owners' messages and decode every range of the model delta.  Its own "
-                    "compress of the gradient set is the first-step record's compress_ms."),
+                    "unpack the 8 owners' messages into one payload of the group and decode the model delta "
+                    "with one grouped decompress.  Its own compress of the gradient set is the first-step "
+                    "record's compress_ms."),
         }
 
     def accumulate_record(self, payload, oracle_payloads=None):

@@ -9,7 +9,8 @@ all-gather shape of SparCML's "Proposed method"), for two rounds:
   each owner unpacks its messages, adds the workers' payloads in worker
   order with one many-payload call, compresses the mean with its own error
   buffer (carried across rounds) and packs one message; every worker unpacks
-  the owners' messages and decodes the model delta.
+  the owners' messages into one payload of the whole group and decodes the
+  model delta with one grouped decompress.
 
 Every message must equal the oracle's message of the oracle's streams, and
 the decoded model delta the oracle's, bit for bit."""
@@ -105,21 +106,26 @@ def test_sharded_exchange_both_directions(workers, owners):
             assert np.array_equal(msg_o, oracle.wire_pack(st_o, M_o)), (rnd, k)
             assert np.array_equal(bits(err_o_d[k].cpu().numpy()), bits(err_o[k])), (rnd, k)
             deltas.append((wire_o, int(wl_o.item()), st_o, M_o))
-        # a worker receives every owner's message and decodes the model delta
-        delta = np.empty(g.total, np.float32)
+        # a worker receives every owner's message into one payload of the whole
+        # group (each at its range's slots) and decodes the model delta at once
+        rx_out = torch.empty(g.stream_bytes, dtype=torch.uint8, device="cuda:0")
+        rx_lens = torch.empty(count, dtype=torch.int64, device="cuda:0")
+        rx_sc = torch.empty(count, dtype=torch.float32, device="cuda:0")
         want_delta = np.empty(g.total, np.float32)
         for (lo, hi, sub), (wire_o, wl_o, st_o, M_o) in zip(shards, deltas):
-            o2, l2, s2, st = sub.wire_unpack(wire_o, wire_bytes=wl_o)
-            e0 = g.elem_offsets[lo]
-            y, st_d = sub.decompress(o2, l2, s2, s)
+            so = g.offsets[lo]
+            _, _, _, st = sub.wire_unpack(wire_o, wire_bytes=wl_o, out=rx_out[so:so + sub.stream_bytes],
+                                          out_lens=rx_lens[lo:hi], scales=rx_sc[lo:hi])
             torch.cuda.synchronize()
-            assert int(st.item()) == 0 and int(st_d.item()) == 0
-            delta[e0:e0 + sub.total] = y.cpu().numpy()
-            off = e0
+            assert int(st.item()) == 0
+            off = g.elem_offsets[lo]
             for t in range(lo, hi):
                 n = sizes[t]
                 want_delta[off:off + n] = oracle.decompress(st_o[t - lo], M_o[t - lo], n, s)
                 off += n
-        assert np.array_equal(bits(delta), bits(want_delta)), rnd
+        delta, st_d = g.decompress(rx_out, rx_lens, rx_sc, s)
+        torch.cuda.synchronize()
+        assert int(st_d.item()) == 0
+        assert np.array_equal(bits(delta.cpu().numpy()), bits(want_delta)), rnd
         for w in range(workers):
             assert np.array_equal(bits(err_w_d[w].cpu().numpy()), bits(err_w[w])), (rnd, w)
