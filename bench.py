@@ -600,7 +600,8 @@ class Bench:
         messages into one payload of the whole group and decodes the model
         delta with one grouped decompress (receive).  The
         messages GPU 0 receives are packed beforehand from the workers'
-        payloads and the owners' results."""
+        payloads and the owners' results.  The 8 messages GPU 0 sends come
+        from one call (tlc_wire_pack_ranges_group)."""
         torch, tlc = self.torch, self.tlc
         g = self.bert_group
         sizes, N = g.sizes, g.total
@@ -646,9 +647,9 @@ class Bench:
             del inp, il, isc, acc, e_srv
         torch.cuda.synchronize()
         # GPU 0's buffers
-        send = [(sub.wire_bound(), sub) for _, _, sub in shards]
-        send_bufs = [torch.empty(b, dtype=torch.uint8, device=dev) for b, _ in send]
-        send_lens = torch.empty(WORKERS, dtype=torch.int64, device=dev)
+        send_buf = torch.empty(g.wire_bound(), dtype=torch.uint8, device=dev)
+        send_lens = torch.empty(len(shards), dtype=torch.int64, device=dev)
+        send_ws = g.wire_workspace()
         wsw = [sub.wire_workspace() for _, _, sub in shards]
         st = torch.zeros(8, dtype=torch.int32, device=dev)
         inp0 = torch.empty((WORKERS, sub0.stream_bytes), dtype=torch.uint8, device=dev)
@@ -674,10 +675,9 @@ class Bench:
         rx_ws = g.workspace()
         rx_hint = tlc.path_hint()
 
-        def do_send():
-            for k, (lo, hi, sub) in enumerate(shards):
-                sub.wire_pack(*view(0, lo, hi, sub), wire=send_bufs[k], wire_len=send_lens[k:k + 1],
-                              workspace=wsw[k], status=st[0:1])
+        def do_send():  # one message per owner, back to back, in one call
+            g.wire_pack_ranges(o[0], ln[0], sc[0], cuts, wire=send_buf, wire_lens=send_lens, workspace=send_ws,
+                               status=st[0:1])
 
         def do_owner():
             for w in range(WORKERS):
@@ -723,8 +723,8 @@ class Bench:
             "bytes_sent_by_gpu0": sent, "bytes_received_as_owner": recv_owner,
             "bytes_received_model_delta": recv_delta,
             "dense_fp32_bytes_per_gpu": 4 * N,
-            "how": ("GPU 0's work in an exchange of first-step payloads without the transport: send = 8 wire "
-                    "messages of its payload; owner = unpack the 8 workers' messages for its range, one "
+            "how": ("GPU 0's work in an exchange of first-step payloads without the transport: send = its "
+                    "payload as 8 wire messages, one per owner, in one call; owner = unpack the 8 workers' messages for its range, one "
                     "many-payload sum, the compress of the mean with its error buffer, one message; receive = "
                     "unpack the 8 owners' messages into one payload of the group and decode the model delta "
                     "with one grouped decompress.  Its own compress of the gradient set is the first-step "

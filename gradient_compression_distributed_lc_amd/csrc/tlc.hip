@@ -2495,6 +2495,16 @@ __global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ sr
 constexpr uint32_t kWireChunk = 4096;  // stream bytes one block copies at a time (16 per lane)
 constexpr uint32_t kWirePer = 16;      // tensors per thread and round of k_wire_scan
 
+// Consecutive tensor ranges packed as messages of their own, back to back:
+// range k is tensors cut[k] .. cut[k+1]-1.  With P(t) the sum of the stream
+// lengths of tensors before t, message k starts at 8 cut[k] + P(cut[k]), the
+// header of tensor t of range k lies at 8 t + P(cut[k]) and its stream at
+// 8 cut[k+1] + P(t).  One range is the group's message.
+struct WireCuts {
+    uint32_t n;           // ranges, 1 .. 64
+    uint32_t cut[65];     // cut[0] = 0 < cut[1] < ... < cut[n] = count
+};
+
 // One block over all tensors, kThreads * kWirePer per round (it also resets
 // *status, which only it raises): each stream's
 // length (pack: from in_lens; unpack: from its header), checked against its
@@ -2505,13 +2515,13 @@ constexpr uint32_t kWirePer = 16;      // tensors per thread and round of k_wire
 // length (pack).  Unpack: a message shorter than its headers and streams is
 // TLC_ERR_CORRUPT, and then no chunk is copied.
 template <bool kPack>
-__global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, const uint64_t* __restrict__ lens_in,
+__global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cuts, const uint64_t* __restrict__ lens_in,
                                                         const float* __restrict__ m_in, uint8_t* __restrict__ hdr_out,
                                                         const uint8_t* __restrict__ hdr_in, uint64_t wire_bytes,
                                                         uint64_t* __restrict__ lens_out, float* __restrict__ m_out,
-                                                        uint64_t* __restrict__ woff, uint32_t* __restrict__ cfirst,
-                                                        uint32_t* __restrict__ ctrl, uint64_t* __restrict__ wire_len,
-                                                        int* __restrict__ status) {
+                                                        uint64_t* __restrict__ woff, uint64_t* __restrict__ dbase,
+                                                        uint32_t* __restrict__ cfirst, uint32_t* __restrict__ ctrl,
+                                                        uint64_t* __restrict__ wire_len, int* __restrict__ status) {
     __shared__ uint64_t s_sm[kWaves];
     __shared__ uint32_t s_u[kWaves];
     const uint32_t count = g.count;
@@ -2545,11 +2555,7 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, const uint6
                     bad = true;
                     l = 0;
                 }
-                if (kPack) {
-                    uint32_t* const h = reinterpret_cast<uint32_t*>(hdr_out) + 2ull * t;
-                    h[0] = (uint32_t)l;
-                    h[1] = mb;
-                } else {
+                if (!kPack) {
                     lens_out[t] = l;
                     m_out[t] = __uint_as_float(mb);
                 }
@@ -2582,7 +2588,32 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, const uint6
         const bool fits = kPack || total <= wire_bytes;
         if (!fits) raise_status(status, TLC_ERR_CORRUPT);
         ctrl[0] = fits ? carry_c : 0u;
-        if (kPack) *wire_len = total;
+    }
+    __syncthreads();  // every woff entry written above is visible to the block
+    // where each stream goes in the messages, and (pack) the headers and each
+    // message's length; a thread's tensors are consecutive, so its range
+    // index only moves forward
+    uint32_t k = 0;
+    for (uint32_t r0 = 0; r0 < count; r0 += kThreads * kWirePer) {
+        const uint32_t t0 = r0 + threadIdx.x * kWirePer;
+        for (uint32_t j = 0; j < kWirePer && t0 + j < count; ++j) {
+            const uint32_t u = t0 + j;
+            while (k + 1 < cuts.n && cuts.cut[k + 1] <= u) ++k;
+            dbase[u] = 8ull * cuts.cut[k + 1] + woff[u];
+            if (kPack) {  // byte stores: a later range's headers need not be 4-byte aligned
+                uint8_t* const h = hdr_out + 8ull * u + woff[cuts.cut[k]];
+                const uint32_t l = (uint32_t)(woff[u + 1] - woff[u]), mb = __float_as_uint(m_in[u]);
+#pragma unroll
+                for (uint32_t b = 0; b < 4; ++b) {
+                    h[b] = (uint8_t)(l >> (8 * b));
+                    h[4 + b] = (uint8_t)(mb >> (8 * b));
+                }
+            }
+        }
+    }
+    if (kPack && threadIdx.x < cuts.n) {
+        const uint32_t a = cuts.cut[threadIdx.x], b = cuts.cut[threadIdx.x + 1];
+        wire_len[threadIdx.x] = 8ull * (b - a) + woff[b] - woff[a];
     }
 }
 
@@ -2608,8 +2639,9 @@ __device__ __forceinline__ uint4 lds_bytes16(const uint32_t* buf, uint32_t off) 
 // are written as 0, still inside the slot).
 template <bool kPack>
 __global__ __launch_bounds__(kThreads) void k_wire_copy(GroupView g, const uint8_t* __restrict__ src,
-                                                        uint8_t* __restrict__ dst, uint64_t body, uint64_t wire_bytes,
+                                                        uint8_t* __restrict__ dst, uint64_t wire_bytes,
                                                         const uint64_t* __restrict__ woff,
+                                                        const uint64_t* __restrict__ dbase,
                                                         const uint32_t* __restrict__ cfirst,
                                                         const uint32_t* __restrict__ ctrl) {
     constexpr uint32_t kWireLdsTensors = 4096;  // groups up to this many tensors search their chunks in LDS
@@ -2642,7 +2674,7 @@ __global__ __launch_bounds__(kThreads) void k_wire_copy(GroupView g, const uint8
         const uint64_t L = woff[t + 1] - woff[t];
         const uint32_t len = (uint32_t)min<uint64_t>(kWireChunk, L - k0);
         const uint64_t slot = sg.stream_off + k0;   // aligned
-        const uint64_t msg = body + woff[t] + k0;   // any alignment
+        const uint64_t msg = dbase[t] + k0;         // any alignment
         if (kPack) {
             // slot words straight into LDS: data byte m at buffer byte m
             if (16u * i < len) reinterpret_cast<uint4*>(s_buf)[i] = reinterpret_cast<const uint4*>(src + slot)[i];
@@ -3203,25 +3235,48 @@ int run_planes(bool gather, const float* src, const uint64_t* src_off, float* ds
 // ---------------------------------------------------------------------------
 // C ABI
 
-// Workspace of the wire pack and unpack: each stream's place in the body
-// (count + 1), its first chunk, the chunk count.
+// Workspace of the wire pack and unpack: the prefix of the stream lengths
+// (count + 1), each stream's place in the messages, its first chunk, the
+// chunk count.
 struct WireLayout {
-    size_t woff, cfirst, ctrl, total;
+    size_t woff, dbase, cfirst, ctrl, total;
 };
 WireLayout wire_layout(uint64_t count) {
     WireLayout l;
     l.woff = 0;
-    l.cfirst = align_up(8 * (count + 1), 256);
+    l.dbase = align_up(8 * (count + 1), 256);
+    l.cfirst = l.dbase + align_up(8 * count, 256);
     l.ctrl = l.cfirst + align_up(4 * count, 256);
     l.total = l.ctrl + 256;
     return l;
 }
 
-int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint8_t* slots_in, const uint64_t* lens_in, const float* m_in,
+// Host ranges -> kernel argument: cuts[0] = 0 < ... < cuts[n] = count, n <= 64.
+bool wire_cuts(const uint32_t* cuts, uint32_t n, uint64_t count, WireCuts* wc) {
+    if (n == 0 || n > 64) return false;
+    if (!cuts) {
+        if (n != 1) return false;
+        wc->n = 1;
+        wc->cut[0] = 0;
+        wc->cut[1] = (uint32_t)count;
+        return true;
+    }
+    if (cuts[0] != 0 || cuts[n] != count) return false;
+    for (uint32_t k = 0; k < n; ++k)
+        if (cuts[k] >= cuts[k + 1]) return false;
+    wc->n = n;
+    for (uint32_t k = 0; k <= n; ++k) wc->cut[k] = cuts[k];
+    return true;
+}
+
+int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint32_t* cuts, uint32_t ranges,
+             const uint8_t* slots_in, const uint64_t* lens_in, const float* m_in,
              uint8_t* wire, uint64_t wire_bytes, uint64_t* wire_len, const uint8_t* wire_in, uint8_t* slots_out,
              uint64_t* lens_out, float* m_out, void* ws, size_t ws_bytes, int* status, hipStream_t st) {
     const uint64_t count = p.d.count;
     if (!status) return TLC_ERR_INVALID_ARG;
+    WireCuts wc;
+    if (!wire_cuts(cuts, ranges, count, &wc)) return TLC_ERR_INVALID_ARG;
     if (pack) {
         if (!slots_in || !lens_in || !m_in || !wire || !wire_len || !aligned16(slots_in) || !aligned16(wire))
             return TLC_ERR_INVALID_ARG;
@@ -3235,6 +3290,7 @@ int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint8_t* slo
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < l.total) return TLC_ERR_WORKSPACE;
     char* const w = static_cast<char*>(ws);
     uint64_t* const woff = reinterpret_cast<uint64_t*>(w + l.woff);
+    uint64_t* const dbase = reinterpret_cast<uint64_t*>(w + l.dbase);
     uint32_t* const cfirst = reinterpret_cast<uint32_t*>(w + l.cfirst);
     uint32_t* const ctrl = reinterpret_cast<uint32_t*>(w + l.ctrl);
     const GroupView g = p.g;
@@ -3242,26 +3298,25 @@ int run_wire(bool pack, const Plan& p, uint64_t stream_bytes, const uint8_t* slo
     const uint64_t chunk_bound = stream_bytes / kWireChunk + count;
     if (pack) {
         rc = launch("tlc_wire_scan", st, [&] {
-            k_wire_scan<true><<<1, kThreads, 0, st>>>(g, lens_in, m_in, wire, nullptr, 0, nullptr, nullptr, woff,
-                                                      cfirst, ctrl, wire_len, status);
+            k_wire_scan<true><<<1, kThreads, 0, st>>>(g, wc, lens_in, m_in, wire, nullptr, 0, nullptr, nullptr, woff,
+                                                      dbase, cfirst, ctrl, wire_len, status);
         });
         if (rc) return rc;
         const uint32_t grid = (uint32_t)std::min<uint64_t>(
             chunk_bound, resident_grid(kGridWirePack, reinterpret_cast<const void*>(k_wire_copy<true>), 1u << 16));
         return launch("tlc_wire_pack", st, [&] {
-            k_wire_copy<true><<<grid, kThreads, 0, st>>>(g, slots_in, wire, 8 * count, wire_bytes, woff, cfirst, ctrl);
+            k_wire_copy<true><<<grid, kThreads, 0, st>>>(g, slots_in, wire, wire_bytes, woff, dbase, cfirst, ctrl);
         });
     }
     rc = launch("tlc_wire_scan", st, [&] {
-        k_wire_scan<false><<<1, kThreads, 0, st>>>(g, nullptr, nullptr, nullptr, wire_in, wire_bytes, lens_out, m_out,
-                                                   woff, cfirst, ctrl, nullptr, status);
+        k_wire_scan<false><<<1, kThreads, 0, st>>>(g, wc, nullptr, nullptr, nullptr, wire_in, wire_bytes, lens_out,
+                                                   m_out, woff, dbase, cfirst, ctrl, nullptr, status);
     });
     if (rc) return rc;
     const uint32_t grid = (uint32_t)std::min<uint64_t>(
         chunk_bound, resident_grid(kGridWireUnpack, reinterpret_cast<const void*>(k_wire_copy<false>), 1u << 16));
     return launch("tlc_wire_unpack", st, [&] {
-        k_wire_copy<false><<<grid, kThreads, 0, st>>>(g, wire_in, slots_out, 8 * count, wire_bytes, woff, cfirst,
-                                                      ctrl);
+        k_wire_copy<false><<<grid, kThreads, 0, st>>>(g, wire_in, slots_out, wire_bytes, woff, dbase, cfirst, ctrl);
     });
 }
 
@@ -3522,8 +3577,21 @@ int tlc_wire_pack_group(const tlc_group_info* info, const void* d_table, const u
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_wire(true, p, info->stream_bytes, in, in_lens, scales, wire, wire_capacity, wire_len, nullptr, nullptr, nullptr, nullptr,
+    return run_wire(true, p, info->stream_bytes, nullptr, 1, in, in_lens, scales, wire, wire_capacity, wire_len, nullptr, nullptr, nullptr, nullptr,
                     workspace, workspace_bytes, status, static_cast<hipStream_t>(stream));
+}
+
+int tlc_wire_pack_ranges_group(const tlc_group_info* info, const void* d_table, const uint32_t* cuts, uint32_t ranges,
+                               const uint8_t* in, const uint64_t* in_lens, const float* scales, uint8_t* wire,
+                               uint64_t wire_capacity, uint64_t* wire_lens, void* workspace, size_t workspace_bytes,
+                               int* status, tlc_stream_t stream) {
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    if (!cuts) return TLC_ERR_INVALID_ARG;
+    return run_wire(true, p, info->stream_bytes, cuts, ranges, in, in_lens, scales, wire, wire_capacity, wire_lens,
+                    nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, status,
+                    static_cast<hipStream_t>(stream));
 }
 
 int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const uint8_t* wire, uint64_t wire_bytes,
@@ -3532,7 +3600,7 @@ int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const
     Plan p;
     int rc = group_plan_of(info, d_table, &p);
     if (rc) return rc;
-    return run_wire(false, p, info->stream_bytes, nullptr, nullptr, nullptr, nullptr, wire_bytes, nullptr, wire, out, out_lens, scales,
+    return run_wire(false, p, info->stream_bytes, nullptr, 1, nullptr, nullptr, nullptr, nullptr, wire_bytes, nullptr, wire, out, out_lens, scales,
                     workspace, workspace_bytes, status, static_cast<hipStream_t>(stream));
 }
 

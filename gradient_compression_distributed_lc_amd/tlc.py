@@ -82,6 +82,8 @@ _SIGS = {
     "tlc_wire_workspace_size": (_U64, [ctypes.POINTER(GroupInfo)]),
     "tlc_wire_pack_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
     "tlc_wire_unpack_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U64, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tlc_wire_pack_ranges_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U32, _P, _P, _P, _P, _U64, _P, _P, _SZ,
+                                        _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_gather_probe": (_I, [_P, _P, _U64, _P, _P]),
@@ -585,6 +587,38 @@ class Group:
                                        _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_wire_pack_group")
         return wire, wire_len, status
+
+    def wire_pack_ranges(self, inp, in_lens, scales, cuts, *, wire=None, wire_lens=None, workspace=None,
+                         status=None, stream=None):
+        """tlc_wire_pack_ranges_group: one message per consecutive range of
+        tensors (range k: tensors cuts[k] .. cuts[k+1]-1), back to back.
+        Returns (wire, wire_lens, status); message k is
+        wire[sum(wire_lens[:k]) : sum(wire_lens[:k+1])]."""
+        dev = self.device
+        cuts = [int(c) for c in cuts]
+        n = len(cuts) - 1
+        if n < 1 or n > 64 or cuts[0] != 0 or cuts[-1] != self.count or any(a >= b for a, b in zip(cuts, cuts[1:])):
+            raise ValueError("cuts must rise from 0 to the tensor count, 1 to 64 ranges")
+        wire = wire if wire is not None else torch.empty(self.wire_bound(), dtype=torch.uint8, device=dev)
+        wire_lens = wire_lens if wire_lens is not None else torch.empty(n, dtype=torch.int64, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        _need(inp, self.stream_bytes, "in")
+        _need(in_lens, self.count, "in_lens")
+        _need(scales, self.count, "scales")
+        _need(wire, self.wire_bound(), "wire")
+        _need(wire_lens, n, "wire_lens")
+        _need(status, 1, "status")
+        workspace = workspace if workspace is not None else self.wire_workspace()
+        c_cuts = (ctypes.c_uint32 * (n + 1))(*cuts)
+        rc = lib().tlc_wire_pack_ranges_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                              c_cuts, n, _ptr(inp, torch.uint8, "in"),
+                                              _ptr(in_lens, torch.int64, "in_lens"),
+                                              _ptr(scales, torch.float32, "scales"), _ptr(wire, torch.uint8, "wire"),
+                                              wire.numel(), _ptr(wire_lens, torch.int64, "wire_lens"),
+                                              _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                              _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_wire_pack_ranges_group")
+        return wire, wire_lens, status
 
     def wire_unpack(self, wire, *, wire_bytes=None, out=None, out_lens=None, scales=None, workspace=None,
                     status=None, stream=None):

@@ -354,6 +354,22 @@ uint64_t tlc_wire_workspace_size(const tlc_group_info* info);
 int tlc_wire_pack_group(const tlc_group_info* info, const void* d_table, const uint8_t* in, const uint64_t* in_lens,
                         const float* scales, uint8_t* wire, uint64_t wire_capacity, uint64_t* wire_len,
                         void* workspace, size_t workspace_bytes, int* status, tlc_stream_t stream);
+/* tlc_wire_pack_ranges_group: the same payload as `ranges` messages, one per
+ * consecutive range of tensors (range k: tensors cuts[k] .. cuts[k+1]-1, for
+ * the owners of a sharded exchange), back to back in wire: message k is the
+ * wire message of its range alone, as tlc_wire_pack_group on that range's
+ * group would write it, and starts where message k-1 ends; wire_lens (device
+ * uint64[ranges]) receives their lengths.  cuts: host uint32[ranges + 1],
+ * cuts[0] = 0 < cuts[1] < ... < cuts[ranges] = count, 1 <= ranges <= 64
+ * (TLC_ERR_INVALID_ARG otherwise).  A range's slots in `in` are the slots of
+ * that range's own group shifted by a multiple of 16 bytes, so each message
+ * unpacks with tlc_wire_unpack_group on the range's group plan (into a
+ * buffer of its own, or into the whole group's at the range's first slot).
+ * Capacity, workspace and errors as tlc_wire_pack_group. */
+int tlc_wire_pack_ranges_group(const tlc_group_info* info, const void* d_table, const uint32_t* cuts, uint32_t ranges,
+                               const uint8_t* in, const uint64_t* in_lens, const float* scales, uint8_t* wire,
+                               uint64_t wire_capacity, uint64_t* wire_lens, void* workspace, size_t workspace_bytes,
+                               int* status, tlc_stream_t stream);
 int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const uint8_t* wire, uint64_t wire_bytes,
                           uint8_t* out, uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
                           int* status, tlc_stream_t stream);

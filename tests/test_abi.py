@@ -377,6 +377,17 @@ def test_wire_host_checks():
     bad.table_bytes += 16
     assert L.tlc_wire_pack_group(ctypes.byref(bad), fake, fake, fake, fake, fake, bound, fake, ws, wsz, fake,
                                  None) == tlc.ERR_INVALID_ARG
+    # ranges: cuts must rise from 0 to the tensor count, 1 to 64 ranges
+    C = ctypes.c_uint32
+    pr = lambda cuts, n: L.tlc_wire_pack_ranges_group(bi, fake, cuts, n, fake, fake, fake, fake, bound, fake, ws, wsz,
+                                                      fake, None)
+    assert pr(None, 1) == tlc.ERR_INVALID_ARG
+    assert pr((C * 3)(0, 3, 3), 2) == tlc.ERR_INVALID_ARG   # an empty range
+    assert pr((C * 3)(1, 2, 3), 2) == tlc.ERR_INVALID_ARG   # not from 0
+    assert pr((C * 3)(0, 1, 2), 2) == tlc.ERR_INVALID_ARG   # not to the count
+    assert pr((C * 2)(0, 3), 0) == tlc.ERR_INVALID_ARG
+    assert L.tlc_wire_pack_ranges_group(bi, fake, (C * 3)(0, 1, 3), 2, fake, fake, fake, fake, bound - 1, fake, ws,
+                                        wsz, fake, None) == tlc.ERR_CAPACITY
 
 
 def test_path_hint_word_is_checked_on_the_host():

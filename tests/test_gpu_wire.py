@@ -155,3 +155,59 @@ def test_workers_messages_into_one_sum():
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert np.array_equal(bits(acc.cpu().numpy()), bits(want))
+
+
+@pytest.mark.parametrize("ranges", [1, 3, 8])
+def test_range_messages(ranges):
+    """tlc_wire_pack_ranges_group: message k is the oracle's message of range k
+    alone; each unpacks into the whole group's payload at its range's first
+    slot, and the group decompresses to the oracle's values.  One range is the
+    group's message."""
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(40 + ranges)
+    sizes = [int(v) for v in rng.integers(1, 30_000, 45)] + [5120, 1, 3]
+    g, out, lens, scales, streams, Ms, s = group_payload(sizes, 40 + ranges, dense_every=2)
+    count = len(sizes)
+    cuts = [0] + sorted(int(v) for v in rng.choice(np.arange(1, count), ranges - 1, replace=False)) + [count]
+    say(f"case wire ranges={ranges}")
+    wire, wlens, st = g.wire_pack_ranges(out, lens, scales, cuts)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    wl = wlens.cpu().numpy()
+    got = wire[:int(wl.sum())].cpu().numpy()
+    want = np.concatenate([oracle.wire_pack(streams[a:b], Ms[a:b]) for a, b in zip(cuts, cuts[1:])])
+    assert np.array_equal(got, want)
+    assert [int(v) for v in wl] == [8 * (b - a) + sum(x.size for x in streams[a:b]) for a, b in zip(cuts, cuts[1:])]
+    if ranges == 1:
+        w1, l1, _ = g.wire_pack(out, lens, scales)
+        torch.cuda.synchronize()
+        assert int(l1.item()) == int(wl[0]) and torch.equal(w1[:int(wl[0])], wire[:int(wl[0])])
+    rx = torch.full_like(out, 0x33)
+    rx_lens = torch.empty_like(lens)
+    rx_sc = torch.empty_like(scales)
+    pos = 0
+    for k, (a, b) in enumerate(zip(cuts, cuts[1:])):
+        sub = tlc.Group(sizes[a:b])
+        so = g.offsets[a]
+        msg = wire[pos:pos + int(wl[k])].clone()  # a message of its own, as a receiver holds it
+        _, _, _, st = sub.wire_unpack(msg, out=rx[so:so + sub.stream_bytes], out_lens=rx_lens[a:b],
+                                      scales=rx_sc[a:b])
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, k
+        pos += int(wl[k])
+    y, st_d = g.decompress(rx, rx_lens, rx_sc, s)
+    torch.cuda.synchronize()
+    assert int(st_d.item()) == 0
+    want_y = np.concatenate([oracle.decompress(x, Ms[t], n, s) for t, (x, n) in enumerate(zip(streams, sizes))])
+    assert np.array_equal(bits(y.cpu().numpy()), bits(want_y))
+    # a length above its capacity in the last range is corrupt, sent empty, and moves no other message
+    bad = lens.clone()
+    bad[count - 1] = -(-sizes[-1] // 5) + 1
+    w2, l2, st2 = g.wire_pack_ranges(out, bad, scales, cuts)
+    torch.cuda.synchronize()
+    assert int(st2.item()) == oracle.ERR_CORRUPT
+    l2 = l2.cpu().numpy()
+    assert np.array_equal(l2[:-1], wl[:-1]) and int(l2[-1]) == int(wl[-1]) - streams[-1].size
+    n_ok = int(wl[:-1].sum())
+    assert torch.equal(w2[:n_ok], wire[:n_ok])
