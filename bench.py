@@ -600,8 +600,10 @@ class Bench:
         messages into one payload of the whole group and decodes the model
         delta with one grouped decompress (receive).  The
         messages GPU 0 receives are packed beforehand from the workers'
-        payloads and the owners' results.  The 8 messages GPU 0 sends come
-        from one call (tlc_wire_pack_ranges_group)."""
+        payloads and the owners' results, and lie back to back as the
+        transport would leave them.  The 8 messages GPU 0 sends come from one
+        call (tlc_wire_pack_ranges_group), and each side's 8 received messages
+        are unpacked by one call (tlc_wire_unpack_ranges_group)."""
         torch, tlc = self.torch, self.tlc
         g = self.bert_group
         sizes, N = g.sizes, g.total
@@ -627,7 +629,7 @@ class Bench:
         to_owner0 = []
         for w in range(WORKERS):
             wire, wl, _ = sub0.wire_pack(*view(w, lo0, hi0, sub0), workspace=ws0)
-            to_owner0.append((wire, wl))
+            to_owner0.append((wire, int(wl.item())))
         owner_msgs = []
         for lo, hi, sub in shards:
             inp = torch.empty((WORKERS, sub.stream_bytes), dtype=torch.uint8, device=dev)
@@ -650,7 +652,6 @@ class Bench:
         send_buf = torch.empty(g.wire_bound(), dtype=torch.uint8, device=dev)
         send_lens = torch.empty(len(shards), dtype=torch.int64, device=dev)
         send_ws = g.wire_workspace()
-        wsw = [sub.wire_workspace() for _, _, sub in shards]
         st = torch.zeros(8, dtype=torch.int32, device=dev)
         inp0 = torch.empty((WORKERS, sub0.stream_bytes), dtype=torch.uint8, device=dev)
         il0 = torch.empty((WORKERS, hi0 - lo0), dtype=torch.int64, device=dev)
@@ -674,27 +675,35 @@ class Bench:
         rx_y = torch.empty(N, dtype=torch.float32, device=dev)
         rx_ws = g.workspace()
         rx_hint = tlc.path_hint()
+        # each side's received messages back to back, as the transport leaves
+        # them; the workers' messages for range 0 are the range messages of
+        # range 0 repeated once per worker, whose slots are the 8 payloads
+        # stacked (each copy's slots start at a multiple of 16)
+        rx_owner = torch.cat([wire[:wl] for wire, wl in to_owner0])
+        rep0 = tlc.Group(list(sub0.sizes) * WORKERS, device=dev)
+        cuts0 = [w * (hi0 - lo0) for w in range(WORKERS + 1)]
+        assert rep0.stream_bytes == WORKERS * sub0.stream_bytes
+        assert all(rep0.offsets[cuts0[w]] == w * sub0.stream_bytes for w in range(WORKERS))
+        ws_rep0 = rep0.wire_workspace()
+        rx_delta = torch.cat([wire[:wl] for wire, wl in owner_msgs])
+        rx_wws = g.wire_workspace()
 
         def do_send():  # one message per owner, back to back, in one call
             g.wire_pack_ranges(o[0], ln[0], sc[0], cuts, wire=send_buf, wire_lens=send_lens, workspace=send_ws,
                                status=st[0:1])
 
-        def do_owner():
-            for w in range(WORKERS):
-                wire, wl = to_owner0[w]
-                sub0.wire_unpack(wire, out=inp0[w], out_lens=il0[w], scales=isc0[w], workspace=ws0, status=st[1:2])
+        def do_owner():  # the 8 workers' messages in one call
+            rep0.wire_unpack_ranges(rx_owner, cuts0, out=inp0.view(-1), out_lens=il0.view(-1), scales=isc0.view(-1),
+                                    workspace=ws_rep0, status=st[1:2])
             sub0.decompress_accumulate_many(inp0, il0.view(-1), isc0.view(-1), s, acc0, workspace=wsm,
                                             status=st[2:3], path_hint=hint_m)
             sub0.server_compress(acc0, WORKERS, e0, s, out=out0, out_lens=lens0, scales=sc0, workspace=wsc,
                                  status=st[3:4])
             sub0.wire_pack(out0, lens0, sc0, wire=wire0, wire_len=wl0, workspace=ws0, status=st[4:5])
 
-        def do_recv():
-            for k, (lo, hi, sub) in enumerate(shards):
-                wire, wl = owner_msgs[k]
-                so = g.offsets[lo]
-                sub.wire_unpack(wire, wire_bytes=wl, out=rx_out[so:so + sub.stream_bytes], out_lens=rx_lens[lo:hi],
-                                scales=rx_sc[lo:hi], workspace=wsw[k], status=st[5:6])
+        def do_recv():  # the 8 owners' messages in one call
+            g.wire_unpack_ranges(rx_delta, cuts, out=rx_out, out_lens=rx_lens, scales=rx_sc, workspace=rx_wws,
+                                 status=st[5:6])
             g.decompress(rx_out, rx_lens, rx_sc, s, y=rx_y, workspace=rx_ws, status=st[6:7], path_hint=rx_hint)
 
         def before(r):
@@ -713,7 +722,7 @@ class Bench:
         if int(st.abs().sum().item()) != 0:
             raise SystemExit(f"device status not ok in the exchange: {st.tolist()}")
         sent = int(send_lens.sum().item())
-        recv_owner = sum(int(wl.item()) for _, wl in to_owner0)
+        recv_owner = sum(wl for _, wl in to_owner0)
         recv_delta = sum(wl for _, wl in owner_msgs)
         return {
             "workers_and_owners": WORKERS,
@@ -724,11 +733,11 @@ class Bench:
             "bytes_received_model_delta": recv_delta,
             "dense_fp32_bytes_per_gpu": 4 * N,
             "how": ("GPU 0's work in an exchange of first-step payloads without the transport: send = its "
-                    "payload as 8 wire messages, one per owner, in one call; owner = unpack the 8 workers' messages for its range, one "
-                    "many-payload sum, the compress of the mean with its error buffer, one message; receive = "
-                    "unpack the 8 owners' messages into one payload of the group and decode the model delta "
-                    "with one grouped decompress.  Its own compress of the gradient set is the first-step "
-                    "record's compress_ms."),
+                    "payload as 8 wire messages, one per owner, in one call; owner = unpack the 8 workers' "
+                    "messages for its range in one call, one many-payload sum, the compress of the mean with its "
+                    "error buffer, one message; receive = unpack the 8 owners' messages in one call into one "
+                    "payload of the group and decode the model delta with one grouped decompress.  Its own "
+                    "compress of the gradient set is the first-step record's compress_ms."),
         }
 
     def accumulate_record(self, payload, oracle_payloads=None):

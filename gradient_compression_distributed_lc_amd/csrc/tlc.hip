@@ -2505,15 +2505,16 @@ struct WireCuts {
     uint32_t cut[65];     // cut[0] = 0 < cut[1] < ... < cut[n] = count
 };
 
-// One block over all tensors, kThreads * kWirePer per round (it also resets
-// *status, which only it raises): each stream's
+// One block over all tensors, range by range and kThreads * kWirePer per
+// round (it also resets *status, which only it raises): each stream's
 // length (pack: from in_lens; unpack: from its header), checked against its
 // slot (a longer one is TLC_ERR_CORRUPT and counts as empty); the headers
 // (pack) or out_lens and scales (unpack); the exclusive prefix of the lengths
 // (woff[t]: where stream t starts in the message body; woff[count]: their
 // sum) and of their 4 KiB chunks (cfirst[t]); ctrl[0] = chunks; the message
-// length (pack).  Unpack: a message shorter than its headers and streams is
-// TLC_ERR_CORRUPT, and then no chunk is copied.
+// length (pack).  Unpack: messages shorter than their headers and streams are
+// TLC_ERR_CORRUPT, and then no chunk is copied (the tensors whose headers were
+// not in them get length 0 and M = 0).
 template <bool kPack>
 __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cuts, const uint64_t* __restrict__ lens_in,
                                                         const float* __restrict__ m_in, uint8_t* __restrict__ hdr_out,
@@ -2529,63 +2530,92 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
     __syncthreads();
     uint64_t carry_b = 0;  // bytes of the rounds before
     uint32_t carry_c = 0;  // chunks of the rounds before
-    bool bad = false;
-    for (uint32_t r0 = 0; r0 < count; r0 += kThreads * kWirePer) {
-        const uint32_t t0 = r0 + threadIdx.x * kWirePer;
-        uint32_t L[kWirePer];
-        uint64_t my_b = 0;
-        uint32_t my_c = 0;
-#pragma unroll
-        for (int k = 0; k < (int)kWirePer; ++k) {
-            const uint32_t t = t0 + (uint32_t)k;
-            L[k] = 0;
-            if (t < count) {
-                const uint64_t cap = quartic_len(load_seg(g, t).n);
-                uint64_t l;
-                uint32_t mb;
-                if (kPack) {
-                    l = lens_in[t];
-                    mb = __float_as_uint(m_in[t]);
-                } else {
-                    const uint32_t* const h = reinterpret_cast<const uint32_t*>(hdr_in) + 2ull * t;
-                    l = h[0];
-                    mb = h[1];
-                }
-                if (l > cap) {
-                    bad = true;
-                    l = 0;
-                }
-                if (!kPack) {
-                    lens_out[t] = l;
-                    m_out[t] = __uint_as_float(mb);
-                }
-                L[k] = (uint32_t)l;
-                my_b += l;
-                my_c += (uint32_t)((l + kWireChunk - 1) / kWireChunk);
-            }
+    bool bad = false, cut_short = false;
+    uint32_t read_to = count;  // tensors below it had their headers read
+    // unpacking, range by range (message q's headers start at 8 cut[q] +
+    // P(cut[q]), known once the ranges before it are summed); packing, all
+    // tensors at once (where the headers go is worked out below); in rounds
+    const uint32_t nq = kPack ? 1u : cuts.n;
+    for (uint32_t q = 0; q < nq && !cut_short; ++q) {
+        const uint32_t a = kPack ? 0u : cuts.cut[q], z = kPack ? count : cuts.cut[q + 1];
+        const uint64_t hbase = 8ull * a + carry_b;  // this range's first header in the messages
+        if (!kPack && hbase + 8ull * (z - a) > wire_bytes) {  // block-uniform
+            cut_short = true;
+            read_to = a;
+            break;
         }
-        uint64_t tot_b;
-        uint32_t tot_c;
-        uint64_t b = carry_b + block_excl_scan(my_b, 0ull, SumCompose(), s_sm, &tot_b);
-        uint32_t c = carry_c + block_excl_sum(my_c, s_u, &tot_c);
+        for (uint32_t r0 = a; r0 < z; r0 += kThreads * kWirePer) {
+            const uint32_t t0 = r0 + threadIdx.x * kWirePer;
+            uint32_t L[kWirePer];
+            uint64_t my_b = 0;
+            uint32_t my_c = 0;
 #pragma unroll
-        for (int k = 0; k < (int)kWirePer; ++k) {
-            const uint32_t t = t0 + (uint32_t)k;
-            if (t < count) {
-                woff[t] = b;
-                cfirst[t] = c;
-                b += L[k];
-                c += (uint32_t)((L[k] + kWireChunk - 1) / kWireChunk);
+            for (int k = 0; k < (int)kWirePer; ++k) {
+                const uint32_t t = t0 + (uint32_t)k;
+                L[k] = 0;
+                if (t < z) {
+                    const uint64_t cap = quartic_len(load_seg(g, t).n);
+                    uint64_t l;
+                    uint32_t mb;
+                    if (kPack) {
+                        l = lens_in[t];
+                        mb = __float_as_uint(m_in[t]);
+                    } else {  // byte loads: a later message's headers need not be 4-byte aligned
+                        const uint8_t* const h = hdr_in + hbase + 8ull * (t - a);
+                        uint32_t lw = 0;
+                        mb = 0;
+#pragma unroll
+                        for (uint32_t b = 0; b < 4; ++b) {
+                            lw |= (uint32_t)h[b] << (8 * b);
+                            mb |= (uint32_t)h[4 + b] << (8 * b);
+                        }
+                        l = lw;
+                    }
+                    if (l > cap) {
+                        bad = true;
+                        l = 0;
+                    }
+                    if (!kPack) {
+                        lens_out[t] = l;
+                        m_out[t] = __uint_as_float(mb);
+                    }
+                    L[k] = (uint32_t)l;
+                    my_b += l;
+                    my_c += (uint32_t)((l + kWireChunk - 1) / kWireChunk);
+                }
             }
+            uint64_t tot_b;
+            uint32_t tot_c;
+            uint64_t b = carry_b + block_excl_scan(my_b, 0ull, SumCompose(), s_sm, &tot_b);
+            uint32_t c = carry_c + block_excl_sum(my_c, s_u, &tot_c);
+#pragma unroll
+            for (int k = 0; k < (int)kWirePer; ++k) {
+                const uint32_t t = t0 + (uint32_t)k;
+                if (t < z) {
+                    woff[t] = b;
+                    cfirst[t] = c;
+                    b += L[k];
+                    c += (uint32_t)((L[k] + kWireChunk - 1) / kWireChunk);
+                }
+            }
+            carry_b += tot_b;
+            carry_c += tot_c;
         }
-        carry_b += tot_b;
-        carry_c += tot_c;
     }
+    // the tensors of the ranges whose headers lie past the messages' end come
+    // out empty with M = 0 (nothing is copied then)
+    if (!kPack)
+        for (uint32_t t = read_to + threadIdx.x; t < count; t += kThreads) {
+            lens_out[t] = 0;
+            m_out[t] = 0.0f;
+            woff[t] = carry_b;
+            cfirst[t] = carry_c;
+        }
     if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
     if (threadIdx.x == 0) {
         woff[count] = carry_b;
         const uint64_t total = 8ull * count + carry_b;
-        const bool fits = kPack || total <= wire_bytes;
+        const bool fits = kPack || (!cut_short && total <= wire_bytes);
         if (!fits) raise_status(status, TLC_ERR_CORRUPT);
         ctrl[0] = fits ? carry_c : 0u;
     }
@@ -3591,6 +3621,19 @@ int tlc_wire_pack_ranges_group(const tlc_group_info* info, const void* d_table, 
     if (!cuts) return TLC_ERR_INVALID_ARG;
     return run_wire(true, p, info->stream_bytes, cuts, ranges, in, in_lens, scales, wire, wire_capacity, wire_lens,
                     nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, status,
+                    static_cast<hipStream_t>(stream));
+}
+
+int tlc_wire_unpack_ranges_group(const tlc_group_info* info, const void* d_table, const uint32_t* cuts,
+                                 uint32_t ranges, const uint8_t* wire, uint64_t wire_bytes, uint8_t* out,
+                                 uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
+                                 int* status, tlc_stream_t stream) {
+    Plan p;
+    int rc = group_plan_of(info, d_table, &p);
+    if (rc) return rc;
+    if (!cuts) return TLC_ERR_INVALID_ARG;
+    return run_wire(false, p, info->stream_bytes, cuts, ranges, nullptr, nullptr, nullptr, nullptr, wire_bytes,
+                    nullptr, wire, out, out_lens, scales, workspace, workspace_bytes, status,
                     static_cast<hipStream_t>(stream));
 }
 

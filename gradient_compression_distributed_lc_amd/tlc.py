@@ -84,6 +84,8 @@ _SIGS = {
     "tlc_wire_unpack_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U64, _P, _P, _P, _P, _SZ, _P, _P]),
     "tlc_wire_pack_ranges_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U32, _P, _P, _P, _P, _U64, _P, _P, _SZ,
                                         _P, _P]),
+    "tlc_wire_unpack_ranges_group": (_I, [ctypes.POINTER(GroupInfo), _P, _P, _U32, _P, _U64, _P, _P, _P, _P, _SZ,
+                                          _P, _P]),
     "tlc_planes_gather": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_planes_scatter": (_I, [_P, _P, _P, _P, _P, _U32, _U64, _P]),
     "tlc_gather_probe": (_I, [_P, _P, _U64, _P, _P]),
@@ -595,10 +597,7 @@ class Group:
         Returns (wire, wire_lens, status); message k is
         wire[sum(wire_lens[:k]) : sum(wire_lens[:k+1])]."""
         dev = self.device
-        cuts = [int(c) for c in cuts]
-        n = len(cuts) - 1
-        if n < 1 or n > 64 or cuts[0] != 0 or cuts[-1] != self.count or any(a >= b for a, b in zip(cuts, cuts[1:])):
-            raise ValueError("cuts must rise from 0 to the tensor count, 1 to 64 ranges")
+        c_cuts, n = self._cuts(cuts)
         wire = wire if wire is not None else torch.empty(self.wire_bound(), dtype=torch.uint8, device=dev)
         wire_lens = wire_lens if wire_lens is not None else torch.empty(n, dtype=torch.int64, device=dev)
         status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
@@ -609,7 +608,6 @@ class Group:
         _need(wire_lens, n, "wire_lens")
         _need(status, 1, "status")
         workspace = workspace if workspace is not None else self.wire_workspace()
-        c_cuts = (ctypes.c_uint32 * (n + 1))(*cuts)
         rc = lib().tlc_wire_pack_ranges_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
                                               c_cuts, n, _ptr(inp, torch.uint8, "in"),
                                               _ptr(in_lens, torch.int64, "in_lens"),
@@ -619,6 +617,38 @@ class Group:
                                               _ptr(status, torch.int32, "status"), _stream(stream))
         _check(rc, "tlc_wire_pack_ranges_group")
         return wire, wire_lens, status
+
+    def _cuts(self, cuts):
+        cuts = [int(c) for c in cuts]
+        n = len(cuts) - 1
+        if n < 1 or n > 64 or cuts[0] != 0 or cuts[-1] != self.count or any(a >= b for a, b in zip(cuts, cuts[1:])):
+            raise ValueError("cuts must rise from 0 to the tensor count, 1 to 64 ranges")
+        return (ctypes.c_uint32 * (n + 1))(*cuts), n
+
+    def wire_unpack_ranges(self, wire, cuts, *, wire_bytes=None, out=None, out_lens=None, scales=None,
+                           workspace=None, status=None, stream=None):
+        """tlc_wire_unpack_ranges_group: the messages of the ranges cuts[k] ..
+        cuts[k+1]-1, back to back in wire, into one payload of the group.
+        Returns (out, out_lens, scales, status)."""
+        dev = self.device
+        c_cuts, n = self._cuts(cuts)
+        out = out if out is not None else torch.empty(self.stream_bytes, dtype=torch.uint8, device=dev)
+        out_lens = out_lens if out_lens is not None else torch.empty(self.count, dtype=torch.int64, device=dev)
+        scales = scales if scales is not None else torch.empty(self.count, dtype=torch.float32, device=dev)
+        status = status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)
+        nb = wire.numel() if wire_bytes is None else int(wire_bytes)
+        if nb > wire.numel():
+            raise ValueError("wire_bytes exceeds the wire tensor")
+        self._need_out(out, out_lens, scales, status)
+        workspace = workspace if workspace is not None else self.wire_workspace()
+        rc = lib().tlc_wire_unpack_ranges_group(ctypes.byref(self.info), _ptr(self.d_table, torch.uint8, "table"),
+                                                c_cuts, n, _ptr(wire, torch.uint8, "wire"), nb,
+                                                _ptr(out, torch.uint8, "out"), _ptr(out_lens, torch.int64, "out_lens"),
+                                                _ptr(scales, torch.float32, "scales"),
+                                                _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                                _ptr(status, torch.int32, "status"), _stream(stream))
+        _check(rc, "tlc_wire_unpack_ranges_group")
+        return out, out_lens, scales, status
 
     def wire_unpack(self, wire, *, wire_bytes=None, out=None, out_lens=None, scales=None, workspace=None,
                     status=None, stream=None):

@@ -370,6 +370,19 @@ int tlc_wire_pack_ranges_group(const tlc_group_info* info, const void* d_table, 
                                const uint8_t* in, const uint64_t* in_lens, const float* scales, uint8_t* wire,
                                uint64_t wire_capacity, uint64_t* wire_lens, void* workspace, size_t workspace_bytes,
                                int* status, tlc_stream_t stream);
+/* tlc_wire_unpack_ranges_group: the inverse of tlc_wire_pack_ranges_group:
+ * wire[0 .. wire_bytes) holds the `ranges` messages of consecutive tensor
+ * ranges back to back (as a receiver gathers its owners' messages), and the
+ * whole group's payload is written to out, out_lens and scales.  Message k's
+ * headers start where message k-1 ends, so the ranges are read in order;
+ * one whose headers or streams run past wire_bytes sets TLC_ERR_CORRUPT
+ * (and no stream is copied), as do lengths above their tensors' ceil(n/5).
+ * cuts as for tlc_wire_pack_ranges_group; capacity, workspace and the other
+ * errors as tlc_wire_unpack_group. */
+int tlc_wire_unpack_ranges_group(const tlc_group_info* info, const void* d_table, const uint32_t* cuts,
+                                 uint32_t ranges, const uint8_t* wire, uint64_t wire_bytes, uint8_t* out,
+                                 uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
+                                 int* status, tlc_stream_t stream);
 int tlc_wire_unpack_group(const tlc_group_info* info, const void* d_table, const uint8_t* wire, uint64_t wire_bytes,
                           uint8_t* out, uint64_t* out_lens, float* scales, void* workspace, size_t workspace_bytes,
                           int* status, tlc_stream_t stream);

@@ -177,6 +177,13 @@ int main() {
         CHECK(tlc_wire_unpack_group(&g, fake, fb, 8 * g.count, fb, fl, nullptr, ws, ww, fs, nullptr) ==
               TLC_ERR_INVALID_ARG);
         CHECK(tlc_wire_bound(nullptr) == 0 && tlc_wire_workspace_size(nullptr) == 0);
+        const uint32_t cuts_ok[2] = {0, (uint32_t)g.count}, cuts_bad[2] = {0, (uint32_t)g.count + 1};
+        CHECK(tlc_wire_unpack_ranges_group(&g, fake, nullptr, 1, fb, 8 * g.count, fb, fl, ff, ws, ww, fs, nullptr) ==
+              TLC_ERR_INVALID_ARG);
+        CHECK(tlc_wire_unpack_ranges_group(&g, fake, cuts_bad, 1, fb, 8 * g.count, fb, fl, ff, ws, ww, fs,
+                                           nullptr) == TLC_ERR_INVALID_ARG);
+        CHECK(tlc_wire_unpack_ranges_group(&g, fake, cuts_ok, 1, fb, 8 * g.count - 1, fb, fl, ff, ws, ww, fs,
+                                           nullptr) == TLC_ERR_CAPACITY);
     }
     CHECK(tlc_planes_gather(ff, fl, ff, fl, nullptr, 3, 100, nullptr) == TLC_ERR_INVALID_ARG);
     CHECK(tlc_planes_scatter(ff, fl, ff, fl, fl, 65536, 100, nullptr) == TLC_ERR_INVALID_ARG);

@@ -388,6 +388,17 @@ def test_wire_host_checks():
     assert pr((C * 2)(0, 3), 0) == tlc.ERR_INVALID_ARG
     assert L.tlc_wire_pack_ranges_group(bi, fake, (C * 3)(0, 1, 3), 2, fake, fake, fake, fake, bound - 1, fake, ws,
                                         wsz, fake, None) == tlc.ERR_CAPACITY
+    ur = lambda cuts, n, nb=24: L.tlc_wire_unpack_ranges_group(bi, fake, cuts, n, fake, nb, fake, fake, fake, ws, wsz,
+                                                               fake, None)
+    assert ur(None, 1) == tlc.ERR_INVALID_ARG
+    assert ur((C * 3)(0, 3, 3), 2) == tlc.ERR_INVALID_ARG
+    assert ur((C * 3)(0, 2, 4), 2) == tlc.ERR_INVALID_ARG
+    assert ur((C * 66)(*range(66)), 65) == tlc.ERR_INVALID_ARG   # more than 64 ranges
+    assert ur((C * 3)(0, 1, 3), 2, 23) == tlc.ERR_CAPACITY      # below 8 * count
+    assert L.tlc_wire_unpack_ranges_group(bi, fake, (C * 3)(0, 1, 3), 2, odd, 24, fake, fake, fake, ws, wsz, fake,
+                                          None) == tlc.ERR_INVALID_ARG
+    assert L.tlc_wire_unpack_ranges_group(bi, fake, (C * 3)(0, 1, 3), 2, fake, 24, fake, fake, fake, ws, wsz - 1,
+                                          fake, None) == tlc.ERR_WORKSPACE
 
 
 def test_path_hint_word_is_checked_on_the_host():

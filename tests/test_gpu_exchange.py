@@ -6,11 +6,12 @@ all-gather shape of SparCML's "Proposed method"), for two rounds:
   each worker compresses its gradient set and packs one wire message per
   owner (the owner's tensors are a contiguous range, and their slots in the
   worker's payload are the owner's group layout shifted by a multiple of 16);
-  each owner unpacks its messages, adds the workers' payloads in worker
-  order with one many-payload call, compresses the mean with its own error
-  buffer (carried across rounds) and packs one message; every worker unpacks
-  the owners' messages into one payload of the whole group and decodes the
-  model delta with one grouped decompress.
+  each owner unpacks its messages (one at a time, or all in one call), adds
+  the workers' payloads in worker order with one many-payload call,
+  compresses the mean with its own error buffer (carried across rounds) and
+  packs one message; every worker unpacks
+  the owners' messages, back to back, with one range unpack into one payload
+  of the whole group and decodes the model delta with one grouped decompress.
 
 Every message must equal the oracle's message of the oracle's streams, and
 the decoded model delta the oracle's, bit for bit."""
@@ -68,16 +69,30 @@ def test_sharded_exchange_both_directions(workers, owners):
             inp = torch.empty((workers, sub.stream_bytes), dtype=torch.uint8, device="cuda:0")
             in_lens = torch.empty((workers, hi - lo), dtype=torch.int64, device="cuda:0")
             in_sc = torch.empty((workers, hi - lo), dtype=torch.float32, device="cuda:0")
+            msgs = []
             for w, (out, lens, scales) in enumerate(pays):
                 wire, wl, st = sub.wire_pack(out[so:so + sub.stream_bytes], lens[lo:hi], scales[lo:hi])
                 torch.cuda.synchronize()
                 assert int(st.item()) == 0
                 msg = wire[:int(wl.item())].cpu().numpy()
                 assert np.array_equal(msg, oracle.wire_pack(want[w][0][lo:hi], want[w][1][lo:hi])), (rnd, k, w)
-                _, _, _, st = sub.wire_unpack(wire, wire_bytes=int(wl.item()), out=inp[w], out_lens=in_lens[w],
-                                              scales=in_sc[w])
+                msgs.append(wire[:int(wl.item())])
+            if k % 2 == 0:
+                # the workers' messages back to back in one call: they are the
+                # range messages of the owner's tensors repeated once per
+                # worker, whose slots are the workers' payloads stacked
+                rep = tlc.Group(sizes[lo:hi] * workers)
+                assert rep.stream_bytes == workers * sub.stream_bytes
+                _, _, _, st = rep.wire_unpack_ranges(torch.cat(msgs), [w * (hi - lo) for w in range(workers + 1)],
+                                                     out=inp.view(-1), out_lens=in_lens.view(-1),
+                                                     scales=in_sc.view(-1))
                 torch.cuda.synchronize()
                 assert int(st.item()) == 0
+            else:  # one message at a time
+                for w, msg in enumerate(msgs):
+                    _, _, _, st = sub.wire_unpack(msg.clone(), out=inp[w], out_lens=in_lens[w], scales=in_sc[w])
+                    torch.cuda.synchronize()
+                    assert int(st.item()) == 0
             # the owner: workers' sum in worker order, then its compress of the mean
             acc = torch.zeros(sub.total, dtype=torch.float32, device="cuda:0")
             _, st = sub.decompress_accumulate_many(inp, in_lens.view(-1), in_sc.view(-1), s, acc)
@@ -106,18 +121,15 @@ def test_sharded_exchange_both_directions(workers, owners):
             assert np.array_equal(msg_o, oracle.wire_pack(st_o, M_o)), (rnd, k)
             assert np.array_equal(bits(err_o_d[k].cpu().numpy()), bits(err_o[k])), (rnd, k)
             deltas.append((wire_o, int(wl_o.item()), st_o, M_o))
-        # a worker receives every owner's message into one payload of the whole
-        # group (each at its range's slots) and decodes the model delta at once
-        rx_out = torch.empty(g.stream_bytes, dtype=torch.uint8, device="cuda:0")
-        rx_lens = torch.empty(count, dtype=torch.int64, device="cuda:0")
-        rx_sc = torch.empty(count, dtype=torch.float32, device="cuda:0")
+        # a worker receives every owner's message, back to back in owner order
+        # (as an all-gather leaves them), unpacks them in one call into one
+        # payload of the whole group and decodes the model delta at once
+        rx = torch.cat([wire_o[:wl_o] for wire_o, wl_o, _, _ in deltas])
+        rx_out, rx_lens, rx_sc, st = g.wire_unpack_ranges(rx, cuts)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
         want_delta = np.empty(g.total, np.float32)
         for (lo, hi, sub), (wire_o, wl_o, st_o, M_o) in zip(shards, deltas):
-            so = g.offsets[lo]
-            _, _, _, st = sub.wire_unpack(wire_o, wire_bytes=wl_o, out=rx_out[so:so + sub.stream_bytes],
-                                          out_lens=rx_lens[lo:hi], scales=rx_sc[lo:hi])
-            torch.cuda.synchronize()
-            assert int(st.item()) == 0
             off = g.elem_offsets[lo]
             for t in range(lo, hi):
                 n = sizes[t]

@@ -1,4 +1,5 @@
-"""GPU parity of the wire message (tlc_wire_pack_group / tlc_wire_unpack_group):
+"""GPU parity of the wire message (tlc_wire_pack_group / tlc_wire_unpack_group,
+and the range messages of tlc_wire_pack_ranges_group / tlc_wire_unpack_ranges_group):
 the message packed from a group's payload must equal, byte for byte, the
 oracle's wire message of the oracle's streams and scales; unpacking it into
 fresh buffers must give back every stream, length and M, so that it
@@ -201,6 +202,48 @@ def test_range_messages(ranges):
     assert int(st_d.item()) == 0
     want_y = np.concatenate([oracle.decompress(x, Ms[t], n, s) for t, (x, n) in enumerate(zip(streams, sizes))])
     assert np.array_equal(bits(y.cpu().numpy()), bits(want_y))
+    # all the messages back to back (and a few bytes after them) in one call
+    total = int(wl.sum())
+    buf = torch.full((total + 5,), 0xA5, dtype=torch.uint8, device=wire.device)
+    buf[:total] = wire[:total]
+    say(f"case wire ranges={ranges}: one unpack of the {ranges} messages")
+    o1, l1, s1, st1 = g.wire_unpack_ranges(buf, cuts, out=torch.full_like(out, 0x5A))
+    torch.cuda.synchronize()
+    assert int(st1.item()) == 0
+    assert np.array_equal(l1.cpu().numpy(), np.array([x.size for x in streams]))
+    assert np.array_equal(bits(s1.cpu().numpy()), bits(Ms))
+    ob, rb = o1.cpu().numpy(), rx.cpu().numpy()
+    for t, x in enumerate(streams):  # each slot: the stream, then zeros to its 16-byte word's end
+        o = g.offsets[t]
+        e = o + x.size + (-(o + x.size)) % 16
+        assert np.array_equal(ob[o:o + x.size], x) and not ob[o + x.size:e].any(), t
+        assert np.array_equal(ob[o:e], rb[o:e]), t
+    # cut short (inside the last message; inside the second message's
+    # headers; at the last message's start; after its headers, before its
+    # streams): corrupt, nothing copied, and the ranges whose headers were not
+    # all inside the bytes given come out empty
+    ends = [int(v) for v in np.cumsum(wl)]
+    starts = [0] + ends[:-1]
+    cases = {total - 1}
+    if ranges > 1:
+        cases |= {ends[0] + 4, starts[-1], starts[-1] + 8 * (cuts[-1] - cuts[-2])}
+    for nb in sorted(cases):
+        if nb < 8 * count:
+            continue  # refused on the host (below 8 bytes per tensor)
+        say(f"case wire ranges={ranges}: unpack of {nb} of {total} bytes")
+        o2, l2, s2, st2 = g.wire_unpack_ranges(buf, cuts, wire_bytes=nb, out=torch.full_like(out, 0x5A))
+        torch.cuda.synchronize()
+        assert int(st2.item()) == oracle.ERR_CORRUPT, nb
+        assert not (o2.cpu().numpy() != 0x5A).any(), nb
+        read_to = count
+        for q in range(ranges):
+            if starts[q] + 8 * (cuts[q + 1] - cuts[q]) > nb:
+                read_to = cuts[q]
+                break
+        l2h, s2h = l2.cpu().numpy(), s2.cpu().numpy()
+        assert np.array_equal(l2h[:read_to], [x.size for x in streams[:read_to]]), nb
+        assert not l2h[read_to:].any() and not s2h[read_to:].any(), nb
+        assert np.array_equal(bits(s2h[:read_to]), bits(Ms[:read_to])), nb
     # a length above its capacity in the last range is corrupt, sent empty, and moves no other message
     bad = lens.clone()
     bad[count - 1] = -(-sizes[-1] // 5) + 1
