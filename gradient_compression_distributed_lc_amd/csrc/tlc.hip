@@ -2525,8 +2525,10 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
                                                         uint64_t* __restrict__ wire_len, int* __restrict__ status) {
     __shared__ uint64_t s_sm[kWaves];
     __shared__ uint32_t s_u[kWaves];
+    __shared__ uint32_t s_cut[65];
     const uint32_t count = g.count;
     if (threadIdx.x == 0) *status = TLC_OK;  // the call's only kernel that reports
+    if (threadIdx.x <= cuts.n) s_cut[threadIdx.x] = cuts.cut[threadIdx.x];
     __syncthreads();
     uint64_t carry_b = 0;  // bytes of the rounds before
     uint32_t carry_c = 0;  // chunks of the rounds before
@@ -2560,6 +2562,10 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
                     if (kPack) {
                         l = lens_in[t];
                         mb = __float_as_uint(m_in[t]);
+                    } else if ((hbase & 3) == 0) {  // block-uniform: the range's headers 4-byte aligned
+                        const uint32_t* const h = reinterpret_cast<const uint32_t*>(hdr_in + hbase) + 2ull * (t - a);
+                        l = h[0];
+                        mb = h[1];
                     } else {  // byte loads: a later message's headers need not be 4-byte aligned
                         const uint8_t* const h = hdr_in + hbase + 8ull * (t - a);
                         uint32_t lw = 0;
@@ -2621,28 +2627,29 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
     }
     __syncthreads();  // every woff entry written above is visible to the block
     // where each stream goes in the messages, and (pack) the headers and each
-    // message's length; a thread's tensors are consecutive, so its range
-    // index only moves forward
-    uint32_t k = 0;
-    for (uint32_t r0 = 0; r0 < count; r0 += kThreads * kWirePer) {
-        const uint32_t t0 = r0 + threadIdx.x * kWirePer;
-        for (uint32_t j = 0; j < kWirePer && t0 + j < count; ++j) {
-            const uint32_t u = t0 + j;
-            while (k + 1 < cuts.n && cuts.cut[k + 1] <= u) ++k;
-            dbase[u] = 8ull * cuts.cut[k + 1] + woff[u];
-            if (kPack) {  // byte stores: a later range's headers need not be 4-byte aligned
-                uint8_t* const h = hdr_out + 8ull * u + woff[cuts.cut[k]];
-                const uint32_t l = (uint32_t)(woff[u + 1] - woff[u]), mb = __float_as_uint(m_in[u]);
+    // message's length: one tensor per thread and round, so that the rounds'
+    // loads are independent; its range by a binary search over the cuts
+    for (uint32_t u = threadIdx.x; u < count; u += kThreads) {
+        uint32_t lo = 0, hi = cuts.n;  // s_cut[lo] <= u < s_cut[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (s_cut[mid] <= u) lo = mid;
+            else hi = mid;
+        }
+        const uint64_t wu = woff[u];
+        dbase[u] = 8ull * s_cut[lo + 1] + wu;
+        if (kPack) {  // byte stores: a later range's headers need not be 4-byte aligned
+            uint8_t* const h = hdr_out + 8ull * u + woff[s_cut[lo]];
+            const uint32_t l = (uint32_t)(woff[u + 1] - wu), mb = __float_as_uint(m_in[u]);
 #pragma unroll
-                for (uint32_t b = 0; b < 4; ++b) {
-                    h[b] = (uint8_t)(l >> (8 * b));
-                    h[4 + b] = (uint8_t)(mb >> (8 * b));
-                }
+            for (uint32_t b = 0; b < 4; ++b) {
+                h[b] = (uint8_t)(l >> (8 * b));
+                h[4 + b] = (uint8_t)(mb >> (8 * b));
             }
         }
     }
     if (kPack && threadIdx.x < cuts.n) {
-        const uint32_t a = cuts.cut[threadIdx.x], b = cuts.cut[threadIdx.x + 1];
+        const uint32_t a = s_cut[threadIdx.x], b = s_cut[threadIdx.x + 1];
         wire_len[threadIdx.x] = 8ull * (b - a) + woff[b] - woff[a];
     }
 }
