@@ -721,6 +721,28 @@ class Bench:
         t = timed(torch, reps, body, before)
         if int(st.abs().sum().item()) != 0:
             raise SystemExit(f"device status not ok in the exchange: {st.tolist()}")
+        # the same share captured once in a HIP graph and replayed (every call
+        # has its buffers, workspaces and status words given, so nothing is
+        # allocated while capturing; the resets stay outside)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        before(0)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                do_send()
+                do_owner()
+                do_recv()
+        torch.cuda.synchronize()
+
+        def replay(r, mark):
+            graph.replay()
+
+        timed(torch, 3, replay, before)
+        tg = timed(torch, reps, replay, before)
+        if int(st.abs().sum().item()) != 0:
+            raise SystemExit(f"device status not ok in the exchange's graph replays: {st.tolist()}")
+        del graph
         sent = int(send_lens.sum().item())
         recv_owner = sum(wl for _, wl in to_owner0)
         recv_delta = sum(wl for _, wl in owner_msgs)
@@ -729,6 +751,7 @@ class Bench:
             "owner0_tensors": hi0 - lo0, "owner0_values": sub0.total,
             "send_ms": stats([v[0] for v in t]), "owner_ms": stats([v[1] for v in t]),
             "receive_ms": stats([v[2] for v in t]), "total_ms": stats([sum(v) for v in t]),
+            "graph_total_ms": stats([v[0] for v in tg]),
             "bytes_sent_by_gpu0": sent, "bytes_received_as_owner": recv_owner,
             "bytes_received_model_delta": recv_delta,
             "dense_fp32_bytes_per_gpu": 4 * N,
