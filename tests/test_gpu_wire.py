@@ -254,3 +254,67 @@ def test_range_messages(ranges):
     assert np.array_equal(l2[:-1], wl[:-1]) and int(l2[-1]) == int(wl[-1]) - streams[-1].size
     n_ok = int(wl[:-1].sum())
     assert torch.equal(w2[:n_ok], wire[:n_ok])
+
+
+def test_range_pack_and_unpack_replayed_from_one_graph():
+    """The send side's range pack and the receive side's range unpack captured
+    once in a HIP graph: every replay, after an eager compress of a new
+    payload into the same buffers, gives the messages and the unpacked payload
+    that the eager calls give for that payload (the unpack takes the whole
+    buffer's size, the messages lying back to back at its start)."""
+    import torch
+    from gradient_compression_distributed_lc_amd import tlc
+    rng = np.random.default_rng(77)
+    sizes = [int(v) for v in rng.integers(1, 40_000, 30)] + [5120, 3, 70_001]
+    g = tlc.Group(sizes)
+    cuts = [0, 4, 19, len(sizes)]
+    dev = "cuda:0"
+    out = torch.empty(g.stream_bytes, dtype=torch.uint8, device=dev)
+    lens = torch.empty(g.count, dtype=torch.int64, device=dev)
+    scales = torch.zeros(g.count, dtype=torch.float32, device=dev)
+    err = torch.zeros(g.total, dtype=torch.float32, device=dev)
+    ws_c = g.workspace()
+    st_c = torch.zeros(1, dtype=torch.int32, device=dev)
+    wire = torch.zeros(g.wire_bound(), dtype=torch.uint8, device=dev)
+    wl = torch.zeros(len(cuts) - 1, dtype=torch.int64, device=dev)
+    rx = torch.zeros(g.stream_bytes, dtype=torch.uint8, device=dev)
+    rl = torch.zeros(g.count, dtype=torch.int64, device=dev)
+    rs = torch.zeros(g.count, dtype=torch.float32, device=dev)
+    ws_p, ws_u = g.wire_workspace(), g.wire_workspace()
+    st_p = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_u = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def calls():
+        g.wire_pack_ranges(out, lens, scales, cuts, wire=wire, wire_lens=wl, workspace=ws_p, status=st_p)
+        g.wire_unpack_ranges(wire, cuts, out=rx, out_lens=rl, scales=rs, workspace=ws_u, status=st_u)
+
+    say("case wire calls in one graph: capture")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        x = (rng.standard_normal(g.total) * 10 ** -rep).astype(np.float32)
+        x[rng.random(g.total) < 0.4] = 0
+        g.compress(to_dev(x), err, 1.5, out=out, out_lens=lens, scales=scales, workspace=ws_c, status=st_c)
+        torch.cuda.synchronize()
+        assert int(st_c.item()) == 0
+        say(f"case wire calls in one graph: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(st_p.item()) == 0 and int(st_u.item()) == 0, rep
+        w_e, wl_e, st_e = g.wire_pack_ranges(out, lens, scales, cuts)
+        torch.cuda.synchronize()
+        assert int(st_e.item()) == 0
+        n = int(wl_e.sum().item())
+        assert torch.equal(wl, wl_e) and torch.equal(wire[:n], w_e[:n]), rep
+        assert torch.equal(rl, lens), rep
+        assert np.array_equal(bits(rs.cpu().numpy()), bits(scales.cpu().numpy())), rep
+        ob, rb, lh = out.cpu().numpy(), rx.cpu().numpy(), lens.cpu().numpy()
+        for t in range(g.count):
+            o = g.offsets[t]
+            assert np.array_equal(rb[o:o + int(lh[t])], ob[o:o + int(lh[t])]), (rep, t)
+    del graph
