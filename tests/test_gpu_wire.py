@@ -318,3 +318,32 @@ def test_range_pack_and_unpack_replayed_from_one_graph():
             o = g.offsets[t]
             assert np.array_equal(rb[o:o + int(lh[t])], ob[o:o + int(lh[t])]), (rep, t)
     del graph
+
+
+def test_range_messages_over_many_scan_rounds():
+    """Ranges of more than 4096 tensors (the scan's round), one of a single
+    tensor, and cuts at a round's edge: each message is the oracle's, and the
+    messages back to back unpack in one call into the group's payload."""
+    import torch
+    rng = np.random.default_rng(91)
+    sizes = [int(v) for v in rng.integers(1, 12, 9000)] + [6000, 1, 20_000]
+    count = len(sizes)
+    g, out, lens, scales, streams, Ms, s = group_payload(sizes, 91, s=1.3, dense_every=2)
+    cuts = [0, 4096, 4097, 8800, count - 1, count]
+    say(f"case wire ranges over scan rounds: {count} tensors, cuts {cuts}")
+    wire, wlens, st = g.wire_pack_ranges(out, lens, scales, cuts)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    total = int(wlens.sum().item())
+    want = np.concatenate([oracle.wire_pack(streams[a:b], Ms[a:b]) for a, b in zip(cuts, cuts[1:])])
+    got = wire[:total].cpu().numpy()
+    assert got.size == want.size and np.array_equal(got, want)
+    o1, l1, s1, st1 = g.wire_unpack_ranges(wire[:total].clone(), cuts, out=torch.full_like(out, 0x5A))
+    torch.cuda.synchronize()
+    assert int(st1.item()) == 0
+    assert np.array_equal(l1.cpu().numpy(), np.array([x.size for x in streams]))
+    assert np.array_equal(bits(s1.cpu().numpy()), bits(Ms))
+    ob = o1.cpu().numpy()
+    for t, x in enumerate(streams):
+        o = g.offsets[t]
+        assert np.array_equal(ob[o:o + x.size], x), t
