@@ -589,7 +589,7 @@ class Bench:
             parity = ok
         return xs, pay, oracle_first, parity
 
-    def exchange_record(self, payload, reps: int = 10):
+    def exchange_record(self, payload, reps: int = 10, marker=None):
         """One GPU's share of the sharded exchange at the BERT-large shape,
         8 workers that are also the 8 owners of contiguous tensor ranges
         (balanced by values), without the transport: GPU 0 packs its payload
@@ -718,9 +718,14 @@ class Bench:
             do_recv()
 
         timed(torch, 2, body, before)
+        if marker is not None:  # a profiler's part: the eager repetitions
+            torch.cuda.synchronize()
+            marker()
         t = timed(torch, reps, body, before)
         if int(st.abs().sum().item()) != 0:
             raise SystemExit(f"device status not ok in the exchange: {st.tolist()}")
+        if marker is not None:  # a profiler's part: the capture and the warm-up replays
+            marker()
         # the same share captured once in a HIP graph and replayed (every call
         # has its buffers, workspaces and status words given, so nothing is
         # allocated while capturing; the resets stay outside)
@@ -739,6 +744,9 @@ class Bench:
             graph.replay()
 
         timed(torch, 3, replay, before)
+        if marker is not None:  # a profiler's part: the graph replays
+            torch.cuda.synchronize()
+            marker()
         tg = timed(torch, reps, replay, before)
         if int(st.abs().sum().item()) != 0:
             raise SystemExit(f"device status not ok in the exchange's graph replays: {st.tolist()}")
@@ -864,7 +872,7 @@ class Bench:
         return rec
 
 
-PROFILE_PHASES = ("early", "steady", "receive", "resnet110", "calibrate")
+PROFILE_PHASES = ("early", "steady", "receive", "resnet110", "exchange", "calibrate")
 
 
 def profile_phase(args):
@@ -875,6 +883,8 @@ def profile_phase(args):
     BERT-large workers' payloads (150 steps each), then the many-payload call
     on each launch sequence and the single-payload accumulates, for the
     steady-state and for the first-step payloads; `resnet110` one-step repetitions of the ResNet-110 group;
+    `exchange` one GPU's share of the sharded exchange of the 8 first-step
+    payloads, as eager calls and as graph replays;
     `calibrate` the copy and gather yardsticks of the traffic counters.  A
     64 KiB tlc_copy_probe marks the start of every part that a summary
     reads (parts in the order listed in the printed line)."""
@@ -962,6 +972,15 @@ def profile_phase(args):
                     g.decompress_accumulate(o[w], ln[w], sc[w], s, acc, workspace=ws, status=st)
         torch.cuda.synchronize()
         out["status"] = int(st.item())
+    elif args.profile == "exchange":
+        bench = Bench(args)
+        xs, pay, _, _ = bench.bert_workers(0, False)
+        del xs
+        torch.cuda.empty_cache()
+        out["parts"] = ["eager calls", "graph capture and warm-up replays", "graph replays"]
+        rec = bench.exchange_record(pay["first"], reps=args.steps, marker=marker)
+        out["total_ms"] = rec["total_ms"]["median"]
+        out["graph_total_ms"] = rec["graph_total_ms"]["median"]
     elif args.profile == "resnet110":
         wl = workloads.get("resnet110")
         sizes, N, s = wl.sizes, wl.total, wl.s_values[0]

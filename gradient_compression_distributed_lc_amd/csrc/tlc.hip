@@ -2505,8 +2505,25 @@ struct WireCuts {
     uint32_t cut[65];     // cut[0] = 0 < cut[1] < ... < cut[n] = count
 };
 
-// One block over all tensors, range by range and kThreads * kWirePer per
-// round (it also resets *status, which only it raises): each stream's
+// A header at h: (L_t, the bits of M_t), each a little-endian uint32; with
+// dword loads where h is 4-byte aligned (a later range's headers need not be)
+__device__ __forceinline__ uint2 wire_hdr(const uint8_t* h) {
+    if ((reinterpret_cast<uintptr_t>(h) & 3) == 0) {
+        const uint32_t* const w = reinterpret_cast<const uint32_t*>(h);
+        return make_uint2(w[0], w[1]);
+    }
+    uint32_t l = 0, m = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b) {
+        l |= (uint32_t)h[b] << (8 * b);
+        m |= (uint32_t)h[4 + b] << (8 * b);
+    }
+    return make_uint2(l, m);
+}
+
+// One block over all tensors, kThreads * kWirePer per round, after (unpack)
+// one wavefront has located each range's headers in order (it also resets
+// *status, which only it raises): each stream's
 // length (pack: from in_lens; unpack: from its header), checked against its
 // slot (a longer one is TLC_ERR_CORRUPT and counts as empty); the headers
 // (pack) or out_lens and scales (unpack); the exclusive prefix of the lengths
@@ -2526,102 +2543,118 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
     __shared__ uint64_t s_sm[kWaves];
     __shared__ uint32_t s_u[kWaves];
     __shared__ uint32_t s_cut[65];
+    __shared__ uint64_t s_hbase[64];  // unpack: where range q's headers start
     const uint32_t count = g.count;
     if (threadIdx.x == 0) *status = TLC_OK;  // the call's only kernel that reports
     if (threadIdx.x <= cuts.n) s_cut[threadIdx.x] = cuts.cut[threadIdx.x];
     __syncthreads();
     uint64_t carry_b = 0;  // bytes of the rounds before
     uint32_t carry_c = 0;  // chunks of the rounds before
-    bool bad = false, cut_short = false;
-    uint32_t read_to = count;  // tensors below it had their headers read
-    // unpacking, range by range (message q's headers start at 8 cut[q] +
-    // P(cut[q]), known once the ranges before it are summed); packing, all
-    // tensors at once (where the headers go is worked out below); in rounds
-    const uint32_t nq = kPack ? 1u : cuts.n;
-    for (uint32_t q = 0; q < nq && !cut_short; ++q) {
-        const uint32_t a = kPack ? 0u : cuts.cut[q], z = kPack ? count : cuts.cut[q + 1];
-        const uint64_t hbase = 8ull * a + carry_b;  // this range's first header in the messages
-        if (!kPack && hbase + 8ull * (z - a) > wire_bytes) {  // block-uniform
-            cut_short = true;
-            read_to = a;
-            break;
-        }
-        for (uint32_t r0 = a; r0 < z; r0 += kThreads * kWirePer) {
-            const uint32_t t0 = r0 + threadIdx.x * kWirePer;
-            uint32_t L[kWirePer];
-            uint64_t my_b = 0;
-            uint32_t my_c = 0;
-#pragma unroll
-            for (int k = 0; k < (int)kWirePer; ++k) {
-                const uint32_t t = t0 + (uint32_t)k;
-                L[k] = 0;
-                if (t < z) {
-                    const uint64_t cap = quartic_len(load_seg(g, t).n);
-                    uint64_t l;
-                    uint32_t mb;
-                    if (kPack) {
-                        l = lens_in[t];
-                        mb = __float_as_uint(m_in[t]);
-                    } else if ((hbase & 3) == 0) {  // block-uniform: the range's headers 4-byte aligned
-                        const uint32_t* const h = reinterpret_cast<const uint32_t*>(hdr_in + hbase) + 2ull * (t - a);
-                        l = h[0];
-                        mb = h[1];
-                    } else {  // byte loads: a later message's headers need not be 4-byte aligned
-                        const uint8_t* const h = hdr_in + hbase + 8ull * (t - a);
-                        uint32_t lw = 0;
-                        mb = 0;
-#pragma unroll
-                        for (uint32_t b = 0; b < 4; ++b) {
-                            lw |= (uint32_t)h[b] << (8 * b);
-                            mb |= (uint32_t)h[4 + b] << (8 * b);
-                        }
-                        l = lw;
-                    }
-                    if (l > cap) {
-                        bad = true;
-                        l = 0;
-                    }
-                    if (!kPack) {
-                        lens_out[t] = l;
-                        m_out[t] = __uint_as_float(mb);
-                    }
-                    L[k] = (uint32_t)l;
-                    my_b += l;
-                    my_c += (uint32_t)((l + kWireChunk - 1) / kWireChunk);
+    bool bad = false;
+    uint32_t read_to = count;  // tensors below it have their headers inside the messages
+    if (!kPack) {
+        // where each range's headers start: message q's headers follow the
+        // bodies of the ranges before it, so one wavefront locates the ranges
+        // in order, summing each range's lengths (a length above its slot
+        // counts as 0, as below); a range whose headers run past wire_bytes
+        // ends the walk
+        __shared__ uint32_t s_readto;
+        if (threadIdx.x < 64) {
+            uint64_t hb = 0;  // the lengths of the ranges before
+            uint32_t rt = count;
+            for (uint32_t q = 0; q < cuts.n; ++q) {
+                const uint32_t a = s_cut[q], z = s_cut[q + 1];
+                const uint64_t base = 8ull * a + hb;
+                if (base + 8ull * (z - a) > wire_bytes) {  // wave-uniform
+                    rt = a;
+                    break;
                 }
-            }
-            uint64_t tot_b;
-            uint32_t tot_c;
-            uint64_t b = carry_b + block_excl_scan(my_b, 0ull, SumCompose(), s_sm, &tot_b);
-            uint32_t c = carry_c + block_excl_sum(my_c, s_u, &tot_c);
-#pragma unroll
-            for (int k = 0; k < (int)kWirePer; ++k) {
-                const uint32_t t = t0 + (uint32_t)k;
-                if (t < z) {
-                    woff[t] = b;
-                    cfirst[t] = c;
-                    b += L[k];
-                    c += (uint32_t)((L[k] + kWireChunk - 1) / kWireChunk);
+                uint64_t sum = 0;
+                for (uint32_t t = a + threadIdx.x; t < z; t += 64) {
+                    const uint64_t l = wire_hdr(hdr_in + base + 8ull * (t - a)).x;
+                    if (l <= quartic_len(load_seg(g, t).n)) sum += l;
                 }
+                for (int d = 32; d >= 1; d >>= 1) {
+                    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)sum, d, 64);
+                    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(sum >> 32), d, 64);
+                    sum += (uint64_t)hi << 32 | lo;
+                }
+                if (threadIdx.x == 0) s_hbase[q] = base;
+                hb += sum;
             }
-            carry_b += tot_b;
-            carry_c += tot_c;
+            if (threadIdx.x == 0) s_readto = rt;
         }
+        __syncthreads();
+        read_to = s_readto;
     }
-    // the tensors of the ranges whose headers lie past the messages' end come
-    // out empty with M = 0 (nothing is copied then)
-    if (!kPack)
-        for (uint32_t t = read_to + threadIdx.x; t < count; t += kThreads) {
-            lens_out[t] = 0;
-            m_out[t] = 0.0f;
-            woff[t] = carry_b;
-            cfirst[t] = carry_c;
+    // all tensors in rounds; a thread's tensors are consecutive, so its range
+    // index only moves forward
+    for (uint32_t r0 = 0; r0 < count; r0 += kThreads * kWirePer) {
+        const uint32_t t0 = r0 + threadIdx.x * kWirePer;
+        uint32_t L[kWirePer];
+        uint64_t my_b = 0;
+        uint32_t my_c = 0;
+        uint32_t k = 0;
+        if (!kPack && t0 < count) {
+            uint32_t hi = cuts.n;  // s_cut[k] <= t0 < s_cut[hi]
+            while (hi - k > 1) {
+                const uint32_t mid = (k + hi) / 2;
+                if (s_cut[mid] <= t0) k = mid;
+                else hi = mid;
+            }
         }
+#pragma unroll
+        for (int j = 0; j < (int)kWirePer; ++j) {
+            const uint32_t t = t0 + (uint32_t)j;
+            L[j] = 0;
+            if (t < count) {
+                const uint64_t cap = quartic_len(load_seg(g, t).n);
+                uint64_t l = 0;
+                uint32_t mb = 0;
+                if (kPack) {
+                    l = lens_in[t];
+                    mb = __float_as_uint(m_in[t]);
+                } else if (t < read_to) {
+                    while (s_cut[k + 1] <= t) ++k;
+                    const uint2 h = wire_hdr(hdr_in + s_hbase[k] + 8ull * (t - s_cut[k]));
+                    l = h.x;
+                    mb = h.y;
+                }
+                if (l > cap) {
+                    bad = true;
+                    l = 0;
+                }
+                if (!kPack) {
+                    lens_out[t] = l;
+                    m_out[t] = __uint_as_float(mb);
+                }
+                L[j] = (uint32_t)l;
+                my_b += l;
+                my_c += (uint32_t)((l + kWireChunk - 1) / kWireChunk);
+            }
+        }
+        uint64_t tot_b;
+        uint32_t tot_c;
+        uint64_t b = carry_b + block_excl_scan(my_b, 0ull, SumCompose(), s_sm, &tot_b);
+        uint32_t c = carry_c + block_excl_sum(my_c, s_u, &tot_c);
+#pragma unroll
+        for (int j = 0; j < (int)kWirePer; ++j) {
+            const uint32_t t = t0 + (uint32_t)j;
+            if (t < count) {
+                woff[t] = b;
+                cfirst[t] = c;
+                b += L[j];
+                c += (uint32_t)((L[j] + kWireChunk - 1) / kWireChunk);
+            }
+        }
+        carry_b += tot_b;
+        carry_c += tot_c;
+    }
     if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(status, TLC_ERR_CORRUPT);
     if (threadIdx.x == 0) {
         woff[count] = carry_b;
         const uint64_t total = 8ull * count + carry_b;
-        const bool fits = kPack || (!cut_short && total <= wire_bytes);
+        const bool fits = kPack || (read_to == count && total <= wire_bytes);
         if (!fits) raise_status(status, TLC_ERR_CORRUPT);
         ctrl[0] = fits ? carry_c : 0u;
     }
