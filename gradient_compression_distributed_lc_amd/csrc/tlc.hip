@@ -2569,6 +2569,8 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
                     rt = a;
                     break;
                 }
+                if (threadIdx.x == 0) s_hbase[q] = base;
+                if (q + 1 == cuts.n) break;  // no range after it: its lengths are not needed here
                 uint64_t sum = 0;
                 for (uint32_t t = a + threadIdx.x; t < z; t += 64) {
                     const uint64_t l = wire_hdr(hdr_in + base + 8ull * (t - a)).x;
@@ -2579,7 +2581,6 @@ __global__ __launch_bounds__(kThreads) void k_wire_scan(GroupView g, WireCuts cu
                     const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(sum >> 32), d, 64);
                     sum += (uint64_t)hi << 32 | lo;
                 }
-                if (threadIdx.x == 0) s_hbase[q] = base;
                 hb += sum;
             }
             if (threadIdx.x == 0) s_readto = rt;
